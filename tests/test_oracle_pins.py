@@ -1,0 +1,366 @@
+"""Pins that tie the fp64 oracle to facts fixed outside itself.
+
+Each check is either a closed form, an independent library routine, an exact
+algebraic identity, a brute-force loop on tiny inputs, or a number the pages
+print (tests/golden/page_facts.json).  The mutation tests at the bottom plant
+plausible mistakes in the oracle and require that some pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import make_inputs, quantize_e4m3_blocks
+from oracle import mla_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def small_inputs(lens, s_q=1, layout="paged_shuffled", cache="bf16", seed=3, q_std=1.0):
+    return make_inputs(dict(batch=len(lens), s_q=s_q, lens=("explicit", list(lens)), layout=layout,
+                            q_std=q_std, cache=cache, num_splits=None, unabsorbed=False, name="small"),
+                       seed=seed)
+
+
+# ----------------------------------------------------------------- page facts
+def test_page_facts_golden():
+    facts = json.load(open(os.path.join(HERE, "golden", "page_facts.json")))
+    assert O.N_H == facts["n_heads"]["value"]
+    assert O.D_C == facts["d_c"]["value"]
+    assert O.D_H_R == facts["d_h_rope"]["value"]
+    assert O.D_H == facts["d_h"]["value"]
+    assert O.FP8_BLOCK == facts["fp8_block"]["value"]
+    mla = O.mla_cache_values_per_token()
+    mha = O.mha_cache_values_per_token()
+    assert mla == facts["mla_values_per_token_layer"]["value"]
+    assert mha == facts["mha_values_per_token_layer"]["value"]
+    assert mha / mla >= facts["compression_factor_at_least"]["value"]
+    assert abs(np.nanmax(O.e4m3_decode(np.arange(256))) - facts["e4m3_max_approx"]["value"]) < 1e-9
+    kb = mla * 2 / 1024.0   # bf16 row
+    assert abs(kb - facts["kv_bytes_per_token_layer_approx_kb"]["value"]) < 0.1
+
+
+def test_scale_reading():
+    # 1/sqrt(d_h + d_h^R) with d_h = 128 and d_h^R = 64
+    assert O.default_scale() == pytest.approx(1.0 / math.sqrt(192.0), rel=0, abs=0)
+
+
+# ------------------------------------------------------ a: uniform scores
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_uniform_scores_give_latent_mean(s_q):
+    inp = small_inputs([1, 7, 64, 65, 200], s_q=s_q)
+    inp.q_absorbed.zero_()
+    inp.q_rope.zero_()
+    out, lse = O.mla_decode(inp)
+    for b in range(inp.batch):
+        for s in range(s_q):
+            n = int(inp.seq_lens[b]) - s_q + s + 1
+            if n <= 0:
+                assert np.all(out[b, s] == 0) and np.all(np.isneginf(lse[b, s]))
+                continue
+            rows = O.sequence_rows(inp, b, n)
+            mean = rows[:, :512].mean(axis=0)
+            np.testing.assert_allclose(out[b, s], np.broadcast_to(mean, (128, 512)), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, s], math.log(n), rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------- b: single row
+def test_single_row_returns_that_latent():
+    inp = small_inputs([1, 1, 2], s_q=1)
+    out, lse = O.mla_decode(inp)
+    for b in range(2):
+        row = O.sequence_rows(inp, b, 1)[0]
+        q = np.concatenate([inp.q_absorbed[b, 0].double().numpy(), inp.q_rope[b, 0].double().numpy()], axis=1)
+        np.testing.assert_array_equal(out[b, 0], np.broadcast_to(row[:512], (128, 512)))
+        np.testing.assert_allclose(lse[b, 0], inp.scale * (q @ row), rtol=1e-15, atol=1e-12)
+    # MTP token 0 at seq_len 2 sees exactly one row
+    mtp = small_inputs([2, 2], s_q=2)
+    out2, _ = O.mla_decode(mtp)
+    for b in range(2):
+        row = O.sequence_rows(mtp, b, 1)[0]
+        np.testing.assert_array_equal(out2[b, 0], np.broadcast_to(row[:512], (128, 512)))
+
+
+# ------------------------------------------------------ c: associativity
+def test_absorbed_equals_unabsorbed_per_head():
+    inp = make_inputs("single_b1_l128", seed=0)
+    q_c = inp.extra["q_c"][0, 0].numpy()
+    W_UK = inp.extra["W_UK"].numpy()
+    W_UV = inp.extra["W_UV"].numpy()
+    n = int(inp.seq_lens[0])
+    rows = O.sequence_rows(inp, 0, n)
+    q_r = inp.q_rope[0, 0].double().numpy()
+    q_abs = O.absorb_query(q_c, W_UK)                      # fp64, no bf16 rounding
+    out_lat, lse_abs = O.attend_latent(np.concatenate([q_abs, q_r], axis=1), rows, inp.scale)
+    o_abs = O.apply_output_absorption(out_lat, W_UV)
+    o_ref, lse_ref, z_ref = O.unabsorbed_attention(q_c, q_r, rows[:, :512], rows[:, 512:], W_UK, W_UV, inp.scale)
+    assert o_abs.shape == (128, 128)
+    np.testing.assert_allclose(o_abs, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse_abs, lse_ref, rtol=1e-13, atol=1e-12)
+    z_abs = inp.scale * (np.concatenate([q_abs, q_r], axis=1) @ rows.T)
+    np.testing.assert_allclose(z_abs, z_ref, rtol=1e-11, atol=1e-11)
+    # the scores are not trivially equal: they spread over several units
+    assert z_ref.std() > 0.3
+
+
+# ---------------------------------------------------- d: cache-size invariant
+def test_cache_row_layout_invariant():
+    inp = small_inputs([100, 64])
+    assert inp.cache.shape[-1] == O.D_ROW == 576
+    assert inp.cache.element_size() * O.D_ROW == 1152
+    assert O.mha_cache_values_per_token() / O.mla_cache_values_per_token() == pytest.approx(32768 / 576)
+    fp8 = small_inputs([100], cache="fp8_e4m3")
+    per_row = (fp8.cache.shape[-1] * 1 + fp8.cache_scales.shape[-1] * 4 + fp8.cache_rope.shape[-1] * 2)
+    assert per_row == 656
+
+
+# ------------------------------------------------------ e: torch SDPA (fp64)
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_oracle_matches_torch_sdpa(s_q):
+    inp = small_inputs([3, 64, 130, 257], s_q=s_q, q_std=1.5)
+    out, lse = O.mla_decode(inp)
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        rows = torch.from_numpy(O.sequence_rows(inp, b, L))            # [L, 576]
+        q = torch.cat([inp.q_absorbed[b].double(), inp.q_rope[b].double()], dim=-1)  # [S, H, 576]
+        qh = q.permute(1, 0, 2).unsqueeze(0)                          # [1, H, S, 576]
+        k = rows.unsqueeze(0).unsqueeze(0).expand(1, 128, L, 576)
+        v = rows[:, :512].unsqueeze(0).unsqueeze(0).expand(1, 128, L, 512)
+        pos = torch.arange(L)
+        mask = torch.stack([pos < (L - s_q + s + 1) for s in range(s_q)])  # [S, L]
+        ref = torch.nn.functional.scaled_dot_product_attention(qh, k, v, attn_mask=mask, scale=inp.scale)
+        scores = inp.scale * torch.matmul(qh, k.transpose(-1, -2)).masked_fill(~mask, float("-inf"))
+        ref_lse = torch.logsumexp(scores, dim=-1)                     # [1, H, S]
+        np.testing.assert_allclose(out[b], ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], ref_lse[0].permute(1, 0).numpy(), rtol=1e-13, atol=1e-12)
+
+
+# -------------------------------------------------- f: split / merge identity
+def test_split_merge_identity():
+    rng = np.random.default_rng(7)
+    inp = small_inputs([500])
+    rows = O.sequence_rows(inp, 0, 500)
+    q = np.concatenate([inp.q_absorbed[0, 0].double().numpy(), inp.q_rope[0, 0].double().numpy()], axis=1)
+    full_out, full_lse = O.attend_latent(q, rows, inp.scale)
+    for trial in range(5):
+        k = int(rng.integers(1, 9))
+        cuts = np.sort(rng.integers(0, 501, size=k - 1))
+        bounds = [0, *cuts.tolist(), 500]                  # may contain empty ranges
+        parts = [O.partial_over_range(q, rows, bounds[i], bounds[i + 1], inp.scale) for i in range(k)]
+        outs = np.stack([p[0] for p in parts])
+        lses = np.stack([p[1] for p in parts])
+        m_out, m_lse = O.merge_partials(outs, lses)
+        np.testing.assert_allclose(m_out, full_out, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(m_lse, full_lse, rtol=1e-14, atol=1e-13)
+    # all splits empty -> out 0, lse -inf
+    e_out, e_lse = O.merge_partials(np.zeros((3, 128, 512)), np.full((3, 128), -np.inf))
+    assert np.all(e_out == 0) and np.all(np.isneginf(e_lse))
+
+
+# --------------------------------------------------- g: brute force, tiny
+def _brute(q_abs, q_r, rows, scale):
+    """Pure-Python loops over heads, rows and dims."""
+    H, n = len(q_abs), len(rows)
+    outs, lses = [], []
+    for h in range(H):
+        z = []
+        for j in range(n):
+            acc = 0.0
+            for k in range(512):
+                acc += q_abs[h][k] * rows[j][k]
+            for k in range(64):
+                acc += q_r[h][k] * rows[j][512 + k]
+            z.append(scale * acc)
+        m = max(z)
+        e = [math.exp(v - m) for v in z]
+        s = sum(e)
+        lses.append(m + math.log(s))
+        outs.append([sum(e[j] / s * rows[j][k] for j in range(n)) for k in range(512)])
+    return np.array(outs), np.array(lses)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_brute_force_tiny(s_q):
+    inp = small_inputs([3, 8, 5], s_q=s_q, seed=11)
+    heads = [0, 5, 77, 127]
+    for b in range(inp.batch):
+        for s in range(s_q):
+            out, lse = O.decode_one(inp, b, s, heads=heads)
+            n = int(inp.seq_lens[b]) - s_q + s + 1
+            # gather rows through the table by hand, slot by slot
+            rows = []
+            for j in range(n):
+                page = int(inp.block_table[b, j // 64])
+                rows.append(inp.cache[page, j % 64].double().tolist())
+            qa = inp.q_absorbed[b, s].double()[heads].tolist()
+            qr = inp.q_rope[b, s].double()[heads].tolist()
+            b_out, b_lse = _brute(qa, qr, rows, inp.scale)
+            np.testing.assert_allclose(out, b_out, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse, b_lse, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------ h: paged == contiguous, row permutation
+def test_paged_equals_contiguous_and_row_permutation():
+    paged = small_inputs([70, 130, 64], layout="paged_shuffled", seed=5)
+    out_p, lse_p = O.mla_decode(paged)
+    # rebuild the same logical rows as a contiguous [B, max_blocks*64, 576] cache
+    cont = small_inputs([70, 130, 64], layout="contiguous", seed=5)
+    B, mb = paged.batch, paged.max_blocks
+    new = torch.empty((B * mb, 64, 576), dtype=torch.bfloat16)
+    for b in range(B):
+        for u in range(mb):
+            new[b * mb + u] = paged.cache[int(paged.block_table[b, u])]
+    cont.cache = new
+    cont.q_absorbed = paged.q_absorbed.clone()
+    cont.q_rope = paged.q_rope.clone()
+    out_c, lse_c = O.mla_decode(cont)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    # permuting rows inside a sequence (S_q = 1) leaves the result unchanged
+    b = 1
+    L = int(paged.seq_lens[b])
+    rows = O.sequence_rows(paged, b, L)
+    perm = np.random.default_rng(0).permutation(L)
+    q = np.concatenate([paged.q_absorbed[b, 0].double().numpy(), paged.q_rope[b, 0].double().numpy()], axis=1)
+    o1, l1 = O.attend_latent(q, rows, paged.scale)
+    o2, l2 = O.attend_latent(q, rows[perm], paged.scale)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14, atol=1e-13)
+
+
+# ---------------------------------------------------- i: MTP consistency
+def test_mtp_tokens_match_single_token_decode():
+    mtp = small_inputs([5, 100, 129], s_q=2, seed=9)
+    out2, lse2 = O.mla_decode(mtp)
+    for s in range(2):
+        single = small_inputs([5, 100, 129], s_q=1, seed=9)
+        single.cache = mtp.cache
+        single.block_table = mtp.block_table
+        single.seq_lens = mtp.seq_lens - (1 - s)
+        single.q_absorbed = mtp.q_absorbed[:, s:s + 1].clone()
+        single.q_rope = mtp.q_rope[:, s:s + 1].clone()
+        out1, lse1 = O.mla_decode(single)
+        np.testing.assert_array_equal(out2[:, s], out1[:, 0])
+        np.testing.assert_array_equal(lse2[:, s], lse1[:, 0])
+
+
+# --------------------------------------------------------------- j: fp8
+def test_e4m3_decoder_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(mine) & np.isnan(ref)
+    assert np.all((mine == ref) | both_nan)
+    assert np.sum(np.isnan(mine)) == 2          # 0x7f and 0xff
+    finite = mine[np.isfinite(mine)]
+    assert finite.max() == 448.0 and finite.min() == -448.0
+    # every finite e4m3 value is exact in bf16
+    as_bf16 = torch.from_numpy(finite).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(as_bf16, finite)
+
+
+def test_quantizer_error_saturation_zero_block():
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn((64, 512), generator=g)
+    x[3, :128] = 0.0          # a zero block
+    x[5, 200] = 1e6           # an outlier affects only its own block
+    codes, scales = quantize_e4m3_blocks(x)
+    deq = O.dequantize_latent(codes.numpy(), scales.numpy())
+    xs = x.double().numpy()
+    assert scales[3, 0] == 1.0 and np.all(deq[3, :128] == 0)
+    # relative error at most half an ulp of a 3-bit mantissa (2^-4) in the normal range
+    s_rep = np.repeat(scales.double().numpy(), 128, axis=1)
+    normal = np.abs(xs / s_rep) >= 2.0 ** -6
+    rel = np.abs(deq - xs)[normal] / np.abs(xs)[normal]
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+    # subnormal range: absolute error at most half the smallest step (2^-10) times the scale
+    sub = ~normal
+    assert np.all(np.abs(deq - xs)[sub] <= 2.0 ** -10 * s_rep[sub] + 1e-12)
+    # the block max maps to exactly +-448
+    assert np.isclose(np.abs(O.e4m3_decode(codes[5, 128:256].numpy())).max(), 448.0)
+    # the outlier did not disturb the other blocks of its row
+    np.testing.assert_array_equal(scales[5, [0, 2, 3]], (x[5].reshape(4, 128).abs().amax(1) / 448)[[0, 2, 3]])
+
+
+def test_fp8_oracle_uses_dequantized_rows():
+    inp = small_inputs([70], cache="fp8_e4m3", seed=2)
+    rows = O.sequence_rows(inp, 0, 70)
+    codes = inp.cache[0].numpy()
+    sc = inp.cache_scales[0].numpy()
+    for j in (0, 17, 63):
+        for blk in range(4):
+            for k in (0, 31, 127):
+                c = blk * 128 + k
+                assert rows[j, c] == O.e4m3_decode(codes[j, c]) * sc[j, blk]
+    pages = [int(inp.block_table[0, u]) for u in range(2)]
+    rope = np.concatenate([inp.cache_rope[p].double().numpy() for p in pages])[:70]
+    np.testing.assert_array_equal(rows[:, 512:], rope)
+
+
+# ------------------------------------------------ mutation sensitivity
+def _mutant_checks():
+    """Run a subset of pins; returns the names of those that failed."""
+    failed = []
+    for name, fn in [("sdpa", lambda: test_oracle_matches_torch_sdpa(2)),
+                     ("uniform", lambda: test_uniform_scores_give_latent_mean(2)),
+                     ("assoc", test_absorbed_equals_unabsorbed_per_head),
+                     ("split", test_split_merge_identity),
+                     ("mtp", test_mtp_tokens_match_single_token_decode),
+                     ("e4m3", test_e4m3_decoder_matches_torch_all_codes),
+                     ("fp8rows", test_fp8_oracle_uses_dequantized_rows)]:
+        try:
+            fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def _bad_attend_scale(q_cat, rows, scale):
+    return _orig_attend(q_cat, rows, 1.0 / math.sqrt(576.0))
+
+
+def _bad_attend_no_rope(q_cat, rows, scale):
+    q2 = q_cat.copy()
+    q2[:, 512:] = 0
+    return _orig_attend(q2, rows, scale)
+
+
+def _bad_attend_v_rope(q_cat, rows, scale):
+    out, lse = _orig_attend(q_cat, rows, scale)
+    shifted = np.concatenate([rows[:, 64:576], rows[:, :64]], axis=1)
+    out2, _ = _orig_attend(q_cat, shifted, scale)
+    return out2 if rows.shape[0] > 0 else out, lse
+
+
+def _bad_visible(seq_len, s_q, s):
+    return max(0, int(seq_len) - int(s_q) + int(s))
+
+
+def _bad_merge(outs, lses):
+    outs = np.asarray(outs)
+    return outs.mean(axis=0), np.asarray(lses).max(axis=0)
+
+
+def _bad_e4m3(codes):
+    return _orig_e4m3(codes) * 2.0
+
+
+_orig_attend = O.attend_latent
+_orig_e4m3 = O.e4m3_decode
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("attend_latent", _bad_attend_scale),
+    ("attend_latent", _bad_attend_no_rope),
+    ("attend_latent", _bad_attend_v_rope),
+    ("visible_rows", _bad_visible),
+    ("merge_partials", _bad_merge),
+    ("e4m3_decode", _bad_e4m3),
+])
+def test_pins_catch_planted_oracle_mistakes(monkeypatch, target, mutant):
+    monkeypatch.setattr(O, target, mutant)
+    failed = _mutant_checks()
+    assert failed, f"no pin caught the planted mistake in {target} ({mutant.__name__})"
