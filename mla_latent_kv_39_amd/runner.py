@@ -1,0 +1,34 @@
+"""One decode step on device-resident tensors: mla_decode then mla_combine.
+
+Holds the output and partial buffers for a (batch, s_q, num_splits) shape so
+that repeated steps allocate nothing.
+"""
+from __future__ import annotations
+
+import torch
+
+from .binding import LATENT_DIM, NUM_HEADS, mla_combine, mla_decode
+
+
+class DecodeWorkspace:
+    """Outputs (out_latent, lse) and split partials for one batch shape."""
+
+    def __init__(self, batch: int, s_q: int, num_splits: int, device="cuda"):
+        self.batch, self.s_q, self.num_splits = int(batch), int(s_q), int(num_splits)
+        f32 = torch.float32
+        self.out = torch.empty((batch, s_q, NUM_HEADS, LATENT_DIM), dtype=f32, device=device)
+        self.lse = torch.empty((batch, s_q, NUM_HEADS), dtype=f32, device=device)
+        if num_splits > 1:
+            self.partial_out = torch.empty((num_splits, 2, s_q, NUM_HEADS, LATENT_DIM), dtype=f32, device=device)
+            self.partial_lse = torch.empty((num_splits, 2, s_q, NUM_HEADS), dtype=f32, device=device)
+        else:
+            self.partial_out = self.partial_lse = None
+
+
+def decode_step(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws: DecodeWorkspace,
+                max_blocks_per_seq=None, stream=None):
+    """Enqueue decode + combine; returns (out_latent, lse) views of the workspace."""
+    mla_decode(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws.num_splits, ws.partial_out,
+               ws.partial_lse, ws.out, ws.lse, max_blocks_per_seq=max_blocks_per_seq, stream=stream)
+    mla_combine(ws.partial_out, ws.partial_lse, seq_lens, ws.num_splits, ws.out, ws.lse, stream=stream)
+    return ws.out, ws.lse

@@ -1,0 +1,152 @@
+"""Parity of the HIP decode path (through the C ABI) with the fp64 oracle.
+
+Small cases compare every output element; they span several 64-row pages,
+ragged tails, both query-token counts, both cache layouts and many partition
+counts, so that sequences are cut across partitions in every way the
+partition map allows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import make_inputs
+from oracle import mla_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(lens, s_q=1, layout="paged_shuffled", seed=0, q_std=1.0, cache="bf16"):
+    return make_inputs(dict(batch=len(lens), s_q=s_q, lens=("explicit", list(lens)), layout=layout, q_std=q_std,
+                            cache=cache, num_splits=None, unabsorbed=False, name="small"), seed=seed)
+
+
+def _run_and_check(inp, num_splits, what, out_tol=None):
+    from gpu_helpers import DeviceInputs, compare, OUT_TOL
+    print(f"[gpu] {what}: B={inp.batch} S_q={inp.s_q} lens={inp.seq_lens.tolist()[:8]} splits={num_splits}",
+          flush=True)
+    dev = DeviceInputs(inp)
+    out, lse = dev.run(num_splits)
+    ref_out, ref_lse = O.mla_decode(inp)
+    e = compare(out, lse, ref_out, ref_lse, what, out_tol=OUT_TOL if out_tol is None else out_tol)
+    print(f"[gpu] {what}: max err out {e[0]:.2e} lse {e[1]:.2e}", flush=True)
+    return out, lse
+
+
+def test_single_sequence_l128_contiguous():
+    inp = make_inputs("single_b1_l128", seed=0)
+    _run_and_check(inp, 1, "single_b1_l128")
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 16, 64])
+def test_paged_ragged_lengths(num_splits):
+    inp = _small([1, 63, 64, 65, 130, 700, 257], seed=1)
+    _run_and_check(inp, num_splits, f"paged ragged splits={num_splits}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 5, 8, 40])
+def test_contiguous_layout(num_splits):
+    inp = _small([100, 1000, 37, 640], layout="contiguous", seed=2)
+    _run_and_check(inp, num_splits, f"contiguous splits={num_splits}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16, 33])
+def test_two_query_tokens_causal(num_splits):
+    inp = _small([2, 3, 64, 65, 66, 129, 500], s_q=2, seed=3)
+    _run_and_check(inp, num_splits, f"mtp splits={num_splits}")
+
+
+def test_nan_in_page_tails_never_reaches_output():
+    from gpu_helpers import DeviceInputs, compare
+    inp = _small([1, 63, 65, 130, 200], seed=4)
+    ref_out, ref_lse = O.mla_decode(inp)
+    dev = DeviceInputs(inp)
+    # poison every page slot past each sequence's end
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        last = int(inp.block_table[b, (L - 1) // 64])
+        if L % 64:
+            dev.cache.rows[last, L % 64:, :] = float("nan")
+    print("[gpu] nan tails", flush=True)
+    for splits in (1, 4, 9):
+        out, lse = dev.run(splits)
+        compare(out, lse, ref_out, ref_lse, f"nan tails splits={splits}")
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_sequences_with_no_visible_row(s_q):
+    inp = _small([0, 1, 5, 70], s_q=s_q, seed=5)
+    for splits in (1, 3):
+        _run_and_check(inp, splits, f"empty rows s_q={s_q} splits={splits}")
+
+
+def test_scores_with_large_spread_restart_path():
+    # A few rows whose k^R part is a large multiple of head 0's q^R: head 0's
+    # score jumps ~100 log2 units above the first rows' maximum, past the
+    # kernel's fixed reference, which forces the restart path.  k^R does not
+    # enter the output, so the output stays on the scale of the latents.
+    inp = _small([300, 700], seed=6)
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        for j in (L - 5, L // 2):
+            page = int(inp.block_table[b, j // 64])
+            inp.cache[page, j % 64, 512:] = (inp.q_rope[b, 0, 0].float() * 16.0).to(torch.bfloat16)
+    # With the softmax concentrated on two rows, rounding P to bf16 (relative
+    # 2^-9 per weight) moves out by up to about 2^-9 max|c|; allow 2^-8 max|c|.
+    cmax = max(float(np.abs(O.sequence_rows(inp, b, int(inp.seq_lens[b]))[:, :512]).max()) for b in range(2))
+    for splits in (1, 5):
+        _run_and_check(inp, splits, f"large spread splits={splits}", out_tol=2.0 ** -8 * cmax)
+
+
+def _partition_map(lens, num_splits):
+    """Units per sequence, partition starts, and for each sequence the (partition, slot)
+    pairs holding its partials -- the partition map include/mla.h describes."""
+    units = [max(1, (int(L) + 63) // 64) for L in lens]
+    U = sum(units)
+    start = [p * U // num_splits for p in range(num_splits + 1)]
+    pre = np.concatenate([[0], np.cumsum(units)]).astype(int)
+    owners = []
+    for b in range(len(lens)):
+        u0, u1 = pre[b], pre[b + 1]
+        parts = [p for p in range(num_splits) if start[p] < start[p + 1] and start[p] < u1 and start[p + 1] > u0]
+        owners.append([(p, 0 if u0 <= start[p] else 1, max(u0, start[p]), min(u1, start[p + 1])) for p in parts])
+    return owners
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_combine_kernel_on_oracle_partials(s_q):
+    """mla_combine alone, fed partials the oracle computed over the partition map."""
+    import mla_latent_kv_39_amd as mla
+    inp = _small([1, 64, 65, 300, 129], s_q=s_q, seed=7)
+    splits = 6
+    owners = _partition_map(inp.seq_lens.tolist(), splits)
+    po = torch.zeros((splits, 2, s_q, 128, 512), dtype=torch.float32)
+    pl = torch.full((splits, 2, s_q, 128), float("-inf"), dtype=torch.float32)
+    out = torch.zeros((inp.batch, s_q, 128, 512), dtype=torch.float32)
+    lse = torch.zeros((inp.batch, s_q, 128), dtype=torch.float32)
+    ref_out, ref_lse = O.mla_decode(inp)
+    for b, own in enumerate(owners):
+        for s in range(s_q):
+            n = O.visible_rows(int(inp.seq_lens[b]), s_q, s)
+            rows = O.sequence_rows(inp, b, n)
+            q = np.concatenate([inp.q_absorbed[b, s].double().numpy(), inp.q_rope[b, s].double().numpy()], 1)
+            if len(own) == 1:
+                out[b, s] = torch.from_numpy(ref_out[b, s]).float()
+                lse[b, s] = torch.from_numpy(ref_lse[b, s]).float()
+                continue
+            for (p, slot, ua, ub) in own:
+                f = _first_unit(inp, b)
+                j0, j1 = max(0, min(n, 64 * (ua - f))), max(0, min(n, 64 * (ub - f)))
+                o_p, l_p = O.partial_over_range(q, rows, j0, j1, inp.scale)
+                po[p, slot, s] = torch.from_numpy(o_p).float()
+                pl[p, slot, s] = torch.from_numpy(l_p).float()
+    d = lambda t: t.cuda()
+    out_d, lse_d = d(out), d(lse)
+    mla.mla_combine(d(po), d(pl), d(inp.seq_lens), splits, out_d, lse_d)
+    torch.cuda.synchronize()
+    from gpu_helpers import compare
+    compare(out_d.cpu().double().numpy(), lse_d.cpu().double().numpy(), ref_out, ref_lse, f"combine s_q={s_q}")
+
+
+def _first_unit(inp, b):
+    units = [max(1, (int(L) + 63) // 64) for L in inp.seq_lens.tolist()]
+    return int(sum(units[:b]))

@@ -1,0 +1,45 @@
+"""The five decode workloads at full size, in the launch configuration bench.py times.
+
+The oracle computes a sample of (sequence, query token) results one by one:
+the first, the last, the shortest and the longest sequence, all 128 heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import WORKLOADS, make_inputs
+from oracle import mla_oracle as O
+
+pytestmark = [pytest.mark.gpu]
+
+
+def _num_splits(inp):
+    import mla_latent_kv_39_amd as mla
+    if inp.num_splits:
+        return int(inp.num_splits)
+    return mla.mla_num_splits_hint(torch.cuda.current_device(), inp.batch, inp.s_q)
+
+
+@pytest.mark.parametrize("name", ["single_b1_l128", "batched_b32_l1k_4k", "paged_b64_l256_32k",
+                                  "mtp_b128_sq2_l4k_8k", "fp8_b4_l128k"])
+def test_workload_sampled_parity(name):
+    from gpu_helpers import DeviceInputs, compare
+    if name.startswith("fp8"):
+        pytest.skip("the e4m3 cache path is not built yet")
+    print(f"[gpu] workload {name}: generating inputs", flush=True)
+    inp = make_inputs(name, seed=0)
+    splits = _num_splits(inp)
+    print(f"[gpu] workload {name}: B={inp.batch} rows={inp.total_rows()} splits={splits}", flush=True)
+    dev = DeviceInputs(inp)
+    out, lse = dev.run(splits)
+    lens = inp.seq_lens.numpy()
+    picks = sorted({0, inp.batch - 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    worst = (0.0, 0.0)
+    for b in picks:
+        for s in range(inp.s_q):
+            ref_out, ref_lse = O.decode_one(inp, b, s)
+            e = compare(out[b, s], lse[b, s], ref_out, ref_lse, f"{name} b={b} s={s}")
+            worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    # properties that hold for every result: finite, lse finite, out inside the rows' range
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    print(f"[gpu] workload {name}: sampled max err out {worst[0]:.2e} lse {worst[1]:.2e}", flush=True)
