@@ -87,6 +87,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (20 times), to scale HBM counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -95,6 +97,15 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}))
+        return 0
     import mla_latent_kv_39_amd as mla
     from mla_latent_kv_39_amd.runner import DecodeWorkspace
     from mla_inputs import make_inputs
