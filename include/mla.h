@@ -96,7 +96,7 @@ typedef struct mla_latent_cache {
  *   seq_lens     int32 [batch], device; requires s_q <= seq_len <= max_blocks_per_seq*64
  *   scale        score scale (1/sqrt(192) for DeepSeek-V3)
  *   num_splits   number of work partitions the rows of the whole batch are cut
- *                into (1 .. MLA_MAX_SPLITS).  The rows of all sequences, in
+ *                into: a power of two, 1 .. MLA_MAX_SPLITS.  The rows of all sequences, in
  *                64-row pages, are dealt out in order and in near-equal shares,
  *                so one partition can cover the tail of one sequence, whole
  *                sequences and the head of another.  mla_num_splits_hint()

@@ -3,6 +3,7 @@
 #include <atomic>
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/mla.h"
@@ -29,6 +30,7 @@ mla_status check_device() {
 mla_status check_common(int32_t batch, int32_t s_q, int32_t num_splits, const float* partial_out,
                         const float* partial_lse) {
   if (batch < 1 || s_q < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SHAPE;
+  if ((num_splits & (num_splits - 1)) != 0) return MLA_ERR_SHAPE;  // partitions are cut with shifts
   if (s_q > 2) return MLA_ERR_UNSUPPORTED;
   if (num_splits > 1 && (partial_out == nullptr || partial_lse == nullptr)) return MLA_ERR_NULL;
   // every output index must fit the kernels' size_t arithmetic with room to spare
@@ -79,8 +81,12 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;
   p.num_parts = num_splits;
-  hipError_t err = cache->dtype == MLA_CACHE_BF16 ? mla::launch_decode_bf16(p, s_q, stream)
-                                                  : mla::launch_decode_fp8(p, s_q, stream);
+  hipError_t err;
+  if (cache->dtype == MLA_CACHE_BF16)
+    err = std::getenv("MLA_DEV_HIP_DECODE") ? mla::launch_decode_bf16(p, s_q, stream)
+                                             : mla::launch_decode_bf16_asm(p, s_q, stream);
+  else
+    err = mla::launch_decode_fp8(p, s_q, stream);
   if (err == hipErrorNotSupported) return MLA_ERR_UNSUPPORTED;
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
@@ -110,7 +116,10 @@ int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q) {
   if (batch < 1 || s_q < 1 || s_q > 2) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) return 0;
-  return s_q == 1 ? cus : (cus / 2 > 0 ? cus / 2 : 1);
+  int parts = s_q == 1 ? cus : cus / 2;
+  int p2 = 1;
+  while (p2 * 2 <= parts) p2 *= 2;  // partitions must be a power of two
+  return p2;
 }
 
 size_t mla_partial_out_bytes(int32_t num_splits, int32_t s_q) {

@@ -69,6 +69,7 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, s_q=3) == E.MLA_ERR_UNSUPPORTED
     assert _decode(lib, splits=0) == E.MLA_ERR_SHAPE
     assert _decode(lib, splits=65537) == E.MLA_ERR_SHAPE
+    assert _decode(lib, splits=6) == E.MLA_ERR_SHAPE            # partitions: a power of two
     assert _decode(lib, dtype=7) == E.MLA_ERR_DTYPE
     assert _decode(lib, dtype=1) == E.MLA_ERR_NULL              # fp8 needs scales and rope
     assert _decode(lib, bs=32) == E.MLA_ERR_UNSUPPORTED
