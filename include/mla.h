@@ -101,10 +101,18 @@ typedef struct mla_latent_cache {
  *                so one partition can cover the tail of one sequence, whole
  *                sequences and the head of another.  mla_num_splits_hint()
  *                gives a value that fills the GPU.
- *   partial_out  fp32 [num_splits, 2, s_q, 128, 512]   may be NULL if num_splits == 1
+ *   partial_out  fp32 [num_splits, 2, s_q, 128 * 512]  may be NULL if num_splits == 1
+ *                (layout below)
  *   partial_lse  fp32 [num_splits, 2, s_q, 128]        may be NULL if num_splits == 1
  *   out_latent   fp32 [batch, s_q, 128, 512]
  *   lse          fp32 [batch, s_q, 128]
+ *
+ * partial_out layout: each (split, slot, token) block of 128 x 512 values is
+ * four groups of 32 heads, 16384 values each, in the order the kernel's lanes
+ * hold them: the value of head 32 j + 16 a + r (a < 2, r < 16) and latent
+ * column 16 c + 4 g + i (c < 32, g < 4, i < 4) is at offset
+ * 16384 j + 4 (64 (32 a + c) + 16 g + r) + i of its block.  partial_lse is
+ * plain [.., head].
  *
  * A sequence whose rows all fall into one partition gets its final out_latent
  * and lse here.  A sequence cut across partitions leaves one normalised partial

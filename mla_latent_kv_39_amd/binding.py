@@ -168,7 +168,7 @@ def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, sc
             raise ValueError("max_blocks_per_seq is required for a contiguous cache")
         mb = int(max_blocks_per_seq)
     if num_splits > 1:
-        _need(partial_out, torch.float32, (num_splits, 2, S, NUM_HEADS, LATENT_DIM), "partial_out")
+        _need(partial_out, torch.float32, (num_splits, 2, S, NUM_HEADS * LATENT_DIM), "partial_out")
         _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
     d = cache.desc()
     st = _lib.mla_decode(_ptr(q_absorbed), _ptr(q_rope), ctypes.byref(d), _ptr(block_table), mb, _ptr(seq_lens),

@@ -13,9 +13,11 @@ include/mla.h:
     sequence; partition p of P (a power of two) owns units
     [(pU) >> log2 P, ((p+1)U) >> log2 P);
   * tile ring: two LDS slots of one page each (72 KB), filled one unit ahead
-    with direct-to-LDS loads; chunk-column-major layout (chunk k of the 64
-    rows at k*1024, row r at slot r ^ 12(k&1), so that both the 16-row score
-    reads and the 4-row x 2-chunk transposed reads hit distinct banks);
+    with direct-to-LDS loads.  A slot is 9 x 8 blocks of 8 rows x 8 chunks
+    (chunk = 16 bytes); one load instruction moves one block, eight whole
+    128-byte lines of the page, and an XOR swizzle of the chunk slot inside
+    a block keeps the 16-row score reads and the transposed output reads
+    free of bank conflicts (lane_constants below);
   * per 32-row sub-step: scores S^T = C Q^T (72 MFMA 16x16x32 bf16),
     softmax against a per-segment reference m_ref (first max + 30, log2
     units), output O += P C (64 MFMAs, B operand read with ds_read_b64_tr_b16);
@@ -42,30 +44,31 @@ LN2 = "0x3f317218"
 
 # ---------------------------------------------------------------- registers
 # VGPRs
-V_TID, V_LANE, V_G, V_R16, V_QKOFF, V_PVOFF, V_ROWE, V_ROWO = 0, 1, 2, 3, 4, 5, 6, 7
+V_TID, V_LANE, V_G, V_R16 = 0, 1, 2, 3
+V_QKE, V_QKO, V_PV0, V_LDROW = 4, 5, 6, 7   # lane constants of the tile layout
 V_MREF = (8, 9)
 V_LRUN = (10, 11)
 V_T = 12                 # v12..v15 temporaries
-V_S = 16                 # S[tb][h] at 16 + (2*tb + h)*4, 16 regs
-V_A = 32                 # QK A-operand ring: NA buffers of 4
-NA = 6
-V_B = 56                 # PV B-operand ring: NB buffers of 4
-NB = 6
-V_P = 80                 # P fragments: P[h] at 80 + 4h
-V_QK, V_QK2, V_PV = 88, 89, 90   # per-unit operand bases (set at the top of every unit)
-V_X = 91                 # v91..v107 temporaries of the softmax and the epilogue
-V_X_END = 108
-V_G4, V_FLAG, V_NEGINF = 109, 110, 111   # set once in the prologue
+V_S = (16, 32)           # scores of sub-step ss: S[ss][tb][h] at V_S[ss] + (2*tb + h)*4
+V_A = 48                 # score-operand ring: NA buffers of 4
+NA = 4
+V_B = 64                 # output-operand ring: NB buffers of 4
+NB = 4
+V_P = (80, 88)           # probabilities of sub-step ss: P[ss][h] at V_P[ss] + 4h
+V_UQ = 96                # per-unit score-read bases: [even, odd chunk group] x [+0, +64 KB]
+V_UP = 100               # per-unit output-read bases, one per 32-byte column phase
+V_LDA, V_LDB, V_LCA, V_LCB = 104, 105, 106, 107   # loader lane constants
+V_LIM = 108              # visible-row limit of the current sub-step (mask)
+V_NEGINF = 109
 V_Q = 112                # Q[ks][h] at 112 + (2*ks + h)*4, 144 regs
-PERSISTENT = {V_LANE, V_G, V_R16, V_QKOFF, V_PVOFF, *V_MREF, *V_LRUN, V_G4, V_FLAG, V_NEGINF}
-
-
-def temps(*regs):
-    """Check that scratch registers stay inside the scratch range."""
-    for r in regs:
-        assert V_X <= r < V_X_END and r not in PERSISTENT, f"v{r} is not a scratch register"
-    return regs
-# AGPRs: O[cb][h] at (2*cb + h)*4
+# loads of the next unit issued during the first score phase use the second score buffer
+V_DMA = (V_S[1], V_S[1] + 1, V_S[1] + 2, V_S[1] + 3)
+# softmax scratch: sub-step 0 borrows P[1], sub-step 1 borrows S[0] (both free at that time)
+V_SMT = (tuple(range(V_P[1], V_P[1] + 4)), tuple(range(V_S[0], V_S[0] + 4)))
+EPI_TEMPS = list(range(16, 48))   # the epilogue runs between units
+PERSISTENT = {V_LANE, V_G, V_R16, V_QKE, V_QKO, V_PV0, V_LDROW, *V_MREF, *V_LRUN,
+              V_LDA, V_LDB, V_LCA, V_LCB, V_NEGINF}
+# AGPRs: O[cb][h] at (2*cb + h)*4, lane (g, r16) holds columns 16cb + 4g .. +3 of head 16h + r16
 
 # SGPRs (s0:1 kernarg, s2 workgroup id)
 S_QA, S_QR, S_ROWS, S_TABLE, S_LENS, S_POUT, S_PLSE, S_OUT = 4, 6, 8, 10, 12, 14, 16, 18
@@ -78,8 +81,17 @@ S_UCUR, S_SEGEND, S_ROW0, S_SLOT = 47, 48, 49, 50
 S_PAGE = 52              # s52:53
 S_QBASE, S_RBASE = 54, 56  # s54:55, s56:57
 S_EXEC = 58              # s58:59
-S_TMP = 60               # s60..s79 scratch
+S_TMP = 60               # s60..s81 scratch
+S_OVF = 82               # s82:83 lanes whose max passed the reference in this unit
+S_ENTRY, S_NVALID, S_DMALDS, S_SMT = 84, 85, 86, 87
 S_MAX = 96
+
+
+def temps(*regs, pool):
+    """Check that scratch registers come from the given scratch pool."""
+    for r in regs:
+        assert r in pool and r not in PERSISTENT, f"v{r} is not a scratch register"
+    return regs
 
 
 def vreg(i):
@@ -220,12 +232,10 @@ def seq_units_pass(a, find_first):
         a(f"s_mov_b32 {s(S_U)}, s{S_TMP + 1}")
 
 
-def issue_unit(a, u_sgpr, slot_sgpr):
-    """Direct-to-LDS copy of unit u into the slot: advance the loader cursor,
-    find the page, 18 x 16 B per lane (wave w fills chunk columns 18w..18w+17;
-    lane L loads row L of even columns and row L ^ 12 of odd ones)."""
-    adv, adv_done, haspage, contig, pagedone = (a.new_label(x) for x in
-                                                ("adv", "advdone", "haspage", "contig", "pagedone"))
+def loader_advance(a, u_sgpr):
+    """Move the loader cursor (LSEQ, LPRE, LUNITS, LLEN) forward to the sequence
+    that holds unit u."""
+    adv, adv_done = a.new_label("adv"), a.new_label("advdone")
     T = S_TMP
     a.label(adv)
     a(f"s_add_u32 s{T}, {s(S_LPRE)}, {s(S_LUNITS)}",
@@ -237,141 +247,267 @@ def issue_unit(a, u_sgpr, slot_sgpr):
     units_of(a, S_LUNITS, S_LLEN)
     a(f"s_branch {adv}")
     a.label(adv_done)
+
+
+def loader_lookup(a, u_sgpr, wait):
+    """S_NVALID = rows of unit u that hold data (<= 0: none); S_ENTRY = its page
+    (block table load left in flight unless wait)."""
+    T = S_TMP
+    done, contig = a.new_label("lkdone"), a.new_label("contig")
     a(f"s_sub_u32 s{T + 1}, {s(u_sgpr)}, {s(S_LPRE)}",        # j
       f"s_lshl_b32 s{T + 2}, s{T + 1}, 6",
-      f"s_sub_i32 s{T + 3}, {s(S_LLEN)}, s{T + 2}",           # valid = len - 64 j
-      f"s_min_i32 s{T + 3}, s{T + 3}, 64",
-      f"s_cmp_gt_i32 s{T + 3}, 0",
-      f"s_cbranch_scc1 {haspage}",
-      f"s_mov_b64 {sp(S_PAGE)}, {sp(S_ROWS)}",                # nothing visible: page 0 row 0
-      f"s_branch {pagedone}")
-    a.label(haspage)
-    a(f"s_mul_i32 s{T + 4}, {s(S_LSEQ)}, {s(S_MAXB)}",
+      f"s_sub_i32 {s(S_NVALID)}, {s(S_LLEN)}, s{T + 2}",     # len - 64 j
+      f"s_min_i32 {s(S_NVALID)}, {s(S_NVALID)}, 64",
+      f"s_cmp_gt_i32 {s(S_NVALID)}, 0",
+      f"s_cbranch_scc0 {done}",
+      f"s_mul_i32 s{T + 4}, {s(S_LSEQ)}, {s(S_MAXB)}",
       f"s_add_u32 s{T + 4}, s{T + 4}, s{T + 1}",
+      f"s_mov_b32 {s(S_ENTRY)}, s{T + 4}",
       f"s_cmp_eq_u64 {sp(S_TABLE)}, 0",
-      f"s_cbranch_scc1 {contig}",
+      f"s_cbranch_scc1 {done}",
       f"s_lshl_b32 s{T + 5}, s{T + 4}, 2",
-      f"s_load_dword s{T + 4}, {sp(S_TABLE)}, s{T + 5}",
-      s_waitcnt_lgkm(0))
-    a.label(contig)
-    a(f"s_mul_i32 s{T + 5}, s{T + 4}, {SLOT_BYTES}",
-      f"s_mul_hi_u32 s{T + 6}, s{T + 4}, {SLOT_BYTES}",
+      f"s_load_dword {s(S_ENTRY)}, {sp(S_TABLE)}, s{T + 5}")
+    if wait:
+        a(s_waitcnt_lgkm(0))
+    a.label(done)
+
+
+def loader_page(a):
+    """S_PAGE = address of page S_ENTRY, or of the pool's first page when the
+    unit holds no rows (its loads are then never used)."""
+    T = S_TMP
+    done = a.new_label("pgdone")
+    a(f"s_mov_b64 {sp(S_PAGE)}, {sp(S_ROWS)}",
+      f"s_cmp_gt_i32 {s(S_NVALID)}, 0",
+      f"s_cbranch_scc0 {done}",
+      f"s_mul_i32 s{T + 5}, {s(S_ENTRY)}, {SLOT_BYTES}",
+      f"s_mul_hi_u32 s{T + 6}, {s(S_ENTRY)}, {SLOT_BYTES}",
       f"s_add_u32 s{S_PAGE}, {s(S_ROWS)}, s{T + 5}",
       f"s_addc_u32 s{S_PAGE + 1}, s{S_ROWS + 1}, s{T + 6}")
-    a.label(pagedone)
-    # per-lane source rows: lane (even columns) and lane ^ 12 (odd columns), clamped to row 0
-    a(f"v_cmp_gt_i32 vcc, s{T + 3}, {vreg(V_LANE)}",
-      f"v_xor_b32 {vreg(V_T)}, 12, {vreg(V_LANE)}",
+    a.label(done)
+
+
+def dma_setup(a, slot_sgpr):
+    """Lane source offsets of the two row groups this wave copies (row 0 past
+    the valid rows) and the LDS base of its blocks in the slot."""
+    va, vb, t0 = V_DMA[0], V_DMA[1], V_DMA[2]
+    a(f"v_cmp_gt_i32 vcc, {s(S_NVALID)}, {vreg(V_LDROW)}",
+      f"v_add_u32 {vreg(t0)}, 8, {vreg(V_LDROW)}",
       "s_nop 1",
-      f"v_cndmask_b32 {vreg(V_ROWE)}, 0, {vreg(V_LANE)}, vcc",
-      f"v_cmp_gt_i32 vcc, s{T + 3}, {vreg(V_T)}",
-      f"v_mul_u32_u24 {vreg(V_ROWE)}, 0x480, {vreg(V_ROWE)}",
-      "s_nop 1",
-      f"v_cndmask_b32 {vreg(V_ROWO)}, 0, {vreg(V_T)}, vcc",
-      f"v_mul_u32_u24 {vreg(V_ROWO)}, 0x480, {vreg(V_ROWO)}",
-      f"s_mul_i32 s{T + 4}, {s(slot_sgpr)}, {SLOT_BYTES}",
-      f"s_mul_i32 s{T + 5}, {s(S_WAVE)}, {18 * 1024}",
-      f"s_add_u32 s{T + 4}, s{T + 4}, s{T + 5}",             # LDS base of this wave's columns
-      f"s_mul_i32 s{T + 5}, {s(S_WAVE)}, {18 * 16}")          # global byte offset of column 18w
+      f"v_cndmask_b32 {vreg(va)}, {vreg(V_LCA)}, {vreg(V_LDA)}, vcc",
+      f"v_cmp_gt_i32 vcc, {s(S_NVALID)}, {vreg(t0)}",
+      f"s_mul_i32 {s(S_DMALDS)}, {s(slot_sgpr)}, {SLOT_BYTES}",
+      f"s_lshl_b32 s{S_TMP + 5}, {s(S_WAVE)}, 11",
+      f"s_add_u32 {s(S_DMALDS)}, {s(S_DMALDS)}, s{S_TMP + 5}",   # slot + block (0, 2w)
+      "s_nop 0",
+      f"v_cndmask_b32 {vreg(vb)}, {vreg(V_LCB)}, {vreg(V_LDB)}, vcc")
+
+
+def dma_groups():
+    """The 18 direct-to-LDS loads of one unit, as separate instruction groups.
+    Wave w fills the tile blocks of rows 16w .. 16w+15 (row groups 2w, 2w+1,
+    all nine chunk groups); one load moves one 8-row x 8-chunk block, i.e.
+    eight 128-byte lines of the page."""
+    va, vb, t0, t1 = V_DMA
+    groups = []
     for i in range(18):
-        src = V_ROWO if (i & 1) else V_ROWE
-        tmp = V_T + 1 + (i & 1)
-        a(f"s_add_u32 s{T + 6}, s{T + 5}, {16 * i}",
-          f"v_add_u32 {vreg(tmp)}, s{T + 6}, {vreg(src)}",
-          f"s_add_u32 m0, s{T + 4}, {1024 * i}",
-          "s_nop 0",
-          f"global_load_lds_dwordx4 {vreg(tmp)}, {sp(S_PAGE)}")
+        k, odd = divmod(i, 2)
+        src = vb if odd else va
+        g = []
+        if k:
+            tmp = t1 if odd else t0
+            g.append(f"\tv_add_u32 {vreg(tmp)}, {128 * k}, {vreg(src)}")
+            src = tmp
+        g += [f"\ts_add_u32 m0, {s(S_DMALDS)}, {1024 * (8 * k + odd)}",
+              "\ts_nop 0",
+              f"\tglobal_load_lds_dwordx4 {vreg(src)}, {sp(S_PAGE)}"]
+        groups.append(g)
+    return groups
 
 
-def qk_read(a, i, ss):
+def issue_unit(a, u_sgpr, slot_sgpr):
+    """Stand-alone copy of unit u into the slot (prologue and restart)."""
+    loader_advance(a, u_sgpr)
+    loader_lookup(a, u_sgpr, wait=True)
+    loader_page(a)
+    dma_setup(a, slot_sgpr)
+    for g in dma_groups():
+        a.lines += g
+
+
+def qk_read(ss, i):
+    """A fragment of rows 32ss + 16tb + r16, chunk 4ks + g (i = 2ks + tb)."""
     ks, tb = divmod(i, 2)
-    buf = V_A + 4 * (i % NA)
-    if ks < 16:
-        base, off = V_QK, ks * 4096 + ss * 512 + tb * 256
-    else:
-        base, off = V_QK2, (ks - 16) * 4096 + ss * 512 + tb * 256
-    a(f"ds_read_b128 {vr(buf, 4)}, {vreg(base)} offset:{off}")
+    hi = ks >= 16
+    base = V_UQ + (ks & 1) + (2 if hi else 0)
+    off = 8192 * ((ks >> 1) - (8 if hi else 0)) + 4096 * ss + 2048 * tb
+    return [f"\tds_read_b128 {{buf}}, {vreg(base)} offset:{off}"]
 
 
-def pv_read(a, cb, ss):
-    buf = V_B + 4 * (cb % NB)
-    off = cb * 2048 + ss * 512
-    a(f"ds_read_b64_tr_b16 {vr(buf, 2)}, {vreg(V_PV)} offset:{off}",
-      f"ds_read_b64_tr_b16 {vr(buf + 2, 2)}, {vreg(V_PV)} offset:{off + 256}")
+def pv_read(ss, cb):
+    """Operand of output columns 16cb..16cb+15: rows 32ss + 4g + r, then
+    32ss + 16 + 4g + r, r < 4 (the row order of the probabilities)."""
+    base = V_UP + (cb & 3)
+    off = 8192 * (cb >> 2) + 4096 * ss
+    return [f"\tds_read_b64_tr_b16 {{lo}}, {vreg(base)} offset:{off}",
+            f"\tds_read_b64_tr_b16 {{hi}}, {vreg(base)} offset:{off + 2048}"]
 
 
-def substep(a, ss, masked_label_stem):
-    """QK, softmax, PV for rows 32ss..32ss+31 of the current unit."""
-    NQK = 36
-    # ---- scores
-    for i in range(min(NA, NQK)):
-        qk_read(a, i, ss)
-    for i in range(NQK):
+class Frag:
+    """One LDS operand fragment and the two MFMAs that consume it."""
+
+    def __init__(self, ring, ring_base, nring, idx, reads, mfmas):
+        self.ring, self.idx = ring, idx
+        buf = ring_base + 4 * (idx % nring)
+        self.reads = [r.format(buf=vr(buf, 4), lo=vr(buf, 2), hi=vr(buf + 2, 2)) for r in reads]
+        self.mfmas = [m.format(buf=vr(buf, 4)) for m in mfmas]
+        self.read_ids = []
+
+
+def qk_frags(ss):
+    out = []
+    for i in range(36):
         ks, tb = divmod(i, 2)
-        ahead = min(NA - 1, NQK - 1 - i)
-        a(s_waitcnt_lgkm(ahead))
-        buf = V_A + 4 * (i % NA)
+        mf = []
         for h in range(2):
-            sreg = V_S + (2 * tb + h) * 4
+            sreg = V_S[ss] + (2 * tb + h) * 4
             qreg = V_Q + (2 * ks + h) * 4
             c = "0" if ks == 0 else vr(sreg, 4)
-            a(f"v_mfma_f32_16x16x32_bf16 {vr(sreg, 4)}, {vr(buf, 4)}, {vr(qreg, 4)}, {c}")
-        if i + NA < NQK:
-            qk_read(a, i + NA, ss)
-    # prefetch the first output-operand fragments while the softmax runs
-    for cb in range(NB):
-        pv_read(a, cb, ss)
-    a("s_nop 7", "s_nop 7", "s_nop 3")   # MFMA results -> VALU
-    # ---- softmax (log2 domain)
-    for r in range(16):
-        a(f"v_mul_f32 {vreg(V_S + r)}, {s(S_SCALE)}, {vreg(V_S + r)}")
-    skip = a.new_label(masked_label_stem)
-    T = S_TMP
-    a(f"s_add_u32 s{T}, {s(S_ROW0)}, {32 * ss + 32}",
-      f"s_cmp_ge_i32 {s(S_NVIS)}, s{T}",
-      f"s_cbranch_scc1 {skip}")
-    # rows at or past nvis get -inf: pos = row0 + 32ss + 16tb + 4g + i < nvis
+            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(sreg, 4)}, {{buf}}, {vr(qreg, 4)}, {c}")
+        out.append(Frag("A", V_A, NA, 36 * ss + i, qk_read(ss, i), mf))
+    return out
+
+
+def pv_frags(ss):
+    """O^T[cols, heads] += C^T P^T: lane (g, r16) accumulates columns 16cb + 4g + i of head r16."""
+    out = []
+    for cb in range(32):
+        mf = []
+        for h in range(2):
+            o = (2 * cb + h) * 4
+            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {ar(o, 4)}, {{buf}}, {vr(V_P[ss] + 4 * h, 4)}, {ar(o, 4)}")
+        out.append(Frag("B", V_B, NB, 32 * ss + cb, pv_read(ss, cb), mf))
+    return out
+
+
+class LdsOrder:
+    """LDS reads in issue order, for exact lgkmcnt waits (LDS ops complete in order)."""
+
+    def __init__(self):
+        self.n = 0
+        self.done = 0
+
+    def issue(self):
+        self.n += 1
+        return self.n - 1
+
+    def wait(self, rid):
+        if rid < self.done:
+            return []
+        k = min(self.n - 1 - rid, 15)
+        self.done = self.n - k
+        return [f"\ts_waitcnt lgkmcnt({k})"]
+
+
+def emit_phases(a, frags, lead, fillers, marks=None):
+    """Emit the MFMA stream `frags` with its LDS reads and interleaved filler.
+
+    Reads of ring fragment f are issued right after the MFMAs of f - ring size
+    (the previous user of its buffer); the first fragments of each ring are
+    issued at the stream position given by `lead` {ring: index of the fragment
+    after whose MFMAs they go, -1 = at the start}.  fillers: list of
+    (first, last, instructions): spread evenly between the MFMAs of fragments
+    first..last (no LDS operations inside)."""
+    lds = LdsOrder()
+    nring = {"A": NA, "B": NB}
+    by_ring = {}
+    for f in frags:
+        by_ring.setdefault(f.ring, []).append(f)
+    pending = {}   # position -> list of frags whose reads go after that position's MFMAs
+
+    def issue_reads(f):
+        for r in f.reads:
+            f.read_ids.append(lds.issue())
+            a.lines.append(r)
+
+    pos_of = {id(f): p for p, f in enumerate(frags)}
+    for ring, lst in by_ring.items():
+        for j, f in enumerate(lst):
+            if j < nring[ring]:
+                at = lead[ring]
+            else:
+                at = pos_of[id(lst[j - nring[ring]])]
+            pending.setdefault(at, []).append(f)
+    # filler slots: after each of the two MFMAs of a fragment
+    slots = {}
+    for first, last, ins in fillers:
+        n = 2 * (last - first + 1)
+        per = [len(ins) * (k + 1) // n - len(ins) * k // n for k in range(n)]
+        it = iter(ins)
+        for k in range(n):
+            slots.setdefault((first + k // 2, k % 2), []).extend(next(it) for _ in range(per[k]))
+    for f in pending.get(-1, []):
+        issue_reads(f)
+    for p, f in enumerate(frags):
+        a.lines += lds.wait(max(f.read_ids))
+        for m, mf in enumerate(f.mfmas):
+            a.lines.append(mf)
+            a.lines += slots.get((p, m), [])
+        for g in pending.get(p, []):
+            issue_reads(g)
+        if marks and p in marks:
+            a.comment(f"phase {marks[p]} issued")
+
+
+def softmax_code(ss):
+    """Softmax of sub-step ss (log2 domain) as a plain instruction list:
+    mask rows at or past the visible count, running reference m_ref (first
+    max + 30; a max more than 64 above it raises it and flags a restart),
+    P = 2^(scale S - m_ref), row sums, bf16 pack into P[ss]."""
+    S, P = V_S[ss], V_P[ss]
+    m, t0, t1, ref = V_SMT[ss]
+    x = Asm()
+    T = S_SMT
+    # lane (g, r16) holds rows 16tb + 4g + i: visible iff 16tb + i < nvis - row0 - 32ss - 4g
+    x(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
+      f"s_sub_i32 s{T}, s{T}, {32 * ss}",
+      f"v_mad_i32_i24 {vreg(V_LIM)}, {vreg(V_G)}, -4, s{T}")
     for tb in range(2):
         for i in range(4):
-            a(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
-              f"s_sub_i32 s{T}, s{T}, {32 * ss + 16 * tb + i}",
-              f"v_cmp_gt_i32 vcc, s{T}, {vreg(V_G4)}",
+            x(f"v_cmp_lt_i32 vcc, {16 * tb + i}, {vreg(V_LIM)}",
               "s_nop 1")
             for h in range(2):
-                r = V_S + (2 * tb + h) * 4 + i
-                a(f"v_cndmask_b32 {vreg(r)}, {vreg(V_NEGINF)}, {vreg(r)}, vcc")
-    a.label(skip)
-    flag_skip = a.new_label("noflag")
-    a(f"s_mov_b64 s[{T + 2}:{T + 3}], 0")
+                r = S + (2 * tb + h) * 4 + i
+                x(f"v_cndmask_b32 {vreg(r)}, {vreg(V_NEGINF)}, {vreg(r)}, vcc")
     for h in range(2):
-        regs = [V_S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
-        m, t0, t1, ref = temps(V_X, V_X + 1, V_X + 2, V_X + 3)
-        a(f"v_max3_f32 {vreg(m)}, {vreg(regs[0])}, {vreg(regs[1])}, {vreg(regs[2])}",
+        regs = [S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
+        x(f"v_max3_f32 {vreg(m)}, {vreg(regs[0])}, {vreg(regs[1])}, {vreg(regs[2])}",
           f"v_max3_f32 {vreg(m)}, {vreg(m)}, {vreg(regs[3])}, {vreg(regs[4])}",
           f"v_max3_f32 {vreg(m)}, {vreg(m)}, {vreg(regs[5])}, {vreg(regs[6])}",
           f"v_max_f32 {vreg(m)}, {vreg(m)}, {vreg(regs[7])}")
-        xor_reduce(a, m, "v_max_f32", t0, t1)
+        xor_reduce(x, m, "v_max_f32", t0, t1)
         mref = V_MREF[h]
-        # first visible rows of the segment: m_ref = max + 30 (stays -inf while all masked)
-        a(f"v_add_f32 {vreg(t0)}, 0x41f00000, {vreg(m)}",        # +30.0
+        x(f"v_mul_f32 {vreg(m)}, {s(S_SCALE)}, {vreg(m)}",
+          # first visible rows of the segment: m_ref = max + 30 (stays -inf while all masked)
+          f"v_add_f32 {vreg(t0)}, 0x41f00000, {vreg(m)}",
           f"v_cmp_eq_f32 vcc, {NEG_INF}, {vreg(mref)}",
           "s_nop 1",
           f"v_cndmask_b32 {vreg(mref)}, {vreg(mref)}, {vreg(t0)}, vcc",
           # overflow guard: max - m_ref > 64 -> raise m_ref, ask for a restart
           f"v_sub_f32 {vreg(t1)}, {vreg(m)}, {vreg(mref)}",
-          f"v_cmp_lt_f32 vcc, 0x42800000, {vreg(t1)}",             # 64.0 < max - m_ref
+          f"v_cmp_lt_f32 vcc, 0x42800000, {vreg(t1)}",
           "s_nop 1",
           f"v_cndmask_b32 {vreg(mref)}, {vreg(mref)}, {vreg(t0)}, vcc",
-          f"s_or_b64 s[{T + 2}:{T + 3}], s[{T + 2}:{T + 3}], vcc",
+          f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc",
           # reference used for P: 0 while nothing is visible yet
           f"v_cmp_eq_f32 vcc, {NEG_INF}, {vreg(mref)}",
           "s_nop 1",
           f"v_cndmask_b32 {vreg(ref)}, {vreg(mref)}, 0, vcc")
         for r in regs:
-            a(f"v_sub_f32 {vreg(r)}, {vreg(r)}, {vreg(ref)}")
+            x(f"v_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(ref)}")
         for r in regs:
-            a(f"v_exp_f32 {vreg(r)}, {vreg(r)}")
-        a("s_nop 0",
+            x(f"v_exp_f32 {vreg(r)}, {vreg(r)}")
+        x("s_nop 0",
           f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
           f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
           f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
@@ -380,28 +516,54 @@ def substep(a, ss, masked_label_stem):
           f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
           f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}",
           f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}")
-        p = V_P + 4 * h
-        a(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
+        p = P + 4 * h
+        x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
           f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
           f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
           f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
-    a(f"s_cmp_eq_u64 s[{T + 2}:{T + 3}], 0",
-      f"s_cbranch_scc1 {flag_skip}",
-      f"v_mov_b32 {vreg(V_T)}, 1",
-      f"ds_write_b32 {vreg(V_FLAG)}, {vreg(V_T)}")
-    a.label(flag_skip)
+    return x.lines
+
+
+def unit_full(a):
+    """Both 32-row sub-steps.  Phases: scores of sub-step 0 (next unit's loads
+    interleaved), scores of 1 with softmax of 0, output of 0 with softmax of
+    1, output of 1."""
+    q0, q1, p0, p1 = qk_frags(0), qk_frags(1), pv_frags(0), pv_frags(1)
+    frags = q0 + q1 + p0 + p1
+    dma = [ins for g in dma_groups() for ins in g]
+    fillers = [(0, 35, dma),
+               (36 + 3, 71 - 1, softmax_code(0)),
+               (72 + 3, 103 - 3, softmax_code(1))]
+    emit_phases(a, frags, {"A": -1, "B": 71 - NB}, fillers, marks={35: 1, 71: 2, 103: 3})
+
+
+def unit_half(a):
+    """Only sub-step 0 has visible rows (last unit of a sequence)."""
+    q0, p0 = qk_frags(0), pv_frags(0)
+    dma = [ins for g in dma_groups() for ins in g]
+    emit_phases(a, q0, {"A": -1}, [(0, 35, dma)])
+    a("s_nop 7", "s_nop 7", "s_nop 3")   # MFMA results -> VALU
+    sm = softmax_code(0)
+    # output-operand reads go out first, overlapping the softmax
+    emit_phases_split(a, p0, sm)
+
+
+def emit_phases_split(a, p0, sm):
+    lds = LdsOrder()
+    for f in p0[:NB]:
+        for r in f.reads:
+            f.read_ids.append(lds.issue())
+            a.lines.append(r)
+    a.lines += sm
     a("s_nop 4")   # VALU writes of P -> MFMA reads
-    # ---- output: O[h] += P[h] C[:, 16cb .. 16cb+15]
-    NPV = 32
-    for cb in range(NPV):
-        ahead = min(NB - 1, NPV - 1 - cb)
-        a(s_waitcnt_lgkm(2 * ahead))
-        buf = V_B + 4 * (cb % NB)
-        for h in range(2):
-            o = (2 * cb + h) * 4
-            a(f"v_mfma_f32_16x16x32_bf16 {ar(o, 4)}, {vr(V_P + 4 * h, 4)}, {vr(buf, 4)}, {ar(o, 4)}")
-        if cb + NB < NPV:
-            pv_read(a, cb + NB, ss)
+    for p, f in enumerate(p0):
+        a.lines += lds.wait(max(f.read_ids))
+        a.lines += f.mfmas
+        if p + NB < len(p0):
+            g = p0[p + NB]
+            for r in g.reads:
+                g.read_ids.append(lds.issue())
+                a.lines.append(r)
 
 
 def zero_o(a):
@@ -428,6 +590,7 @@ def epilogue(a):
       f"s_lshl_b32 s{T + 1}, s{T + 1}, 7",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_OUT)}",
       f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_LSE)}",
+      f"s_mov_b32 s{T + 3}, 0",
       f"s_branch {addr_done}")
     a.label(whole_no)
     a(f"s_mov_b32 s{T + 2}, 0",
@@ -441,12 +604,22 @@ def epilogue(a):
       f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_STOK)}",
       f"s_lshl_b32 s{T + 1}, s{T + 1}, 7",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_POUT)}",
-      f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_PLSE)}")
+      f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_PLSE)}",
+      f"s_mov_b32 s{T + 3}, 1")
     a.label(addr_done)
-    a(f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_HEAD0)}")   # first row of this wave's heads
-    x = V_X
+    a(f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_HEAD0)}",   # first row of this wave's heads
+      # lse row pointer and out row pointer (row * 2048 B)
+      f"s_lshl_b32 s{T + 8}, s{T + 1}, 2",
+      f"s_add_u32 s{T + 10}, s{T + 6}, s{T + 8}",
+      f"s_addc_u32 s{T + 11}, s{T + 7}, 0",
+      f"s_mul_i32 s{T + 9}, s{T + 1}, 2048",
+      f"s_mul_hi_u32 s{T + 12}, s{T + 1}, 2048",
+      f"s_add_u32 s{T + 12 + 2}, s{T + 4}, s{T + 9}",
+      f"s_addc_u32 s{T + 12 + 3}, s{T + 5}, s{T + 12}")
+    x = EPI_TEMPS
+    obase = sp(T + 14)
     for h in range(2):
-        lt, inv, lse, t0, t1 = temps(x, x + 1, x + 2, x + 3, x + 4)
+        lt, inv, lse, t0, t1, off = temps(*x[0:6], pool=x)
         a(f"v_mov_b32 {vreg(lt)}, {vreg(V_LRUN[h])}")
         xor_reduce(a, lt, "v_add_f32", t0, t1)
         a(f"v_rcp_f32 {vreg(inv)}, {vreg(lt)}",
@@ -458,46 +631,133 @@ def epilogue(a):
           "s_nop 1",
           f"v_cndmask_b32 {vreg(inv)}, 0, {vreg(inv)}, vcc",
           f"v_cndmask_b32 {vreg(lse)}, {vreg(V_NEGINF)}, {vreg(lse)}, vcc")
-        # lse of head r16 from lanes with g == 0: address (row + 16h + r16) * 4
-        a(f"s_add_u32 s{T + 8}, s{T + 1}, {16 * h}",
-          f"s_lshl_b32 s{T + 8}, s{T + 8}, 2",
-          f"s_add_u32 s{T + 10}, s{T + 6}, s{T + 8}",
-          f"s_addc_u32 s{T + 11}, s{T + 7}, 0",
-          f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
+        # lse of head 16h + r16 from the lanes with g == 0
+        a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
           f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
           f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
-          f"global_store_dword {vreg(t0)}, {vreg(lse)}, s[{T + 10}:{T + 11}]",
+          f"global_store_dword {vreg(t0)}, {vreg(lse)}, s[{T + 10}:{T + 11}] offset:{64 * h}",
           f"s_mov_b64 exec, {sp(S_EXEC)}")
-        # 1/l of head 4g+i, from lane 4g+i
-        invs = list(temps(*[x + 5 + i for i in range(4)]))
-        for i in range(4):
-            a(f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_G)}",
-              f"v_add_u32 {vreg(t0)}, {i}, {vreg(t0)}",
-              f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(t0)}",
-              f"ds_bpermute_b32 {vreg(invs[i])}, {vreg(t0)}, {vreg(inv)}")
-        a(s_waitcnt_lgkm(0))
-        # out rows: base + (row + 16h) * 2048 B; lane offset (4g+i)*2048 + r16*4; column block cb at 64 cb
-        a(f"s_add_u32 s{T + 8}, s{T + 1}, {16 * h}",
-          f"s_mul_i32 s{T + 9}, s{T + 8}, 2048",
-          f"s_mul_hi_u32 s{T + 12}, s{T + 8}, 2048",
-          f"s_add_u32 s{T + 10}, s{T + 4}, s{T + 9}",
-          f"s_addc_u32 s{T + 11}, s{T + 5}, s{T + 12}")
-        offs = list(temps(*[x + 9 + i for i in range(4)]))
-        for i in range(4):
-            a(f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_G)}",
-              f"v_add_u32 {vreg(t0)}, {i}, {vreg(t0)}",
-              f"v_lshlrev_b32 {vreg(t0)}, 11, {vreg(t0)}",
-              f"v_lshl_add_u32 {vreg(offs[i])}, {vreg(V_R16)}, 2, {vreg(t0)}")
-        vv = list(temps(*[x + 13 + i for i in range(4)]))
+        bufs = [x[8:12], x[12:16], x[16:20], x[20:24]]
+        rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
+        a(f"s_cmp_eq_u32 s{T + 3}, 0",
+          f"s_cbranch_scc1 {rowwise}")
+        # partial: lane order, store (h, cb) of lane L at (32h + cb) KB + 16 L of the wave's 64 KB
+        a(f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
+          f"s_add_u32 s{T + 16}, s{T + 14}, {32 * 1024 * h}",
+          f"s_addc_u32 s{T + 17}, s{T + 15}, 0")
         for cb in range(32):
-            o = (2 * cb + h) * 4
-            for i in range(4):
-                a(f"v_accvgpr_read_b32 {vreg(vv[i])}, a{o + i}")
-            a("s_nop 1")
-            for i in range(4):
-                a(f"v_mul_f32 {vreg(vv[i])}, {vreg(vv[i])}, {vreg(invs[i])}")
-            for i in range(4):
-                a(f"global_store_dword {vreg(offs[i])}, {vreg(vv[i])}, s[{T + 10}:{T + 11}] offset:{64 * cb}")
+            if cb and cb % 4 == 0:
+                a(f"s_add_u32 s{T + 16}, s{T + 16}, 4096", f"s_addc_u32 s{T + 17}, s{T + 17}, 0")
+            epi_store(a, h, cb, bufs[cb % 4], inv, f"{vreg(off)}, {{v}}, s[{T + 16}:{T + 17}] offset:{1024 * (cb % 4)}")
+        a(f"s_branch {stored}")
+        # final result: row layout, lane (g, r16) -> (16h + r16) * 2048 + 16g + 64cb
+        a.label(rowwise)
+        a(f"v_lshlrev_b32 {vreg(t0)}, 4, {vreg(V_G)}",
+          f"v_lshl_add_u32 {vreg(off)}, {vreg(V_R16)}, 11, {vreg(t0)}")
+        if h:
+            a(f"v_add_u32 {vreg(off)}, {16 * 2048}, {vreg(off)}")
+        for cb in range(32):
+            epi_store(a, h, cb, bufs[cb % 4], inv, f"{vreg(off)}, {{v}}, {obase} offset:{64 * cb}")
+        a.label(stored)
+
+
+def epi_store(a, h, cb, vv, inv, operands):
+    """O[cb][h] * inv -> one 16-byte store per lane."""
+    o = (2 * cb + h) * 4
+    for i in range(4):
+        a(f"v_accvgpr_read_b32 {vreg(vv[i])}, a{o + i}")
+    a("s_nop 1")
+    for i in range(4):
+        a(f"v_mul_f32 {vreg(vv[i])}, {vreg(vv[i])}, {vreg(inv)}")
+    a("global_store_dwordx4 " + operands.format(v=vr(vv[0], 4)))
+
+
+def emit_t(a, dst, q, tmp):
+    """dst = t(q) = 2 (q & 3) + (q >> 2) for 0 <= q < 8: the chunk swizzle of a
+    row within its 8-row block."""
+    a(f"v_and_b32 {vreg(tmp)}, 3, {vreg(q)}",
+      f"v_lshrrev_b32 {vreg(dst)}, 2, {vreg(q)}",
+      f"v_lshl_or_b32 {vreg(dst)}, {vreg(tmp)}, 1, {vreg(dst)}")
+
+
+def lane_constants(a):
+    """Per-lane offsets of the tile layout.  A page tile is 9 x 8 blocks of
+    1 KB: block (K, R) at (8K + R) KB holds rows 8R..8R+7, chunks 8K..8K+7
+    (chunk = 8 bf16); row r sits at 128 (r % 8) in its block and chunk c at
+    16 ((c % 8) ^ tp(r)), tp(r) = t(r % 8) ^ 2 ((r / 8) % 2).  The swizzle puts
+    the 16 rows of a score read and the 4 rows x 2 chunks of a transposed read
+    on distinct bank groups."""
+    g, j = V_G, V_R16
+    t0, t1, t2, t3 = V_T, V_T + 1, V_T + 2, V_T + 3
+    u0, u1, u2, u3 = V_S[0], V_S[0] + 1, V_S[0] + 2, V_S[0] + 3
+    # score reads: lane (g, j) reads row j, chunk g of a 16-row tile -> j*128 + 16 (g ^ tp(j))
+    a(f"v_and_b32 {vreg(t0)}, 7, {vreg(j)}")
+    emit_t(a, t1, t0, t2)
+    a(f"v_lshrrev_b32 {vreg(t2)}, 2, {vreg(j)}",
+      f"v_and_b32 {vreg(t2)}, 2, {vreg(t2)}",
+      f"v_xor_b32 {vreg(t1)}, {vreg(t1)}, {vreg(t2)}",
+      f"v_xor_b32 {vreg(t1)}, {vreg(g)}, {vreg(t1)}",
+      f"v_lshlrev_b32 {vreg(t1)}, 4, {vreg(t1)}",
+      f"v_lshl_add_u32 {vreg(V_QKE)}, {vreg(j)}, 7, {vreg(t1)}",
+      f"v_xor_b32 {vreg(V_QKO)}, 64, {vreg(V_QKE)}")
+    # transposed reads: source lane j of group g supplies row 4g + (j >> 2) (+16 for the
+    # second read), columns 4 (j & 3) .. +3 of a 16-column block:
+    #   r8 = 4 (g & 1) + (j >> 2), tpp = t(r8) ^ (g & 2), e = (j >> 1) & 1
+    #   pv0 = 1024 (g >> 1) + 128 r8 + 16 (e ^ tpp) + 8 (j & 1)
+    a(f"v_and_b32 {vreg(t0)}, 1, {vreg(g)}",
+      f"v_lshrrev_b32 {vreg(t1)}, 2, {vreg(j)}",
+      f"v_lshl_or_b32 {vreg(t0)}, {vreg(t0)}, 2, {vreg(t1)}")      # r8
+    emit_t(a, t1, t0, t2)
+    a(f"v_and_b32 {vreg(t2)}, 2, {vreg(g)}",
+      f"v_xor_b32 {vreg(t1)}, {vreg(t1)}, {vreg(t2)}",              # tpp
+      f"v_bfe_u32 {vreg(t2)}, {vreg(j)}, 1, 1",                      # e
+      f"v_xor_b32 {vreg(t1)}, {vreg(t1)}, {vreg(t2)}",
+      f"v_lshlrev_b32 {vreg(t1)}, 4, {vreg(t1)}",
+      f"v_lshl_add_u32 {vreg(t1)}, {vreg(t0)}, 7, {vreg(t1)}",
+      f"v_and_b32 {vreg(t2)}, 1, {vreg(j)}",
+      f"v_lshl_add_u32 {vreg(t1)}, {vreg(t2)}, 3, {vreg(t1)}",
+      f"v_lshrrev_b32 {vreg(t2)}, 1, {vreg(g)}",
+      f"v_lshl_add_u32 {vreg(V_PV0)}, {vreg(t2)}, 10, {vreg(t1)}")
+    # loader: lane L of a block load writes row-in-block lr = L >> 3 and slot lx = L & 7,
+    # i.e. chunk lx ^ t(lr) (even row groups) or that ^ 2 (odd ones)
+    T = S_TMP
+    a(f"v_lshrrev_b32 {vreg(u0)}, 3, {vreg(V_LANE)}",                # lr
+      f"v_and_b32 {vreg(u1)}, 7, {vreg(V_LANE)}")                    # lx
+    emit_t(a, u2, u0, u3)
+    a(f"v_xor_b32 {vreg(u2)}, {vreg(u1)}, {vreg(u2)}",
+      f"v_lshlrev_b32 {vreg(V_LCA)}, 4, {vreg(u2)}",
+      f"v_xor_b32 {vreg(V_LCB)}, 32, {vreg(V_LCA)}",
+      f"s_mul_i32 s{T}, {s(S_WAVE)}, {16 * 1152}",
+      f"v_mul_u32_u24 {vreg(u3)}, {1152}, {vreg(u0)}",
+      f"v_add_u32 {vreg(u3)}, s{T}, {vreg(u3)}",                      # row term of row 16w + lr
+      f"v_add_u32 {vreg(V_LDA)}, {vreg(u3)}, {vreg(V_LCA)}",
+      f"v_add_u32 {vreg(V_LDB)}, {vreg(u3)}, {vreg(V_LCB)}",
+      f"v_add_u32 {vreg(V_LDB)}, {8 * 1152}, {vreg(V_LDB)}",
+      f"s_lshl_b32 s{T}, {s(S_WAVE)}, 4",
+      f"v_add_u32 {vreg(V_LDROW)}, s{T}, {vreg(u0)}")
+
+
+def flag_write(a, value, all_waves=False):
+    """Write the restart flag (wave 0 only unless all_waves)."""
+    skip = a.new_label("flagw")
+    if not all_waves:
+        a(f"s_cmp_eq_u32 {s(S_WAVE)}, 0",
+          f"s_cbranch_scc0 {skip}")
+    a(f"v_mov_b32 {vreg(V_T)}, {value}",
+      f"v_mov_b32 {vreg(V_T + 1)}, {FLAG_ADDR}",
+      f"ds_write_b32 {vreg(V_T + 1)}, {vreg(V_T)}")
+    a.label(skip)
+
+
+def flag_check(a):
+    """After a barrier: restart the segment if any wave raised the flag."""
+    a(f"v_mov_b32 {vreg(V_T)}, {FLAG_ADDR}",
+      f"ds_read_b32 {vreg(V_T)}, {vreg(V_T)}",
+      s_waitcnt_lgkm(0),
+      "s_nop 1",
+      f"v_readfirstlane_b32 s{S_TMP}, {vreg(V_T)}",
+      f"s_cmp_eq_u32 s{S_TMP}, 0",
+      "s_cbranch_scc0 .Lrestart")
 
 
 def kernel():
@@ -565,36 +825,11 @@ def kernel():
       f"s_ff1_i32_b32 s{T + 1}, {s(S_HB)}",
       f"s_lshr_b32 {s(S_STOK)}, s{T}, s{T + 1}")
     # ------------------------------------------------ lane-constant LDS offsets
+    lane_constants(a)
     t = V_T
-    a(f"v_and_b32 {vreg(t)}, 1, {vreg(V_G)}",
-      f"v_mul_u32_u24 {vreg(t)}, 12, {vreg(t)}",
-      f"v_xor_b32 {vreg(t)}, {vreg(V_R16)}, {vreg(t)}",
-      f"v_lshlrev_b32 {vreg(t)}, 4, {vreg(t)}",
-      f"v_lshlrev_b32 {vreg(t + 1)}, 10, {vreg(V_G)}",
-      f"v_add_u32 {vreg(V_QKOFF)}, {vreg(t)}, {vreg(t + 1)}",
-      f"v_lshrrev_b32 {vreg(t)}, 1, {vreg(V_R16)}",
-      f"v_and_b32 {vreg(t)}, 1, {vreg(t)}",
-      f"v_lshlrev_b32 {vreg(t + 1)}, 2, {vreg(V_G)}",
-      f"v_lshrrev_b32 {vreg(t + 2)}, 2, {vreg(V_R16)}",
-      f"v_add_u32 {vreg(t + 1)}, {vreg(t + 1)}, {vreg(t + 2)}",
-      f"v_mul_u32_u24 {vreg(t + 2)}, 12, {vreg(t)}",
-      f"v_xor_b32 {vreg(t + 1)}, {vreg(t + 1)}, {vreg(t + 2)}",
-      f"v_lshlrev_b32 {vreg(t + 1)}, 4, {vreg(t + 1)}",
-      f"v_lshlrev_b32 {vreg(t + 2)}, 10, {vreg(t)}",
-      f"v_add_u32 {vreg(t + 1)}, {vreg(t + 1)}, {vreg(t + 2)}",
-      f"v_and_b32 {vreg(t + 2)}, 1, {vreg(V_R16)}",
-      f"v_lshlrev_b32 {vreg(t + 2)}, 3, {vreg(t + 2)}",
-      f"v_add_u32 {vreg(V_PVOFF)}, {vreg(t + 1)}, {vreg(t + 2)}",
-      f"v_lshlrev_b32 {vreg(V_G4)}, 2, {vreg(V_G)}",
-      f"v_mov_b32 {vreg(V_FLAG)}, {FLAG_ADDR}",
-      f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
+    a(f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
     # restart flag = 0
-    nowrite = a.new_label("flaginit")
-    a(f"s_cmp_eq_u32 {s(S_WAVE)}, 0",
-      f"s_cbranch_scc0 {nowrite}",
-      f"v_mov_b32 {vreg(t)}, 0",
-      f"ds_write_b32 {vreg(V_FLAG)}, {vreg(t)}")
-    a.label(nowrite)
+    flag_write(a, 0)
     a(s_waitcnt_lgkm(0), "s_barrier")
     # ------------------------------------------------ loader cursor, first unit
     a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
@@ -649,43 +884,65 @@ def kernel():
       f"v_mov_b32 {vreg(V_LRUN[1])}, 0")
     zero_o(a)
     # ------------------------------------------------ units of the segment
+    # On entry the loads of unit S_UCUR into its slot are in flight.
     a.label(".Lunit")
-    a(f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
+    nonext, looked = a.new_label("nonext"), a.new_label("looked")
+    a(f"s_mov_b64 {sp(S_OVF)}, 0",
+      f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
       f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1",
       f"s_add_u32 s{T + 20}, {s(S_UCUR)}, 1",
       f"s_cmp_lt_u32 s{T + 20}, {s(S_UB)}",
-      "s_cbranch_scc0 .Lnomore",
-      f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
-    issue_unit(a, T + 20, T + 21)
-    a(s_waitcnt_vm(18), "s_branch .Lwaited")
-    a.label(".Lnomore")
-    a(s_waitcnt_vm(0))
-    a.label(".Lwaited")
-    a("s_barrier")
+      f"s_cbranch_scc0 {nonext}")
+    loader_advance(a, T + 20)
+    loader_lookup(a, T + 20, wait=False)
+    a(f"s_branch {looked}")
+    a.label(nonext)
+    a(f"s_mov_b32 {s(S_NVALID)}, 0")   # no next unit: a harmless copy of row 0 of page 0
+    a.label(looked)
+    # this unit's rows have landed (own loads) and every wave is past the previous unit
+    a(s_waitcnt_vm(0), s_waitcnt_lgkm(0), "s_barrier")
+    flag_check(a)
+    loader_page(a)
+    a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
+    dma_setup(a, T + 21)
     a(f"s_sub_u32 {s(S_ROW0)}, {s(S_UCUR)}, {s(S_CPRE)}",
       f"s_lshl_b32 {s(S_ROW0)}, {s(S_ROW0)}, 6",
       f"s_mul_i32 s{T}, {s(S_SLOT)}, {SLOT_BYTES}",
-      f"v_add_u32 {vreg(V_QK)}, s{T}, {vreg(V_QKOFF)}",
-      f"v_add_u32 {vreg(V_PV)}, s{T}, {vreg(V_PVOFF)}",
-      f"v_add_u32 {vreg(V_QK2)}, 0x10000, {vreg(V_QK)}")
-    for ss in range(2):
-        skip = a.new_label(f"skipss{ss}")
-        a(f"s_add_u32 s{T}, {s(S_ROW0)}, {32 * ss}",
-          f"s_cmp_gt_i32 {s(S_NVIS)}, s{T}",
-          f"s_cbranch_scc0 {skip}")
-        substep(a, ss, f"nomask{ss}")
-        a.label(skip)
-    a(s_waitcnt_lgkm(0), "s_barrier")
-    # restart requested?
-    a(f"ds_read_b32 {vreg(t)}, {vreg(V_FLAG)}",
-      s_waitcnt_lgkm(0),
-      "s_nop 1",
-      f"v_readfirstlane_b32 s{T}, {vreg(t)}",
-      f"s_cmp_eq_u32 s{T}, 0",
-      "s_cbranch_scc0 .Lrestart",
-      f"s_add_u32 {s(S_UCUR)}, {s(S_UCUR)}, 1",
+      f"v_add_u32 {vreg(V_UQ)}, s{T}, {vreg(V_QKE)}",
+      f"v_add_u32 {vreg(V_UQ + 1)}, s{T}, {vreg(V_QKO)}",
+      f"v_add_u32 {vreg(V_UQ + 2)}, 0x10000, {vreg(V_UQ)}",
+      f"v_add_u32 {vreg(V_UQ + 3)}, 0x10000, {vreg(V_UQ + 1)}",
+      f"v_add_u32 {vreg(V_UP)}, s{T}, {vreg(V_PV0)}")
+    for m in range(1, 4):
+        a(f"v_xor_b32 {vreg(V_UP + m)}, {32 * m}, {vreg(V_PV0)}",
+          f"v_add_u32 {vreg(V_UP + m)}, s{T}, {vreg(V_UP + m)}")
+    # rows of this unit this wave's query token sees: none, only the first 32, or more
+    half, none, uend = a.new_label("half"), a.new_label("none"), a.new_label("uend")
+    a(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
+      f"s_cmp_le_i32 s{T}, 0",
+      f"s_cbranch_scc1 {none}",
+      f"s_cmp_le_i32 s{T}, 32",
+      f"s_cbranch_scc1 {half}")
+    unit_full(a)
+    a(f"s_branch {uend}")
+    a.label(half)
+    unit_half(a)
+    a(f"s_branch {uend}")
+    a.label(none)
+    for g in dma_groups():
+        a.lines += g
+    a.label(uend)
+    noflag = a.new_label("noflag")
+    a(f"s_cmp_eq_u64 {sp(S_OVF)}, 0",
+      f"s_cbranch_scc1 {noflag}")
+    flag_write(a, 1, all_waves=True)
+    a.label(noflag)
+    a(f"s_add_u32 {s(S_UCUR)}, {s(S_UCUR)}, 1",
       f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_SEGEND)}",
       "s_cbranch_scc1 .Lunit")
+    # end of the segment: a restart request of its last unit?
+    a(s_waitcnt_lgkm(0), "s_barrier")
+    flag_check(a)
     epilogue(a)
     a(f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_add_u32 {s(S_CSEQ)}, {s(S_CSEQ)}, 1",
@@ -694,13 +951,8 @@ def kernel():
       "s_branch .Lkernel_end")
     # ------------------------------------------------ restart of the segment
     a.label(".Lrestart")
-    a(s_waitcnt_vm(0), "s_barrier")
-    noclear = a.new_label("noclear")
-    a(f"s_cmp_eq_u32 {s(S_WAVE)}, 0",
-      f"s_cbranch_scc0 {noclear}",
-      f"v_mov_b32 {vreg(t)}, 0",
-      f"ds_write_b32 {vreg(V_FLAG)}, {vreg(t)}")
-    a.label(noclear)
+    a(s_waitcnt_vm(0), "s_barrier")   # every wave has read the flag; no loads in flight
+    flag_write(a, 0)
     a(f"s_max_u32 {s(S_UCUR)}, {s(S_UA)}, {s(S_CPRE)}",
       f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
       f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}",
@@ -712,9 +964,9 @@ def kernel():
     a(f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
       f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
     issue_unit(a, S_UCUR, S_SLOT)
-    a(s_waitcnt_lgkm(0), "s_barrier", "s_branch .Lunit")
+    a("s_branch .Lunit")
     a.label(".Lkernel_end")
-    a("s_endpgm")
+    a(s_waitcnt_vm(0), "s_endpgm")   # the last unit's spare copy must land before the LDS is released
     a.lines += [f".L{KNAME}_end:", f"\t.size {KNAME}, .L{KNAME}_end-{KNAME}", ""]
     a.lines += descriptor()
     return a.text()

@@ -19,7 +19,7 @@ class DecodeWorkspace:
         self.out = torch.empty((batch, s_q, NUM_HEADS, LATENT_DIM), dtype=f32, device=device)
         self.lse = torch.empty((batch, s_q, NUM_HEADS), dtype=f32, device=device)
         if num_splits > 1:
-            self.partial_out = torch.empty((num_splits, 2, s_q, NUM_HEADS, LATENT_DIM), dtype=f32, device=device)
+            self.partial_out = torch.empty((num_splits, 2, s_q, NUM_HEADS * LATENT_DIM), dtype=f32, device=device)
             self.partial_lse = torch.empty((num_splits, 2, s_q, NUM_HEADS), dtype=f32, device=device)
         else:
             self.partial_out = self.partial_lse = None

@@ -45,3 +45,13 @@ def compare(out, lse, ref_out, ref_lse, what="", out_tol=OUT_TOL):
     assert e_out <= out_tol, f"{what}: max |out - oracle| = {e_out:.3e} > {out_tol}"
     assert e_lse <= LSE_TOL, f"{what}: max |lse - oracle| = {e_lse:.3e} > {LSE_TOL}"
     return e_out, e_lse
+
+
+def pack_partial_out(po):
+    """[splits, 2, s_q, 128, 512] partials in head/column order -> the library's
+    partial_out layout [splits, 2, s_q, 128 * 512]: per group of 32 heads, the
+    value of head 32j + 16a + r and column 16c + 4g + i at 16384 j + 4 (64 (32a + c) + 16g + r) + i."""
+    n, k, s = po.shape[:3]
+    v = po.reshape(n, k, s, 4, 2, 16, 32, 4, 4)          # j, a, r, c, g, i
+    return v.permute(0, 1, 2, 3, 4, 6, 7, 5, 8).contiguous().reshape(n, k, s, 128 * 512)   # j, a, c, g, r, i
+

@@ -141,7 +141,8 @@ def test_combine_kernel_on_oracle_partials(s_q):
                 pl[p, slot, s] = torch.from_numpy(l_p).float()
     d = lambda t: t.cuda()
     out_d, lse_d = d(out), d(lse)
-    mla.mla_combine(d(po), d(pl), d(inp.seq_lens), splits, out_d, lse_d)
+    from gpu_helpers import pack_partial_out
+    mla.mla_combine(d(pack_partial_out(po)), d(pl), d(inp.seq_lens), splits, out_d, lse_d)
     torch.cuda.synchronize()
     from gpu_helpers import compare
     compare(out_d.cpu().double().numpy(), lse_d.cpu().double().numpy(), ref_out, ref_lse, f"combine s_q={s_q}")
