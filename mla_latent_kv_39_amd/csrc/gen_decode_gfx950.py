@@ -41,6 +41,7 @@ FLAG_ADDR = 2 * SLOT_BYTES      # restart flag (LDS)
 LDS_BYTES = FLAG_ADDR + 16
 NEG_INF = "0xff800000"
 LN2 = "0x3f317218"
+OVF_SUM = "0x5f800000"   # 2^64
 
 # ---------------------------------------------------------------- registers
 # VGPRs
@@ -58,16 +59,18 @@ V_P = (80, 88)           # probabilities of sub-step ss: P[ss][h] at V_P[ss] + 4
 V_UQ = 96                # per-unit score-read bases: [even, odd chunk group] x [+0, +64 KB]
 V_UP = 100               # per-unit output-read bases, one per 32-byte column phase
 V_LDA, V_LDB, V_LCA, V_LCB = 104, 105, 106, 107   # loader lane constants
-V_LIM = 108              # visible-row limit of the current sub-step (mask)
+V_LIM = 15               # visible-row limit of the current sub-step (mask; a temporary outside the phases)
+V_ENT = 108              # block-table entry of the unit after next (vector load, one unit ahead)
 V_NEGINF = 109
+V_PEAK = (110, 111)      # largest 8-row probability sum seen per lane in this segment (lean softmax)
 V_Q = 112                # Q[ks][h] at 112 + (2*ks + h)*4, 144 regs
-# loads of the next unit issued during the first score phase use the second score buffer
-V_DMA = (V_S[1], V_S[1] + 1, V_S[1] + 2, V_S[1] + 3)
+# source offsets of the next unit's loads (row groups 2w, 2w+1): live through the phases
+V_DMA = (V_T + 1, V_T + 2)
 # softmax scratch: sub-step 0 borrows P[1], sub-step 1 borrows S[0] (both free at that time)
 V_SMT = (tuple(range(V_P[1], V_P[1] + 4)), tuple(range(V_S[0], V_S[0] + 4)))
 EPI_TEMPS = list(range(16, 48))   # the epilogue runs between units
 PERSISTENT = {V_LANE, V_G, V_R16, V_QKE, V_QKO, V_PV0, V_LDROW, *V_MREF, *V_LRUN,
-              V_LDA, V_LDB, V_LCA, V_LCB, V_NEGINF}
+              V_LDA, V_LDB, V_LCA, V_LCB, V_NEGINF, *V_PEAK}
 # AGPRs: O[cb][h] at (2*cb + h)*4, lane (g, r16) holds columns 16cb + 4g .. +3 of head 16h + r16
 
 # SGPRs (s0:1 kernarg, s2 workgroup id)
@@ -84,6 +87,11 @@ S_EXEC = 58              # s58:59
 S_TMP = 60               # s60..s81 scratch
 S_OVF = 82               # s82:83 lanes whose max passed the reference in this unit
 S_ENTRY, S_NVALID, S_DMALDS, S_SMT = 84, 85, 86, 87
+S_EXACT = 88             # 1 after a restart: the rest of the segment keeps the max-based softmax
+S_NV2, S_ENT2 = 89, 90   # prefetched valid rows / page of the unit after next (-1: page in V_ENT)
+S_DPAGE = 80             # s80:81 page address + chunk-group offset of one load (S_TMP + 20, + 21)
+# loads of the next unit issued in phases 1, 2, 3 of a full unit
+DMA_SPLIT = (8, 6, 4)
 S_MAX = 96
 
 
@@ -272,6 +280,57 @@ def loader_lookup(a, u_sgpr, wait):
     a.label(done)
 
 
+def loader_prefetch(a, u_sgpr):
+    """Look up unit u one unit before its loads are issued: S_NV2 = its valid
+    rows (<= 0: none), S_ENT2 = its page for a contiguous cache, or -1 with the
+    page on its way into V_ENT (a vector load, so that the LDS waits of the
+    phases never wait on it; it lands before the next unit's barrier)."""
+    T = S_TMP
+    done = a.new_label("pfdone")
+    a(f"s_mov_b32 {s(S_ENT2)}, 0",
+      f"s_sub_u32 s{T + 1}, {s(u_sgpr)}, {s(S_LPRE)}",        # j
+      f"s_lshl_b32 s{T + 2}, s{T + 1}, 6",
+      f"s_sub_i32 {s(S_NV2)}, {s(S_LLEN)}, s{T + 2}",
+      f"s_min_i32 {s(S_NV2)}, {s(S_NV2)}, 64",
+      f"s_cmp_gt_i32 {s(S_NV2)}, 0",
+      f"s_cbranch_scc0 {done}",
+      f"s_mul_i32 s{T + 4}, {s(S_LSEQ)}, {s(S_MAXB)}",
+      f"s_add_u32 {s(S_ENT2)}, s{T + 4}, s{T + 1}",
+      f"s_cmp_eq_u64 {sp(S_TABLE)}, 0",
+      f"s_cbranch_scc1 {done}",
+      f"s_lshl_b32 s{T + 5}, {s(S_ENT2)}, 2",
+      f"v_mov_b32 {vreg(V_T + 3)}, s{T + 5}",       # v13/v14 hold the next unit's load offsets
+      f"global_load_dword {vreg(V_ENT)}, {vreg(V_T + 3)}, {sp(S_TABLE)}",
+      f"s_mov_b32 {s(S_ENT2)}, -1")
+    a.label(done)
+
+
+def prefetch_next(a, u_sgpr):
+    """Prefetch the page of unit u + 1 if the partition has it (else none)."""
+    T = S_TMP
+    nonext, done = a.new_label("pfnone"), a.new_label("pfend")
+    a(f"s_add_u32 s{T + 20}, {s(u_sgpr)}, 1",
+      f"s_cmp_lt_u32 s{T + 20}, {s(S_UB)}",
+      f"s_cbranch_scc0 {nonext}")
+    loader_advance(a, T + 20)
+    loader_prefetch(a, T + 20)
+    a(f"s_branch {done}")
+    a.label(nonext)
+    a(f"s_mov_b32 {s(S_NV2)}, 0", f"s_mov_b32 {s(S_ENT2)}, 0")
+    a.label(done)
+
+
+def take_prefetched(a):
+    """S_NVALID / S_ENTRY of the next unit from the prefetch (vector loads done)."""
+    fromtab, done = a.new_label("fromtab"), a.new_label("takedone")
+    a(f"s_mov_b32 {s(S_NVALID)}, {s(S_NV2)}",
+      f"s_mov_b32 {s(S_ENTRY)}, {s(S_ENT2)}",
+      f"s_cmp_eq_i32 {s(S_ENT2)}, -1",
+      f"s_cbranch_scc0 {done}",
+      f"v_readfirstlane_b32 {s(S_ENTRY)}, {vreg(V_ENT)}")
+    a.label(done)
+
+
 def loader_page(a):
     """S_PAGE = address of page S_ENTRY, or of the pool's first page when the
     unit holds no rows (its loads are then never used)."""
@@ -290,7 +349,8 @@ def loader_page(a):
 def dma_setup(a, slot_sgpr):
     """Lane source offsets of the two row groups this wave copies (row 0 past
     the valid rows) and the LDS base of its blocks in the slot."""
-    va, vb, t0 = V_DMA[0], V_DMA[1], V_DMA[2]
+    va, vb = V_DMA
+    t0 = V_T + 3
     a(f"v_cmp_gt_i32 vcc, {s(S_NVALID)}, {vreg(V_LDROW)}",
       f"v_add_u32 {vreg(t0)}, 8, {vreg(V_LDROW)}",
       "s_nop 1",
@@ -308,20 +368,16 @@ def dma_groups():
     Wave w fills the tile blocks of rows 16w .. 16w+15 (row groups 2w, 2w+1,
     all nine chunk groups); one load moves one 8-row x 8-chunk block, i.e.
     eight 128-byte lines of the page."""
-    va, vb, t0, t1 = V_DMA
+    va, vb = V_DMA
     groups = []
     for i in range(18):
         k, odd = divmod(i, 2)
         src = vb if odd else va
-        g = []
-        if k:
-            tmp = t1 if odd else t0
-            g.append(f"\tv_add_u32 {vreg(tmp)}, {128 * k}, {vreg(src)}")
-            src = tmp
-        g += [f"\ts_add_u32 m0, {s(S_DMALDS)}, {1024 * (8 * k + odd)}",
-              "\ts_nop 0",
-              f"\tglobal_load_lds_dwordx4 {vreg(src)}, {sp(S_PAGE)}"]
-        groups.append(g)
+        groups.append([f"\ts_add_u32 s{S_DPAGE}, s{S_PAGE}, {128 * k}",
+                       f"\ts_addc_u32 s{S_DPAGE + 1}, s{S_PAGE + 1}, 0",
+                       f"\ts_add_u32 m0, {s(S_DMALDS)}, {1024 * (8 * k + odd)}",
+                       "\ts_nop 0",
+                       f"\tglobal_load_lds_dwordx4 {vreg(src)}, {sp(S_DPAGE)}"])
     return groups
 
 
@@ -524,17 +580,72 @@ def softmax_code(ss):
     return x.lines
 
 
-def unit_full(a):
+def softmax_lean(ss):
+    """Softmax of a fully visible sub-step once the segment's reference is
+    set: P = 2^(scale S - m_ref), row sums, bf16 pack.  No max: a lane whose
+    8-row sum passes 2^64 (the largest score more than ~64 above m_ref) flags a
+    restart, and V_PEAK keeps the largest such sum so that the restart can
+    raise m_ref past it."""
+    S, P = V_S[ss], V_P[ss]
+    t0, t1 = V_SMT[ss][0], V_SMT[ss][1]
+    x = Asm()
+    for h in range(2):
+        regs = [S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
+        mref = V_MREF[h]
+        for r in regs:
+            x(f"v_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(mref)}")
+        for r in regs:
+            x(f"v_exp_f32 {vreg(r)}, {vreg(r)}")
+        x("s_nop 0",
+          f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
+          f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
+          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[5])}",
+          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[6])}",
+          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
+          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}",
+          f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}",
+          f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(t0)}",
+          f"v_max_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
+          f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc")
+        p = P + 4 * h
+        x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
+          f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+          f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
+          f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
+    return x.lines
+
+
+def unit_full(a, lean):
     """Both 32-row sub-steps.  Phases: scores of sub-step 0 (next unit's loads
     interleaved), scores of 1 with softmax of 0, output of 0 with softmax of
     1, output of 1."""
     q0, q1, p0, p1 = qk_frags(0), qk_frags(1), pv_frags(0), pv_frags(1)
     frags = q0 + q1 + p0 + p1
-    dma = [ins for g in dma_groups() for ins in g]
-    fillers = [(0, 35, dma),
-               (36 + 3, 71 - 1, softmax_code(0)),
-               (72 + 3, 103 - 3, softmax_code(1))]
+    groups = dma_groups()
+    n1, n2, n3 = DMA_SPLIT
+    assert n1 + n2 + n3 == len(groups)
+    sm = softmax_lean if lean else softmax_code
+    fillers = [(0, 35, [ins for g in groups[:n1] for ins in g]),
+               (36 + 3, 71 - 1, merge_filler(sm(0), groups[n1:n1 + n2])),
+               (72 + 3, 103 - 3, merge_filler(sm(1), groups[n1 + n2:]))]
     emit_phases(a, frags, {"A": -1, "B": 71 - NB}, fillers, marks={35: 1, 71: 2, 103: 3})
+
+
+def merge_filler(ins, groups):
+    """Spread the load groups evenly through an instruction list (order kept)."""
+    if not groups:
+        return list(ins)
+    out, step = [], len(ins) / len(groups)
+    gi = 0
+    for k, x in enumerate(ins):
+        while gi < len(groups) and k >= gi * step:
+            out += groups[gi]
+            gi += 1
+        out.append(x)
+    for g in groups[gi:]:
+        out += g
+    return out
 
 
 def unit_half(a):
@@ -839,6 +950,7 @@ def kernel():
     a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
       f"s_mov_b32 {s(S_SLOT)}, 0")
     issue_unit(a, S_UCUR, S_SLOT)
+    prefetch_next(a, S_UCUR)
     # ------------------------------------------------ segments
     a.label(".Lseg")
     load_len(a, S_CLEN, S_CSEQ)
@@ -881,30 +993,28 @@ def kernel():
     a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
       f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
       f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
-      f"v_mov_b32 {vreg(V_LRUN[1])}, 0")
+      f"v_mov_b32 {vreg(V_LRUN[1])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
+      f"s_mov_b32 {s(S_EXACT)}, 0")
     zero_o(a)
     # ------------------------------------------------ units of the segment
     # On entry the loads of unit S_UCUR into its slot are in flight.
     a.label(".Lunit")
-    nonext, looked = a.new_label("nonext"), a.new_label("looked")
     a(f"s_mov_b64 {sp(S_OVF)}, 0",
       f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
-      f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1",
-      f"s_add_u32 s{T + 20}, {s(S_UCUR)}, 1",
-      f"s_cmp_lt_u32 s{T + 20}, {s(S_UB)}",
-      f"s_cbranch_scc0 {nonext}")
-    loader_advance(a, T + 20)
-    loader_lookup(a, T + 20, wait=False)
-    a(f"s_branch {looked}")
-    a.label(nonext)
-    a(f"s_mov_b32 {s(S_NVALID)}, 0")   # no next unit: a harmless copy of row 0 of page 0
-    a.label(looked)
-    # this unit's rows have landed (own loads) and every wave is past the previous unit
+      f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
+    # this unit's rows have landed (own loads), the table prefetch too, and
+    # every wave is past the previous unit
     a(s_waitcnt_vm(0), s_waitcnt_lgkm(0), "s_barrier")
-    flag_check(a)
+    a(f"v_mov_b32 {vreg(V_T)}, {FLAG_ADDR}",
+      f"ds_read_b32 {vreg(V_T)}, {vreg(V_T)}")       # restart flag, checked below
+    take_prefetched(a)
     loader_page(a)
     a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
     dma_setup(a, T + 21)
+    a(f"s_add_u32 s{T + 19}, {s(S_UCUR)}, 1")
+    prefetch_next(a, T + 19)
     a(f"s_sub_u32 {s(S_ROW0)}, {s(S_UCUR)}, {s(S_CPRE)}",
       f"s_lshl_b32 {s(S_ROW0)}, {s(S_ROW0)}, 6",
       f"s_mul_i32 s{T}, {s(S_SLOT)}, {SLOT_BYTES}",
@@ -917,13 +1027,29 @@ def kernel():
         a(f"v_xor_b32 {vreg(V_UP + m)}, {32 * m}, {vreg(V_PV0)}",
           f"v_add_u32 {vreg(V_UP + m)}, s{T}, {vreg(V_UP + m)}")
     # rows of this unit this wave's query token sees: none, only the first 32, or more
-    half, none, uend = a.new_label("half"), a.new_label("none"), a.new_label("uend")
+    a(s_waitcnt_lgkm(0),
+      "s_nop 1",
+      f"v_readfirstlane_b32 s{T}, {vreg(V_T)}",
+      f"s_cmp_eq_u32 s{T}, 0",
+      "s_cbranch_scc0 .Lrestart")
+    # fully visible units after the first of the segment take the lean softmax
+    half, none, uend, classic = (a.new_label(x) for x in ("half", "none", "uend", "classic"))
     a(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
       f"s_cmp_le_i32 s{T}, 0",
       f"s_cbranch_scc1 {none}",
       f"s_cmp_le_i32 s{T}, 32",
-      f"s_cbranch_scc1 {half}")
-    unit_full(a)
+      f"s_cbranch_scc1 {half}",
+      f"s_cmp_lt_i32 s{T}, 64",
+      f"s_cbranch_scc1 {classic}",
+      f"s_max_u32 s{T + 1}, {s(S_UA)}, {s(S_CPRE)}",
+      f"s_cmp_eq_u32 {s(S_UCUR)}, s{T + 1}",
+      f"s_cbranch_scc1 {classic}",
+      f"s_cmp_eq_u32 {s(S_EXACT)}, 0",
+      f"s_cbranch_scc0 {classic}")
+    unit_full(a, lean=True)
+    a(f"s_branch {uend}")
+    a.label(classic)
+    unit_full(a, lean=False)
     a(f"s_branch {uend}")
     a.label(half)
     unit_half(a)
@@ -953,6 +1079,24 @@ def kernel():
     a.label(".Lrestart")
     a(s_waitcnt_vm(0), "s_barrier")   # every wave has read the flag; no loads in flight
     flag_write(a, 0)
+    # the re-run keeps the exact (max-based) reference for the whole segment, so
+    # every further restart raises m_ref past an observed maximum: at most one
+    # restart per sub-step whose max passes the reference
+    a(f"s_mov_b32 {s(S_EXACT)}, 1")
+    # a lean sub-step overflowed: m_ref += log2(peak sum of the head) + 27, at most 128 + 27
+    for h in range(2):
+        pk, t0, t1, lp = V_T, V_T + 1, V_T + 2, V_T + 3
+        a(f"v_mov_b32 {vreg(pk)}, {vreg(V_PEAK[h])}")
+        xor_reduce(a, pk, "v_max_f32", t0, t1)
+        a(f"v_log_f32 {vreg(lp)}, {vreg(pk)}",
+          f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(pk)}",
+          "s_nop 0",
+          f"v_min_f32 {vreg(lp)}, 0x43000000, {vreg(lp)}",          # 128
+          f"v_add_f32 {vreg(lp)}, 0x41d80000, {vreg(lp)}",          # + 27
+          f"v_add_f32 {vreg(lp)}, {vreg(V_MREF[h])}, {vreg(lp)}",
+          "s_nop 1",
+          f"v_cndmask_b32 {vreg(V_MREF[h])}, {vreg(V_MREF[h])}, {vreg(lp)}, vcc",
+          f"v_mov_b32 {vreg(V_PEAK[h])}, 0")
     a(f"s_max_u32 {s(S_UCUR)}, {s(S_UA)}, {s(S_CPRE)}",
       f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
       f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}",
@@ -964,6 +1108,7 @@ def kernel():
     a(f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
       f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
     issue_unit(a, S_UCUR, S_SLOT)
+    prefetch_next(a, S_UCUR)
     a("s_branch .Lunit")
     a.label(".Lkernel_end")
     a(s_waitcnt_vm(0), "s_endpgm")   # the last unit's spare copy must land before the LDS is released

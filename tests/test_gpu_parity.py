@@ -79,22 +79,25 @@ def test_sequences_with_no_visible_row(s_q):
         _run_and_check(inp, splits, f"empty rows s_q={s_q} splits={splits}")
 
 
-def test_scores_with_large_spread_restart_path():
+@pytest.mark.parametrize("factor", [16.0, 48.0])
+def test_scores_with_large_spread_restart_path(factor):
     # A few rows whose k^R part is a large multiple of head 0's q^R: head 0's
-    # score jumps ~100 log2 units above the first rows' maximum, past the
-    # kernel's fixed reference, which forces the restart path.  k^R does not
-    # enter the output, so the output stays on the scale of the latents.
+    # score jumps ~100 (factor 16) or ~300 (factor 48: 2^(z - m_ref) overflows
+    # fp32) log2 units above the first rows' maximum, past the kernel's
+    # reference, which forces the restart path, in a middle unit and in the
+    # last one.  k^R does not enter the output, so the output stays on the
+    # scale of the latents.
     inp = _small([300, 700], seed=6)
     for b in range(inp.batch):
         L = int(inp.seq_lens[b])
         for j in (L - 5, L // 2):
             page = int(inp.block_table[b, j // 64])
-            inp.cache[page, j % 64, 512:] = (inp.q_rope[b, 0, 0].float() * 16.0).to(torch.bfloat16)
+            inp.cache[page, j % 64, 512:] = (inp.q_rope[b, 0, 0].float() * factor).to(torch.bfloat16)
     # With the softmax concentrated on two rows, rounding P to bf16 (relative
     # 2^-9 per weight) moves out by up to about 2^-9 max|c|; allow 2^-8 max|c|.
     cmax = max(float(np.abs(O.sequence_rows(inp, b, int(inp.seq_lens[b]))[:, :512]).max()) for b in range(2))
     for splits in (1, 4):
-        _run_and_check(inp, splits, f"large spread splits={splits}", out_tol=2.0 ** -8 * cmax)
+        _run_and_check(inp, splits, f"large spread x{factor:g} splits={splits}", out_tol=2.0 ** -8 * cmax)
 
 
 def _partition_map(lens, num_splits):
