@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_decode_asm.cpp", "mla_combine.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode_asm.cpp", "mla_combine.hip"]
 ARCH = "gfx950"
 
 

@@ -35,10 +35,34 @@ from __future__ import annotations
 
 import sys
 
+SLOT_BYTES = 64 * 1152          # one page of bf16 rows = one LDS tile
+KARG_BYTES = 120                # kernel argument block (both kernels)
+
+# bf16 kernel: two tile slots, the restart flag after them
 KNAME = "mla_decode_bf16_gfx950"
-SLOT_BYTES = 64 * 1152          # one page of bf16 rows
-FLAG_ADDR = 2 * SLOT_BYTES      # restart flag (LDS)
+FP8 = False
+FLAG_ADDR = 2 * SLOT_BYTES
 LDS_BYTES = FLAG_ADDR + 16
+PAGE_BYTES = SLOT_BYTES         # global bytes of one page of the row array
+
+# fp8 kernel: one bf16 tile, two staging slots of raw pages (e4m3 codes, bf16
+# rope, fp32 scales), the current unit's scales as [block][row], the flag
+F8_CODES, F8_ROPE, F8_SCALES = 64 * 512, 64 * 128, 64 * 16
+F8_RAW = F8_CODES + F8_ROPE + F8_SCALES          # 41984
+F8_RAW0 = SLOT_BYTES
+F8_SCL = F8_RAW0 + 2 * F8_RAW                    # 157696
+F8_FLAG = F8_SCL + 1024
+
+
+def configure(fp8):
+    """Select the kernel the generator functions emit."""
+    global KNAME, FP8, FLAG_ADDR, LDS_BYTES, PAGE_BYTES
+    FP8 = fp8
+    if fp8:
+        KNAME, FLAG_ADDR, PAGE_BYTES = "mla_decode_fp8_gfx950", F8_FLAG, F8_CODES
+    else:
+        KNAME, FLAG_ADDR, PAGE_BYTES = "mla_decode_bf16_gfx950", 2 * SLOT_BYTES, SLOT_BYTES
+    LDS_BYTES = FLAG_ADDR + 16
 NEG_INF = "0xff800000"
 LN2 = "0x3f317218"
 OVF_SUM = "0x5f800000"   # 2^64
@@ -87,12 +111,14 @@ S_EXEC = 58              # s58:59
 S_TMP = 60               # s60..s81 scratch
 S_OVF = 82               # s82:83 lanes whose max passed the reference in this unit
 S_ENTRY, S_NVALID, S_DMALDS, S_SMT = 84, 85, 86, 87
+S_FSC, S_FRO = 92, 94    # fp8 scales / rope arrays (s92:93, s94:95)
+S_CURVALID = 96          # fp8: valid rows of the unit being dequantized
 S_EXACT = 88             # 1 after a restart: the rest of the segment keeps the max-based softmax
 S_NV2, S_ENT2 = 89, 90   # prefetched valid rows / page of the unit after next (-1: page in V_ENT)
 S_DPAGE = 80             # s80:81 page address + chunk-group offset of one load (S_TMP + 20, + 21)
 # loads of the next unit issued in phases 1, 2, 3 of a full unit
 DMA_SPLIT = (8, 6, 4)
-S_MAX = 96
+S_MAX = 98
 
 
 def temps(*regs, pool):
@@ -339,8 +365,8 @@ def loader_page(a):
     a(f"s_mov_b64 {sp(S_PAGE)}, {sp(S_ROWS)}",
       f"s_cmp_gt_i32 {s(S_NVALID)}, 0",
       f"s_cbranch_scc0 {done}",
-      f"s_mul_i32 s{T + 5}, {s(S_ENTRY)}, {SLOT_BYTES}",
-      f"s_mul_hi_u32 s{T + 6}, {s(S_ENTRY)}, {SLOT_BYTES}",
+      f"s_mul_i32 s{T + 5}, {s(S_ENTRY)}, {PAGE_BYTES}",
+      f"s_mul_hi_u32 s{T + 6}, {s(S_ENTRY)}, {PAGE_BYTES}",
       f"s_add_u32 s{S_PAGE}, {s(S_ROWS)}, s{T + 5}",
       f"s_addc_u32 s{S_PAGE + 1}, s{S_ROWS + 1}, s{T + 6}")
     a.label(done)
@@ -871,11 +897,10 @@ def flag_check(a):
       "s_cbranch_scc0 .Lrestart")
 
 
-def kernel():
+def kernel(fp8=False):
+    configure(fp8)
     a = Asm()
     a.lines += [
-        '\t.amdgcn_target "amdgcn-amd-amdhsa--gfx950"',
-        "\t.amdhsa_code_object_version 6",
         "\t.text",
         f"\t.globl {KNAME}",
         "\t.p2align 8",
@@ -1123,7 +1148,7 @@ def descriptor():
 	.amdhsa_kernel {KNAME}
 		.amdhsa_group_segment_fixed_size {LDS_BYTES}
 		.amdhsa_private_segment_fixed_size 0
-		.amdhsa_kernarg_size 104
+		.amdhsa_kernarg_size {KARG_BYTES}
 		.amdhsa_user_sgpr_count 2
 		.amdhsa_user_sgpr_kernarg_segment_ptr 1
 		.amdhsa_system_sgpr_workgroup_id_x 1
@@ -1137,49 +1162,53 @@ def descriptor():
 		.amdhsa_ieee_mode 1
 		.amdhsa_dx10_clamp 1
 	.end_amdhsa_kernel
-
-	.amdgpu_metadata
----
-amdhsa.kernels:
-  - .agpr_count:     256
-    .args:
-      - {{ .address_space: global, .offset: 0, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 8, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 16, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 24, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 32, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 40, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 48, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 56, .size: 8, .value_kind: global_buffer }}
-      - {{ .address_space: global, .offset: 64, .size: 8, .value_kind: global_buffer }}
-      - {{ .offset: 72, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 76, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 80, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 84, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 88, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 92, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 96, .size: 4, .value_kind: by_value }}
-      - {{ .offset: 100, .size: 4, .value_kind: by_value }}
-    .group_segment_fixed_size: {LDS_BYTES}
-    .kernarg_segment_align: 8
-    .kernarg_segment_size: 104
-    .max_flat_workgroup_size: 256
-    .name:           {KNAME}
-    .private_segment_fixed_size: 0
-    .sgpr_count:     {S_MAX + 6}
-    .symbol:         {KNAME}.kd
-    .vgpr_count:     512
-    .wavefront_size: 64
-amdhsa.target:   amdgcn-amd-amdhsa--gfx950
-amdhsa.version:
-  - 1
-  - 2
-...
-	.end_amdgpu_metadata
+	.text
 """.splitlines()
+
+
+def metadata(kernels):
+    """Code-object metadata for the given (name, lds_bytes) kernels, which all
+    take the same argument block: 11 pointers, then 8 scalars."""
+    lines = ["\t.amdgpu_metadata", "---", "amdhsa.kernels:"]
+    for name, lds in kernels:
+        lines += [f"  - .agpr_count:     256", "    .args:"]
+        for k in range(9):
+            lines.append(f"      - {{ .address_space: global, .offset: {8 * k}, .size: 8, .value_kind: global_buffer }}")
+        for k in range(8):
+            lines.append(f"      - {{ .offset: {72 + 4 * k}, .size: 4, .value_kind: by_value }}")
+        for k in range(2):
+            lines.append(f"      - {{ .address_space: global, .offset: {104 + 8 * k}, .size: 8, .value_kind: global_buffer }}")
+        lines += [f"    .group_segment_fixed_size: {lds}",
+                  "    .kernarg_segment_align: 8",
+                  f"    .kernarg_segment_size: {KARG_BYTES}",
+                  "    .max_flat_workgroup_size: 256",
+                  f"    .name:           {name}",
+                  "    .private_segment_fixed_size: 0",
+                  f"    .sgpr_count:     {S_MAX + 6}",
+                  f"    .symbol:         {name}.kd",
+                  "    .vgpr_count:     512",
+                  "    .wavefront_size: 64"]
+    lines += ["amdhsa.target:   amdgcn-amd-amdhsa--gfx950", "amdhsa.version:", "  - 1", "  - 2", "...",
+              "\t.end_amdgpu_metadata"]
+    return lines
+
+
+def code_object_source():
+    """Both kernels (bf16 and fp8 cache) in one assembly file."""
+    import re
+    parts, kernels = ['\t.amdgcn_target "amdgcn-amd-amdhsa--gfx950"', "\t.amdhsa_code_object_version 6"], []
+    for fp8 in (False, True):
+        text = kernel(fp8)
+        tag = "f8" if fp8 else "bf"
+        code, desc = text.split("\t.rodata", 1)
+        code = re.sub(r"\.L(\w+)", lambda m: f".L{tag}_{m.group(1)}", code)   # labels local to each kernel
+        parts += [code, "\t.rodata" + desc]
+        kernels.append((KNAME, LDS_BYTES))
+    configure(False)
+    return "\n".join(parts) + "\n" + "\n".join(metadata(kernels)) + "\n"
 
 
 if __name__ == "__main__":
     out = sys.argv[1] if len(sys.argv) > 1 else "mla_decode_gfx950.s"
     with open(out, "w") as f:
-        f.write(kernel())
+        f.write(code_object_source())

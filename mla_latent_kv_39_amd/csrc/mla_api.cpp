@@ -3,7 +3,6 @@
 #include <atomic>
 #include <climits>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 
 #include "../../include/mla.h"
@@ -81,13 +80,8 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;
   p.num_parts = num_splits;
-  hipError_t err;
-  if (cache->dtype == MLA_CACHE_BF16)
-    err = std::getenv("MLA_DEV_HIP_DECODE") ? mla::launch_decode_bf16(p, s_q, stream)
-                                             : mla::launch_decode_bf16_asm(p, s_q, stream);
-  else
-    err = mla::launch_decode_fp8(p, s_q, stream);
-  if (err == hipErrorNotSupported) return MLA_ERR_UNSUPPORTED;
+  if (cache->dtype == MLA_CACHE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;   // fp8 kernel not wired yet
+  const hipError_t err = mla::launch_decode(p, s_q, cache->dtype == MLA_CACHE_FP8_E4M3, stream);
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

@@ -1,6 +1,6 @@
-// Host launcher of the assembly decode kernel (generated by gen_decode_gfx950.py,
-// assembled into a code object that is embedded in libmla.so and loaded once
-// per device on first use).
+// Host launcher of the assembly decode kernels (bf16 and fp8 cache), generated
+// by gen_decode_gfx950.py and assembled into one code object that is embedded
+// in libmla.so and loaded once per device on first use.
 #include <mutex>
 
 #include "mla_internal.h"
@@ -30,35 +30,43 @@ struct AsmArgs {
   int32_t heads_per_block;
   int32_t head_blocks;
   int32_t log2_parts;
+  const float* fp8_scales;  // fp8 cache only
+  const void* fp8_rope;     // fp8 cache only
 };
-static_assert(sizeof(AsmArgs) == 104, "kernel argument layout");
+static_assert(sizeof(AsmArgs) == 120, "kernel argument layout");
 
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 hipModule_t g_mod[kMaxDevices];
-hipFunction_t g_fn[kMaxDevices];
+hipFunction_t g_fn[kMaxDevices][2];   // [bf16, fp8]
 
-hipError_t decode_function(hipFunction_t* fn) {
+hipError_t decode_function(bool fp8, hipFunction_t* fn) {
   int dev = -1;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_fn[dev]) {
-    err = hipModuleLoadData(&g_mod[dev], mla_decode_gfx950_co);
+  if (!g_mod[dev]) {
+    hipModule_t mod;
+    err = hipModuleLoadData(&mod, mla_decode_gfx950_co);
     if (err != hipSuccess) return err;
-    err = hipModuleGetFunction(&g_fn[dev], g_mod[dev], "mla_decode_bf16_gfx950");
-    if (err != hipSuccess) return err;
+    err = hipModuleGetFunction(&g_fn[dev][0], mod, "mla_decode_bf16_gfx950");
+    if (err == hipSuccess) err = hipModuleGetFunction(&g_fn[dev][1], mod, "mla_decode_fp8_gfx950");
+    if (err != hipSuccess) {
+      hipModuleUnload(mod);
+      return err;
+    }
+    g_mod[dev] = mod;
   }
-  *fn = g_fn[dev];
+  *fn = g_fn[dev][fp8 ? 1 : 0];
   return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16_asm(const DecodeParams& p, int s_q, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int s_q, bool fp8, hipStream_t stream) {
   hipFunction_t fn;
-  hipError_t err = decode_function(&fn);
+  hipError_t err = decode_function(fp8, &fn);
   if (err != hipSuccess) return err;
   AsmArgs a;
   a.q_abs = p.q_abs;
@@ -80,6 +88,8 @@ hipError_t launch_decode_bf16_asm(const DecodeParams& p, int s_q, hipStream_t st
   int lg = 0;
   while ((1 << lg) < p.num_parts) ++lg;
   a.log2_parts = lg;
+  a.fp8_scales = p.fp8_scales;
+  a.fp8_rope = p.fp8_rope;
   size_t size = sizeof(a);
   void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size, HIP_LAUNCH_PARAM_END};
   return hipModuleLaunchKernel(fn, (unsigned)(p.num_parts * a.head_blocks), 1, 1, 256, 1, 1, 0, stream, nullptr,

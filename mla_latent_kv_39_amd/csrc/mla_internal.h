@@ -47,9 +47,7 @@ inline int heads_per_block(int s_q) { return s_q == 1 ? 128 : 64; }
 
 // Kernel launchers (defined next to the kernels).  They return the HIP error
 // of the launch.
-hipError_t launch_decode_bf16(const DecodeParams& p, int s_q, hipStream_t stream);
-hipError_t launch_decode_bf16_asm(const DecodeParams& p, int s_q, hipStream_t stream);
-hipError_t launch_decode_fp8(const DecodeParams& p, int s_q, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int s_q, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -1,4 +1,5 @@
-// Work partition map shared by the decode and combine kernels.
+// Work partition map of the decode kernels (which compute it in assembly with
+// the same formulas) and the combine kernel.
 //
 // The rows of the whole batch are cut into 64-row units (one cache page each),
 // sequence after sequence: sequence b owns units [u0(b), u0(b) + units(b)),
@@ -23,25 +24,6 @@ __device__ __forceinline__ int part_start(int p, int total_units, int parts) {
 // The partition whose range holds unit u: the largest p with start(p) <= u.
 __device__ __forceinline__ int part_of_unit(int u, int total_units, int parts) {
   return (int)((((long long)u + 1) * parts - 1) / total_units);
-}
-
-// Block-wide exclusive scan of per-thread counts over 256 threads.
-// Returns the exclusive prefix of this thread; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan_256(int v, int* s_buf, int* total) {
-  const int tid = threadIdx.x;
-  s_buf[tid] = v;
-  __syncthreads();
-#pragma unroll
-  for (int off = 1; off < 256; off <<= 1) {
-    int add = tid >= off ? s_buf[tid - off] : 0;
-    __syncthreads();
-    s_buf[tid] += add;
-    __syncthreads();
-  }
-  int incl = s_buf[tid];
-  *total = s_buf[255];
-  __syncthreads();
-  return incl - v;
 }
 
 }  // namespace mla
