@@ -115,7 +115,8 @@ def main(argv=None):
     rows, nbytes, flops = algorithmic_work(inp)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    splits = args.num_splits or (inp.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q))
+    # the partition count only changes how the work is cut (the merge is exact): fill the GPU
+    splits = args.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q)
 
     # rotate enough copies of cache + queries that the MALL cannot hold them across steps
     footprint = inp.cache.numel() * inp.cache.element_size() + inp.q_absorbed.numel() * 2 + inp.q_rope.numel() * 2

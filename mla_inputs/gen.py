@@ -151,6 +151,8 @@ def make_inputs(workload, seed: int = 0, **overrides) -> MlaInputs:
             for u in range(blocks_per_seq[b], max_blocks):
                 tail.append((b * max_blocks + u, 0))
 
+    if cfg["cache"] not in ("bf16", "fp8_e4m3"):
+        raise ValueError(f"unknown cache type {cfg['cache']!r} (bf16 or fp8_e4m3)")
     fp8 = cfg["cache"] == "fp8_e4m3"
     if fp8:
         cache = torch.empty((num_pages, BLOCK_SIZE, D_LATENT), dtype=torch.uint8)

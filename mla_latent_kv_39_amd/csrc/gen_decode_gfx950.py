@@ -541,13 +541,15 @@ def emit_phases(a, frags, lead, fillers, marks=None):
             a.comment(f"phase {marks[p]} issued")
 
 
-def softmax_code(ss):
+def softmax_code(ss, S=None, P=None, tmp=None):
     """Softmax of sub-step ss (log2 domain) as a plain instruction list:
     mask rows at or past the visible count, running reference m_ref (first
     max + 30; a max more than 64 above it raises it and flags a restart),
-    P = 2^(scale S - m_ref), row sums, bf16 pack into P[ss]."""
-    S, P = V_S[ss], V_P[ss]
-    m, t0, t1, ref = V_SMT[ss]
+    P = 2^(scale S - m_ref), row sums, bf16 pack into P (kept in S as fp32
+    when P is None)."""
+    if S is None:
+        S, P, tmp = V_S[ss], V_P[ss], V_SMT[ss]
+    m, t0, t1, ref = tmp
     x = Asm()
     T = S_SMT
     # lane (g, r16) holds rows 16tb + 4g + i: visible iff 16tb + i < nvis - row0 - 32ss - 4g
@@ -598,22 +600,24 @@ def softmax_code(ss):
           f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
           f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}",
           f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}")
-        p = P + 4 * h
-        x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
+        if P is not None:
+            p = P + 4 * h
+            x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
     return x.lines
 
 
-def softmax_lean(ss):
+def softmax_lean(ss, S=None, P=None, tmp=None):
     """Softmax of a fully visible sub-step once the segment's reference is
     set: P = 2^(scale S - m_ref), row sums, bf16 pack.  No max: a lane whose
     8-row sum passes 2^64 (the largest score more than ~64 above m_ref) flags a
     restart, and V_PEAK keeps the largest such sum so that the restart can
     raise m_ref past it."""
-    S, P = V_S[ss], V_P[ss]
-    t0, t1 = V_SMT[ss][0], V_SMT[ss][1]
+    if S is None:
+        S, P, tmp = V_S[ss], V_P[ss], V_SMT[ss]
+    t0, t1 = tmp[0], tmp[1]
     x = Asm()
     for h in range(2):
         regs = [S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
@@ -634,11 +638,12 @@ def softmax_lean(ss):
           f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(t0)}",
           f"v_max_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
           f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc")
-        p = P + 4 * h
-        x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
-          f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
+        if P is not None:
+            p = P + 4 * h
+            x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
     return x.lines
 
 
@@ -701,6 +706,309 @@ def emit_phases_split(a, p0, sm):
             for r in g.reads:
                 g.read_ids.append(lds.issue())
                 a.lines.append(r)
+
+
+# ============================================================== fp8 cache
+# The fp8 kernel keeps one bf16 tile (same layout as above) and two staging
+# slots of raw pages.  Per unit: the raw pages of the next unit are loaded
+# into the free staging slot; the current unit's e4m3 codes are widened to
+# bf16 (exact) into the tile, with the rows past the sequence zeroed, and its
+# scales are stored as [block][row] fp32.  Scores then take the four 128-wide
+# latent blocks one at a time: T = C8_blk Q_blk by MFMA, S += T * s_blk in
+# fp32, so that z = scale * (sum_blk s_blk (q_blk . c8_blk) + q^R . k^R) holds
+# with the e4m3 values exact; the output takes P * s_blk (rounded to bf16 like
+# P in the bf16 kernel) against the widened codes, block by block.
+# (DeepSeek-V3 详解, yudonglee.me, §4.2: 1x128 fine-grained scaling, E4M3.)
+F8_S = V_S[0]           # scores, then probabilities (fp32) of the current sub-step
+F8_T = V_S[1]           # block accumulator; scale values and products in the output phase
+F8_P = V_P              # P * s_blk (bf16) of even / odd blocks
+V_DWE0, V_L16, V_CSRC, V_SCLB = V_LDA, V_LDB, V_LCA, V_LCB   # fp8 lane constants
+S_RPAGE, S_SPAGE = S_TMP + 8, S_TMP + 10                       # rope / scale pages of the next unit
+
+
+def lane_constants_fp8(a):
+    """fp8 lane constants (after the shared ones).
+    V_DWE0: tile offset of (row-in-block L>>3, chunk slot of L&7) for an even
+    row group (the odd one is V_DWE0 ^ 32); V_L16 = 16 L; V_CSRC: byte offset
+    in a page of e4m3 codes read by lane L of a staging load (rows (L&31)>>2,
+    8-byte chunks 2 (L&3) and +1 of chunk group L>>5); V_SCLB: LDS address of
+    the scales of rows 4g .. 4g+3 (block 0)."""
+    t0, t1 = V_T, V_T + 1
+    a(f"v_lshrrev_b32 {vreg(t0)}, 3, {vreg(V_LANE)}",
+      f"v_lshl_add_u32 {vreg(V_DWE0)}, {vreg(t0)}, 7, {vreg(V_LCA)}",     # uses LCA before it is replaced
+      f"v_lshlrev_b32 {vreg(V_L16)}, 4, {vreg(V_LANE)}",
+      f"v_bfe_u32 {vreg(t0)}, {vreg(V_LANE)}, 2, 3",                     # rb = (L & 31) >> 2
+      f"v_lshlrev_b32 {vreg(t0)}, 9, {vreg(t0)}",
+      f"v_lshrrev_b32 {vreg(t1)}, 5, {vreg(V_LANE)}",                     # Ksel
+      f"v_lshl_add_u32 {vreg(t0)}, {vreg(t1)}, 6, {vreg(t0)}",
+      f"v_and_b32 {vreg(t1)}, 3, {vreg(V_LANE)}",
+      f"v_lshl_add_u32 {vreg(V_CSRC)}, {vreg(t1)}, 4, {vreg(t0)}",        # + 16 (L & 3)
+      f"v_lshlrev_b32 {vreg(V_SCLB)}, 4, {vreg(V_G)}",
+      f"v_add_u32 {vreg(V_SCLB)}, {F8_SCL}, {vreg(V_SCLB)}")
+
+
+def loader_page_fp8(a):
+    """S_PAGE / S_RPAGE / S_SPAGE = the code, rope and scale pages of S_ENTRY
+    (page 0 of each array when the unit holds no rows)."""
+    T = S_TMP
+    done = a.new_label("pgdone")
+    a(f"s_mov_b64 {sp(S_PAGE)}, {sp(S_ROWS)}",
+      f"s_mov_b64 {sp(S_RPAGE)}, {sp(S_FRO)}",
+      f"s_mov_b64 {sp(S_SPAGE)}, {sp(S_FSC)}",
+      f"s_cmp_gt_i32 {s(S_NVALID)}, 0",
+      f"s_cbranch_scc0 {done}")
+    for dst, base, nbytes in ((S_PAGE, S_ROWS, F8_CODES), (S_RPAGE, S_FRO, F8_ROPE), (S_SPAGE, S_FSC, F8_SCALES)):
+        a(f"s_mul_i32 s{T + 5}, {s(S_ENTRY)}, {nbytes}",
+          f"s_mul_hi_u32 s{T + 6}, {s(S_ENTRY)}, {nbytes}",
+          f"s_add_u32 s{dst}, s{base}, s{T + 5}",
+          f"s_addc_u32 s{dst + 1}, s{base + 1}, s{T + 6}")
+    a.label(done)
+
+
+def dma_fp8(a, slot_sgpr):
+    """Copy the rows 16w .. 16w+15 of the next unit's raw pages into staging
+    slot `slot`: 8 loads of codes (8 rows x 128 B each), 2 of rope, 1 of
+    scales (16 lanes)."""
+    T = S_TMP
+    m0c, m0r, m0s = T + 12, T + 13, T + 14
+    a(f"s_mul_i32 s{m0c}, {s(slot_sgpr)}, {F8_RAW}",
+      f"s_add_u32 s{m0c}, s{m0c}, {F8_RAW0}",
+      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 11",                 # 2048 w
+      f"s_add_u32 s{m0r}, s{m0c}, {F8_CODES}",
+      f"s_add_u32 s{m0r}, s{m0r}, s{T + 15}",
+      f"s_add_u32 s{S_RPAGE}, s{S_RPAGE}, s{T + 15}",
+      f"s_addc_u32 s{S_RPAGE + 1}, s{S_RPAGE + 1}, 0",
+      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 13",                 # 8192 w
+      f"s_add_u32 s{m0c}, s{m0c}, s{T + 15}",
+      f"s_add_u32 s{S_PAGE}, s{S_PAGE}, s{T + 15}",
+      f"s_addc_u32 s{S_PAGE + 1}, s{S_PAGE + 1}, 0",
+      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 8",                  # 256 w
+      f"s_add_u32 s{S_SPAGE}, s{S_SPAGE}, s{T + 15}",
+      f"s_addc_u32 s{S_SPAGE + 1}, s{S_SPAGE + 1}, 0",
+      f"s_mul_i32 s{m0s}, {s(slot_sgpr)}, {F8_RAW}",
+      f"s_add_u32 s{m0s}, s{m0s}, {F8_RAW0 + F8_CODES + F8_ROPE}",
+      f"s_add_u32 s{m0s}, s{m0s}, s{T + 15}")
+    for j in range(8):
+        a(f"s_add_u32 s{S_DPAGE}, s{S_PAGE}, {(j >> 2) * 4096 + (j & 3) * 128}",
+          f"s_addc_u32 s{S_DPAGE + 1}, s{S_PAGE + 1}, 0",
+          f"s_add_u32 m0, s{m0c}, {1024 * j}",
+          "s_nop 0",
+          f"global_load_lds_dwordx4 {vreg(V_CSRC)}, {sp(S_DPAGE)}")
+    for i in range(2):
+        a(f"s_add_u32 s{S_DPAGE}, s{S_RPAGE}, {1024 * i}",
+          f"s_addc_u32 s{S_DPAGE + 1}, s{S_RPAGE + 1}, 0",
+          f"s_add_u32 m0, s{m0r}, {1024 * i}",
+          "s_nop 0",
+          f"global_load_lds_dwordx4 {vreg(V_L16)}, {sp(S_DPAGE)}")
+    a(f"s_mov_b64 exec, 0xffff",
+      f"s_mov_b32 m0, s{m0s}",
+      "s_nop 0",
+      f"global_load_lds_dwordx4 {vreg(V_L16)}, {sp(S_SPAGE)}",
+      "s_mov_b64 exec, -1")
+
+
+def issue_unit_fp8(a, u_sgpr, slot_sgpr):
+    """Stand-alone staging copy of unit u (prologue and restart)."""
+    loader_advance(a, u_sgpr)
+    loader_lookup(a, u_sgpr, wait=True)
+    loader_page_fp8(a)
+    dma_fp8(a, slot_sgpr)
+
+
+def dequant_fp8(a):
+    """Rows 16w .. 16w+15 of the current unit: staging slot S_SLOT -> bf16
+    tile (codes widened exactly, rows at or past S_CURVALID zeroed), rope
+    copied, scales transposed to [block][row].  Ends with the LDS writes in
+    flight."""
+    T = S_TMP
+    lds = LdsOrder()
+    lds.issue()                                 # the restart-flag read issued before
+    raw = T + 12
+    mk = (T + 16, T + 18)                       # row masks of the two row groups (SGPR pairs)
+    rdb, w0, w1, t0 = V_B, V_B + 1, V_B + 2, V_B + 3      # output-ring registers are free here
+    a(f"s_mul_i32 s{raw}, {s(S_SLOT)}, {F8_RAW}",
+      f"s_add_u32 s{raw}, s{raw}, {F8_RAW0}",
+      f"s_lshl_b32 s{T + 13}, {s(S_WAVE)}, 13",
+      f"s_add_u32 s{T + 13}, s{raw}, s{T + 13}",             # raw + 8192 w
+      f"v_lshlrev_b32 {vreg(rdb)}, 3, {vreg(V_LANE)}",
+      f"v_add_u32 {vreg(rdb)}, s{T + 13}, {vreg(rdb)}",
+      f"s_lshl_b32 s{T + 14}, {s(S_WAVE)}, 11",              # 2048 w
+      f"v_add_u32 {vreg(w0)}, s{T + 14}, {vreg(V_DWE0)}",
+      f"v_xor_b32 {vreg(w1)}, 32, {vreg(V_DWE0)}",
+      f"s_add_u32 s{T + 15}, s{T + 14}, 1024",
+      f"v_add_u32 {vreg(w1)}, s{T + 15}, {vreg(w1)}",
+      # row 16w + 8 Rsel + (L >> 3) < valid
+      f"v_lshrrev_b32 {vreg(t0)}, 3, {vreg(V_LANE)}",
+      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 4",
+      f"v_add_u32 {vreg(t0)}, s{T + 15}, {vreg(t0)}",
+      f"v_cmp_gt_i32 s[{mk[0]}:{mk[0] + 1}], {s(S_CURVALID)}, {vreg(t0)}",
+      f"v_add_u32 {vreg(t0)}, 8, {vreg(t0)}",
+      f"v_cmp_gt_i32 s[{mk[1]}:{mk[1] + 1}], {s(S_CURVALID)}, {vreg(t0)}")
+    # codes: 16 reads of 8 bytes per lane up front (v16..v47), 4 output sets (v48..v63)
+    rid = []
+    for n in range(16):
+        rsel, kk = divmod(n, 8)
+        d = 16 + 2 * n
+        a(f"ds_read_b64 {vr(d, 2)}, {vreg(rdb)} offset:{(rsel * 4 + kk // 2) * 1024 + (kk & 1) * 512}")
+        rid.append(lds.issue())
+    for n in range(16):
+        rsel, kk = divmod(n, 8)
+        d, o = 16 + 2 * n, 48 + 4 * (n % 4)
+        m = f"s[{mk[rsel]}:{mk[rsel] + 1}]"
+        a.lines += lds.wait(rid[n])
+        a(f"v_cndmask_b32 {vreg(d)}, 0, {vreg(d)}, {m}",
+          f"v_cndmask_b32 {vreg(d + 1)}, 0, {vreg(d + 1)}, {m}",
+          f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o)}, {vreg(d)}, 1.0",
+          f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 1)}, {vreg(d)}, 1.0 op_sel:[1,0,0]",
+          f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 2)}, {vreg(d + 1)}, 1.0",
+          f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 3)}, {vreg(d + 1)}, 1.0 op_sel:[1,0,0]",
+          "s_nop 1",
+          f"ds_write_b128 {vreg(w1 if rsel else w0)}, {vr(o, 4)} offset:{8192 * kk}")
+        lds.issue()
+    # rope: rows 16w + 8 Rsel + (L >> 3), chunk 64 + (L & 7)
+    rrb = V_B + 4
+    a(f"s_add_u32 s{T + 13}, s{raw}, {F8_CODES}",
+      f"s_lshl_b32 s{T + 14}, {s(S_WAVE)}, 11",
+      f"s_add_u32 s{T + 13}, s{T + 13}, s{T + 14}",
+      f"v_add_u32 {vreg(rrb)}, s{T + 13}, {vreg(V_L16)}")
+    rr = []
+    for rsel in range(2):
+        d = 64 + 8 + 4 * rsel
+        a(f"ds_read_b128 {vr(d, 4)}, {vreg(rrb)} offset:{1024 * rsel}")
+        rr.append(lds.issue())
+    for rsel in range(2):
+        d = 64 + 8 + 4 * rsel
+        m = f"s[{mk[rsel]}:{mk[rsel] + 1}]"
+        a.lines += lds.wait(rr[rsel])
+        for q in range(4):
+            a(f"v_cndmask_b32 {vreg(d + q)}, 0, {vreg(d + q)}, {m}")
+        a(f"v_add_u32 {vreg(t0)}, 0x10000, {vreg(w1 if rsel else w0)}",
+          "s_nop 1",
+          f"ds_write_b128 {vreg(t0)}, {vr(d, 4)}")
+        lds.issue()
+        if rsel == 0:
+            t0 = V_B + 5
+    # scales of rows 16w + L (lanes 0..15) -> [block][row]
+    sc, sa, st = 80, V_B + 6, V_B + 7
+    a(f"s_add_u32 s{T + 13}, s{raw}, {F8_CODES + F8_ROPE}",
+      f"s_lshl_b32 s{T + 14}, {s(S_WAVE)}, 8",
+      f"s_add_u32 s{T + 13}, s{T + 13}, s{T + 14}",
+      "s_mov_b64 exec, 0xffff",
+      f"v_add_u32 {vreg(st)}, s{T + 13}, {vreg(V_L16)}",
+      f"ds_read_b128 {vr(sc, 4)}, {vreg(st)}")
+    r = lds.issue()
+    a(f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 4",
+      f"v_add_u32 {vreg(st)}, s{T + 15}, {vreg(V_LANE)}",       # row 16w + L
+      f"v_cmp_gt_i32 vcc, {s(S_CURVALID)}, {vreg(st)}",
+      f"v_lshlrev_b32 {vreg(sa)}, 2, {vreg(st)}",
+      f"v_add_u32 {vreg(sa)}, {F8_SCL}, {vreg(sa)}")
+    a.lines += lds.wait(r)
+    for q in range(4):
+        a(f"v_cndmask_b32 {vreg(sc + q)}, 0, {vreg(sc + q)}, vcc")
+    a("s_nop 1")
+    for q in range(4):
+        a(f"ds_write_b32 {vreg(sa)}, {vreg(sc + q)} offset:{256 * q}")
+    a("s_mov_b64 exec, -1")
+
+
+def f8_scale_reads(ss, blk, dst):
+    """Scales of rows 32ss + 16tb + 4g .. +3, block blk -> dst + 4tb (tb = 0, 1)."""
+    return [f"\tds_read_b128 {vr(dst + 4 * tb, 4)}, {vreg(V_SCLB)} offset:{blk * 256 + (32 * ss + 16 * tb) * 4}"
+            for tb in range(2)]
+
+
+def qk_fp8(a, ss):
+    """Scores of sub-step ss: k^R part into S, then per latent block
+    T = C8_blk Q_blk (MFMA) and S += T * s_blk (fp32)."""
+    order = [(16, tb) for tb in range(2)] + [(17, tb) for tb in range(2)]
+    order += [(ks, tb) for ks in range(16) for tb in range(2)]
+    frags = []
+    for n, (ks, tb) in enumerate(order):
+        acc = F8_S if ks >= 16 else F8_T
+        first = ks == 16 or (ks < 16 and ks % 4 == 0)
+        mf = []
+        for h in range(2):
+            d = acc + (2 * tb + h) * 4
+            qreg = V_Q + (2 * ks + h) * 4
+            c = "0" if first else vr(d, 4)
+            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(d, 4)}, {{buf}}, {vr(qreg, 4)}, {c}")
+        frags.append(Frag("A", V_A, NA, n, qk_read(ss, 2 * ks + tb), mf))
+    lds = LdsOrder()
+    for f in frags[:NA]:
+        for r in f.reads:
+            f.read_ids.append(lds.issue())
+            a.lines.append(r)
+    sc_ids = None
+    for p, f in enumerate(frags):
+        ks = order[p][0]
+        if ks < 16 and ks % 4 == 0 and order[p][1] == 0:      # block start: its scales
+            for r in f8_scale_reads(ss, ks // 4, F8_P[0]):
+                a.lines.append(r)
+            sc_ids = lds.issue(), lds.issue()
+        a.lines += lds.wait(max(f.read_ids))
+        a.lines += f.mfmas
+        if p + NA < len(frags):
+            g = frags[p + NA]
+            for r in g.reads:
+                g.read_ids.append(lds.issue())
+                a.lines.append(r)
+        if ks < 16 and ks % 4 == 3 and order[p][1] == 1:      # block end: S += T * s
+            a.lines += lds.wait(sc_ids[1])
+            a("s_nop 7", "s_nop 7", "s_nop 3")
+            for tb in range(2):
+                for h in range(2):
+                    for i in range(4):
+                        r = (2 * tb + h) * 4 + i
+                        a(f"v_fma_f32 {vreg(F8_S + r)}, {vreg(F8_T + r)}, {vreg(F8_P[0] + 4 * tb + i)}, {vreg(F8_S + r)}")
+    a("s_nop 7", "s_nop 7", "s_nop 3")
+
+
+def pv_fp8(a, ss):
+    """O^T += C8^T (P * s_blk)^T block by block (8 column blocks of 16 per latent block)."""
+    frags = pv_frags(ss)
+    lds = LdsOrder()
+    for f in frags[:NB]:
+        for r in f.reads:
+            f.read_ids.append(lds.issue())
+            a.lines.append(r)
+    for blk in range(4):
+        pb = F8_P[blk & 1]
+        for r in f8_scale_reads(ss, blk, F8_T):
+            a.lines.append(r)
+        sid = lds.issue(), lds.issue()
+        a.lines += lds.wait(sid[1])
+        for h in range(2):
+            regs = [F8_S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
+            prod = [F8_T + 8 + j for j in range(8)]
+            for j, r in enumerate(regs):
+                a(f"v_mul_f32 {vreg(prod[j])}, {vreg(r)}, {vreg(F8_T + j)}")
+            p = pb + 4 * h
+            a(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(prod[0])}, {vreg(prod[1])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(prod[2])}, {vreg(prod[3])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(prod[4])}, {vreg(prod[5])}",
+              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(prod[6])}, {vreg(prod[7])}")
+        a("s_nop 4")   # VALU writes of P -> MFMA reads
+        for cb in range(8 * blk, 8 * blk + 8):
+            f = frags[cb]
+            a.lines += lds.wait(max(f.read_ids))
+            for h in range(2):
+                o = (2 * cb + h) * 4
+                buf = V_B + 4 * (f.idx % NB)
+                a(f"v_mfma_f32_16x16x32_bf16 {ar(o, 4)}, {vr(buf, 4)}, {vr(pb + 4 * h, 4)}, {ar(o, 4)}")
+            if cb + NB < len(frags):
+                g = frags[cb + NB]
+                for r in g.reads:
+                    g.read_ids.append(lds.issue())
+                    a.lines.append(r)
+
+
+def substep_fp8(a, ss, lean):
+    qk_fp8(a, ss)
+    if lean:
+        a.lines += softmax_lean(ss, S=F8_S, P=None, tmp=(F8_T, F8_T + 1))
+    else:
+        a.lines += softmax_code(ss, S=F8_S, P=None, tmp=(F8_T, F8_T + 1, F8_T + 2, F8_T + 3))
+    pv_fp8(a, ss)
 
 
 def zero_o(a):
@@ -897,134 +1205,9 @@ def flag_check(a):
       "s_cbranch_scc0 .Lrestart")
 
 
-def kernel(fp8=False):
-    configure(fp8)
-    a = Asm()
-    a.lines += [
-        "\t.text",
-        f"\t.globl {KNAME}",
-        "\t.p2align 8",
-        f"\t.type {KNAME},@function",
-        f"{KNAME}:",
-    ]
+def unit_body_bf16(a):
+    """One unit of the bf16 kernel up to the unit-end label (returned)."""
     T = S_TMP
-    # ------------------------------------------------------------ prologue
-    a(f"s_load_dwordx16 s[{S_QA}:{S_QA + 15}], s[0:1], 0x0",
-      f"s_load_dwordx8 s[{S_LSE}:{S_LSE + 7}], s[0:1], 0x40",
-      f"s_load_dwordx2 s[{S_NHB}:{S_NHB + 1}], s[0:1], 0x60",
-      f"v_and_b32 {vreg(V_LANE)}, 63, {vreg(V_TID)}",
-      f"v_lshrrev_b32 {vreg(V_G)}, 4, {vreg(V_LANE)}",
-      f"v_and_b32 {vreg(V_R16)}, 15, {vreg(V_LANE)}",
-      f"v_lshrrev_b32 {vreg(V_T)}, 6, {vreg(V_TID)}",
-      "s_nop 1",
-      f"v_readfirstlane_b32 {s(S_WAVE)}, {vreg(V_T)}",
-      s_waitcnt_lgkm(0))
-    # ------------------------------------------------ workgroup -> (partition, head block)
-    plain, mapped = a.new_label("mapplain"), a.new_label("mapdone")
-    a(f"s_sub_u32 s{T}, {s(S_NHB)}, 1",
-      f"s_and_b32 s{T + 1}, {s(S_NPART)}, 7",
-      f"s_cmp_eq_u32 s{T + 1}, 0",
-      f"s_cbranch_scc0 {plain}",
-      # consecutive partitions on one XCD: xcd = wg & 7 owns partitions xcd*P/8 ..
-      f"s_lshr_b32 s{T + 1}, s2, 3",
-      f"s_and_b32 s{T + 2}, s2, 7",
-      f"s_lshr_b32 s{T + 3}, {s(S_NPART)}, 3",
-      f"s_mul_i32 s{T + 2}, s{T + 2}, s{T + 3}",
-      f"s_lshr_b32 {s(S_PART)}, s{T + 1}, s{T}",
-      f"s_add_u32 {s(S_PART)}, {s(S_PART)}, s{T + 2}",
-      f"s_and_b32 {s(S_HBLK)}, s{T + 1}, s{T}",
-      f"s_branch {mapped}")
-    a.label(plain)
-    a(f"s_lshr_b32 {s(S_PART)}, s2, s{T}",
-      f"s_and_b32 {s(S_HBLK)}, s2, s{T}")
-    a.label(mapped)
-    # ------------------------------------------------ partition map
-    seq_units_pass(a, find_first=False)
-    a(f"s_mul_i32 s{T}, {s(S_PART)}, {s(S_U)}",
-      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, {s(S_U)}",
-      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 {s(S_UA)}, s{T}",
-      f"s_add_u32 s{T + 2}, {s(S_PART)}, 1",
-      f"s_mul_i32 s{T}, s{T + 2}, {s(S_U)}",
-      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, {s(S_U)}",
-      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 {s(S_UB)}, s{T}",
-      f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
-      "s_cbranch_scc1 .Lkernel_end")
-    seq_units_pass(a, find_first=True)
-    # ------------------------------------------------ this wave's query rows
-    a(f"s_lshl_b32 s{T}, {s(S_WAVE)}, 5",
-      f"s_sub_u32 s{T + 1}, {s(S_HB)}, 1",
-      f"s_and_b32 s{T + 2}, s{T}, s{T + 1}",
-      f"s_mul_i32 s{T + 3}, {s(S_HBLK)}, {s(S_HB)}",
-      f"s_add_u32 {s(S_HEAD0)}, s{T + 2}, s{T + 3}",
-      f"s_ff1_i32_b32 s{T + 1}, {s(S_HB)}",
-      f"s_lshr_b32 {s(S_STOK)}, s{T}, s{T + 1}")
-    # ------------------------------------------------ lane-constant LDS offsets
-    lane_constants(a)
-    t = V_T
-    a(f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
-    # restart flag = 0
-    flag_write(a, 0)
-    a(s_waitcnt_lgkm(0), "s_barrier")
-    # ------------------------------------------------ loader cursor, first unit
-    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
-      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
-    load_len(a, S_LLEN, S_LSEQ)
-    units_of(a, S_LUNITS, S_LLEN)
-    a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
-      f"s_mov_b32 {s(S_SLOT)}, 0")
-    issue_unit(a, S_UCUR, S_SLOT)
-    prefetch_next(a, S_UCUR)
-    # ------------------------------------------------ segments
-    a.label(".Lseg")
-    load_len(a, S_CLEN, S_CSEQ)
-    units_of(a, S_CUNITS, S_CLEN)
-    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
-      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
-      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
-      # Q row index (c_seq * s_q + s_tok) * 128 + head0
-      f"s_mul_i32 s{T}, {s(S_CSEQ)}, {s(S_SQ)}",
-      f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
-      f"s_lshl_b32 s{T}, s{T}, 7",
-      f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
-      f"s_mov_b32 s{T + 1}, 0",
-      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 10",
-      f"s_add_u32 s{S_QBASE}, {s(S_QA)}, s{T + 2}",
-      f"s_addc_u32 s{S_QBASE + 1}, s{S_QA + 1}, s{T + 3}",
-      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 7",
-      f"s_add_u32 s{S_RBASE}, {s(S_QR)}, s{T + 2}",
-      f"s_addc_u32 s{S_RBASE + 1}, s{S_QR + 1}, s{T + 3}",
-      # lane offsets: latent (16h + r16)*1024 + 16g ; rope (16h + r16)*128 + 16g
-      f"v_lshlrev_b32 {vreg(t)}, 10, {vreg(V_R16)}",
-      f"v_lshlrev_b32 {vreg(t + 1)}, 4, {vreg(V_G)}",
-      f"v_add_u32 {vreg(t)}, {vreg(t)}, {vreg(t + 1)}",
-      f"v_add_u32 {vreg(t + 2)}, 0x4000, {vreg(t)}",
-      f"v_lshlrev_b32 {vreg(t + 3)}, 7, {vreg(V_R16)}",
-      f"v_add_u32 {vreg(t + 3)}, {vreg(t + 3)}, {vreg(t + 1)}",
-      f"v_add_u32 {vreg(t + 1)}, 0x800, {vreg(t + 3)}")
-    for h in range(2):
-        off = vreg(t) if h == 0 else vreg(t + 2)
-        for ks in range(16):
-            q = V_Q + (2 * ks + h) * 4
-            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_QBASE}:{S_QBASE + 1}] offset:{64 * ks}")
-    for h in range(2):
-        off = vreg(t + 3) if h == 0 else vreg(t + 1)
-        for ks in range(2):
-            q = V_Q + (2 * (16 + ks) + h) * 4
-            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
-    a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
-      f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
-      f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
-      f"v_mov_b32 {vreg(V_LRUN[1])}, 0",
-      f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
-      f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
-      f"s_mov_b32 {s(S_EXACT)}, 0")
-    zero_o(a)
-    # ------------------------------------------------ units of the segment
-    # On entry the loads of unit S_UCUR into its slot are in flight.
     a.label(".Lunit")
     a(f"s_mov_b64 {sp(S_OVF)}, 0",
       f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
@@ -1082,6 +1265,200 @@ def kernel(fp8=False):
     a.label(none)
     for g in dma_groups():
         a.lines += g
+    return uend
+
+
+def unit_body_fp8(a):
+    """One unit of the fp8 kernel up to the unit-end label (returned)."""
+    T = S_TMP
+    a.label(".Lunit")
+    a(f"s_mov_b64 {sp(S_OVF)}, 0",
+      f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
+      f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
+    # this unit's raw pages have landed (own loads), the table prefetch too,
+    # and every wave is past the previous unit (the tile is free)
+    a(s_waitcnt_vm(0), s_waitcnt_lgkm(0), "s_barrier")
+    a(f"v_mov_b32 {vreg(V_T)}, {FLAG_ADDR}",
+      f"ds_read_b32 {vreg(V_T)}, {vreg(V_T)}",         # restart flag, checked below
+      f"s_mov_b32 {s(S_CURVALID)}, {s(S_NVALID)}")
+    take_prefetched(a)
+    loader_page_fp8(a)
+    a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
+    dma_fp8(a, T + 21)
+    a(f"s_add_u32 s{T + 19}, {s(S_UCUR)}, 1")
+    prefetch_next(a, T + 19)
+    dequant_fp8(a)
+    a(s_waitcnt_lgkm(0), "s_barrier",
+      "s_nop 1",
+      f"v_readfirstlane_b32 s{T}, {vreg(V_T)}",
+      f"s_cmp_eq_u32 s{T}, 0",
+      "s_cbranch_scc0 .Lrestart")
+    a(f"s_sub_u32 {s(S_ROW0)}, {s(S_UCUR)}, {s(S_CPRE)}",
+      f"s_lshl_b32 {s(S_ROW0)}, {s(S_ROW0)}, 6",
+      f"v_mov_b32 {vreg(V_UQ)}, {vreg(V_QKE)}",
+      f"v_mov_b32 {vreg(V_UQ + 1)}, {vreg(V_QKO)}",
+      f"v_add_u32 {vreg(V_UQ + 2)}, 0x10000, {vreg(V_QKE)}",
+      f"v_add_u32 {vreg(V_UQ + 3)}, 0x10000, {vreg(V_QKO)}",
+      f"v_mov_b32 {vreg(V_UP)}, {vreg(V_PV0)}")
+    for m in range(1, 4):
+        a(f"v_xor_b32 {vreg(V_UP + m)}, {32 * m}, {vreg(V_PV0)}")
+    half, uend, classic = (a.new_label(x) for x in ("half", "uend", "classic"))
+    a(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
+      f"s_cmp_le_i32 s{T}, 0",
+      f"s_cbranch_scc1 {uend}",
+      f"s_cmp_le_i32 s{T}, 32",
+      f"s_cbranch_scc1 {half}",
+      f"s_cmp_lt_i32 s{T}, 64",
+      f"s_cbranch_scc1 {classic}",
+      f"s_max_u32 s{T + 1}, {s(S_UA)}, {s(S_CPRE)}",
+      f"s_cmp_eq_u32 {s(S_UCUR)}, s{T + 1}",
+      f"s_cbranch_scc1 {classic}",
+      f"s_cmp_eq_u32 {s(S_EXACT)}, 0",
+      f"s_cbranch_scc0 {classic}")
+    for ss in range(2):
+        substep_fp8(a, ss, lean=True)
+    a(f"s_branch {uend}")
+    a.label(classic)
+    for ss in range(2):
+        substep_fp8(a, ss, lean=False)
+    a(f"s_branch {uend}")
+    a.label(half)
+    substep_fp8(a, 0, lean=False)
+    return uend
+
+
+def kernel(fp8=False):
+    configure(fp8)
+    a = Asm()
+    a.lines += [
+        "\t.text",
+        f"\t.globl {KNAME}",
+        "\t.p2align 8",
+        f"\t.type {KNAME},@function",
+        f"{KNAME}:",
+    ]
+    T = S_TMP
+    # ------------------------------------------------------------ prologue
+    a(f"s_load_dwordx16 s[{S_QA}:{S_QA + 15}], s[0:1], 0x0",
+      f"s_load_dwordx8 s[{S_LSE}:{S_LSE + 7}], s[0:1], 0x40",
+      f"s_load_dwordx2 s[{S_NHB}:{S_NHB + 1}], s[0:1], 0x60",
+      *([f"s_load_dwordx4 s[{S_FSC}:{S_FSC + 3}], s[0:1], 0x68"] if FP8 else []),
+      f"v_and_b32 {vreg(V_LANE)}, 63, {vreg(V_TID)}",
+      f"v_lshrrev_b32 {vreg(V_G)}, 4, {vreg(V_LANE)}",
+      f"v_and_b32 {vreg(V_R16)}, 15, {vreg(V_LANE)}",
+      f"v_lshrrev_b32 {vreg(V_T)}, 6, {vreg(V_TID)}",
+      "s_nop 1",
+      f"v_readfirstlane_b32 {s(S_WAVE)}, {vreg(V_T)}",
+      s_waitcnt_lgkm(0))
+    # ------------------------------------------------ workgroup -> (partition, head block)
+    plain, mapped = a.new_label("mapplain"), a.new_label("mapdone")
+    a(f"s_sub_u32 s{T}, {s(S_NHB)}, 1",
+      f"s_and_b32 s{T + 1}, {s(S_NPART)}, 7",
+      f"s_cmp_eq_u32 s{T + 1}, 0",
+      f"s_cbranch_scc0 {plain}",
+      # consecutive partitions on one XCD: xcd = wg & 7 owns partitions xcd*P/8 ..
+      f"s_lshr_b32 s{T + 1}, s2, 3",
+      f"s_and_b32 s{T + 2}, s2, 7",
+      f"s_lshr_b32 s{T + 3}, {s(S_NPART)}, 3",
+      f"s_mul_i32 s{T + 2}, s{T + 2}, s{T + 3}",
+      f"s_lshr_b32 {s(S_PART)}, s{T + 1}, s{T}",
+      f"s_add_u32 {s(S_PART)}, {s(S_PART)}, s{T + 2}",
+      f"s_and_b32 {s(S_HBLK)}, s{T + 1}, s{T}",
+      f"s_branch {mapped}")
+    a.label(plain)
+    a(f"s_lshr_b32 {s(S_PART)}, s2, s{T}",
+      f"s_and_b32 {s(S_HBLK)}, s2, s{T}")
+    a.label(mapped)
+    # ------------------------------------------------ partition map
+    seq_units_pass(a, find_first=False)
+    a(f"s_mul_i32 s{T}, {s(S_PART)}, {s(S_U)}",
+      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, {s(S_U)}",
+      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
+      f"s_mov_b32 {s(S_UA)}, s{T}",
+      f"s_add_u32 s{T + 2}, {s(S_PART)}, 1",
+      f"s_mul_i32 s{T}, s{T + 2}, {s(S_U)}",
+      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, {s(S_U)}",
+      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
+      f"s_mov_b32 {s(S_UB)}, s{T}",
+      f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
+      "s_cbranch_scc1 .Lkernel_end")
+    seq_units_pass(a, find_first=True)
+    # ------------------------------------------------ this wave's query rows
+    a(f"s_lshl_b32 s{T}, {s(S_WAVE)}, 5",
+      f"s_sub_u32 s{T + 1}, {s(S_HB)}, 1",
+      f"s_and_b32 s{T + 2}, s{T}, s{T + 1}",
+      f"s_mul_i32 s{T + 3}, {s(S_HBLK)}, {s(S_HB)}",
+      f"s_add_u32 {s(S_HEAD0)}, s{T + 2}, s{T + 3}",
+      f"s_ff1_i32_b32 s{T + 1}, {s(S_HB)}",
+      f"s_lshr_b32 {s(S_STOK)}, s{T}, s{T + 1}")
+    # ------------------------------------------------ lane-constant LDS offsets
+    lane_constants(a)
+    if FP8:
+        lane_constants_fp8(a)
+    t = V_T
+    a(f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
+    # restart flag = 0
+    flag_write(a, 0)
+    a(s_waitcnt_lgkm(0), "s_barrier")
+    # ------------------------------------------------ loader cursor, first unit
+    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
+      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
+    load_len(a, S_LLEN, S_LSEQ)
+    units_of(a, S_LUNITS, S_LLEN)
+    a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
+      f"s_mov_b32 {s(S_SLOT)}, 0")
+    (issue_unit_fp8 if FP8 else issue_unit)(a, S_UCUR, S_SLOT)
+    prefetch_next(a, S_UCUR)
+    # ------------------------------------------------ segments
+    a.label(".Lseg")
+    load_len(a, S_CLEN, S_CSEQ)
+    units_of(a, S_CUNITS, S_CLEN)
+    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
+      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
+      # Q row index (c_seq * s_q + s_tok) * 128 + head0
+      f"s_mul_i32 s{T}, {s(S_CSEQ)}, {s(S_SQ)}",
+      f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
+      f"s_lshl_b32 s{T}, s{T}, 7",
+      f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
+      f"s_mov_b32 s{T + 1}, 0",
+      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 10",
+      f"s_add_u32 s{S_QBASE}, {s(S_QA)}, s{T + 2}",
+      f"s_addc_u32 s{S_QBASE + 1}, s{S_QA + 1}, s{T + 3}",
+      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 7",
+      f"s_add_u32 s{S_RBASE}, {s(S_QR)}, s{T + 2}",
+      f"s_addc_u32 s{S_RBASE + 1}, s{S_QR + 1}, s{T + 3}",
+      # lane offsets: latent (16h + r16)*1024 + 16g ; rope (16h + r16)*128 + 16g
+      f"v_lshlrev_b32 {vreg(t)}, 10, {vreg(V_R16)}",
+      f"v_lshlrev_b32 {vreg(t + 1)}, 4, {vreg(V_G)}",
+      f"v_add_u32 {vreg(t)}, {vreg(t)}, {vreg(t + 1)}",
+      f"v_add_u32 {vreg(t + 2)}, 0x4000, {vreg(t)}",
+      f"v_lshlrev_b32 {vreg(t + 3)}, 7, {vreg(V_R16)}",
+      f"v_add_u32 {vreg(t + 3)}, {vreg(t + 3)}, {vreg(t + 1)}",
+      f"v_add_u32 {vreg(t + 1)}, 0x800, {vreg(t + 3)}")
+    for h in range(2):
+        off = vreg(t) if h == 0 else vreg(t + 2)
+        for ks in range(16):
+            q = V_Q + (2 * ks + h) * 4
+            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_QBASE}:{S_QBASE + 1}] offset:{64 * ks}")
+    for h in range(2):
+        off = vreg(t + 3) if h == 0 else vreg(t + 1)
+        for ks in range(2):
+            q = V_Q + (2 * (16 + ks) + h) * 4
+            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
+    a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
+      f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
+      f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
+      f"v_mov_b32 {vreg(V_LRUN[1])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
+      f"s_mov_b32 {s(S_EXACT)}, 0")
+    zero_o(a)
+    # ------------------------------------------------ units of the segment
+    # On entry the loads of unit S_UCUR into its slot are in flight.
+    uend = (unit_body_fp8 if FP8 else unit_body_bf16)(a)
     a.label(uend)
     noflag = a.new_label("noflag")
     a(f"s_cmp_eq_u64 {sp(S_OVF)}, 0",
@@ -1132,7 +1509,7 @@ def kernel(fp8=False):
     zero_o(a)
     a(f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
       f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
-    issue_unit(a, S_UCUR, S_SLOT)
+    (issue_unit_fp8 if FP8 else issue_unit)(a, S_UCUR, S_SLOT)
     prefetch_next(a, S_UCUR)
     a("s_branch .Lunit")
     a.label(".Lkernel_end")

@@ -80,7 +80,6 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
   p.max_blocks = max_blocks_per_seq;
   p.batch = batch;
   p.num_parts = num_splits;
-  if (cache->dtype == MLA_CACHE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;   // fp8 kernel not wired yet
   const hipError_t err = mla::launch_decode(p, s_q, cache->dtype == MLA_CACHE_FP8_E4M3, stream);
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }

@@ -364,3 +364,11 @@ def test_pins_catch_planted_oracle_mistakes(monkeypatch, target, mutant):
     monkeypatch.setattr(O, target, mutant)
     failed = _mutant_checks()
     assert failed, f"no pin caught the planted mistake in {target} ({mutant.__name__})"
+
+
+def test_input_generator_rejects_unknown_cache_type():
+    import pytest
+    from mla_inputs import make_inputs
+    with pytest.raises(ValueError):
+        make_inputs(dict(batch=1, s_q=1, lens=("explicit", [8]), layout="paged_shuffled", q_std=1.0,
+                         cache="fp8", num_splits=None, unabsorbed=False, name="bad"), seed=0)
