@@ -102,6 +102,8 @@ mla_status mla_combine(const float* partial_out, const float* partial_lse, const
   p.batch = batch;
   p.s_q = s_q;
   p.num_parts = num_splits;
+  p.log2_parts = 0;
+  while ((1 << p.log2_parts) < num_splits) ++p.log2_parts;
   return mla::launch_combine(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

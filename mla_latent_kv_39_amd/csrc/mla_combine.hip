@@ -4,13 +4,14 @@
 // the log-sum-exp identity of one softmax over the union of the partitions'
 // rows.
 //
-// One workgroup merges one quarter of the latent columns (128) of one group
-// of 32 heads of one (sequence, query token).  Partials are stored in the
-// decode kernel's lane order (see the partial_out layout in include/mla.h):
-// the quarter is two contiguous 8 KB runs (head halves a = 0, 1), so thread t
-// reads 16-byte chunks t and t + 256 of each run, consecutive threads reading
-// consecutive memory, and touches two heads (16a + (t & 15)).  The merged
-// quarter goes through LDS once to be written back in row order.
+// One workgroup merges one slice of the latent columns (16 CB of them, CB = 8,
+// 4 or 2 column blocks; the host picks the narrowest slice that still gives
+// the GPU enough workgroups) of one group of 32 heads of one (sequence, query
+// token).  Partials are stored in the decode kernel's lane order (see the
+// partial_out layout in include/mla.h): a slice is two contiguous runs of
+// CB KB (head halves a = 0, 1), so consecutive threads read consecutive
+// 16-byte chunks.  The merged slice goes through LDS once to be written back in
+// row order.
 #include "mla_internal.h"
 #include "mla_schedule.h"
 
@@ -19,22 +20,50 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kGroupHeads = 32;
-constexpr int kQuarterChunks = kGroupHeads * kLatent / 16;   // 16-byte chunks per quarter (1024)
-constexpr int kPerThread = kQuarterChunks / 256;             // 4: chunks k = 0, 1 head half 0; 2, 3 head half 1
 
 // LDS slot of lane-order chunk c: XOR the head bits with the column phase so
 // that both the lane-order writes and the row-order reads spread over all banks.
 __device__ __forceinline__ int lds_slot(int c) { return c ^ ((((c >> 6) & 3) << 2) | ((c >> 4) & 3)); }
 
+// Online merge of one partition's share into (m, wsum, acc): rescale when a
+// larger lse arrives.  Used where sequences are short and shares are few.
+template <int N>
+__device__ __forceinline__ void merge_share(const CombineParams& p, size_t row, int grp, const int* head,
+                                            const int* coff, float* m, float* wsum, float4* acc) {
+  const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float l = p.part_lse[row + head[k]];
+    if (l == kNegInf) continue;  // this share saw no row of this query token
+    float w = 1.f;
+    if (l > m[k]) {
+      const float r = __expf(m[k] - l);
+      wsum[k] *= r;
+      acc[k].x *= r; acc[k].y *= r; acc[k].z *= r; acc[k].w *= r;
+      m[k] = l;
+    } else {
+      w = __expf(l - m[k]);
+    }
+    wsum[k] += w;
+    const float4 v = src[coff[k]];
+    acc[k].x += w * v.x; acc[k].y += w * v.y; acc[k].z += w * v.z; acc[k].w += w * v.w;
+  }
+}
+
+template <int CB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  __shared__ float4 s_tile[kQuarterChunks];
+  constexpr int kSlices = 32 / CB;
+  constexpr int kRun = 64 * CB;                // chunks per head half of a slice
+  constexpr int kPerThread = 2 * kRun / 256;   // 4, 2 or 1
+  constexpr int kUnroll = 16 / kPerThread;     // about 16 loads of 16 bytes in flight per thread
+  __shared__ float4 s_tile[2 * kRun];
   __shared__ int s_red[8];
   const int tid = threadIdx.x;
-  const int per_tok = (kHeads / kGroupHeads) * 4;
+  const int per_tok = (kHeads / kGroupHeads) * kSlices;
   const int b = blockIdx.x / (p.s_q * per_tok);
   const int s = (blockIdx.x / per_tok) % p.s_q;
-  const int grp = (blockIdx.x >> 2) % (kHeads / kGroupHeads);
-  const int quarter = blockIdx.x & 3;
+  const int grp = (blockIdx.x / kSlices) % (kHeads / kGroupHeads);
+  const int slice = blockIdx.x % kSlices;
 
   // rebuild the partition map: total units U and the first unit u0 of sequence b
   int cnt = 0, before = 0;
@@ -60,75 +89,89 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int p1 = part_of_unit(u1 - 1, total_units, p.num_parts);
   if (p0 == p1) return;  // finished by the decode kernel
 
-  const int r = tid & 15;
-  const int head0 = grp * kGroupHeads + r;  // head of chunks k < 2; chunks k >= 2 hold head0 + 16
-  // lane-order offset (in chunks) of chunk k inside the group: run a = k >> 1 at 2048 a, quarter at 512 q
-  int coff[kPerThread];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) coff[k] = 2048 * (k >> 1) + 512 * quarter + tid + 256 * (k & 1);
-  // pass 1: the largest lse of each of the thread's two heads
-  float m[2] = {kNegInf, kNegInf};
-  for (int q = p0; q <= p1; ++q) {
-    const int q_start = part_start(q, total_units, p.num_parts);
-    if (q_start == part_start(q + 1, total_units, p.num_parts)) continue;  // empty partition (more partitions than units)
-    const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
-    const size_t row = ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
-    m[0] = fmaxf(m[0], p.part_lse[row + head0]);
-    m[1] = fmaxf(m[1], p.part_lse[row + head0 + 16]);
-  }
-  // pass 2: weighted sums; the loop body has no data-dependent branch, so the
-  // loads of successive partitions can be in flight together.  An empty
-  // partition reads partition p0's share (always written) with weight 0.
-  float wsum[2] = {0.f, 0.f};
-  float4 acc[kPerThread];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  const size_t row0 = ((size_t)(p0 * 2 + (u0 != part_start(p0, total_units, p.num_parts) ? 1 : 0)) * p.s_q + s) * kHeads;
-#pragma unroll 4
-  for (int q = p0; q <= p1; ++q) {
-    const int q_start = part_start(q, total_units, p.num_parts);
-    const bool empty = q_start == part_start(q + 1, total_units, p.num_parts);
-    const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
-    const size_t row = empty ? row0 : ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
-    const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
-    float w[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const float l = p.part_lse[row + head0 + 16 * a];
-      // -inf: this share saw no row of this query token
-      w[a] = (empty || l == kNegInf) ? 0.f : __expf(l - m[a]);
-      wsum[a] += w[a];
-    }
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const float wk = w[k >> 1];
-      const float4 v = src[coff[k]];
-      acc[k].x += wk * v.x; acc[k].y += wk * v.y; acc[k].z += wk * v.z; acc[k].w += wk * v.w;
-    }
-  }
-  float inv[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) inv[a] = wsum[a] > 0.f ? 1.f / wsum[a] : 0.f;
-  // quarter-local lane-order chunk: 512 a + 64 (cb - 8 quarter) + lane
+  // chunk k of this thread: slice-local index t + 256 k, head half a, lane-order offset in the group
+  int head[kPerThread], coff[kPerThread];
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
-    const float ik = inv[k >> 1];
-    s_tile[lds_slot(512 * (k >> 1) + tid + 256 * (k & 1))] =
-        make_float4(acc[k].x * ik, acc[k].y * ik, acc[k].z * ik, acc[k].w * ik);
+    const int lc = tid + 256 * k;
+    const int a = lc / kRun;
+    head[k] = grp * kGroupHeads + 16 * a + (tid & 15);
+    coff[k] = 2048 * a + kRun * slice + lc % kRun;
+  }
+  float m[kPerThread], wsum[kPerThread];
+  float4 acc[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    m[k] = kNegInf;
+    wsum[k] = 0.f;
+    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (2 * (u1 - u0) < p1 - p0 + 1) {
+    // more partitions than units (short sequences): visit only the partitions
+    // that hold a unit of sequence b, stepping u to the next partition's start
+    for (int u = u0; u < u1;) {
+      const int q = part_of_unit(u, total_units, p.num_parts);
+      const int q_start = part_start(q, total_units, p.log2_parts);
+      const size_t row = ((size_t)(q * 2 + ((q == p0 && u0 != q_start) ? 1 : 0)) * p.s_q + s) * kHeads;
+      merge_share<kPerThread>(p, row, grp, head, coff, m, wsum, acc);
+      u = part_start(q + 1, total_units, p.log2_parts);
+    }
+  } else {
+    // pass 1: the largest lse of each chunk's head
+#pragma unroll kUnroll
+    for (int q = p0; q <= p1; ++q) {
+      const int q_start = part_start(q, total_units, p.log2_parts);
+      if (q_start == part_start(q + 1, total_units, p.log2_parts)) continue;  // empty partition
+      const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
+      const size_t row = ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) m[k] = fmaxf(m[k], p.part_lse[row + head[k]]);
+    }
+    // pass 2: weighted sums; the loop body has no data-dependent branch, so
+    // the loads of successive partitions can be in flight together.  An empty
+    // partition reads partition p0's share (always written) with weight 0.
+    const size_t row0 =
+        ((size_t)(p0 * 2 + (u0 != part_start(p0, total_units, p.log2_parts) ? 1 : 0)) * p.s_q + s) * kHeads;
+#pragma unroll kUnroll
+    for (int q = p0; q <= p1; ++q) {
+      const int q_start = part_start(q, total_units, p.log2_parts);
+      const bool empty = q_start == part_start(q + 1, total_units, p.log2_parts);
+      const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
+      const size_t row = empty ? row0 : ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
+      const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const float l = p.part_lse[row + head[k]];
+        // -inf: this share saw no row of this query token
+        const float w = (empty || l == kNegInf) ? 0.f : __expf(l - m[k]);
+        wsum[k] += w;
+        const float4 v = src[coff[k]];
+        acc[k].x += w * v.x; acc[k].y += w * v.y; acc[k].z += w * v.z; acc[k].w += w * v.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const float ik = wsum[k] > 0.f ? 1.f / wsum[k] : 0.f;
+    s_tile[lds_slot(tid + 256 * k)] = make_float4(acc[k].x * ik, acc[k].y * ik, acc[k].z * ik, acc[k].w * ik);
   }
   const size_t orow = ((size_t)b * p.s_q + s) * kHeads + grp * kGroupHeads;
-  if (tid < 16 && quarter == 0) {
+  if (slice == 0) {
+    // lse of the group's heads: the threads whose chunk k sits in column block 0, g == 0
 #pragma unroll
-    for (int a = 0; a < 2; ++a) p.lse[orow + r + 16 * a] = wsum[a] > 0.f ? m[a] + __logf(wsum[a]) : kNegInf;
+    for (int k = 0; k < kPerThread; ++k) {
+      const int lc = tid + 256 * k;
+      if ((lc % kRun) < 16) p.lse[head[k]  - grp * kGroupHeads + orow] = wsum[k] > 0.f ? m[k] + __logf(wsum[k]) : kNegInf;
+    }
   }
   __syncthreads();
-  // row order: chunk e of the quarter is head e >> 5, columns 128 quarter + 4 (e & 31) .. +3
+  // row order: chunk e of the slice is head e / (4 CB), columns 16 CB slice + 4 (e % (4 CB)) .. +3
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int e = tid + 256 * k;
-    const int hl = e >> 5, cc = e & 31;
-    const int c = 512 * (hl >> 4) + 64 * (cc >> 2) + 16 * (cc & 3) + (hl & 15);
-    float4* dst = (float4*)(p.out + (orow + hl) * kLatent + 128 * quarter) + cc;
+    const int hl = e / (4 * CB), cc = e % (4 * CB);
+    const int c = kRun * (hl >> 4) + 64 * (cc >> 2) + 16 * (cc & 3) + (hl & 15);
+    float4* dst = (float4*)(p.out + (orow + hl) * kLatent + 16 * CB * slice) + cc;
     *dst = s_tile[lds_slot(c)];
   }
 }
@@ -136,8 +179,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const int blocks = p.batch * p.s_q * (kHeads / kGroupHeads) * 4;
-  combine_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(p);
+  // narrowest column slice that still gives about two workgroups per compute unit
+  const long long base = (long long)p.batch * p.s_q * (kHeads / kGroupHeads);
+  const long long want = 512;
+  if (base * 4 >= want) {
+    combine_kernel<8><<<dim3((unsigned)(base * 4)), dim3(256), 0, stream>>>(p);
+  } else if (base * 8 >= want) {
+    combine_kernel<4><<<dim3((unsigned)(base * 8)), dim3(256), 0, stream>>>(p);
+  } else {
+    combine_kernel<2><<<dim3((unsigned)(base * 16)), dim3(256), 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct CombineParams {
   int32_t batch;
   int32_t s_q;
   int32_t num_parts;
+  int32_t log2_parts;        // num_parts is a power of two
 };
 
 // Heads handled by one workgroup for a given number of query tokens.

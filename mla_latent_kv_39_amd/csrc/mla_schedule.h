@@ -17,8 +17,9 @@ namespace mla {
 
 __device__ __forceinline__ int units_of_len(int len) { return len > 64 ? (len + 63) >> 6 : 1; }
 
-__device__ __forceinline__ int part_start(int p, int total_units, int parts) {
-  return (int)(((long long)p * total_units) / parts);
+// parts = 2^log2_parts, so the division is a shift
+__device__ __forceinline__ int part_start(int p, int total_units, int log2_parts) {
+  return (int)(((long long)p * total_units) >> log2_parts);
 }
 
 // The partition whose range holds unit u: the largest p with start(p) <= u.
