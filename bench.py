@@ -51,6 +51,24 @@ def algorithmic_work(inp):
     return rows, nbytes, flops
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes (profiles/decode_traffic.json, scaled by the copy
+    calibration), or None when they were taken on another version of the
+    kernel generator or not for this workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    gen = os.path.join(ROOT, "mla_latent_kv_39_amd", "csrc", "gen_decode_gfx950.py")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(gen, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("generator_sha256") != sha or workload not in rec.get("workloads", {}):
+        return None
+    return rec["workloads"][workload]["bytes"]
+
+
 def cpu_baseline(inp, budget_s: float):
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences in order until about budget_s seconds of CPU work."""
@@ -181,6 +199,7 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
 
+    roof["traffic"] = measured_traffic(args.workload)
     result = {
         "metric": "MLA decode cache-tokens/s and achieved HBM GB/s (% of roofline), 1 MI355X",
         "value": round(value, 1), "unit": "cache-tokens/s", "n_gpus": 1, "steps": args.steps,
