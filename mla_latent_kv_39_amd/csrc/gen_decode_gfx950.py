@@ -38,11 +38,17 @@ import sys
 SLOT_BYTES = 64 * 1152          # one page of bf16 rows = one LDS tile
 KARG_BYTES = 120                # kernel argument block (both kernels)
 
-# bf16 kernel: two tile slots, the restart flag after them
+# bf16 kernel: two tile slots, then the probability exchange buffer (16 KB):
+# the bf16 probabilities of all 128 query rows for the two 32-row sub-steps of
+# a unit, as MFMA B-operand fragments: (sub-step ss, 16-row block hb) at
+# P_BASE + 1024 (8 ss + hb), lane L's 16 bytes at + 16 L.  The whole 160 KB of
+# a compute unit's LDS.
 KNAME = "mla_decode_bf16_gfx950"
 FP8 = False
-FLAG_ADDR = 2 * SLOT_BYTES
-LDS_BYTES = FLAG_ADDR + 16
+P_BASE = 2 * SLOT_BYTES
+P_BYTES = 2 * 8 * 1024
+FLAG_ADDR = None                # the fp8 kernel's restart flag
+LDS_BYTES = P_BASE + P_BYTES
 PAGE_BYTES = SLOT_BYTES         # global bytes of one page of the row array
 
 # fp8 kernel: one bf16 tile, two staging slots of raw pages (e4m3 codes, bf16
@@ -60,9 +66,10 @@ def configure(fp8):
     FP8 = fp8
     if fp8:
         KNAME, FLAG_ADDR, PAGE_BYTES = "mla_decode_fp8_gfx950", F8_FLAG, F8_CODES
+        LDS_BYTES = F8_FLAG + 16
     else:
-        KNAME, FLAG_ADDR, PAGE_BYTES = "mla_decode_bf16_gfx950", 2 * SLOT_BYTES, SLOT_BYTES
-    LDS_BYTES = FLAG_ADDR + 16
+        KNAME, FLAG_ADDR, PAGE_BYTES = "mla_decode_bf16_gfx950", None, SLOT_BYTES
+        LDS_BYTES = P_BASE + P_BYTES
 NEG_INF = "0xff800000"
 LN2 = "0x3f317218"
 OVF_SUM = "0x5f800000"   # 2^64
@@ -93,6 +100,13 @@ V_DMA = (V_T + 1, V_T + 2)
 # softmax scratch: sub-step 0 borrows P[1], sub-step 1 borrows S[0] (both free at that time)
 V_SMT = (tuple(range(V_P[1], V_P[1] + 4)), tuple(range(V_S[0], V_S[0] + 4)))
 EPI_TEMPS = list(range(16, 48))   # the epilogue runs between units
+# bf16 kernel (output columns split over the waves):
+V_PX = 0                 # P_BASE + 16 lane (after the prologue)
+V_PXW = V_T              # P_BASE + 16 lane + 2048 w: this wave's fragments (set per unit)
+P_OWN = (80, 48)         # this wave's packed probabilities of sub-step ss: + 4h for heads 16h..
+SMT_SPLIT = ((88, 89, 90, 91), (56, 57, 58, 59))   # softmax scratch per sub-step
+# probability fragments of all 128 query rows read back for the output MFMAs
+PF = ((16, 20, 24, 28, 80, 84, 88, 92), tuple(range(32, 64, 4)))
 PERSISTENT = {V_LANE, V_G, V_R16, V_QKE, V_QKO, V_PV0, V_LDROW, *V_MREF, *V_LRUN,
               V_LDA, V_LDB, V_LCA, V_LCB, V_NEGINF, *V_PEAK}
 # AGPRs: O[cb][h] at (2*cb + h)*4, lane (g, r16) holds columns 16cb + 4g .. +3 of head 16h + r16
@@ -116,6 +130,9 @@ S_CURVALID = 96          # fp8: valid rows of the unit being dequantized
 S_EXACT = 88             # 1 after a restart: the rest of the segment keeps the max-based softmax
 S_NV2, S_ENT2 = 89, 90   # prefetched valid rows / page of the unit after next (-1: page in V_ENT)
 S_DPAGE = 80             # s80:81 page address + chunk-group offset of one load (S_TMP + 20, + 21)
+S_NVLO, S_NVHI = 91, 97  # bf16: rows visible to the workgroup's first / last query token
+S_MODE = S_TMP + 13      # bf16: kind of the current unit (0 none, 1 half, 2 classic, 3 lean)
+S_PFOFF = S_TMP + 14     # bf16: block-table byte offset of the page prefetch to issue
 # loads of the next unit issued in phases 1, 2, 3 of a full unit
 DMA_SPLIT = (8, 6, 4)
 S_MAX = 98
@@ -148,10 +165,12 @@ def sp(i):
     return f"s[{i}:{i + 1}]"
 
 
+_LABELS = [0]
+
+
 class Asm:
     def __init__(self):
         self.lines = []
-        self.nlabel = 0
 
     def __call__(self, *lines):
         for line in lines:
@@ -161,8 +180,8 @@ class Asm:
         self.lines.append(f"{name}:")
 
     def new_label(self, stem):
-        self.nlabel += 1
-        return f".L{stem}_{self.nlabel}"
+        _LABELS[0] += 1
+        return f".L{stem}_{_LABELS[0]}"
 
     def comment(self, text):
         self.lines.append(f"\t; {text}")
@@ -306,11 +325,13 @@ def loader_lookup(a, u_sgpr, wait):
     a.label(done)
 
 
-def loader_prefetch(a, u_sgpr):
+def loader_prefetch(a, u_sgpr, issue=True):
     """Look up unit u one unit before its loads are issued: S_NV2 = its valid
     rows (<= 0: none), S_ENT2 = its page for a contiguous cache, or -1 with the
     page on its way into V_ENT (a vector load, so that the LDS waits of the
-    phases never wait on it; it lands before the next unit's barrier)."""
+    phases never wait on it; it lands before the next unit's barrier).  With
+    issue=False the load is left to the caller (issue_prefetch): its table
+    offset is in S_PFOFF."""
     T = S_TMP
     done = a.new_label("pfdone")
     a(f"s_mov_b32 {s(S_ENT2)}, 0",
@@ -324,14 +345,17 @@ def loader_prefetch(a, u_sgpr):
       f"s_add_u32 {s(S_ENT2)}, s{T + 4}, s{T + 1}",
       f"s_cmp_eq_u64 {sp(S_TABLE)}, 0",
       f"s_cbranch_scc1 {done}",
-      f"s_lshl_b32 s{T + 5}, {s(S_ENT2)}, 2",
-      f"v_mov_b32 {vreg(V_T + 3)}, s{T + 5}",       # v13/v14 hold the next unit's load offsets
-      f"global_load_dword {vreg(V_ENT)}, {vreg(V_T + 3)}, {sp(S_TABLE)}",
-      f"s_mov_b32 {s(S_ENT2)}, -1")
+      f"s_lshl_b32 s{T + 5}, {s(S_ENT2)}, 2")
+    if issue:
+        a(f"v_mov_b32 {vreg(V_T + 3)}, s{T + 5}",       # v13/v14 hold the next unit's load offsets
+          f"global_load_dword {vreg(V_ENT)}, {vreg(V_T + 3)}, {sp(S_TABLE)}")
+    else:
+        a(f"s_mov_b32 {s(S_PFOFF)}, s{T + 5}")
+    a(f"s_mov_b32 {s(S_ENT2)}, -1")
     a.label(done)
 
 
-def prefetch_next(a, u_sgpr):
+def prefetch_next(a, u_sgpr, issue=True):
     """Prefetch the page of unit u + 1 if the partition has it (else none)."""
     T = S_TMP
     nonext, done = a.new_label("pfnone"), a.new_label("pfend")
@@ -339,7 +363,7 @@ def prefetch_next(a, u_sgpr):
       f"s_cmp_lt_u32 s{T + 20}, {s(S_UB)}",
       f"s_cbranch_scc0 {nonext}")
     loader_advance(a, T + 20)
-    loader_prefetch(a, T + 20)
+    loader_prefetch(a, T + 20, issue)
     a(f"s_branch {done}")
     a.label(nonext)
     a(f"s_mov_b32 {s(S_NV2)}, 0", f"s_mov_b32 {s(S_ENT2)}, 0")
@@ -372,51 +396,6 @@ def loader_page(a):
     a.label(done)
 
 
-def dma_setup(a, slot_sgpr):
-    """Lane source offsets of the two row groups this wave copies (row 0 past
-    the valid rows) and the LDS base of its blocks in the slot."""
-    va, vb = V_DMA
-    t0 = V_T + 3
-    a(f"v_cmp_gt_i32 vcc, {s(S_NVALID)}, {vreg(V_LDROW)}",
-      f"v_add_u32 {vreg(t0)}, 8, {vreg(V_LDROW)}",
-      "s_nop 1",
-      f"v_cndmask_b32 {vreg(va)}, {vreg(V_LCA)}, {vreg(V_LDA)}, vcc",
-      f"v_cmp_gt_i32 vcc, {s(S_NVALID)}, {vreg(t0)}",
-      f"s_mul_i32 {s(S_DMALDS)}, {s(slot_sgpr)}, {SLOT_BYTES}",
-      f"s_lshl_b32 s{S_TMP + 5}, {s(S_WAVE)}, 11",
-      f"s_add_u32 {s(S_DMALDS)}, {s(S_DMALDS)}, s{S_TMP + 5}",   # slot + block (0, 2w)
-      "s_nop 0",
-      f"v_cndmask_b32 {vreg(vb)}, {vreg(V_LCB)}, {vreg(V_LDB)}, vcc")
-
-
-def dma_groups():
-    """The 18 direct-to-LDS loads of one unit, as separate instruction groups.
-    Wave w fills the tile blocks of rows 16w .. 16w+15 (row groups 2w, 2w+1,
-    all nine chunk groups); one load moves one 8-row x 8-chunk block, i.e.
-    eight 128-byte lines of the page."""
-    va, vb = V_DMA
-    groups = []
-    for i in range(18):
-        k, odd = divmod(i, 2)
-        src = vb if odd else va
-        groups.append([f"\ts_add_u32 s{S_DPAGE}, s{S_PAGE}, {128 * k}",
-                       f"\ts_addc_u32 s{S_DPAGE + 1}, s{S_PAGE + 1}, 0",
-                       f"\ts_add_u32 m0, {s(S_DMALDS)}, {1024 * (8 * k + odd)}",
-                       "\ts_nop 0",
-                       f"\tglobal_load_lds_dwordx4 {vreg(src)}, {sp(S_DPAGE)}"])
-    return groups
-
-
-def issue_unit(a, u_sgpr, slot_sgpr):
-    """Stand-alone copy of unit u into the slot (prologue and restart)."""
-    loader_advance(a, u_sgpr)
-    loader_lookup(a, u_sgpr, wait=True)
-    loader_page(a)
-    dma_setup(a, slot_sgpr)
-    for g in dma_groups():
-        a.lines += g
-
-
 def qk_read(ss, i):
     """A fragment of rows 32ss + 16tb + r16, chunk 4ks + g (i = 2ks + tb)."""
     ks, tb = divmod(i, 2)
@@ -438,11 +417,12 @@ def pv_read(ss, cb):
 class Frag:
     """One LDS operand fragment and the two MFMAs that consume it."""
 
-    def __init__(self, ring, ring_base, nring, idx, reads, mfmas):
-        self.ring, self.idx = ring, idx
+    def __init__(self, ring, ring_base, nring, idx, reads, mfmas, deps=None):
+        self.ring, self.idx, self.nring = ring, idx, nring
         buf = ring_base + 4 * (idx % nring)
         self.reads = [r.format(buf=vr(buf, 4), lo=vr(buf, 2), hi=vr(buf + 2, 2)) for r in reads]
         self.mfmas = [m.format(buf=vr(buf, 4)) for m in mfmas]
+        self.deps = deps or [()] * len(mfmas)   # per MFMA: keys of other LDS reads it waits for
         self.read_ids = []
 
 
@@ -489,56 +469,6 @@ class LdsOrder:
         k = min(self.n - 1 - rid, 15)
         self.done = self.n - k
         return [f"\ts_waitcnt lgkmcnt({k})"]
-
-
-def emit_phases(a, frags, lead, fillers, marks=None):
-    """Emit the MFMA stream `frags` with its LDS reads and interleaved filler.
-
-    Reads of ring fragment f are issued right after the MFMAs of f - ring size
-    (the previous user of its buffer); the first fragments of each ring are
-    issued at the stream position given by `lead` {ring: index of the fragment
-    after whose MFMAs they go, -1 = at the start}.  fillers: list of
-    (first, last, instructions): spread evenly between the MFMAs of fragments
-    first..last (no LDS operations inside)."""
-    lds = LdsOrder()
-    nring = {"A": NA, "B": NB}
-    by_ring = {}
-    for f in frags:
-        by_ring.setdefault(f.ring, []).append(f)
-    pending = {}   # position -> list of frags whose reads go after that position's MFMAs
-
-    def issue_reads(f):
-        for r in f.reads:
-            f.read_ids.append(lds.issue())
-            a.lines.append(r)
-
-    pos_of = {id(f): p for p, f in enumerate(frags)}
-    for ring, lst in by_ring.items():
-        for j, f in enumerate(lst):
-            if j < nring[ring]:
-                at = lead[ring]
-            else:
-                at = pos_of[id(lst[j - nring[ring]])]
-            pending.setdefault(at, []).append(f)
-    # filler slots: after each of the two MFMAs of a fragment
-    slots = {}
-    for first, last, ins in fillers:
-        n = 2 * (last - first + 1)
-        per = [len(ins) * (k + 1) // n - len(ins) * k // n for k in range(n)]
-        it = iter(ins)
-        for k in range(n):
-            slots.setdefault((first + k // 2, k % 2), []).extend(next(it) for _ in range(per[k]))
-    for f in pending.get(-1, []):
-        issue_reads(f)
-    for p, f in enumerate(frags):
-        a.lines += lds.wait(max(f.read_ids))
-        for m, mf in enumerate(f.mfmas):
-            a.lines.append(mf)
-            a.lines += slots.get((p, m), [])
-        for g in pending.get(p, []):
-            issue_reads(g)
-        if marks and p in marks:
-            a.comment(f"phase {marks[p]} issued")
 
 
 def softmax_code(ss, S=None, P=None, tmp=None):
@@ -647,22 +577,6 @@ def softmax_lean(ss, S=None, P=None, tmp=None):
     return x.lines
 
 
-def unit_full(a, lean):
-    """Both 32-row sub-steps.  Phases: scores of sub-step 0 (next unit's loads
-    interleaved), scores of 1 with softmax of 0, output of 0 with softmax of
-    1, output of 1."""
-    q0, q1, p0, p1 = qk_frags(0), qk_frags(1), pv_frags(0), pv_frags(1)
-    frags = q0 + q1 + p0 + p1
-    groups = dma_groups()
-    n1, n2, n3 = DMA_SPLIT
-    assert n1 + n2 + n3 == len(groups)
-    sm = softmax_lean if lean else softmax_code
-    fillers = [(0, 35, [ins for g in groups[:n1] for ins in g]),
-               (36 + 3, 71 - 1, merge_filler(sm(0), groups[n1:n1 + n2])),
-               (72 + 3, 103 - 3, merge_filler(sm(1), groups[n1 + n2:]))]
-    emit_phases(a, frags, {"A": -1, "B": 71 - NB}, fillers, marks={35: 1, 71: 2, 103: 3})
-
-
 def merge_filler(ins, groups):
     """Spread the load groups evenly through an instruction list (order kept)."""
     if not groups:
@@ -671,41 +585,90 @@ def merge_filler(ins, groups):
     gi = 0
     for k, x in enumerate(ins):
         while gi < len(groups) and k >= gi * step:
-            out += groups[gi]
+            out.append(list(groups[gi]))
             gi += 1
         out.append(x)
     for g in groups[gi:]:
-        out += g
+        out.append(list(g))
     return out
 
 
-def unit_half(a):
-    """Only sub-step 0 has visible rows (last unit of a sequence)."""
-    q0, p0 = qk_frags(0), pv_frags(0)
-    dma = [ins for g in dma_groups() for ins in g]
-    emit_phases(a, q0, {"A": -1}, [(0, 35, dma)])
-    a("s_nop 7", "s_nop 7", "s_nop 3")   # MFMA results -> VALU
-    sm = softmax_code(0)
-    # output-operand reads go out first, overlapping the softmax
-    emit_phases_split(a, p0, sm)
+# ======================================================= bf16: split output
+# In the bf16 kernel each wave scores its own 32 query rows against all 64 rows
+# of a unit (Q stays in its registers), publishes its bf16 probabilities in the
+# exchange buffer, and then accumulates the output of its own 128 latent
+# columns for all 128 query rows: O^T[cols, rows] += C^T P^T with one
+# transposed tile read per 16 columns feeding eight MFMAs.  Each tile byte is
+# then read once per wave for the scores and once per workgroup for the
+# output, instead of four times for both.
+def emit_stream(a, frags, lead, fillers, events=None, marks=None):
+    """Emit the MFMA stream `frags` with its LDS reads, filler and events.
 
-
-def emit_phases_split(a, p0, sm):
+    Ring reads as in emit_phases.  fillers: (first, last, instructions),
+    spread evenly over the MFMAs of fragments first..last (no LDS operations
+    inside).  events: {p: items} emitted after the MFMAs (and ring reads) of
+    fragment p (-1: before the stream); an item is an instruction, ("lds",
+    instruction, key) for an LDS operation whose completion others wait on,
+    or ("wait", key).  An MFMA with dependency keys waits for those
+    operations first (LDS operations complete in issue order)."""
     lds = LdsOrder()
-    for f in p0[:NB]:
+    keys = {}
+    nring = {f.ring: f.nring for f in frags}
+    by_ring = {}
+    for f in frags:
+        by_ring.setdefault(f.ring, []).append(f)
+    pending = {}
+    pos_of = {id(f): p for p, f in enumerate(frags)}
+    for ring, lst in by_ring.items():
+        for j, f in enumerate(lst):
+            at = lead[ring] if j < nring[ring] else pos_of[id(lst[j - nring[ring]])]
+            pending.setdefault(at, []).append(f)
+    slots = {}
+    for item in fillers:
+        if item[0] == "slots":           # precomputed {(fragment, MFMA): instructions}
+            for sl, ins in item[1].items():
+                slots.setdefault(sl, []).extend(ins)
+            continue
+        first, last, ins = item
+        mslots = [(p, m) for p in range(first, last + 1) for m in range(len(frags[p].mfmas))]
+        n = len(mslots)
+        per = [len(ins) * (k + 1) // n - len(ins) * k // n for k in range(n)]
+        it = iter(ins)
+        for k, sl in enumerate(mslots):
+            for _ in range(per[k]):
+                item = next(it)     # a list is an atomic group: emitted together
+                slots.setdefault(sl, []).extend(item if isinstance(item, list) else [item])
+
+    def issue_reads(f):
         for r in f.reads:
             f.read_ids.append(lds.issue())
             a.lines.append(r)
-    a.lines += sm
-    a("s_nop 4")   # VALU writes of P -> MFMA reads
-    for p, f in enumerate(p0):
+
+    def run_events(p):
+        for item in (events or {}).get(p, []):
+            if isinstance(item, str):
+                a.lines.append(item)
+            elif item[0] == "lds":
+                keys[item[2]] = lds.issue()
+                a.lines.append(item[1])
+            else:
+                a.lines += lds.wait(keys[item[1]])
+
+    for f in pending.get(-1, []):
+        issue_reads(f)
+    run_events(-1)
+    for p, f in enumerate(frags):
         a.lines += lds.wait(max(f.read_ids))
-        a.lines += f.mfmas
-        if p + NB < len(p0):
-            g = p0[p + NB]
-            for r in g.reads:
-                g.read_ids.append(lds.issue())
-                a.lines.append(r)
+        for m, mf in enumerate(f.mfmas):
+            if f.deps[m]:
+                a.lines += lds.wait(max(keys[k] for k in f.deps[m]))
+            a.lines.append(mf)
+            a.lines += slots.get((p, m), [])
+        for g in pending.get(p, []):
+            issue_reads(g)
+        run_events(p)
+        if marks and p in marks:
+            a.comment(f"phase {marks[p]} issued")
 
 
 # ============================================================== fp8 cache
@@ -1106,6 +1069,179 @@ def epilogue(a):
         a.label(stored)
 
 
+def epilogue_split(a):
+    """bf16 kernel, end of a segment (after a barrier that every wave reaches
+    past its last output MFMA): publish this wave's row sums and its restart
+    request; restart the segment if any wave asks; else normalise this wave's
+    128 output columns of all 128 query rows by their row sums and store them
+    (final result, or partial slot 0 / 1 of the partition), with the lse of
+    the wave's own rows."""
+    T = S_TMP
+    L, t0, t1 = (16, 17), 18, 19
+    for h in range(2):
+        a(f"v_mov_b32 {vreg(L[h])}, {vreg(V_LRUN[h])}")
+        xor_reduce(a, L[h], "v_add_f32", t0, t1)
+    # row sum of query row 32w + 16h + r16 at P_BASE + 4 (32w + 16h + r16); request at P_BASE + 512 + 4w
+    a(f"s_lshl_b32 s{T}, {s(S_WAVE)}, 7",
+      f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
+      f"v_add_u32 {vreg(t0)}, s{T}, {vreg(t0)}",
+      f"v_add_u32 {vreg(t0)}, {P_BASE}, {vreg(t0)}",
+      f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
+      f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
+      f"ds_write_b32 {vreg(t0)}, {vreg(L[0])}",
+      f"ds_write_b32 {vreg(t0)}, {vreg(L[1])} offset:64",
+      f"s_mov_b64 exec, {sp(S_EXEC)}",
+      f"s_cmp_lg_u64 {sp(S_OVF)}, 0",
+      f"s_cselect_b32 s{T + 1}, 1, 0",
+      f"s_lshl_b32 s{T}, {s(S_WAVE)}, 2",
+      f"s_add_u32 s{T}, s{T}, {P_BASE + 512}",
+      f"v_mov_b32 {vreg(t0)}, s{T}",
+      f"v_mov_b32 {vreg(t1)}, s{T + 1}",
+      f"ds_write_b32 {vreg(t0)}, {vreg(t1)}",
+      s_waitcnt_lgkm(0),
+      "s_barrier",
+      f"v_mov_b32 {vreg(t0)}, {P_BASE + 512}",
+      f"ds_read_b128 {vr(20, 4)}, {vreg(t0)}",
+      s_waitcnt_lgkm(0),
+      "v_or3_b32 v20, v20, v21, v22",
+      "v_or_b32 v20, v20, v23",
+      "s_nop 1",
+      f"v_readfirstlane_b32 s{T}, v20",
+      f"s_cmp_eq_u32 s{T}, 0",
+      "s_cbranch_scc0 .Lrestart")
+    # row sums of all 128 query rows -> 1 / l (0 for a row that saw nothing): lane (g, r16), block hb
+    inv = list(range(24, 32))
+    a(f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
+      f"v_add_u32 {vreg(t0)}, {P_BASE}, {vreg(t0)}")
+    for hb in range(8):
+        a(f"ds_read_b32 {vreg(inv[hb])}, {vreg(t0)} offset:{64 * hb}")
+    # destination: R = first token row of the (sequence | partition slot), flag s[T+3] = partial
+    whole_no, pslot1, addr_done = a.new_label("notwhole"), a.new_label("pslot1"), a.new_label("addrdone")
+    a(f"s_cmp_lt_u32 {s(S_CPRE)}, {s(S_UA)}",
+      f"s_cbranch_scc1 {whole_no}",
+      f"s_add_u32 s{T}, {s(S_CPRE)}, {s(S_CUNITS)}",
+      f"s_cmp_gt_u32 s{T}, {s(S_UB)}",
+      f"s_cbranch_scc1 {whole_no}",
+      f"s_mul_i32 s{T + 1}, {s(S_CSEQ)}, {s(S_SQ)}",
+      f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_OUT)}",
+      f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_LSE)}",
+      f"s_mov_b32 s{T + 3}, 0",
+      f"s_branch {addr_done}")
+    a.label(whole_no)
+    a(f"s_mov_b32 s{T + 2}, 0",
+      f"s_cmp_le_u32 {s(S_CPRE)}, {s(S_UA)}",
+      f"s_cbranch_scc1 {pslot1}",
+      f"s_mov_b32 s{T + 2}, 1")
+    a.label(pslot1)
+    a(f"s_lshl_b32 s{T + 1}, {s(S_PART)}, 1",
+      f"s_add_u32 s{T + 1}, s{T + 1}, s{T + 2}",
+      f"s_mul_i32 s{T + 1}, s{T + 1}, {s(S_SQ)}",
+      f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_POUT)}",
+      f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_PLSE)}",
+      f"s_mov_b32 s{T + 3}, 1")
+    a.label(addr_done)
+    # lse of this wave's rows (lanes g == 0): row (R + stok) * 128 + head0 + 16h + r16
+    a(f"s_add_u32 s{T + 8}, s{T + 1}, {s(S_STOK)}",
+      f"s_lshl_b32 s{T + 8}, s{T + 8}, 7",
+      f"s_add_u32 s{T + 8}, s{T + 8}, {s(S_HEAD0)}",
+      f"s_lshl_b32 s{T + 8}, s{T + 8}, 2",
+      f"s_add_u32 s{T + 10}, s{T + 6}, s{T + 8}",
+      f"s_addc_u32 s{T + 11}, s{T + 7}, 0")
+    for h in range(2):
+        lse = t1
+        a(f"v_log_f32 {vreg(lse)}, {vreg(L[h])}",
+          "s_nop 1",
+          f"v_cmp_lt_f32 vcc, 0, {vreg(L[h])}",
+          f"v_add_f32 {vreg(lse)}, {vreg(V_MREF[h])}, {vreg(lse)}",
+          f"v_mul_f32 {vreg(lse)}, {LN2}, {vreg(lse)}",
+          "s_nop 1",
+          f"v_cndmask_b32 {vreg(lse)}, {vreg(V_NEGINF)}, {vreg(lse)}, vcc",
+          f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
+          f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
+          f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
+          f"global_store_dword {vreg(t0)}, {vreg(lse)}, s[{T + 10}:{T + 11}] offset:{64 * h}",
+          f"s_mov_b64 exec, {sp(S_EXEC)}")
+    a(s_waitcnt_lgkm(0))
+    for hb in range(8):
+        a(f"v_rcp_f32 {vreg(t1)}, {vreg(inv[hb])}",
+          f"v_cmp_lt_f32 vcc, 0, {vreg(inv[hb])}",
+          "s_nop 1",
+          f"v_cndmask_b32 {vreg(inv[hb])}, 0, {vreg(t1)}, vcc")
+    a("s_nop 7", "s_nop 7", "s_nop 3")   # last MFMAs -> accvgpr reads
+    # per owner group j (query rows 32j ..): token (32j) >> log2(heads per block), head
+    # (32j & (heads per block - 1)) + head block * heads per block; base pointer s[T+12+2j : +1]
+    a(f"s_ff1_i32_b32 s{T + 9}, {s(S_HB)}",
+      f"s_sub_u32 s{T + 10}, {s(S_HB)}, 1",
+      f"s_mul_i32 s{T + 11}, {s(S_HBLK)}, {s(S_HB)}")
+    for j in range(4):
+        b = T + 12 + 2 * j
+        a(f"s_lshr_b32 s{b}, {32 * j}, s{T + 9}",
+          f"s_add_u32 s{b}, s{b}, s{T + 1}",
+          f"s_lshl_b32 s{b}, s{b}, 7",
+          f"s_and_b32 s{b + 1}, {32 * j}, s{T + 10}",
+          f"s_add_u32 s{b}, s{b}, s{b + 1}",
+          f"s_add_u32 s{b}, s{b}, s{T + 11}",
+          f"s_mul_hi_u32 s{b + 1}, s{b}, 2048",
+          f"s_mul_i32 s{b}, s{b}, 2048",
+          f"s_add_u32 s{b}, s{b}, s{T + 4}",
+          f"s_addc_u32 s{b + 1}, s{b + 1}, s{T + 5}")
+    bufs = [list(range(32 + 4 * k, 36 + 4 * k)) for k in range(4)]
+    off = 48
+    rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
+    a(f"s_cmp_eq_u32 s{T + 3}, 0",
+      f"s_cbranch_scc1 {rowwise}")
+    # partial: lane order, block (hb = 2j + a, column block c = 8w + cb) at (32a + c) KB + 16 L
+    # of group j's 64 KB
+    a(f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
+      f"s_lshl_b32 s{T + 8}, {s(S_WAVE)}, 13")
+    n = 0
+    for j in range(4):
+        b = T + 12 + 2 * j
+        for h in range(2):
+            a(f"s_add_u32 s{T + 6}, s{b}, s{T + 8}",
+              f"s_addc_u32 s{T + 7}, s{b + 1}, 0")
+            if h:
+                a(f"s_add_u32 s{T + 6}, s{T + 6}, 0x8000",
+                  f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
+            for cb in range(8):
+                if cb == 4:
+                    a(f"s_add_u32 s{T + 6}, s{T + 6}, 4096", f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
+                epi_store_split(a, 2 * j + h, cb, bufs[n % 4], inv[2 * j + h],
+                                f"{vreg(off)}, {{v}}, s[{T + 6}:{T + 7}] offset:{1024 * (cb % 4)}")
+                n += 1
+    a(f"s_branch {stored}")
+    # final result: row layout, lane (g, r16) of block (hb, cb) -> row head + 16h + r16,
+    # columns 128w + 16cb + 4g ..
+    a.label(rowwise)
+    a(f"v_lshlrev_b32 {vreg(t0)}, 4, {vreg(V_G)}",
+      f"v_lshl_add_u32 {vreg(off)}, {vreg(V_R16)}, 11, {vreg(t0)}",
+      f"s_lshl_b32 s{T + 8}, {s(S_WAVE)}, 9")
+    for j in range(4):
+        b = T + 12 + 2 * j
+        for h in range(2):
+            a(f"s_add_u32 s{T + 6}, s{b}, s{T + 8}",
+              f"s_addc_u32 s{T + 7}, s{b + 1}, 0")
+            if h:
+                a(f"s_add_u32 s{T + 6}, s{T + 6}, 0x8000",
+                  f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
+            for cb in range(8):
+                epi_store_split(a, 2 * j + h, cb, bufs[n % 4], inv[2 * j + h],
+                                f"{vreg(off)}, {{v}}, s[{T + 6}:{T + 7}] offset:{64 * cb}")
+                n += 1
+    a.label(stored)
+
+
+def epi_store_split(a, hb, cb, vv, inv, operands):
+    """O[cb][hb] / l -> one 16-byte store per lane."""
+    o = (8 * cb + hb) * 4
+    for i in range(4):
+        a(f"v_accvgpr_read_b32 {vreg(vv[i])}, a{o + i}")
+    a("s_nop 1")
+    for i in range(4):
+        a(f"v_mul_f32 {vreg(vv[i])}, {vreg(vv[i])}, {vreg(inv)}")
+    a("global_store_dwordx4 " + operands.format(v=vr(vv[0], 4)))
+
+
 def epi_store(a, h, cb, vv, inv, operands):
     """O[cb][h] * inv -> one 16-byte store per lane."""
     o = (2 * cb + h) * 4
@@ -1205,69 +1341,6 @@ def flag_check(a):
       "s_cbranch_scc0 .Lrestart")
 
 
-def unit_body_bf16(a):
-    """One unit of the bf16 kernel up to the unit-end label (returned)."""
-    T = S_TMP
-    a.label(".Lunit")
-    a(f"s_mov_b64 {sp(S_OVF)}, 0",
-      f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
-      f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")
-    # this unit's rows have landed (own loads), the table prefetch too, and
-    # every wave is past the previous unit
-    a(s_waitcnt_vm(0), s_waitcnt_lgkm(0), "s_barrier")
-    a(f"v_mov_b32 {vreg(V_T)}, {FLAG_ADDR}",
-      f"ds_read_b32 {vreg(V_T)}, {vreg(V_T)}")       # restart flag, checked below
-    take_prefetched(a)
-    loader_page(a)
-    a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
-    dma_setup(a, T + 21)
-    a(f"s_add_u32 s{T + 19}, {s(S_UCUR)}, 1")
-    prefetch_next(a, T + 19)
-    a(f"s_sub_u32 {s(S_ROW0)}, {s(S_UCUR)}, {s(S_CPRE)}",
-      f"s_lshl_b32 {s(S_ROW0)}, {s(S_ROW0)}, 6",
-      f"s_mul_i32 s{T}, {s(S_SLOT)}, {SLOT_BYTES}",
-      f"v_add_u32 {vreg(V_UQ)}, s{T}, {vreg(V_QKE)}",
-      f"v_add_u32 {vreg(V_UQ + 1)}, s{T}, {vreg(V_QKO)}",
-      f"v_add_u32 {vreg(V_UQ + 2)}, 0x10000, {vreg(V_UQ)}",
-      f"v_add_u32 {vreg(V_UQ + 3)}, 0x10000, {vreg(V_UQ + 1)}",
-      f"v_add_u32 {vreg(V_UP)}, s{T}, {vreg(V_PV0)}")
-    for m in range(1, 4):
-        a(f"v_xor_b32 {vreg(V_UP + m)}, {32 * m}, {vreg(V_PV0)}",
-          f"v_add_u32 {vreg(V_UP + m)}, s{T}, {vreg(V_UP + m)}")
-    # rows of this unit this wave's query token sees: none, only the first 32, or more
-    a(s_waitcnt_lgkm(0),
-      "s_nop 1",
-      f"v_readfirstlane_b32 s{T}, {vreg(V_T)}",
-      f"s_cmp_eq_u32 s{T}, 0",
-      "s_cbranch_scc0 .Lrestart")
-    # fully visible units after the first of the segment take the lean softmax
-    half, none, uend, classic = (a.new_label(x) for x in ("half", "none", "uend", "classic"))
-    a(f"s_sub_i32 s{T}, {s(S_NVIS)}, {s(S_ROW0)}",
-      f"s_cmp_le_i32 s{T}, 0",
-      f"s_cbranch_scc1 {none}",
-      f"s_cmp_le_i32 s{T}, 32",
-      f"s_cbranch_scc1 {half}",
-      f"s_cmp_lt_i32 s{T}, 64",
-      f"s_cbranch_scc1 {classic}",
-      f"s_max_u32 s{T + 1}, {s(S_UA)}, {s(S_CPRE)}",
-      f"s_cmp_eq_u32 {s(S_UCUR)}, s{T + 1}",
-      f"s_cbranch_scc1 {classic}",
-      f"s_cmp_eq_u32 {s(S_EXACT)}, 0",
-      f"s_cbranch_scc0 {classic}")
-    unit_full(a, lean=True)
-    a(f"s_branch {uend}")
-    a.label(classic)
-    unit_full(a, lean=False)
-    a(f"s_branch {uend}")
-    a.label(half)
-    unit_half(a)
-    a(f"s_branch {uend}")
-    a.label(none)
-    for g in dma_groups():
-        a.lines += g
-    return uend
-
-
 def unit_body_fp8(a):
     """One unit of the fp8 kernel up to the unit-end label (returned)."""
     T = S_TMP
@@ -1326,6 +1399,546 @@ def unit_body_fp8(a):
     substep_fp8(a, 0, lean=False)
     return uend
 
+
+# ======================================================= bf16: half-page steps
+# The bf16 kernel works in steps of 32 rows (half a page).  LDS holds four
+# half-page tiles (9 x 4 blocks of 1 KB: block (K, R) at (4K + R) KB holds rows
+# 8R..8R+7, chunks 8K..8K+7, swizzled as in the page tile) and two 8 KB
+# probability buffers.  Step t reads tile t % 4 for its scores, tile
+# (t - 1) % 4 for the output of step t - 1, publishes its probabilities in
+# buffer t % 2 and issues the loads of step t + 2 into tile (t + 2) % 4, which
+# step t - 2 (output done during step t - 1) has freed.  One barrier per step.
+HS_BYTES = 32 * 1152
+PB_BYTES = 8192
+H_S = 16                          # S[tb][h] at 16 + (2tb + h) * 4; packed P at 16 + 4h after the softmax
+H_SMT = (32, 33, 34, 35)          # softmax scratch
+H_A, H_NA = 36, 4                 # score-operand ring (v36..v51)
+H_PF = tuple(range(52, 84, 4))    # probability fragments of the previous step, one per 16-row block
+H_B, H_NB = 84, 3                 # output-operand ring (v84..v95)
+V_PXR = 106                       # P_BASE + 16 lane + 8192 ((t - 1) % 2): the previous step's fragments
+V_LDZ = 105                       # source offset of a load lane whose row holds no data (row 0 of the half)
+V_DMAS = V_T + 1                  # source offsets of this wave's loads of the next step (masked)
+S_T, S_TL, S_PH, S_NSTEP = 92, 93, 94, 96   # step of the partition, of the segment; half-page address; steps
+S_PNONE = 51                      # 1: the previous step had no visible row (its output is skipped:
+                                  # the rows of its tile may lie past the sequence's data)
+V_PVM = (V_PV0, 98, 99, 107)      # output-read lane offsets of the four 16-column phases of a chunk group
+# values of the next step, computed during the current one (scalar temporaries the
+# steps leave alone; the epilogue does not, so a segment start recomputes them)
+N_PH, N_STEP, N_NVH, N_ROW0, N_MODE, N_DMALDS = 70, 72, 74, 75, 76, 77
+S_LKUP = 3                        # page to look up (the loader items' own; s3 holds nothing else)
+DMA_EARLY = 9                     # > 0: the loads of step t + 2 go out over fragments 0..DMA_EARLY
+
+
+def lane_constants_hp(a):
+    """bf16 step constants (after lane_constants): wave w loads row group w
+    of a half page (rows 8w + lr, lr = lane >> 3), V_LDA its source offset
+    in the half page, V_LDZ that of row 0 (rows past the data); the wave's
+    output columns 128w .. in V_PV0 (8 KB per 128 columns of a half tile);
+    the exchange-buffer lane address V_PX."""
+    T = S_TMP
+    u0, u3 = V_S[0], V_S[0] + 3
+    a(f"v_lshrrev_b32 {vreg(u0)}, 3, {vreg(V_LANE)}",
+      f"s_and_b32 s{T}, {s(S_WAVE)}, 1",
+      f"s_lshl_b32 s{T}, s{T}, 5",
+      f"v_xor_b32 {vreg(V_LDZ)}, s{T}, {vreg(V_LCA)}",
+      f"s_lshl_b32 s{T}, {s(S_WAVE)}, 3",
+      f"v_add_u32 {vreg(V_LDROW)}, s{T}, {vreg(u0)}",
+      f"v_mul_u32_u24 {vreg(u3)}, 1152, {vreg(V_LDROW)}",
+      f"v_add_u32 {vreg(V_LDA)}, {vreg(u3)}, {vreg(V_LDZ)}",
+      f"v_lshlrev_b32 {vreg(V_PX)}, 4, {vreg(V_LANE)}",
+      f"v_add_u32 {vreg(V_PX)}, {P_BASE}, {vreg(V_PX)}",
+      f"s_lshl_b32 s{T}, {s(S_WAVE)}, 13",
+      f"v_add_u32 {vreg(V_PV0)}, s{T}, {vreg(V_PV0)}")
+    for m in range(1, 4):
+        a(f"v_xor_b32 {vreg(V_PVM[m])}, {32 * m}, {vreg(V_PV0)}")
+
+
+def qk_read_hp(i):
+    """A fragment (ks, tb) = divmod(i, 2): rows 16tb + r16 of the half tile, chunk 4ks + g."""
+    ks, tb = divmod(i, 2)
+    return [f"\tds_read_b128 {{buf}}, {vreg(V_UQ + (ks & 1))} offset:{4096 * (ks >> 1) + 2048 * tb}"]
+
+
+def pv_read_hp(cb):
+    """V^T operand of this wave's column block cb: rows 4g + r, then 16 + 4g + r."""
+    off = 4096 * (cb >> 2)
+    base = V_UP + (cb & 3)
+    return [f"\tds_read_b64_tr_b16 {{lo}}, {vreg(base)} offset:{off}",
+            f"\tds_read_b64_tr_b16 {{hi}}, {vreg(base)} offset:{off + 2048}"]
+
+
+def qk_frags_hp():
+    out = []
+    for i in range(36):
+        ks, tb = divmod(i, 2)
+        mf = []
+        for h in range(2):
+            sreg = H_S + (2 * tb + h) * 4
+            qreg = V_Q + (2 * ks + h) * 4
+            c = "0" if ks == 0 else vr(sreg, 4)
+            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(sreg, 4)}, {{buf}}, {vr(qreg, 4)}, {c}")
+        out.append(Frag("A", H_A, H_NA, i, qk_read_hp(i), mf))
+    return out
+
+
+def pv_frags_hp():
+    """Output of the previous step: fragment cb (this wave's columns 16cb ..)
+    times the probability fragment of every 16-row block hb of query rows."""
+    out = []
+    for cb in range(8):
+        mf, deps = [], []
+        for hb in range(8):
+            o = (8 * cb + hb) * 4
+            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {ar(o, 4)}, {{buf}}, {vr(H_PF[hb], 4)}, {ar(o, 4)}")
+            deps.append((("pf", hb),))
+        out.append(Frag("B", H_B, H_NB, cb, pv_read_hp(cb), mf, deps))
+    return out
+
+
+def p_gather_hp():
+    """Events: the previous step's probability fragments of all query rows."""
+    return [("lds", f"\tds_read_b128 {vr(H_PF[hb], 4)}, {vreg(V_PXR)} offset:{1024 * hb}", ("pf", hb))
+            for hb in range(8)]
+
+
+def p_publish_hp():
+    """This wave's packed probabilities (fragments 2w, 2w + 1 of its buffer)."""
+    return [f"\tds_write_b128 {vreg(V_PXW)}, {vr(H_S + 4 * h, 4)} offset:{1024 * h}" for h in range(2)]
+
+
+def dma_groups_hp():
+    """The 9 direct-to-LDS loads of this wave for one half page: row group
+    w, chunk groups K = 0..8 (one 8-row x 8-chunk block each)."""
+    groups = []
+    for k in range(9):
+        groups.append([f"\ts_add_u32 s{S_DPAGE}, s{S_PH}, {128 * k}",
+                       f"\ts_addc_u32 s{S_DPAGE + 1}, s{S_PH + 1}, 0",
+                       f"\ts_add_u32 m0, {s(S_DMALDS)}, {4096 * k}",
+                       "\ts_nop 0",
+                       f"\tglobal_load_lds_dwordx4 {vreg(V_DMAS)}, {sp(S_DPAGE)}"])
+    return groups
+
+
+def dma_setup_hp(a, half, step_sgpr):
+    """Loads of half `half` of page S_PAGE (S_NVALID rows hold data) into the
+    tile of step s[step_sgpr]: lane source offsets (row 0 of the half for rows
+    past the data), LDS base, half-page address."""
+    T = S_TMP
+    a(f"s_sub_i32 s{T + 6}, {s(S_NVALID)}, {32 * half}",
+      f"v_cmp_gt_i32 vcc, s{T + 6}, {vreg(V_LDROW)}",
+      f"s_and_b32 s{T + 7}, s{step_sgpr}, 3",
+      f"s_mul_i32 {s(S_DMALDS)}, s{T + 7}, {HS_BYTES}",
+      f"s_lshl_b32 s{T + 7}, {s(S_WAVE)}, 10",
+      f"s_add_u32 {s(S_DMALDS)}, {s(S_DMALDS)}, s{T + 7}",
+      f"v_cndmask_b32 {vreg(V_DMAS)}, {vreg(V_LDZ)}, {vreg(V_LDA)}, vcc",
+      f"s_add_u32 s{S_PH}, s{S_PAGE}, {HS_BYTES * half}",
+      f"s_addc_u32 s{S_PH + 1}, s{S_PAGE + 1}, 0")
+
+
+def issue_page_hp(a):
+    """Stand-alone loads of both halves of page S_UCUR into the tiles of steps
+    S_T and S_T + 1 (segment start after a restart, and the first page)."""
+    T = S_TMP
+    loader_advance(a, S_UCUR)
+    loader_lookup(a, S_UCUR, wait=True)
+    loader_page(a)
+    for half in range(2):
+        a(f"s_add_u32 s{T + 8}, {s(S_T)}, {half}")
+        dma_setup_hp(a, half, T + 8)
+        for g in dma_groups_hp():
+            a.lines += g
+
+
+def _atomic(lines):
+    """Instruction lines (an Asm's) -> one filler item kept together."""
+    return [list(lines)]
+
+
+def take_items(n_sgpr):
+    """Filler items, loader side of step n (= s[n_sgpr]): the loads issued in
+    step n are those of step n + 2, page UA + ((n + 2) >> 1), half n & 1.  For
+    even n that page is new: take its prefetched rows / entry and address."""
+    T = S_TMP
+    return [["\ts_bitcmp1_b32 s%d, 0" % n_sgpr,
+             f"\ts_cselect_b32 {s(S_NVALID)}, {s(S_NVALID)}, {s(S_NV2)}",
+             f"\ts_cselect_b32 {s(S_ENTRY)}, {s(S_ENTRY)}, {s(S_ENT2)}"],
+            f"\ts_mul_i32 s{T + 4}, {s(S_ENTRY)}, {PAGE_BYTES}",
+            f"\ts_mul_hi_u32 s{T + 5}, {s(S_ENTRY)}, {PAGE_BYTES}",
+            [f"\ts_add_u32 s{T + 4}, {s(S_ROWS)}, s{T + 4}",
+             f"\ts_addc_u32 s{T + 5}, {s(S_ROWS + 1)}, s{T + 5}"],
+            [f"\ts_cmp_gt_i32 {s(S_NVALID)}, 0",
+             f"\ts_cselect_b64 {sp(S_PAGE)}, s[{T + 4}:{T + 5}], {sp(S_ROWS)}"]]
+
+
+def lookup_items(u_sgpr):
+    """Filler items: look up page u (= s[u_sgpr], may lie past the partition):
+    S_NV2 = its rows holding data (0 past the partition), S_ENT2 = its page
+    (for a paged cache a scalar load left in flight: read only after a later
+    lgkmcnt(0)).  The loader cursor moves to the sequence of min(u, UB - 1)."""
+    T = S_TMP
+    items = [f"\ts_sub_u32 s{T + 3}, {s(S_UB)}, 1",
+             f"\ts_min_u32 s{T + 19}, s{u_sgpr}, s{T + 3}"]
+    a2 = Asm()
+    loader_advance(a2, T + 19)
+    items += _atomic(a2.lines)
+    skip = Asm().new_label("pfskip")
+    items += [f"\ts_sub_u32 s{T + 1}, s{T + 19}, {s(S_LPRE)}",
+              f"\ts_lshl_b32 s{T + 2}, s{T + 1}, 6",
+              f"\ts_sub_i32 {s(S_NV2)}, {s(S_LLEN)}, s{T + 2}",
+              f"\ts_min_i32 {s(S_NV2)}, {s(S_NV2)}, 64",
+              f"\ts_mul_i32 s{T + 4}, {s(S_LSEQ)}, {s(S_MAXB)}",
+              f"\ts_add_u32 {s(S_ENT2)}, s{T + 4}, s{T + 1}",
+              [f"\ts_cmp_lt_u32 s{u_sgpr}, {s(S_UB)}",
+               f"\ts_cselect_b32 {s(S_NV2)}, {s(S_NV2)}, 0"],
+              [f"\ts_cmp_gt_i32 {s(S_NV2)}, 0",
+               f"\ts_cbranch_scc0 {skip}",
+               f"\ts_cmp_eq_u64 {sp(S_TABLE)}, 0",
+               f"\ts_cbranch_scc1 {skip}",
+               f"\ts_lshl_b32 s{T + 5}, {s(S_ENT2)}, 2",
+               f"\ts_load_dword {s(S_ENT2)}, {sp(S_TABLE)}, s{T + 5}",
+               f"{skip}:"]]
+    return items
+
+
+def loader_items(n_sgpr):
+    """take_items(n), then the lookup of the page after the loads' page
+    (every step; an odd step repeats the even one's)."""
+    T = S_TMP
+    return (take_items(n_sgpr) +
+            [f"\ts_lshr_b32 s{S_LKUP}, s{n_sgpr}, 1",
+             f"\ts_add_u32 s{S_LKUP}, s{S_LKUP}, {s(S_UA)}",
+             f"\ts_add_u32 s{S_LKUP}, s{S_LKUP}, 2"] + lookup_items(S_LKUP))
+
+
+def next_items(n_sgpr, tl_first):
+    """Filler items: the values step n (= s[n_sgpr]) starts from (N_*): its
+    loads (half page, LDS base, rows holding data), its first row in the
+    sequence and its kind (tl_first: n is a segment's first step)."""
+    T = S_TMP
+    n = n_sgpr
+    items = [f"\ts_and_b32 s{T + 6}, s{n}, 1",                       # half of the loads / buffer parity
+             f"\ts_mul_i32 s{T + 7}, s{T + 6}, {HS_BYTES}",
+             [f"\ts_add_u32 s{N_PH}, s{S_PAGE}, s{T + 7}",
+              f"\ts_addc_u32 s{N_PH + 1}, s{S_PAGE + 1}, 0"],
+             f"\ts_lshl_b32 s{T + 7}, s{T + 6}, 5",
+             f"\ts_sub_i32 s{N_NVH}, {s(S_NVALID)}, s{T + 7}",
+             f"\ts_add_u32 s{T + 7}, s{n}, 2",
+             f"\ts_and_b32 s{T + 7}, s{T + 7}, 3",
+             f"\ts_mul_i32 s{N_DMALDS}, s{T + 7}, {HS_BYTES}",
+             f"\ts_lshl_b32 s{T + 7}, {s(S_WAVE)}, 10",
+             f"\ts_add_u32 s{N_DMALDS}, s{N_DMALDS}, s{T + 7}",
+             # first row of the step in its sequence: 64 (page - first page of the sequence) + 32 half
+             f"\ts_lshr_b32 s{N_ROW0}, s{n}, 1",
+             f"\ts_add_u32 s{N_ROW0}, s{N_ROW0}, {s(S_UA)}",
+             f"\ts_sub_u32 s{N_ROW0}, s{N_ROW0}, {s(S_CPRE)}",
+             f"\ts_lshl_b32 s{N_ROW0}, s{N_ROW0}, 1",
+             f"\ts_add_u32 s{N_ROW0}, s{N_ROW0}, s{T + 6}",
+             f"\ts_lshl_b32 s{N_ROW0}, s{N_ROW0}, 5",
+             # kind: 0 none (no query token of the workgroup sees a row of it),
+             # 3 lean (every token sees all 32 rows, not a segment's first step,
+             # no restart), else 2 classic
+             f"\ts_sub_i32 s{T + 8}, {s(S_NVHI)}, s{N_ROW0}",
+             f"\ts_sub_i32 s{T + 9}, {s(S_NVLO)}, s{N_ROW0}",
+             f"\ts_mov_b32 s{N_MODE}, {2 if tl_first else 3}",
+             [f"\ts_cmp_lt_i32 s{T + 9}, 32",
+              f"\ts_cselect_b32 s{N_MODE}, 2, s{N_MODE}"],
+             [f"\ts_cmp_lg_u32 {s(S_EXACT)}, 0",
+              f"\ts_cselect_b32 s{N_MODE}, 2, s{N_MODE}"],
+             [f"\ts_cmp_le_i32 s{T + 8}, 0",
+              f"\ts_cselect_b32 s{N_MODE}, 0, s{N_MODE}"]]
+    return items
+
+
+def pre_step_items():
+    """Filler items of a step: everything the next step starts from."""
+    return ([f"\ts_add_u32 s{N_STEP}, {s(S_T)}, 1"] + loader_items(N_STEP) + next_items(N_STEP, False))
+
+
+def flatten(items):
+    out = []
+    for x in items:
+        out += x if isinstance(x, list) else [x]
+    return out
+
+
+def step_body_hp(a, kind, with_pv):
+    """kind: 'lean' | 'classic' | 'none'.  Scores and softmax of this step
+    (none: P = 0), the output of the previous step (with_pv), the loads of
+    step t + 2, the values the next step starts from, the publication of this
+    step's probabilities."""
+    qk = qk_frags_hp() if kind != "none" else []
+    pv = pv_frags_hp() if with_pv else []
+    groups = [list(g) for g in dma_groups_hp()]
+    pre = pre_step_items()
+    if kind == "none":
+        a(*[f"v_mov_b32 {vreg(H_S + i)}, 0" for i in range(8)])
+    if qk and pv:
+        # scores interleaved with the first three output fragments (balances
+        # the LDS traffic), the last five output fragments carry the softmax
+        order = qk[0:9] + [pv[0]] + qk[9:18] + [pv[1]] + qk[18:27] + [pv[2]] + qk[27:36] + pv[3:]
+        tail = order.index(pv[3])
+        sm = (softmax_lean if kind == "lean" else softmax_code)(0, S=H_S, P=H_S, tmp=H_SMT)
+        # the softmax starts one fragment after the last score MFMA (MFMA
+        # results -> VALU); the load groups stay whole (their carry chains)
+        if DMA_EARLY:
+            fillers = [(0, DMA_EARLY, groups), (0, tail - 1, pre),
+                       (tail + 1, len(order) - 1, merge_filler(sm, []))]
+        else:
+            fillers = [(0, tail - 1, pre),
+                       (tail, tail, groups[:2]),
+                       (tail + 1, len(order) - 1, merge_filler(sm, groups[2:]))]
+        events = {-1: p_gather_hp(), len(order) - 1: p_publish_hp()}
+        emit_stream(a, order, {"A": -1, "B": -1}, fillers, events, marks={tail - 1: 1, len(order) - 1: 2})
+    elif qk:
+        emit_stream(a, qk, {"A": -1}, [(0, 35, groups), (0, 35, pre)])
+        a("s_nop 7", "s_nop 7", "s_nop 3")   # MFMA results -> VALU
+        a.lines += (softmax_lean if kind == "lean" else softmax_code)(0, S=H_S, P=H_S, tmp=H_SMT)
+        a.lines += p_publish_hp()
+    elif pv:
+        emit_stream(a, pv, {"B": -1}, [(0, 7, groups), (0, 7, pre)], {-1: p_gather_hp(), 7: p_publish_hp()})
+    else:
+        a.lines += flatten(groups) + flatten(pre)
+        a.lines += p_publish_hp()
+
+
+def drain_hp(a):
+    """The output of a segment's last step (its probabilities published
+    before the barrier), unless that step had no visible row."""
+    skip = a.new_label("nodrain")
+    a(f"s_cmp_lg_u32 {s(S_PNONE)}, 0",
+      f"s_cbranch_scc1 {skip}",
+      s_waitcnt_lgkm(0), "s_barrier")
+    drain_bases_hp(a)
+    pv = pv_frags_hp()
+    emit_stream(a, pv, {"B": -1}, [], {-1: p_gather_hp()})
+    a.label(skip)
+
+
+def step_hp(a):
+    """One step: take the precomputed values, wait for this step's rows and
+    for every wave, run the body for the step's kind."""
+    T = S_TMP
+    a.label(".Lstep")
+    a(f"s_mov_b32 {s(S_ROW0)}, s{N_ROW0}",
+      f"s_mov_b32 {s(S_MODE)}, s{N_MODE}",
+      f"s_mov_b64 {sp(S_PH)}, s[{N_PH}:{N_PH + 1}]",
+      f"s_mov_b32 {s(S_DMALDS)}, s{N_DMALDS}",
+      # this step's tile, the previous step's; this step's probability buffer (plus
+      # the wave's fragments), the previous step's
+      f"s_and_b32 s{T}, {s(S_T)}, 3",
+      f"s_mul_i32 s{T}, s{T}, {HS_BYTES}",
+      f"s_add_u32 s{T + 1}, {s(S_T)}, 3",
+      f"s_and_b32 s{T + 1}, s{T + 1}, 3",
+      f"s_mul_i32 s{T + 1}, s{T + 1}, {HS_BYTES}",
+      f"s_and_b32 s{T + 2}, {s(S_T)}, 1",
+      f"s_lshl_b32 s{T + 2}, s{T + 2}, 13",
+      f"s_lshl_b32 s{T + 3}, {s(S_WAVE)}, 11",
+      f"s_add_u32 s{T + 3}, s{T + 3}, s{T + 2}",
+      f"s_xor_b32 s{T + 2}, s{T + 2}, {PB_BYTES}",
+      f"v_add_u32 {vreg(V_UQ)}, s{T}, {vreg(V_QKE)}",
+      f"v_add_u32 {vreg(V_UQ + 1)}, s{T}, {vreg(V_QKO)}",
+      *[f"v_add_u32 {vreg(V_UP + m)}, s{T + 1}, {vreg(V_PVM[m])}" for m in range(4)],
+      f"v_add_u32 {vreg(V_PXW)}, s{T + 3}, {vreg(V_PX)}",
+      f"v_add_u32 {vreg(V_PXR)}, s{T + 2}, {vreg(V_PX)}",
+      f"v_cmp_gt_i32 vcc, s{N_NVH}, {vreg(V_LDROW)}",
+      "s_nop 1",
+      f"v_cndmask_b32 {vreg(V_DMAS)}, {vreg(V_LDZ)}, {vreg(V_LDA)}, vcc")
+    # this step's rows have landed (the next step's nine loads may still be in
+    # flight; a segment's first step also waits for its Q loads)
+    w0, wdone = a.new_label("w0"), a.new_label("wdone")
+    a(f"s_cmp_eq_u32 {s(S_TL)}, 0",
+      f"s_cbranch_scc1 {w0}",
+      s_waitcnt_vm(9),
+      f"s_branch {wdone}")
+    a.label(w0)
+    a(s_waitcnt_vm(0))
+    a.label(wdone)
+    a(s_waitcnt_lgkm(0), "s_barrier")
+    first, notlean, nonepv, nonefirst, send = (a.new_label(x) for x in
+                                               ("first", "notlean", "nonepv", "nonefirst", "send"))
+    # steps without visible rows come last in a segment: after the first of
+    # them (whose output of the step before it is still due) none has an output
+    a(f"s_cmp_eq_u32 {s(S_TL)}, 0",
+      f"s_cbranch_scc1 {first}",
+      f"s_cmp_lg_u32 {s(S_PNONE)}, 0",
+      f"s_cbranch_scc1 {nonefirst}",
+      f"s_cmp_lt_u32 {s(S_MODE)}, 3",
+      f"s_cbranch_scc1 {notlean}")
+    step_body_hp(a, "lean", True)
+    a(f"s_branch {send}")
+    a.label(notlean)
+    a(f"s_cmp_eq_u32 {s(S_MODE)}, 0",
+      f"s_cbranch_scc1 {nonepv}")
+    step_body_hp(a, "classic", True)
+    a(f"s_branch {send}")
+    a.label(nonepv)
+    step_body_hp(a, "none", True)
+    a(f"s_branch {send}")
+    a.label(first)
+    a(f"s_cmp_eq_u32 {s(S_MODE)}, 0",
+      f"s_cbranch_scc1 {nonefirst}")
+    step_body_hp(a, "classic", False)
+    a(f"s_branch {send}")
+    a.label(nonefirst)
+    step_body_hp(a, "none", False)
+    a.label(send)
+    a(f"s_cmp_eq_u32 {s(S_MODE)}, 0",
+      f"s_cselect_b32 {s(S_PNONE)}, 1, 0")
+
+
+def drain_bases_hp(a):
+    """Output-read bases of step S_T - 1 (the segment's last step)."""
+    T = S_TMP
+    a(f"s_add_u32 s{T + 1}, {s(S_T)}, 3",
+      f"s_and_b32 s{T + 1}, s{T + 1}, 3",
+      f"s_mul_i32 s{T + 1}, s{T + 1}, {HS_BYTES}",
+      *[f"v_add_u32 {vreg(V_UP + m)}, s{T + 1}, {vreg(V_PVM[m])}" for m in range(4)],
+      f"s_and_b32 s{T + 2}, {s(S_T)}, 1",
+      f"s_lshl_b32 s{T + 2}, s{T + 2}, 13",
+      f"s_xor_b32 s{T + 2}, s{T + 2}, {PB_BYTES}",
+      f"v_add_u32 {vreg(V_PXR)}, s{T + 2}, {vreg(V_PX)}")
+
+
+def start_loads_hp(a):
+    """Loads of the steps S_T, S_T + 1 (page S_UCUR) and the loader state the
+    step S_T starts from (kernel start, restart)."""
+    T = S_TMP
+    issue_page_hp(a)
+    a(f"s_add_u32 s{S_LKUP}, {s(S_UCUR)}, 1")
+    a.lines += flatten(lookup_items(S_LKUP))
+    a(s_waitcnt_lgkm(0))
+    a.lines += flatten(loader_items(S_T))
+
+
+def kernel_tail_hp(a):
+    """bf16 kernel after the prologue: loader start, segments of steps,
+    restart, end."""
+    T = S_TMP
+    lane_constants_hp(a)
+    a(f"v_mov_b32 {vreg(V_ENT)}, 0")
+    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
+      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
+    load_len(a, S_LLEN, S_LSEQ)
+    units_of(a, S_LUNITS, S_LLEN)
+    a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
+      f"s_mov_b32 {s(S_T)}, 0")
+    start_loads_hp(a)
+    # ------------------------------------------------ segments
+    a.label(".Lseg")
+    segment_setup(a)
+    a(f"s_sub_u32 {s(S_NSTEP)}, {s(S_SEGEND)}, {s(S_UCUR)}",
+      f"s_lshl_b32 {s(S_NSTEP)}, {s(S_NSTEP)}, 1",
+      f"s_mov_b32 {s(S_TL)}, 0",
+      f"s_mov_b32 {s(S_PNONE)}, 0")
+    a.lines += flatten(next_items(S_T, True))
+    step_hp(a)
+    a(f"s_add_u32 {s(S_T)}, {s(S_T)}, 1",
+      f"s_add_u32 {s(S_TL)}, {s(S_TL)}, 1",
+      f"s_lshr_b32 s{T}, {s(S_T)}, 1",
+      f"s_add_u32 {s(S_UCUR)}, {s(S_UA)}, s{T}",
+      f"s_cmp_lt_u32 {s(S_TL)}, {s(S_NSTEP)}",
+      "s_cbranch_scc1 .Lstep")
+    drain_hp(a)
+    # end of the segment: every wave past its output reads
+    a(s_waitcnt_lgkm(0), "s_barrier")
+    epilogue_split(a)
+    a(f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+      f"s_add_u32 {s(S_CSEQ)}, {s(S_CSEQ)}, 1",
+      f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_UB)}",
+      "s_cbranch_scc1 .Lseg",
+      "s_branch .Lkernel_end")
+    # ------------------------------------------------ restart of the segment
+    a.label(".Lrestart")
+    a(s_waitcnt_vm(0), "s_barrier")   # every wave has read the requests; no loads in flight
+    a(f"s_mov_b64 {sp(S_OVF)}, 0",
+      f"s_mov_b32 {s(S_EXACT)}, 1")
+    for h in range(2):
+        pk, t0, t1 = V_T, V_T + 1, V_T + 2
+        a(f"v_mov_b32 {vreg(pk)}, {vreg(V_PEAK[h])}")
+        xor_reduce(a, pk, "v_max_f32", t0, t1)
+        # the restart comes at the segment's end, after steps that may have
+        # moved the reference since the overflow: a head whose lean sub-step
+        # overflowed starts over from its first maximum (max-based from now on)
+        a(f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(pk)}",
+          "s_nop 1",
+          f"v_cndmask_b32 {vreg(V_MREF[h])}, {vreg(V_MREF[h])}, {vreg(V_NEGINF)}, vcc",
+          f"v_mov_b32 {vreg(V_PEAK[h])}, 0")
+    a(f"s_max_u32 {s(S_UCUR)}, {s(S_UA)}, {s(S_CPRE)}",
+      f"s_sub_u32 {s(S_T)}, {s(S_UCUR)}, {s(S_UA)}",
+      f"s_lshl_b32 {s(S_T)}, {s(S_T)}, 1",
+      f"s_mov_b32 {s(S_TL)}, 0",
+      f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
+      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}",
+      f"s_mov_b32 {s(S_LUNITS)}, {s(S_CUNITS)}",
+      f"s_mov_b32 {s(S_LLEN)}, {s(S_CLEN)}",
+      f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
+      f"v_mov_b32 {vreg(V_LRUN[1])}, 0")
+    zero_o(a)
+    start_loads_hp(a)
+    a(f"s_mov_b32 {s(S_PNONE)}, 0")
+    a.lines += flatten(next_items(S_T, True))
+    a("s_branch .Lstep")
+    a.label(".Lkernel_end")
+    a(s_waitcnt_vm(0), "s_endpgm")   # the last loads must land before the LDS is released
+
+
+def segment_setup(a):
+    """Start of a segment (the sequence S_CSEQ from unit S_UCUR on): its
+    length, units and visible rows, the query rows of this wave (Q into
+    registers), the running softmax state, O = 0."""
+    T = S_TMP
+    t = V_T
+    load_len(a, S_CLEN, S_CSEQ)
+    units_of(a, S_CUNITS, S_CLEN)
+    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
+      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
+      f"s_add_i32 {s(S_NVLO)}, {s(S_NVIS)}, 1",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
+      # the workgroup's last query token: (32 * 3) >> log2(heads per block)
+      f"s_ff1_i32_b32 s{T}, {s(S_HB)}",
+      f"s_lshr_b32 s{T}, 96, s{T}",
+      f"s_add_i32 {s(S_NVHI)}, {s(S_NVLO)}, s{T}",
+      f"s_mov_b64 {sp(S_OVF)}, 0",
+      # Q row index (c_seq * s_q + s_tok) * 128 + head0
+      f"s_mul_i32 s{T}, {s(S_CSEQ)}, {s(S_SQ)}",
+      f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
+      f"s_lshl_b32 s{T}, s{T}, 7",
+      f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
+      f"s_mov_b32 s{T + 1}, 0",
+      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 10",
+      f"s_add_u32 s{S_QBASE}, {s(S_QA)}, s{T + 2}",
+      f"s_addc_u32 s{S_QBASE + 1}, s{S_QA + 1}, s{T + 3}",
+      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 7",
+      f"s_add_u32 s{S_RBASE}, {s(S_QR)}, s{T + 2}",
+      f"s_addc_u32 s{S_RBASE + 1}, s{S_QR + 1}, s{T + 3}",
+      # lane offsets: latent (16h + r16)*1024 + 16g ; rope (16h + r16)*128 + 16g
+      f"v_lshlrev_b32 {vreg(t)}, 10, {vreg(V_R16)}",
+      f"v_lshlrev_b32 {vreg(t + 1)}, 4, {vreg(V_G)}",
+      f"v_add_u32 {vreg(t)}, {vreg(t)}, {vreg(t + 1)}",
+      f"v_add_u32 {vreg(t + 2)}, 0x4000, {vreg(t)}",
+      f"v_lshlrev_b32 {vreg(t + 3)}, 7, {vreg(V_R16)}",
+      f"v_add_u32 {vreg(t + 3)}, {vreg(t + 3)}, {vreg(t + 1)}",
+      f"v_add_u32 {vreg(t + 1)}, 0x800, {vreg(t + 3)}")
+    for h in range(2):
+        off = vreg(t) if h == 0 else vreg(t + 2)
+        for ks in range(16):
+            q = V_Q + (2 * ks + h) * 4
+            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_QBASE}:{S_QBASE + 1}] offset:{64 * ks}")
+    for h in range(2):
+        off = vreg(t + 3) if h == 0 else vreg(t + 1)
+        for ks in range(2):
+            q = V_Q + (2 * (16 + ks) + h) * 4
+            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
+    a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
+      f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
+      f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
+      f"v_mov_b32 {vreg(V_LRUN[1])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
+      f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
+      f"s_mov_b32 {s(S_EXACT)}, 0")
+    zero_o(a)
 
 def kernel(fp8=False):
     configure(fp8)
@@ -1397,9 +2010,14 @@ def kernel(fp8=False):
         lane_constants_fp8(a)
     t = V_T
     a(f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
-    # restart flag = 0
-    flag_write(a, 0)
+    if FP8:
+        flag_write(a, 0)    # restart flag = 0
     a(s_waitcnt_lgkm(0), "s_barrier")
+    if not FP8:
+        kernel_tail_hp(a)
+        a.lines += [f".L{KNAME}_end:", f"\t.size {KNAME}, .L{KNAME}_end-{KNAME}", ""]
+        a.lines += descriptor()
+        return a.text()
     # ------------------------------------------------ loader cursor, first unit
     a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
       f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
@@ -1411,67 +2029,27 @@ def kernel(fp8=False):
     prefetch_next(a, S_UCUR)
     # ------------------------------------------------ segments
     a.label(".Lseg")
-    load_len(a, S_CLEN, S_CSEQ)
-    units_of(a, S_CUNITS, S_CLEN)
-    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
-      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
-      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
-      # Q row index (c_seq * s_q + s_tok) * 128 + head0
-      f"s_mul_i32 s{T}, {s(S_CSEQ)}, {s(S_SQ)}",
-      f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
-      f"s_lshl_b32 s{T}, s{T}, 7",
-      f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
-      f"s_mov_b32 s{T + 1}, 0",
-      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 10",
-      f"s_add_u32 s{S_QBASE}, {s(S_QA)}, s{T + 2}",
-      f"s_addc_u32 s{S_QBASE + 1}, s{S_QA + 1}, s{T + 3}",
-      f"s_lshl_b64 s[{T + 2}:{T + 3}], s[{T}:{T + 1}], 7",
-      f"s_add_u32 s{S_RBASE}, {s(S_QR)}, s{T + 2}",
-      f"s_addc_u32 s{S_RBASE + 1}, s{S_QR + 1}, s{T + 3}",
-      # lane offsets: latent (16h + r16)*1024 + 16g ; rope (16h + r16)*128 + 16g
-      f"v_lshlrev_b32 {vreg(t)}, 10, {vreg(V_R16)}",
-      f"v_lshlrev_b32 {vreg(t + 1)}, 4, {vreg(V_G)}",
-      f"v_add_u32 {vreg(t)}, {vreg(t)}, {vreg(t + 1)}",
-      f"v_add_u32 {vreg(t + 2)}, 0x4000, {vreg(t)}",
-      f"v_lshlrev_b32 {vreg(t + 3)}, 7, {vreg(V_R16)}",
-      f"v_add_u32 {vreg(t + 3)}, {vreg(t + 3)}, {vreg(t + 1)}",
-      f"v_add_u32 {vreg(t + 1)}, 0x800, {vreg(t + 3)}")
-    for h in range(2):
-        off = vreg(t) if h == 0 else vreg(t + 2)
-        for ks in range(16):
-            q = V_Q + (2 * ks + h) * 4
-            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_QBASE}:{S_QBASE + 1}] offset:{64 * ks}")
-    for h in range(2):
-        off = vreg(t + 3) if h == 0 else vreg(t + 1)
-        for ks in range(2):
-            q = V_Q + (2 * (16 + ks) + h) * 4
-            a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
-    a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
-      f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
-      f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
-      f"v_mov_b32 {vreg(V_LRUN[1])}, 0",
-      f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
-      f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
-      f"s_mov_b32 {s(S_EXACT)}, 0")
-    zero_o(a)
+    segment_setup(a)
     # ------------------------------------------------ units of the segment
     # On entry the loads of unit S_UCUR into its slot are in flight.
-    uend = (unit_body_fp8 if FP8 else unit_body_bf16)(a)
+    uend = unit_body_fp8(a)
     a.label(uend)
-    noflag = a.new_label("noflag")
-    a(f"s_cmp_eq_u64 {sp(S_OVF)}, 0",
-      f"s_cbranch_scc1 {noflag}")
-    flag_write(a, 1, all_waves=True)
-    a.label(noflag)
+    if FP8:
+        noflag = a.new_label("noflag")
+        a(f"s_cmp_eq_u64 {sp(S_OVF)}, 0",
+          f"s_cbranch_scc1 {noflag}")
+        flag_write(a, 1, all_waves=True)
+        a.label(noflag)
     a(f"s_add_u32 {s(S_UCUR)}, {s(S_UCUR)}, 1",
       f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_SEGEND)}",
       "s_cbranch_scc1 .Lunit")
-    # end of the segment: a restart request of its last unit?
+    # end of the segment: a restart request of its last unit (fp8), or of any of its units (bf16)?
     a(s_waitcnt_lgkm(0), "s_barrier")
-    flag_check(a)
-    epilogue(a)
+    if FP8:
+        flag_check(a)
+        epilogue(a)
+    else:
+        epilogue_split(a)
     a(f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_add_u32 {s(S_CSEQ)}, {s(S_CSEQ)}, 1",
       f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_UB)}",
@@ -1480,25 +2058,36 @@ def kernel(fp8=False):
     # ------------------------------------------------ restart of the segment
     a.label(".Lrestart")
     a(s_waitcnt_vm(0), "s_barrier")   # every wave has read the flag; no loads in flight
-    flag_write(a, 0)
+    if FP8:
+        flag_write(a, 0)
+    a(f"s_mov_b64 {sp(S_OVF)}, 0")
     # the re-run keeps the exact (max-based) reference for the whole segment, so
     # every further restart raises m_ref past an observed maximum: at most one
     # restart per sub-step whose max passes the reference
     a(f"s_mov_b32 {s(S_EXACT)}, 1")
-    # a lean sub-step overflowed: m_ref += log2(peak sum of the head) + 27, at most 128 + 27
     for h in range(2):
         pk, t0, t1, lp = V_T, V_T + 1, V_T + 2, V_T + 3
         a(f"v_mov_b32 {vreg(pk)}, {vreg(V_PEAK[h])}")
         xor_reduce(a, pk, "v_max_f32", t0, t1)
-        a(f"v_log_f32 {vreg(lp)}, {vreg(pk)}",
-          f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(pk)}",
-          "s_nop 0",
-          f"v_min_f32 {vreg(lp)}, 0x43000000, {vreg(lp)}",          # 128
-          f"v_add_f32 {vreg(lp)}, 0x41d80000, {vreg(lp)}",          # + 27
-          f"v_add_f32 {vreg(lp)}, {vreg(V_MREF[h])}, {vreg(lp)}",
-          "s_nop 1",
-          f"v_cndmask_b32 {vreg(V_MREF[h])}, {vreg(V_MREF[h])}, {vreg(lp)}, vcc",
-          f"v_mov_b32 {vreg(V_PEAK[h])}, 0")
+        if FP8:
+            # the restart follows the unit whose lean sub-step overflowed:
+            # m_ref += log2(peak sum of the head) + 27, at most 128 + 27
+            a(f"v_log_f32 {vreg(lp)}, {vreg(pk)}",
+              f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(pk)}",
+              "s_nop 0",
+              f"v_min_f32 {vreg(lp)}, 0x43000000, {vreg(lp)}",          # 128
+              f"v_add_f32 {vreg(lp)}, 0x41d80000, {vreg(lp)}",          # + 27
+              f"v_add_f32 {vreg(lp)}, {vreg(V_MREF[h])}, {vreg(lp)}",
+              "s_nop 1",
+              f"v_cndmask_b32 {vreg(V_MREF[h])}, {vreg(V_MREF[h])}, {vreg(lp)}, vcc")
+        else:
+            # the restart comes at the segment's end, after units that may have
+            # moved the reference since the overflow: a head whose lean sub-step
+            # overflowed starts over from its first maximum (max-based from now on)
+            a(f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(pk)}",
+              "s_nop 1",
+              f"v_cndmask_b32 {vreg(V_MREF[h])}, {vreg(V_MREF[h])}, {vreg(V_NEGINF)}, vcc")
+        a(f"v_mov_b32 {vreg(V_PEAK[h])}, 0")
     a(f"s_max_u32 {s(S_UCUR)}, {s(S_UA)}, {s(S_CPRE)}",
       f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
       f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}",

@@ -1,0 +1,105 @@
+"""Run the generated decode kernels on the CPU emulator (tests/gcn_emu.py).
+
+Host-side test infrastructure: builds the kernel argument block the library's
+launcher builds, runs every workgroup of the launch, and merges the partials
+of the sequences cut across partitions with the oracle's log-sum-exp merge,
+so that the result can be compared with the oracle directly.
+"""
+from __future__ import annotations
+
+import os
+import struct
+import sys
+
+import numpy as np
+
+import gcn_emu as E
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.join(HERE, "..", "mla_latent_kv_39_amd", "csrc"))
+import gen_decode_gfx950 as G  # noqa: E402
+
+N_HEADS, D_C = 128, 512
+
+
+def units_of_len(n):
+    return max(1, (n + 63) >> 6)
+
+
+def part_start(p, total, log2p):
+    return (p * total) >> log2p
+
+
+def unpack_partial(flat, s_q):
+    """partial_out [splits, 2, s_q, 128 * 512] in the library's lane order ->
+    [splits, 2, s_q, 128, 512]: the value of head 32j + 16a + r, column
+    16c + 4g + i sits at 16384 j + 4 (64 (32a + c) + 16g + r) + i."""
+    n = flat.shape[0]
+    v = flat.reshape(n, 2, s_q, 4, 2, 32, 4, 16, 4)                # j, a, c, g, r, i
+    return v.transpose(0, 1, 2, 3, 4, 7, 5, 6, 8).reshape(n, 2, s_q, N_HEADS, D_C)
+
+
+def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
+    """The decode kernel's outputs for MlaInputs `inp`: (out, lse, part_out,
+    part_lse) as written (partials unpacked to head/column order)."""
+    fp8 = inp.cache_dtype == "fp8_e4m3" if fp8 is None else fp8
+    if text is None:
+        text = G.kernel(fp8)
+    kname, lds = G.KNAME, G.LDS_BYTES
+    G.configure(False)
+    B, S = inp.batch, inp.s_q
+    import torch
+    mem = E.Memory()
+    q_abs = mem.add(inp.q_absorbed.contiguous().view(torch.uint8).numpy())
+    q_rope = mem.add(inp.q_rope.contiguous().view(torch.uint8).numpy())
+    rows = mem.add(inp.cache.contiguous().view(torch.uint8).numpy())
+    table = 0 if inp.block_table is None else mem.add(inp.block_table.numpy().astype(np.int32))
+    lens = mem.add(inp.seq_lens.numpy().astype(np.int32))
+    pout = mem.add(np.full(num_splits * 2 * S * N_HEADS * D_C, np.nan, np.float32))
+    plse = mem.add(np.full(num_splits * 2 * S * N_HEADS, np.nan, np.float32))
+    out = mem.add(np.full(B * S * N_HEADS * D_C, np.nan, np.float32))
+    lse = mem.add(np.full(B * S * N_HEADS, np.nan, np.float32))
+    fsc = mem.add(inp.cache_scales.numpy()) if fp8 else 0
+    fro = mem.add(inp.cache_rope.contiguous().view(torch.uint8).numpy()) if fp8 else 0
+    hpb = 128 if S == 1 else 64
+    lg = 0
+    while (1 << lg) < num_splits:
+        lg += 1
+    scale_log2 = float(np.float32(inp.scale) * np.float32(1.4426950408889634))
+    karg = struct.pack("<9Qf7i2Q", q_abs, q_rope, rows, table, lens, pout, plse, out, lse,
+                       scale_log2, inp.max_blocks, B, num_splits, S, hpb, N_HEADS // hpb, lg, fsc, fro)
+    assert len(karg) == G.KARG_BYTES
+    E.run_kernel(text, kname, lds, mem, karg, num_splits * (N_HEADS // hpb), seed=seed, hook=hook)
+    f = lambda base, shape: mem.buffer(base).view(np.float32).reshape(shape).astype(np.float64)
+    return (f(out, (B, S, N_HEADS, D_C)), f(lse, (B, S, N_HEADS)),
+            unpack_partial(mem.buffer(pout).view(np.float32).reshape(num_splits, 2, S, N_HEADS * D_C), S).astype(np.float64),
+            f(plse, (num_splits, 2, S, N_HEADS)))
+
+
+def merged(inp, num_splits, out, lse, pout, plse, merge):
+    """Final (out, lse): the kernel's own for sequences inside one partition,
+    the merge of their partition shares for the others."""
+    lens = [int(x) for x in inp.seq_lens]
+    U = sum(units_of_len(n) for n in lens)
+    lg = (num_splits - 1).bit_length()
+    starts = [part_start(p, U, lg) for p in range(num_splits + 1)]
+    out, lse = out.copy(), lse.copy()
+    u0 = 0
+    for b, n in enumerate(lens):
+        u1 = u0 + units_of_len(n)
+        shares = []
+        for q in range(num_splits):
+            lo, hi = max(starts[q], u0), min(starts[q + 1], u1)
+            if lo >= hi:
+                continue
+            whole = starts[q] <= u0 and u1 <= starts[q + 1]
+            if whole:
+                break
+            slot = 1 if (starts[q] < u0) else 0
+            shares.append((q, slot))
+        else:
+            for s in range(inp.s_q):
+                o, l = merge([pout[q, k, s] for q, k in shares], [plse[q, k, s] for q, k in shares])
+                out[b, s], lse[b, s] = o, l
+        u0 = u1
+    return out, lse

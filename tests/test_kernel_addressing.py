@@ -1,9 +1,10 @@
 """Host-side checks of the decode kernels' LDS and global addressing.
 
-The assembly generator's load, dequantize and read sequences are run lane by
-lane by a small interpreter of the instructions they use, and the resulting
-addresses are compared with the tile layout the kernels rely on: a tile slot
-is 9 x 8 blocks of 1 KB; block (K, R) holds rows 8R..8R+7 and 16-byte chunks
+The assembly generator's load, dequantize and read sequences are run on the
+CPU (the fp8 kernel's by a small symbolic interpreter, the bf16 kernel's by
+the emulator of tests/gcn_emu.py) and the data they move is compared with the
+tile layout the kernels rely on: a page tile is 9 x 8 blocks of 1 KB (a half
+page tile 9 x 4); block (K, R) holds rows 8R..8R+7 and 16-byte chunks
 8K..8K+7; row r sits at 128 (r % 8) in its block and chunk c at
 16 ((c % 8) ^ tp(r)), tp(r) = t(r % 8) ^ 2 ((r / 8) % 2), t(q) = 2 (q & 3) + (q >> 2).
 """
@@ -164,63 +165,106 @@ def fp8_mode():
     G.configure(False)
 
 
-@pytest.mark.parametrize("slot", [0, 1])
-@pytest.mark.parametrize("valid", [64, 37, 8, 1])
-def test_bf16_tile_loads(bf16_mode, slot, valid):
-    """Each 16-byte tile chunk comes from its own row and chunk of the page
-    (row 0 past the valid rows); each load moves eight whole 128-byte lines."""
-    lds = {}
-    for w in range(4):
-        m = Wave(w, lds)
-        m.run(lines_of(G.lane_constants))
-        m.s[G.S_NVALID], m.s[G.S_TMP + 21] = valid, slot
-        m.s[G.S_PAGE], m.s[G.S_PAGE + 1] = 0, 0
-        m.run(lines_of(G.dma_setup, G.S_TMP + 21) + [i for g in G.dma_groups() for i in g])
-        assert len(m.loads) == 18 * 64
-        for k in range(18):
-            lines = {src // 128 for src, _ in m.loads[64 * k:64 * k + 64]}
-            if valid == 64:
-                assert len(lines) == 8
-    for r in range(64):
+# ---------------------------------------------------------------- bf16 kernel
+# The bf16 kernel works on half pages: a tile is 9 x 4 blocks of 1 KB, block
+# (K, R) at (4K + R) KB, with the same row / chunk swizzle inside a block.
+# These checks run the generated instructions on the emulator of
+# tests/gcn_emu.py and look at the data each lane ends up with.
+import numpy as np  # noqa: E402
+
+import gcn_emu as E  # noqa: E402
+
+
+def half_byte(r, c):
+    return (4 * (c // 8) + r // 8) * 1024 + ((r % 8) * 8 + ((c % 8) ^ _tp(r))) * 16
+
+
+def _workgroup(lines, mem):
+    text = "k:\n" + "\n".join(lines) + "\n\ts_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_endpgm\n"
+    wg = E.Workgroup(E.Program(text, "k"), mem, G.P_BASE + G.P_BYTES, 0, mem.add(np.zeros(16, np.uint8)))
+    lanes = np.arange(64, dtype=np.uint32)
+    for w in wg.waves:
+        w.s[G.S_WAVE] = w.wid
+        w.v[G.V_LANE], w.v[G.V_G], w.v[G.V_R16] = lanes, lanes >> 4, lanes & 15
+    return wg
+
+
+def _lane_setup():
+    a = G.Asm()
+    G.lane_constants(a)
+    G.lane_constants_hp(a)
+    return a.lines
+
+
+@pytest.mark.parametrize("half", [0, 1])
+@pytest.mark.parametrize("valid", [64, 40, 33, 9, 1])
+def test_bf16_half_page_loads(bf16_mode, half, valid):
+    """Tile chunk (r, c) of the half page holds page row 32 half + r, chunk c
+    (row 32 half for rows past the data); all loads stay inside the page."""
+    page = np.zeros((64, 72, 4), np.uint32)
+    page[..., 0] = np.arange(64)[:, None]
+    page[..., 1] = np.arange(72)[None, :]
+    page[..., 2] = 0xA5A5A5A5
+    mem = E.Memory()
+    base = mem.add(page)
+    step = 6 + half
+    a = G.Asm()
+    G.dma_setup_hp(a, half, G.S_TMP + 8)
+    for g in G.dma_groups_hp():
+        a.lines += g
+    wg = _workgroup(_lane_setup() + a.lines, mem)
+    for w in wg.waves:
+        w.s[G.S_PAGE], w.s[G.S_PAGE + 1] = base & 0xFFFFFFFF, base >> 32
+        w.s[G.S_NVALID], w.s[G.S_TMP + 8] = valid, step
+    wg.run()
+    tile = wg.lds[(step & 3) * G.HS_BYTES:((step & 3) + 1) * G.HS_BYTES]
+    for r in range(32):
+        src = 32 * half + r if 32 * half + r < valid else 32 * half
         for c in range(72):
-            src = lds[slot * G.SLOT_BYTES + tile_byte(r, c)][1]
-            row, rem = divmod(src, 1152)
-            assert rem % 16 == 0 and 0 <= src and src + 16 <= 64 * 1152
-            if r < valid:
-                assert (row, rem // 16) == (r, c)
-            else:
-                assert row == 0 and rem // 16 // 8 == c // 8
+            got = tile[half_byte(r, c):half_byte(r, c) + 16].view(np.uint32)
+            assert (got[0], got[1], got[2]) == (src, c, 0xA5A5A5A5), (r, c, got)
 
 
-def test_bf16_score_and_output_reads(bf16_mode):
-    """Score reads: lane (g, r16) of fragment (ks, tb) reads row 32ss+16tb+r16,
-    chunk 4ks+g.  Transposed output reads: lane (g, j) of column block cb reads
-    row 32ss + 16 half + 4g + (j >> 2), columns 16cb + 4 (j & 3)."""
-    m = Wave(0, {})
-    m.run(lines_of(G.lane_constants))
+def test_bf16_half_tile_reads(bf16_mode):
+    """Score reads: lane (g, r16) of fragment (ks, tb) gets row 16tb + r16,
+    chunk 4ks + g.  Output reads of wave w, column block cb: lane (g, j) gets
+    column 128w + 16cb + j of rows 4g .. 4g+3 (first read) and 16 + 4g ..
+    (second read)."""
+    slot = 2
+    mem = E.Memory()
+    lines = _lane_setup()
     T = G.S_TMP
-    for slot in (0, 1):
-        m.s[T] = slot * G.SLOT_BYTES
-        bases = [f"v_add_u32 v{G.V_UQ}, s{T}, v{G.V_QKE}", f"v_add_u32 v{G.V_UQ + 1}, s{T}, v{G.V_QKO}",
-                 f"v_add_u32 v{G.V_UQ + 2}, 0x10000, v{G.V_UQ}", f"v_add_u32 v{G.V_UQ + 3}, 0x10000, v{G.V_UQ + 1}",
-                 f"v_add_u32 v{G.V_UP}, s{T}, v{G.V_PV0}"]
-        for k in range(1, 4):
-            bases += [f"v_xor_b32 v{G.V_UP + k}, {32 * k}, v{G.V_PV0}", f"v_add_u32 v{G.V_UP + k}, s{T}, v{G.V_UP + k}"]
-        m.run(bases)
-        for ss in range(2):
-            for i in range(36):
-                m.reads = []
-                m.run([x.format(buf="v[48:51]") for x in G.qk_read(ss, i)])
-                ks, tb = divmod(i, 2)
-                for op, addr, L in m.reads:
-                    assert addr == slot * G.SLOT_BYTES + tile_byte(32 * ss + 16 * tb + (L & 15), 4 * ks + (L >> 4))
-            for cb in range(32):
-                m.reads = []
-                m.run([x.format(lo="v[64:65]", hi="v[66:67]") for x in G.pv_read(ss, cb)])
-                for n, (op, addr, L) in enumerate(m.reads):
-                    half, g, j = n // 64, L >> 4, L & 15
-                    row, col = 32 * ss + 16 * half + 4 * g + (j >> 2), 16 * cb + 4 * (j & 3)
-                    assert addr == slot * G.SLOT_BYTES + tile_byte(row, col // 8) + (col % 8) * 2
+    lines += [f"\ts_mov_b32 s{T}, {slot * G.HS_BYTES}",
+              f"\tv_add_u32 v{G.V_UQ}, s{T}, v{G.V_QKE}", f"\tv_add_u32 v{G.V_UQ + 1}, s{T}, v{G.V_QKO}"]
+    lines += [f"\tv_add_u32 v{G.V_UP + m}, s{T}, v{G.V_PVM[m]}" for m in range(4)]
+    wg = _workgroup(lines, mem)
+    wg.run()
+    # tile element (row, col) holds the bf16 bit pattern row * 576 + col
+    for r in range(32):
+        for c in range(72):
+            off = slot * G.HS_BYTES + half_byte(r, c)
+            wg.lds[off:off + 16] = np.arange(r * 576 + 8 * c, r * 576 + 8 * c + 8, dtype=np.uint16).view(np.uint8)
+    for w in wg.waves:
+        for i in range(36):
+            ks, tb = divmod(i, 2)
+            prog = E.Program("k:\n" + G.qk_read_hp(i)[0].format(buf="v[16:19]") + "\n\ts_waitcnt lgkmcnt(0)\n", "k")
+            for ins in prog.code:
+                E.OPS[ins.op](wg, w, ins)
+            got = w.v[16:20].T.copy().view(np.uint16)            # [lane, 8]
+            lanes = np.arange(64)
+            want = ((16 * tb + (lanes & 15)) * 576 + 8 * (4 * ks + (lanes >> 4)))[:, None] + np.arange(8)[None, :]
+            assert np.array_equal(got, want.astype(np.uint16)), (w.wid, i)
+        for cb in range(8):
+            reads = [x.format(lo="v[20:21]", hi="v[22:23]") for x in G.pv_read_hp(cb)]
+            prog = E.Program("k:\n" + "\n".join(reads) + "\n\ts_waitcnt lgkmcnt(0)\n", "k")
+            for ins in prog.code:
+                E.OPS[ins.op](wg, w, ins)
+            got = w.v[20:24].T.copy().view(np.uint16)             # [lane, 8]: rows 4g+r, then 16+4g+r
+            lanes = np.arange(64)
+            col = 128 * w.wid + 16 * cb + (lanes & 15)
+            rows = np.concatenate([4 * (lanes >> 4)[:, None] + np.arange(4)[None, :],
+                                   16 + 4 * (lanes >> 4)[:, None] + np.arange(4)[None, :]], axis=1)
+            assert np.array_equal(got, (rows * 576 + col[:, None]).astype(np.uint16)), (w.wid, cb)
 
 
 CODES, ROPE, SCALES = 0x10000000, 0x20000000, 0x30000000

@@ -1,0 +1,88 @@
+"""The generated decode kernels, run instruction by instruction on the CPU
+emulator (tests/gcn_emu.py), against the fp64 oracle.
+
+These cover what the GPU parity tests cover (ragged pages, both cache
+layouts, partitions that cut sequences, two query tokens, the restart path,
+empty sequences, NaN in page tails, the e4m3 cache) on small inputs, and in
+addition what a GPU run cannot show: every global and LDS access stays inside
+its buffer (the emulator raises on any other), every register a memory
+operation fills is read only after the wait that covers it, and the result
+does not depend on the order in which the waves run between barriers.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_inputs import make_inputs
+from oracle import mla_oracle as O
+
+import emu_decode as ED
+
+OUT_TOL, LSE_TOL = 1e-2, 1e-3
+
+
+def _small(lens, s_q=1, layout="paged_shuffled", seed=0, cache="bf16"):
+    return make_inputs(dict(batch=len(lens), s_q=s_q, lens=("explicit", list(lens)), layout=layout, q_std=1.0,
+                            cache=cache, num_splits=None, unabsorbed=False, name="small"), seed=seed)
+
+
+def _check(inp, splits, out_tol=OUT_TOL, seed=3, ref=None):
+    out, lse, po, pl = ED.emulate_decode(inp, splits, seed=seed)
+    out, lse = ED.merged(inp, splits, out, lse, po, pl, O.merge_partials)
+    ref_out, ref_lse = O.mla_decode(inp) if ref is None else ref
+    assert np.all(np.isfinite(out))
+    neg = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), neg)
+    assert np.max(np.abs(out - ref_out)) <= out_tol
+    if (~neg).any():
+        assert np.max(np.abs(lse[~neg] - ref_lse[~neg])) <= LSE_TOL
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_bf16_paged_ragged(splits):
+    _check(_small([1, 63, 64, 65, 130, 257], seed=1), splits)
+
+
+def test_bf16_contiguous():
+    _check(_small([100, 37], layout="contiguous", seed=2), 2)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_bf16_two_query_tokens(splits):
+    _check(_small([2, 65, 129], s_q=2, seed=3), splits)
+
+
+def test_bf16_restart_path():
+    # head 0 sees two rows whose score jumps ~300 log2 units past the first
+    # rows' maximum: the lean sub-steps overflow and the segment restarts
+    inp = _small([300], seed=6)
+    for j in (150, 295):
+        page = int(inp.block_table[0, j // 64])
+        inp.cache[page, j % 64, 512:] = (inp.q_rope[0, 0, 0].float() * 48.0).to(torch.bfloat16)
+    cmax = float(np.abs(O.sequence_rows(inp, 0, 300)[:, :512]).max())
+    _check(inp, 1, out_tol=2.0 ** -8 * cmax)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_bf16_empty_sequences_and_nan_tails(s_q):
+    inp = _small([0, 1, 33, 70], s_q=s_q, seed=4)
+    ref = O.mla_decode(inp)
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        if L % 64:
+            inp.cache[int(inp.block_table[b, (L - 1) // 64]), L % 64:, :] = float("nan")
+    for splits in (1, 4):
+        _check(inp, splits, ref=ref)
+
+
+def test_bf16_result_independent_of_wave_order():
+    inp = _small([65, 130, 200], seed=7)
+    a = ED.emulate_decode(inp, 4, seed=1)
+    b = ED.emulate_decode(inp, 4, seed=2)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+@pytest.mark.parametrize("lens,s_q,splits", [([100, 70], 1, 1), ([300, 70, 129, 1], 1, 4), ([200, 65], 2, 2)])
+def test_fp8_cache(lens, s_q, splits):
+    _check(_small(lens, s_q=s_q, seed=1, cache="fp8_e4m3"), splits)
