@@ -96,11 +96,18 @@ typedef struct mla_latent_cache {
  *   seq_lens     int32 [batch], device; requires s_q <= seq_len <= max_blocks_per_seq*64
  *   scale        score scale (1/sqrt(192) for DeepSeek-V3)
  *   num_splits   number of work partitions the rows of the whole batch are cut
- *                into: a power of two, 1 .. MLA_MAX_SPLITS.  The rows of all sequences, in
- *                64-row pages, are dealt out in order and in near-equal shares,
+ *                into: a power of two P, 1 .. MLA_MAX_SPLITS.  The rows of all
+ *                sequences, in 64-row pages (units; a sequence owns
+ *                max(1, ceil(seq_len / 64)) of them), are dealt out in order,
  *                so one partition can cover the tail of one sequence, whole
- *                sequences and the head of another.  mla_num_splits_hint()
- *                gives a value that fills the GPU.
+ *                sequences and the head of another.  The shares are equal in
+ *                cost rather than in units: every sequence also weighs 3
+ *                units (its fixed cost), placed before its pages, so unit j of
+ *                sequence b sits at position u0(b) + 3 (b + 1) + j (u0(b): the
+ *                units of the sequences before it), and partition p takes the
+ *                units whose positions lie in [floor(p W / P),
+ *                floor((p + 1) W / P)), W = total units + 3 batch.
+ *                mla_num_splits_hint() gives a value that fills the GPU.
  *   partial_out  fp32 [num_splits, 2, s_q, 128 * 512]  may be NULL if num_splits == 1
  *                (layout below)
  *   partial_lse  fp32 [num_splits, 2, s_q, 128]        may be NULL if num_splits == 1

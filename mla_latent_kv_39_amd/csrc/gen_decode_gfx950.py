@@ -242,6 +242,50 @@ def xor_reduce(a, v, op, t0, t1):
           f"{op} {vreg(v)}, {vreg(t0)}, {vreg(t1)}")
 
 
+SEG_WEIGHT = 3    # the fixed cost of one sequence in a partition, in units (must equal kSegWeight)
+
+
+def pages_before_pass(a, x_sgpr, dst_sgpr):
+    """s[dst] = number of units (pages) whose weighted position lies below
+    s[x_sgpr]: the sum over sequences b of clamp(x - (u0_b + (b + 1) W), 0,
+    n_b), n_b the units of b, u0_b those before it, W = SEG_WEIGHT."""
+    t = V_T
+    T = S_TMP
+    loop = a.new_label("pbpass")
+    a(f"s_mov_b32 s{T}, 0",            # b0
+      f"s_mov_b32 s{T + 1}, 0",        # units before the chunk
+      f"s_mov_b32 s{dst_sgpr}, 0")
+    a.label(loop)
+    a(f"v_add_u32 {vreg(t)}, s{T}, {vreg(V_LANE)}",
+      f"v_mov_b32 {vreg(t + 1)}, 0",
+      f"v_cmp_gt_i32 vcc, {s(S_BATCH)}, {vreg(t)}",
+      f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
+      f"v_lshlrev_b32 {vreg(t + 2)}, 2, {vreg(t)}",
+      f"global_load_dword {vreg(t + 3)}, {vreg(t + 2)}, {sp(S_LENS)}",
+      s_waitcnt_vm(0),
+      f"v_add_u32 {vreg(t + 3)}, 63, {vreg(t + 3)}",
+      f"v_ashrrev_i32 {vreg(t + 3)}, 6, {vreg(t + 3)}",
+      f"v_max_i32 {vreg(t + 1)}, 1, {vreg(t + 3)}",
+      f"s_mov_b64 exec, {sp(S_EXEC)}",
+      "s_nop 1")
+    wave_incl_scan(a, t + 2, t + 1)
+    a(f"v_add_u32 {vreg(t + 2)}, s{T + 1}, {vreg(t + 2)}",          # u0 + n (with the carry)
+      f"v_sub_u32 {vreg(t + 3)}, {vreg(t + 2)}, {vreg(t + 1)}",     # u0
+      f"v_mad_u32_u24 {vreg(t + 3)}, {vreg(t)}, {SEG_WEIGHT}, {vreg(t + 3)}",
+      f"v_add_u32 {vreg(t + 3)}, {SEG_WEIGHT}, {vreg(t + 3)}",     # weighted position of page 0
+      f"v_sub_u32 {vreg(t + 3)}, s{x_sgpr}, {vreg(t + 3)}",
+      f"v_max_i32 {vreg(t + 3)}, 0, {vreg(t + 3)}",
+      f"v_min_i32 {vreg(t + 3)}, {vreg(t + 1)}, {vreg(t + 3)}",
+      "s_nop 1")
+    wave_incl_scan(a, t, t + 3)
+    a(f"v_readlane_b32 s{T + 2}, {vreg(t)}, 63",
+      f"v_readlane_b32 s{T + 1}, {vreg(t + 2)}, 63",
+      f"s_add_u32 s{dst_sgpr}, s{dst_sgpr}, s{T + 2}",
+      f"s_add_u32 s{T}, s{T}, 64",
+      f"s_cmp_lt_u32 s{T}, {s(S_BATCH)}",
+      f"s_cbranch_scc1 {loop}")
+
+
 def seq_units_pass(a, find_first):
     """Walk seq_lens in chunks of 64 lanes.  Without find_first: S_U = total
     units.  With find_first: S_CSEQ/S_CPRE = the sequence holding unit S_UA and
@@ -1426,6 +1470,8 @@ V_PVM = (V_PV0, 98, 99, 107)      # output-read lane offsets of the four 16-colu
 # steps leave alone; the epilogue does not, so a segment start recomputes them)
 N_PH, N_STEP, N_NVH, N_ROW0, N_MODE, N_DMALDS = 70, 72, 74, 75, 76, 77
 S_LKUP = 3                        # page to look up (the loader items' own; s3 holds nothing else)
+S_EPI = 50                        # 1: the segment follows an epilogue (its Q loads went out before
+                                  # the epilogue's 66 stores)
 DMA_EARLY = 9                     # > 0: the loads of step t + 2 go out over fragments 0..DMA_EARLY
 
 
@@ -1741,7 +1787,6 @@ def step_hp(a):
       f"v_add_u32 {vreg(V_PXW)}, s{T + 3}, {vreg(V_PX)}",
       f"v_add_u32 {vreg(V_PXR)}, s{T + 2}, {vreg(V_PX)}",
       f"v_cmp_gt_i32 vcc, s{N_NVH}, {vreg(V_LDROW)}",
-      "s_nop 1",
       f"v_cndmask_b32 {vreg(V_DMAS)}, {vreg(V_LDZ)}, {vreg(V_LDA)}, vcc")
     # this step's rows have landed (the next step's nine loads may still be in
     # flight; a segment's first step also waits for its Q loads)
@@ -1751,6 +1796,15 @@ def step_hp(a):
       s_waitcnt_vm(9),
       f"s_branch {wdone}")
     a.label(w0)
+    # a segment's first step: Q and this step's rows.  After an epilogue at
+    # least 63 stores went out after the Q loads, so at most 63 may stay
+    # outstanding; else none
+    wz = a.new_label("wz")
+    a(f"s_cmp_eq_u32 {s(S_EPI)}, 0",
+      f"s_cbranch_scc1 {wz}",
+      s_waitcnt_vm(63),
+      f"s_branch {wdone}")
+    a.label(wz)
     a(s_waitcnt_vm(0))
     a.label(wdone)
     a(s_waitcnt_lgkm(0), "s_barrier")
@@ -1821,11 +1875,13 @@ def kernel_tail_hp(a):
     load_len(a, S_LLEN, S_LSEQ)
     units_of(a, S_LUNITS, S_LLEN)
     a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
-      f"s_mov_b32 {s(S_T)}, 0")
+      f"s_mov_b32 {s(S_T)}, 0",
+      f"s_mov_b32 {s(S_EPI)}, 0")
     start_loads_hp(a)
+    load_q(a, S_CSEQ)
     # ------------------------------------------------ segments
     a.label(".Lseg")
-    segment_setup(a)
+    segment_setup(a, with_q=False)
     a(f"s_sub_u32 {s(S_NSTEP)}, {s(S_SEGEND)}, {s(S_UCUR)}",
       f"s_lshl_b32 {s(S_NSTEP)}, {s(S_NSTEP)}, 1",
       f"s_mov_b32 {s(S_TL)}, 0",
@@ -1838,11 +1894,20 @@ def kernel_tail_hp(a):
       f"s_add_u32 {s(S_UCUR)}, {s(S_UA)}, s{T}",
       f"s_cmp_lt_u32 {s(S_TL)}, {s(S_NSTEP)}",
       "s_cbranch_scc1 .Lstep")
+    # the scores are done: Q of the next segment (if the partition has one) now,
+    # under the last output and the epilogue
+    noq = a.new_label("noq")
+    a(f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_UB)}",
+      f"s_cbranch_scc0 {noq}",
+      f"s_add_u32 s{S_LKUP}, {s(S_CSEQ)}, 1")
+    load_q(a, S_LKUP)
+    a.label(noq)
     drain_hp(a)
     # end of the segment: every wave past its output reads
     a(s_waitcnt_lgkm(0), "s_barrier")
     epilogue_split(a)
-    a(f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+    a(f"s_mov_b32 {s(S_EPI)}, 1",
+      f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_add_u32 {s(S_CSEQ)}, {s(S_CSEQ)}, 1",
       f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_UB)}",
       "s_cbranch_scc1 .Lseg",
@@ -1875,34 +1940,21 @@ def kernel_tail_hp(a):
       f"v_mov_b32 {vreg(V_LRUN[1])}, 0")
     zero_o(a)
     start_loads_hp(a)
-    a(f"s_mov_b32 {s(S_PNONE)}, 0")
+    load_q(a, S_CSEQ)         # Q may hold the next segment's rows by now
+    a(f"s_mov_b32 {s(S_PNONE)}, 0",
+      f"s_mov_b32 {s(S_EPI)}, 0")
     a.lines += flatten(next_items(S_T, True))
     a("s_branch .Lstep")
     a.label(".Lkernel_end")
     a(s_waitcnt_vm(0), "s_endpgm")   # the last loads must land before the LDS is released
 
 
-def segment_setup(a):
-    """Start of a segment (the sequence S_CSEQ from unit S_UCUR on): its
-    length, units and visible rows, the query rows of this wave (Q into
-    registers), the running softmax state, O = 0."""
+def load_q(a, seq_sgpr):
+    """Q of this wave's query rows of sequence s[seq_sgpr] into V_Q (36
+    loads): row (seq * s_q + s_tok) * 128 + head0 .. + 31, latent then rope."""
     T = S_TMP
     t = V_T
-    load_len(a, S_CLEN, S_CSEQ)
-    units_of(a, S_CUNITS, S_CLEN)
-    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
-      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
-      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
-      f"s_add_i32 {s(S_NVLO)}, {s(S_NVIS)}, 1",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
-      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
-      # the workgroup's last query token: (32 * 3) >> log2(heads per block)
-      f"s_ff1_i32_b32 s{T}, {s(S_HB)}",
-      f"s_lshr_b32 s{T}, 96, s{T}",
-      f"s_add_i32 {s(S_NVHI)}, {s(S_NVLO)}, s{T}",
-      f"s_mov_b64 {sp(S_OVF)}, 0",
-      # Q row index (c_seq * s_q + s_tok) * 128 + head0
-      f"s_mul_i32 s{T}, {s(S_CSEQ)}, {s(S_SQ)}",
+    a(f"s_mul_i32 s{T}, s{seq_sgpr}, {s(S_SQ)}",
       f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
       f"s_lshl_b32 s{T}, s{T}, 7",
       f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
@@ -1931,6 +1983,29 @@ def segment_setup(a):
         for ks in range(2):
             q = V_Q + (2 * (16 + ks) + h) * 4
             a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
+
+
+def segment_setup(a, with_q=True):
+    """Start of a segment (the sequence S_CSEQ from unit S_UCUR on): its
+    length, units and visible rows, the query rows of this wave (Q into
+    registers unless with_q is False: then they are on their way already),
+    the running softmax state, O = 0."""
+    T = S_TMP
+    load_len(a, S_CLEN, S_CSEQ)
+    units_of(a, S_CUNITS, S_CLEN)
+    a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+      f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
+      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
+      f"s_add_i32 {s(S_NVLO)}, {s(S_NVIS)}, 1",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
+      # the workgroup's last query token: (32 * 3) >> log2(heads per block)
+      f"s_ff1_i32_b32 s{T}, {s(S_HB)}",
+      f"s_lshr_b32 s{T}, 96, s{T}",
+      f"s_add_i32 {s(S_NVHI)}, {s(S_NVLO)}, s{T}",
+      f"s_mov_b64 {sp(S_OVF)}, 0")
+    if with_q:
+        load_q(a, S_CSEQ)
     a(f"v_mov_b32 {vreg(V_MREF[0])}, {NEG_INF}",
       f"v_mov_b32 {vreg(V_MREF[1])}, {NEG_INF}",
       f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
@@ -1939,6 +2014,7 @@ def segment_setup(a):
       f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
       f"s_mov_b32 {s(S_EXACT)}, 0")
     zero_o(a)
+
 
 def kernel(fp8=False):
     configure(fp8)
@@ -1983,17 +2059,24 @@ def kernel(fp8=False):
       f"s_and_b32 {s(S_HBLK)}, s2, s{T}")
     a.label(mapped)
     # ------------------------------------------------ partition map
+    # every sequence weighs its units + SEG_WEIGHT; partition p of P takes the
+    # weighted positions [(p W) >> log2 P, ((p + 1) W) >> log2 P), W the total,
+    # i.e. the units [UA, UB) whose positions fall there
     seq_units_pass(a, find_first=False)
-    a(f"s_mul_i32 s{T}, {s(S_PART)}, {s(S_U)}",
-      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, {s(S_U)}",
+    a(f"s_mul_i32 s{T + 3}, {s(S_BATCH)}, {SEG_WEIGHT}",
+      f"s_add_u32 s{T + 3}, s{T + 3}, {s(S_U)}",
+      f"s_mul_i32 s{T}, {s(S_PART)}, s{T + 3}",
+      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, s{T + 3}",
       f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 {s(S_UA)}, s{T}",
+      f"s_mov_b32 s{T + 10}, s{T}",
       f"s_add_u32 s{T + 2}, {s(S_PART)}, 1",
-      f"s_mul_i32 s{T}, s{T + 2}, {s(S_U)}",
-      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, {s(S_U)}",
+      f"s_mul_i32 s{T}, s{T + 2}, s{T + 3}",
+      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, s{T + 3}",
       f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 {s(S_UB)}, s{T}",
-      f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
+      f"s_mov_b32 s{T + 11}, s{T}")
+    pages_before_pass(a, T + 10, S_UA)
+    pages_before_pass(a, T + 11, S_UB)
+    a(f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
       "s_cbranch_scc1 .Lkernel_end")
     seq_units_pass(a, find_first=True)
     # ------------------------------------------------ this wave's query rows

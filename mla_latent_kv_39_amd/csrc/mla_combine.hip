@@ -84,10 +84,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   __syncthreads();
   const int total_units = s_red[0] + s_red[2] + s_red[4] + s_red[6];
   const int u0 = s_red[1] + s_red[3] + s_red[5] + s_red[7];
-  const int u1 = u0 + units_of_len(p.seq_lens[b]);
-  const int p0 = part_of_unit(u0, total_units, p.num_parts);
-  const int p1 = part_of_unit(u1 - 1, total_units, p.num_parts);
+  const int nb = units_of_len(p.seq_lens[b]);
+  const int weight = total_units + p.batch * kSegWeight;
+  // weighted positions of the sequence's first and last units
+  const int x0 = u0 + (b + 1) * kSegWeight;
+  const int x1 = x0 + nb - 1;
+  const int p0 = part_of_pos(x0, weight, p.num_parts);
+  const int p1 = part_of_pos(x1, weight, p.num_parts);
   if (p0 == p1) return;  // finished by the decode kernel
+  // partition p0 also holds units of the sequence before (it ends in this one:
+  // slot 1) iff that sequence's last unit lies at or past its start
+  const int slot0 = (b > 0 && u0 - 1 + b * kSegWeight >= part_start(p0, weight, p.log2_parts)) ? 1 : 0;
 
   // chunk k of this thread: slice-local index t + 256 k, head half a, lane-order offset in the group
   int head[kPerThread], coff[kPerThread];
@@ -106,23 +113,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     wsum[k] = 0.f;
     acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (2 * (u1 - u0) < p1 - p0 + 1) {
+  if (2 * nb < p1 - p0 + 1) {
     // more partitions than units (short sequences): visit only the partitions
-    // that hold a unit of sequence b, stepping u to the next partition's start
-    for (int u = u0; u < u1;) {
-      const int q = part_of_unit(u, total_units, p.num_parts);
-      const int q_start = part_start(q, total_units, p.log2_parts);
-      const size_t row = ((size_t)(q * 2 + ((q == p0 && u0 != q_start) ? 1 : 0)) * p.s_q + s) * kHeads;
+    // that hold a unit of sequence b, stepping x to the next partition's start
+    for (int x = x0; x <= x1;) {
+      const int q = part_of_pos(x, weight, p.num_parts);
+      const size_t row = ((size_t)(q * 2 + (q == p0 ? slot0 : 0)) * p.s_q + s) * kHeads;
       merge_share<kPerThread>(p, row, grp, head, coff, m, wsum, acc);
-      u = part_start(q + 1, total_units, p.log2_parts);
+      x = part_start(q + 1, weight, p.log2_parts);
     }
   } else {
     // pass 1: the largest lse of each chunk's head
 #pragma unroll kUnroll
     for (int q = p0; q <= p1; ++q) {
-      const int q_start = part_start(q, total_units, p.log2_parts);
-      if (q_start == part_start(q + 1, total_units, p.log2_parts)) continue;  // empty partition
-      const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
+      const int q_start = part_start(q, weight, p.log2_parts);
+      if (q_start == part_start(q + 1, weight, p.log2_parts)) continue;  // empty partition
+      const int slot = q == p0 ? slot0 : 0;
       const size_t row = ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) m[k] = fmaxf(m[k], p.part_lse[row + head[k]]);
@@ -130,13 +136,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     // pass 2: weighted sums; the loop body has no data-dependent branch, so
     // the loads of successive partitions can be in flight together.  An empty
     // partition reads partition p0's share (always written) with weight 0.
-    const size_t row0 =
-        ((size_t)(p0 * 2 + (u0 != part_start(p0, total_units, p.log2_parts) ? 1 : 0)) * p.s_q + s) * kHeads;
+    const size_t row0 = ((size_t)(p0 * 2 + slot0) * p.s_q + s) * kHeads;
 #pragma unroll kUnroll
     for (int q = p0; q <= p1; ++q) {
-      const int q_start = part_start(q, total_units, p.log2_parts);
-      const bool empty = q_start == part_start(q + 1, total_units, p.log2_parts);
-      const int slot = (q == p0 && u0 != q_start) ? 1 : 0;
+      const int q_start = part_start(q, weight, p.log2_parts);
+      const bool empty = q_start == part_start(q + 1, weight, p.log2_parts);
+      const int slot = q == p0 ? slot0 : 0;
       const size_t row = empty ? row0 : ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
       const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
 #pragma unroll

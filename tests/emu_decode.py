@@ -22,14 +22,6 @@ import gen_decode_gfx950 as G  # noqa: E402
 N_HEADS, D_C = 128, 512
 
 
-def units_of_len(n):
-    return max(1, (n + 63) >> 6)
-
-
-def part_start(p, total, log2p):
-    return (p * total) >> log2p
-
-
 def unpack_partial(flat, s_q):
     """partial_out [splits, 2, s_q, 128 * 512] in the library's lane order ->
     [splits, 2, s_q, 128, 512]: the value of head 32j + 16a + r, column
@@ -78,28 +70,16 @@ def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
 
 def merged(inp, num_splits, out, lse, pout, plse, merge):
     """Final (out, lse): the kernel's own for sequences inside one partition,
-    the merge of their partition shares for the others."""
+    the merge of their partition shares (partition map of tests/partition_map.py)
+    for the others."""
+    from partition_map import partition_map
     lens = [int(x) for x in inp.seq_lens]
-    U = sum(units_of_len(n) for n in lens)
-    lg = (num_splits - 1).bit_length()
-    starts = [part_start(p, U, lg) for p in range(num_splits + 1)]
+    _, owners = partition_map(lens, num_splits)
     out, lse = out.copy(), lse.copy()
-    u0 = 0
-    for b, n in enumerate(lens):
-        u1 = u0 + units_of_len(n)
-        shares = []
-        for q in range(num_splits):
-            lo, hi = max(starts[q], u0), min(starts[q + 1], u1)
-            if lo >= hi:
-                continue
-            whole = starts[q] <= u0 and u1 <= starts[q + 1]
-            if whole:
-                break
-            slot = 1 if (starts[q] < u0) else 0
-            shares.append((q, slot))
-        else:
-            for s in range(inp.s_q):
-                o, l = merge([pout[q, k, s] for q, k in shares], [plse[q, k, s] for q, k in shares])
-                out[b, s], lse[b, s] = o, l
-        u0 = u1
+    for b, own in enumerate(owners):
+        if len(own) < 2:
+            continue
+        for s in range(inp.s_q):
+            o, l = merge([pout[p, k, s] for p, k, _, _ in own], [plse[p, k, s] for p, k, _, _ in own])
+            out[b, s], lse[b, s] = o, l
     return out, lse

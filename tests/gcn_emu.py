@@ -637,7 +637,7 @@ def _vmov(g, w, i):
 
 
 @op("v_add_u32", "v_sub_u32", "v_and_b32", "v_or_b32", "v_xor_b32", "v_lshlrev_b32", "v_lshrrev_b32",
-    "v_ashrrev_i32", "v_max_i32", "v_mul_u32_u24")
+    "v_ashrrev_i32", "v_max_i32", "v_min_i32", "v_mul_u32_u24")
 def _vint2(g, w, i):
     a, b = _vu(w, i, 1), _vu(w, i, 2)
     if i.op == "v_add_u32":
@@ -658,12 +658,14 @@ def _vint2(g, w, i):
         r = (b.astype(np.uint32).view(np.int32) >> (a & 31).astype(np.int32)).view(np.uint32).astype(np.uint64)
     elif i.op == "v_max_i32":
         r = np.maximum(a.astype(np.uint32).view(np.int32), b.astype(np.uint32).view(np.int32)).view(np.uint32)
+    elif i.op == "v_min_i32":
+        r = np.minimum(a.astype(np.uint32).view(np.int32), b.astype(np.uint32).view(np.int32)).view(np.uint32)
     else:
         r = (a & 0xFFFFFF) * (b & 0xFFFFFF)
     w.vset(i.args[0], (np.asarray(r, np.uint64) & M32).astype(np.uint32))
 
 
-@op("v_lshl_add_u32", "v_lshl_or_b32", "v_bfe_u32", "v_or3_b32", "v_mad_i32_i24")
+@op("v_lshl_add_u32", "v_lshl_or_b32", "v_bfe_u32", "v_or3_b32", "v_mad_i32_i24", "v_mad_u32_u24")
 def _vint3(g, w, i):
     a, b, c = _vu(w, i, 1), _vu(w, i, 2), _vu(w, i, 3)
     if i.op == "v_lshl_add_u32":
@@ -674,6 +676,8 @@ def _vint3(g, w, i):
         r = (a >> (b & 31)) & ((np.uint64(1) << (c & 31)) - np.uint64(1))
     elif i.op == "v_or3_b32":
         r = a | b | c
+    elif i.op == "v_mad_u32_u24":
+        r = (a & 0xFFFFFF) * (b & 0xFFFFFF) + c
     else:
         def s24(x):
             x = (x & 0xFFFFFF).astype(np.int64)

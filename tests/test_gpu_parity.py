@@ -101,18 +101,10 @@ def test_scores_with_large_spread_restart_path(factor):
 
 
 def _partition_map(lens, num_splits):
-    """Units per sequence, partition starts, and for each sequence the (partition, slot)
-    pairs holding its partials -- the partition map include/mla.h describes."""
-    units = [max(1, (int(L) + 63) // 64) for L in lens]
-    U = sum(units)
-    start = [p * U // num_splits for p in range(num_splits + 1)]
-    pre = np.concatenate([[0], np.cumsum(units)]).astype(int)
-    owners = []
-    for b in range(len(lens)):
-        u0, u1 = pre[b], pre[b + 1]
-        parts = [p for p in range(num_splits) if start[p] < start[p + 1] and start[p] < u1 and start[p + 1] > u0]
-        owners.append([(p, 0 if u0 <= start[p] else 1, max(u0, start[p]), min(u1, start[p + 1])) for p in parts])
-    return owners
+    """For each sequence the (partition, slot, first unit, end unit) tuples
+    holding its partials -- the partition map include/mla.h describes."""
+    from partition_map import partition_map
+    return partition_map(lens, num_splits)[1]
 
 
 @pytest.mark.parametrize("s_q", [1, 2])

@@ -23,3 +23,60 @@ def test_pack_partial_out_is_a_permutation():
     po = torch.arange(128 * 512, dtype=torch.float32).reshape(1, 1, 1, 128, 512)
     packed = pack_partial_out(po).flatten()
     assert torch.equal(torch.sort(packed).values, po.flatten())
+
+
+# ------------------------------------------------------- partition map
+def test_partition_map_covers_every_unit_once():
+    """Every unit of every sequence belongs to exactly one partition; the
+    units of a partition are consecutive; slot 1 only for a sequence that
+    starts inside the partition."""
+    import random
+    from partition_map import partition_map, units_of_len
+    rng = random.Random(0)
+    for _ in range(200):
+        lens = [rng.choice([0, 1, 63, 64, 65, rng.randint(1, 5000)]) for _ in range(rng.randint(1, 40))]
+        parts = 2 ** rng.randint(0, 9)
+        ranges, owners = partition_map(lens, parts)
+        total = sum(units_of_len(L) for L in lens)
+        assert ranges[0][0] == 0 and ranges[-1][1] == total
+        for (a0, b0), (a1, b1) in zip(ranges, ranges[1:]):
+            assert a0 <= b0 == a1 <= b1
+        u0 = 0
+        for b, own in enumerate(owners):
+            n = units_of_len(lens[b])
+            covered = sorted((lo, hi) for _, _, lo, hi in own)
+            assert covered[0][0] == u0 and covered[-1][1] == u0 + n
+            assert all(x[1] == y[0] for x, y in zip(covered, covered[1:]))
+            for p, slot, lo, hi in own:
+                assert slot == (1 if u0 > ranges[p][0] else 0)
+            u0 += n
+
+
+def test_partition_map_weighs_sequence_boundaries():
+    """A partition that holds more sequences gets fewer units: the cost
+    units + SEG_WEIGHT x (sequences it touches) varies across partitions by
+    at most about one sequence's weight, where equal unit counts would let it
+    vary by several."""
+    from partition_map import partition_map, SEG_WEIGHT
+    lens = [64 * 7] * 12 + [64 * 3] * 20
+    parts = 16
+    ranges, owners = partition_map(lens, parts)
+    cost = []
+    for p, (ua, ub) in enumerate(ranges):
+        seqs = sum(1 for own in owners if any(q == p for q, *_ in own))
+        cost.append((ub - ua) + SEG_WEIGHT * seqs)
+    assert max(cost) - min(cost) <= 2 * SEG_WEIGHT + 1
+
+
+def test_partition_weight_is_the_same_everywhere():
+    """The decode kernels (generator), the combine kernel (header) and this
+    reference use one sequence weight."""
+    import os
+    import re
+    import sys
+    import partition_map
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, os.path.join(root, "mla_latent_kv_39_amd", "csrc"))
+    import gen_decode_gfx950 as G
+    hdr = open(os.path.join(root, "mla_latent_kv_39_amd", "csrc", "mla_schedule.h")).read()
+    assert int(re.search(r"kSegWeight = (\d+);", hdr).group(1)) == G.SEG_WEIGHT == partition_map.SEG_WEIGHT
