@@ -54,6 +54,10 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmla.so is not built at {LIB_PATH}; run __graft_entry__.build() "
                           "or python -m mla_latent_kv_39_amd.build_lib")
+    # torch first: its HIP runtime is then the one libmla.so binds to.  Loaded
+    # the other way round the process holds two HIP runtimes, and the tensors
+    # of one are not valid in the other.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.mla_decode.restype = i32

@@ -5,13 +5,15 @@
 // rows.
 //
 // One workgroup merges one slice of the latent columns (16 CB of them, CB = 8,
-// 4 or 2 column blocks; the host picks the narrowest slice that still gives
+// 4 or 2 column blocks; the host picks the widest slice that still gives
 // the GPU enough workgroups) of one group of 32 heads of one (sequence, query
 // token).  Partials are stored in the decode kernel's lane order (see the
 // partial_out layout in include/mla.h): a slice is two contiguous runs of
 // CB KB (head halves a = 0, 1), so consecutive threads read consecutive
-// 16-byte chunks.  The merged slice goes through LDS once to be written back in
-// row order.
+// 16-byte chunks.  Partitions are taken in chunks whose loads are all issued
+// before any is used, each chunk merged into a running (max, sum, accumulator)
+// triple, so a sequence cut into few partitions costs one memory round trip.
+// The merged slice goes through LDS once to be written back in row order.
 #include "mla_internal.h"
 #include "mla_schedule.h"
 
@@ -25,37 +27,12 @@ constexpr int kGroupHeads = 32;
 // that both the lane-order writes and the row-order reads spread over all banks.
 __device__ __forceinline__ int lds_slot(int c) { return c ^ ((((c >> 6) & 3) << 2) | ((c >> 4) & 3)); }
 
-// Online merge of one partition's share into (m, wsum, acc): rescale when a
-// larger lse arrives.  Used where sequences are short and shares are few.
-template <int N>
-__device__ __forceinline__ void merge_share(const CombineParams& p, size_t row, int grp, const int* head,
-                                            const int* coff, float* m, float* wsum, float4* acc) {
-  const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
-#pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const float l = p.part_lse[row + head[k]];
-    if (l == kNegInf) continue;  // this share saw no row of this query token
-    float w = 1.f;
-    if (l > m[k]) {
-      const float r = __expf(m[k] - l);
-      wsum[k] *= r;
-      acc[k].x *= r; acc[k].y *= r; acc[k].z *= r; acc[k].w *= r;
-      m[k] = l;
-    } else {
-      w = __expf(l - m[k]);
-    }
-    wsum[k] += w;
-    const float4 v = src[coff[k]];
-    acc[k].x += w * v.x; acc[k].y += w * v.y; acc[k].z += w * v.z; acc[k].w += w * v.w;
-  }
-}
-
 template <int CB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int kSlices = 32 / CB;
   constexpr int kRun = 64 * CB;                // chunks per head half of a slice
   constexpr int kPerThread = 2 * kRun / 256;   // 4, 2 or 1
-  constexpr int kUnroll = 16 / kPerThread;     // about 16 loads of 16 bytes in flight per thread
+  constexpr int kChunk = 4;                    // partitions whose loads are in flight together
   __shared__ float4 s_tile[2 * kRun];
   __shared__ int s_red[8];
   const int tid = threadIdx.x;
@@ -113,45 +90,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     wsum[k] = 0.f;
     acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (2 * nb < p1 - p0 + 1) {
-    // more partitions than units (short sequences): visit only the partitions
-    // that hold a unit of sequence b, stepping x to the next partition's start
-    for (int x = x0; x <= x1;) {
-      const int q = part_of_pos(x, weight, p.num_parts);
-      const size_t row = ((size_t)(q * 2 + (q == p0 ? slot0 : 0)) * p.s_q + s) * kHeads;
-      merge_share<kPerThread>(p, row, grp, head, coff, m, wsum, acc);
-      x = part_start(q + 1, weight, p.log2_parts);
-    }
-  } else {
-    // pass 1: the largest lse of each chunk's head
-#pragma unroll kUnroll
-    for (int q = p0; q <= p1; ++q) {
-      const int q_start = part_start(q, weight, p.log2_parts);
-      if (q_start == part_start(q + 1, weight, p.log2_parts)) continue;  // empty partition
-      const int slot = q == p0 ? slot0 : 0;
-      const size_t row = ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
+  // partitions in chunks of kChunk: all loads of a chunk go out before any is
+  // used (one memory round trip per chunk), then the chunk is merged into the
+  // running (m, wsum, acc) with a rescale when its largest lse is new
+  for (int qb = p0; qb <= p1; qb += kChunk) {
+    float l[kChunk][kPerThread];
+    float4 v[kChunk][kPerThread];
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) m[k] = fmaxf(m[k], p.part_lse[row + head[k]]);
-    }
-    // pass 2: weighted sums; the loop body has no data-dependent branch, so
-    // the loads of successive partitions can be in flight together.  An empty
-    // partition reads partition p0's share (always written) with weight 0.
-    const size_t row0 = ((size_t)(p0 * 2 + slot0) * p.s_q + s) * kHeads;
-#pragma unroll kUnroll
-    for (int q = p0; q <= p1; ++q) {
-      const int q_start = part_start(q, weight, p.log2_parts);
-      const bool empty = q_start == part_start(q + 1, weight, p.log2_parts);
-      const int slot = q == p0 ? slot0 : 0;
-      const size_t row = empty ? row0 : ((size_t)(q * 2 + slot) * p.s_q + s) * kHeads;
+    for (int i = 0; i < kChunk; ++i) {
+      const int q = qb + i;
+      // a partition past the sequence or without units holds no share
+      const bool live = q <= p1 && part_start(q, weight, p.log2_parts) != part_start(q + 1, weight, p.log2_parts);
+      const size_t row = ((size_t)(q * 2 + (q == p0 ? slot0 : 0)) * p.s_q + s) * kHeads;
       const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
-        const float l = p.part_lse[row + head[k]];
-        // -inf: this share saw no row of this query token
-        const float w = (empty || l == kNegInf) ? 0.f : __expf(l - m[k]);
+        l[i][k] = kNegInf;
+        v[i][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) {
+          l[i][k] = p.part_lse[row + head[k]];     // -inf: the share saw no row of this token
+          v[i][k] = src[coff[k]];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      float mc = m[k];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) mc = fmaxf(mc, l[i][k]);
+      if (mc == kNegInf) continue;          // nothing seen yet
+      const float r = __expf(m[k] - mc);    // 0 while m is -inf
+      wsum[k] *= r;
+      acc[k].x *= r; acc[k].y *= r; acc[k].z *= r; acc[k].w *= r;
+      m[k] = mc;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const float w = __expf(l[i][k] - mc);   // 0 for -inf
         wsum[k] += w;
-        const float4 v = src[coff[k]];
-        acc[k].x += w * v.x; acc[k].y += w * v.y; acc[k].z += w * v.z; acc[k].w += w * v.w;
+        acc[k].x += w * v[i][k].x; acc[k].y += w * v[i][k].y; acc[k].z += w * v[i][k].z; acc[k].w += w * v[i][k].w;
       }
     }
   }
@@ -184,9 +160,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  // narrowest column slice that still gives about two workgroups per compute unit
+  // widest column slice that still gives about eight workgroups per compute
+  // unit: the shares of short and long sequences then mix on every unit
   const long long base = (long long)p.batch * p.s_q * (kHeads / kGroupHeads);
-  const long long want = 512;
+  const long long want = 2048;
   if (base * 4 >= want) {
     combine_kernel<8><<<dim3((unsigned)(base * 4)), dim3(256), 0, stream>>>(p);
   } else if (base * 8 >= want) {

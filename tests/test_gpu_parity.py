@@ -107,12 +107,20 @@ def _partition_map(lens, num_splits):
     return partition_map(lens, num_splits)[1]
 
 
-@pytest.mark.parametrize("s_q", [1, 2])
-def test_combine_kernel_on_oracle_partials(s_q):
+def _combine_lens(n):
+    return [int(x) for x in np.random.default_rng(n).integers(1, 260, size=n)]
+
+
+# (lens, s_q, partitions): the third cuts one sequence into about thirty
+# shares; the last two give the launcher enough workgroups to pick its wider
+# column slices (4 and 8 column blocks)
+@pytest.mark.parametrize("lens,s_q,splits", [([1, 64, 65, 300, 129], 1, 8), ([1, 64, 65, 300, 129], 2, 8),
+                                             ([3, 2000, 70], 1, 32),
+                                             (_combine_lens(32), 2, 32), (_combine_lens(64), 2, 64)])
+def test_combine_kernel_on_oracle_partials(lens, s_q, splits):
     """mla_combine alone, fed partials the oracle computed over the partition map."""
     import mla_latent_kv_39_amd as mla
-    inp = _small([1, 64, 65, 300, 129], s_q=s_q, seed=7)
-    splits = 8
+    inp = _small(lens, s_q=s_q, seed=7)
     owners = _partition_map(inp.seq_lens.tolist(), splits)
     po = torch.zeros((splits, 2, s_q, 128, 512), dtype=torch.float32)
     pl = torch.full((splits, 2, s_q, 128), float("-inf"), dtype=torch.float32)
