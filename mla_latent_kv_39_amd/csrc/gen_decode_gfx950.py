@@ -329,6 +329,133 @@ def seq_units_pass(a, find_first):
         a(f"s_mov_b32 {s(S_U)}, s{S_TMP + 1}")
 
 
+FAST_LENS = 4     # chunks of 64 sequence lengths the prologue keeps in registers
+V_LENS = 52       # v52..v55: seq_lens[64 c + lane] (free until the first step)
+
+
+def load_lens_fast(a):
+    """v[V_LENS + c] = seq_lens[min(64 c + lane, batch - 1)], c < FAST_LENS:
+    every length the partition map needs in one memory round trip."""
+    t = V_T
+    a(f"s_sub_u32 s{S_TMP}, {s(S_BATCH)}, 1")
+    for c in range(FAST_LENS):
+        a(f"v_add_u32 {vreg(t + c)}, {64 * c}, {vreg(V_LANE)}",
+          f"v_min_u32 {vreg(t + c)}, s{S_TMP}, {vreg(t + c)}",
+          f"v_lshlrev_b32 {vreg(t + c)}, 2, {vreg(t + c)}",
+          f"global_load_dword {vreg(V_LENS + c)}, {vreg(t + c)}, {sp(S_LENS)}")
+    a(s_waitcnt_vm(0))
+
+
+def units_fast(a, c):
+    """v[t+1] = units of sequence 64 c + lane (0 past the batch), v[t] = 64 c + lane."""
+    t = V_T
+    a(f"v_add_u32 {vreg(t)}, {64 * c}, {vreg(V_LANE)}",
+      f"v_cmp_gt_i32 vcc, {s(S_BATCH)}, {vreg(t)}",
+      f"v_add_u32 {vreg(t + 3)}, 63, {vreg(V_LENS + c)}",
+      f"v_ashrrev_i32 {vreg(t + 3)}, 6, {vreg(t + 3)}",
+      f"v_max_i32 {vreg(t + 3)}, 1, {vreg(t + 3)}",
+      f"v_cndmask_b32 {vreg(t + 1)}, 0, {vreg(t + 3)}, vcc",
+      "s_nop 1")
+
+
+def pages_before_fast(a, x_sgpr, dst_sgpr):
+    """pages_before_pass over the lengths in registers (batch <= 64 FAST_LENS)."""
+    t = V_T
+    T = S_TMP
+    done = a.new_label("pbfdone")
+    a(f"s_mov_b32 s{T + 1}, 0",
+      f"s_mov_b32 s{dst_sgpr}, 0")
+    for c in range(FAST_LENS):
+        if c:
+            a(f"s_cmp_le_u32 {s(S_BATCH)}, {64 * c}",
+              f"s_cbranch_scc1 {done}")
+        units_fast(a, c)
+        wave_incl_scan(a, t + 2, t + 1)
+        a(f"v_add_u32 {vreg(t + 2)}, s{T + 1}, {vreg(t + 2)}",
+          f"v_sub_u32 {vreg(t + 3)}, {vreg(t + 2)}, {vreg(t + 1)}",
+          f"v_mad_u32_u24 {vreg(t + 3)}, {vreg(t)}, {SEG_WEIGHT}, {vreg(t + 3)}",
+          f"v_add_u32 {vreg(t + 3)}, {SEG_WEIGHT}, {vreg(t + 3)}",
+          f"v_sub_u32 {vreg(t + 3)}, s{x_sgpr}, {vreg(t + 3)}",
+          f"v_max_i32 {vreg(t + 3)}, 0, {vreg(t + 3)}",
+          f"v_min_i32 {vreg(t + 3)}, {vreg(t + 1)}, {vreg(t + 3)}",
+          "s_nop 1")
+        wave_incl_scan(a, t, t + 3)
+        a(f"v_readlane_b32 s{T + 2}, {vreg(t)}, 63",
+          f"v_readlane_b32 s{T + 1}, {vreg(t + 2)}, 63",
+          f"s_add_u32 s{dst_sgpr}, s{dst_sgpr}, s{T + 2}")
+    a.label(done)
+
+
+def seq_units_fast(a, find_first):
+    """seq_units_pass over the lengths in registers; with find_first also
+    S_LLEN = the length of the sequence found."""
+    t = V_T
+    T = S_TMP
+    done = a.new_label("suf")
+    a(f"s_mov_b32 s{T + 1}, 0")
+    founds = []
+    for c in range(FAST_LENS):
+        if c:
+            a(f"s_cmp_le_u32 {s(S_BATCH)}, {64 * c}",
+              f"s_cbranch_scc1 {done}")
+        units_fast(a, c)
+        wave_incl_scan(a, t + 2, t + 1)
+        a(f"v_add_u32 {vreg(t + 2)}, s{T + 1}, {vreg(t + 2)}", "s_nop 1")
+        if find_first:
+            founds.append(a.new_label("suffound"))
+            a(f"v_cmp_lt_u32 vcc, {s(S_UA)}, {vreg(t + 2)}",
+              f"s_ff1_i32_b64 s{T + 2}, vcc",
+              f"s_cmp_lt_i32 s{T + 2}, 0",
+              f"s_cbranch_scc0 {founds[-1]}")
+        a(f"v_readlane_b32 s{T + 1}, {vreg(t + 2)}, 63")
+    a.label(done)
+    if not find_first:
+        a(f"s_mov_b32 {s(S_U)}, s{T + 1}")
+        return
+    a("s_branch .Lkernel_end")   # cannot happen when ua < U
+    out = a.new_label("sufout")
+    for c, f in enumerate(founds):
+        a.label(f)
+        a(f"s_add_u32 {s(S_CSEQ)}, s{T + 2}, {64 * c}",
+          f"v_sub_u32 {vreg(t + 3)}, {vreg(t + 2)}, {vreg(t + 1)}",
+          "s_nop 4",
+          f"v_readlane_b32 {s(S_CPRE)}, {vreg(t + 3)}, s{T + 2}",
+          f"v_readlane_b32 {s(S_LLEN)}, {vreg(V_LENS + c)}, s{T + 2}",
+          f"s_branch {out}")
+    a.label(out)
+
+
+def partition_map(a, fast):
+    """S_U, then this partition's units [S_UA, S_UB) (ends the kernel when
+    empty), the sequence S_CSEQ holding S_UA with its first unit S_CPRE and
+    length S_LLEN: every sequence weighs its units + SEG_WEIGHT; partition p of
+    P takes the weighted positions [(p W) >> log2 P, ((p + 1) W) >> log2 P), W
+    the total, i.e. the units whose positions fall there."""
+    T = S_TMP
+    (seq_units_fast(a, False) if fast else seq_units_pass(a, find_first=False))
+    a(f"s_mul_i32 s{T + 3}, {s(S_BATCH)}, {SEG_WEIGHT}",
+      f"s_add_u32 s{T + 3}, s{T + 3}, {s(S_U)}",
+      f"s_mul_i32 s{T}, {s(S_PART)}, s{T + 3}",
+      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, s{T + 3}",
+      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
+      f"s_mov_b32 s{T + 10}, s{T}",
+      f"s_add_u32 s{T + 2}, {s(S_PART)}, 1",
+      f"s_mul_i32 s{T}, s{T + 2}, s{T + 3}",
+      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, s{T + 3}",
+      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
+      f"s_mov_b32 s{T + 11}, s{T}")
+    pb = pages_before_fast if fast else pages_before_pass
+    pb(a, T + 10, S_UA)
+    pb(a, T + 11, S_UB)
+    a(f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
+      "s_cbranch_scc1 .Lkernel_end")
+    if fast:
+        seq_units_fast(a, True)
+    else:
+        seq_units_pass(a, find_first=True)
+        load_len(a, S_LLEN, S_CSEQ)
+
+
 def loader_advance(a, u_sgpr):
     """Move the loader cursor (LSEQ, LPRE, LUNITS, LLEN) forward to the sequence
     that holds unit u."""
@@ -1276,11 +1403,13 @@ def epilogue_split(a):
 
 
 def epi_store_split(a, hb, cb, vv, inv, operands):
-    """O[cb][hb] / l -> one 16-byte store per lane."""
+    """O[cb][hb] / l -> one 16-byte store per lane; the accumulators are
+    cleared for the next segment as they are read (under the store issue)."""
     o = (8 * cb + hb) * 4
     for i in range(4):
         a(f"v_accvgpr_read_b32 {vreg(vv[i])}, a{o + i}")
-    a("s_nop 1")
+    for i in range(4):
+        a(f"v_accvgpr_write_b32 a{o + i}, 0")
     for i in range(4):
         a(f"v_mul_f32 {vreg(vv[i])}, {vreg(vv[i])}, {vreg(inv)}")
     a("global_store_dwordx4 " + operands.format(v=vr(vv[0], 4)))
@@ -1581,20 +1710,6 @@ def dma_setup_hp(a, half, step_sgpr):
       f"s_addc_u32 s{S_PH + 1}, s{S_PAGE + 1}, 0")
 
 
-def issue_page_hp(a):
-    """Stand-alone loads of both halves of page S_UCUR into the tiles of steps
-    S_T and S_T + 1 (segment start after a restart, and the first page)."""
-    T = S_TMP
-    loader_advance(a, S_UCUR)
-    loader_lookup(a, S_UCUR, wait=True)
-    loader_page(a)
-    for half in range(2):
-        a(f"s_add_u32 s{T + 8}, {s(S_T)}, {half}")
-        dma_setup_hp(a, half, T + 8)
-        for g in dma_groups_hp():
-            a.lines += g
-
-
 def _atomic(lines):
     """Instruction lines (an Asm's) -> one filler item kept together."""
     return [list(lines)]
@@ -1855,12 +1970,20 @@ def drain_bases_hp(a):
 
 def start_loads_hp(a):
     """Loads of the steps S_T, S_T + 1 (page S_UCUR) and the loader state the
-    step S_T starts from (kernel start, restart)."""
+    step S_T starts from (kernel start, restart).  The block-table entries of
+    page S_UCUR and the next one are fetched together (one wait)."""
     T = S_TMP
-    issue_page_hp(a)
+    loader_advance(a, S_UCUR)
+    loader_lookup(a, S_UCUR, wait=False)
     a(f"s_add_u32 s{S_LKUP}, {s(S_UCUR)}, 1")
     a.lines += flatten(lookup_items(S_LKUP))
     a(s_waitcnt_lgkm(0))
+    loader_page(a)
+    for half in range(2):
+        a(f"s_add_u32 s{T + 8}, {s(S_T)}, {half}")
+        dma_setup_hp(a, half, T + 8)
+        for g in dma_groups_hp():
+            a.lines += g
     a.lines += flatten(loader_items(S_T))
 
 
@@ -1870,18 +1993,15 @@ def kernel_tail_hp(a):
     T = S_TMP
     lane_constants_hp(a)
     a(f"v_mov_b32 {vreg(V_ENT)}, 0")
-    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
-      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
-    load_len(a, S_LLEN, S_LSEQ)
-    units_of(a, S_LUNITS, S_LLEN)
     a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
       f"s_mov_b32 {s(S_T)}, 0",
       f"s_mov_b32 {s(S_EPI)}, 0")
+    load_q(a, S_CSEQ)      # Q first: its loads overlap the block-table lookups
     start_loads_hp(a)
-    load_q(a, S_CSEQ)
+    zero_o(a)              # later segments find O cleared by the epilogue
     # ------------------------------------------------ segments
     a.label(".Lseg")
-    segment_setup(a, with_q=False)
+    segment_setup(a, with_q=False, zero=False)
     a(f"s_sub_u32 {s(S_NSTEP)}, {s(S_SEGEND)}, {s(S_UCUR)}",
       f"s_lshl_b32 {s(S_NSTEP)}, {s(S_NSTEP)}, 1",
       f"s_mov_b32 {s(S_TL)}, 0",
@@ -1985,13 +2105,21 @@ def load_q(a, seq_sgpr):
             a(f"global_load_dwordx4 {vr(q, 4)}, {off}, s[{S_RBASE}:{S_RBASE + 1}] offset:{64 * ks}")
 
 
-def segment_setup(a, with_q=True):
+def segment_setup(a, with_q=True, zero=True):
     """Start of a segment (the sequence S_CSEQ from unit S_UCUR on): its
     length, units and visible rows, the query rows of this wave (Q into
     registers unless with_q is False: then they are on their way already),
-    the running softmax state, O = 0."""
+    the running softmax state, O = 0 (unless zero is False: the previous
+    epilogue, or the kernel start, cleared it)."""
     T = S_TMP
+    own, got = a.new_label("lenown"), a.new_label("lengot")
+    a(f"s_cmp_eq_u32 {s(S_LSEQ)}, {s(S_CSEQ)}",
+      f"s_cbranch_scc0 {own}",
+      f"s_mov_b32 {s(S_CLEN)}, {s(S_LLEN)}",     # the loader holds this sequence's length
+      f"s_branch {got}")
+    a.label(own)
     load_len(a, S_CLEN, S_CSEQ)
+    a.label(got)
     units_of(a, S_CUNITS, S_CLEN)
     a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
@@ -2013,7 +2141,8 @@ def segment_setup(a, with_q=True):
       f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
       f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
       f"s_mov_b32 {s(S_EXACT)}, 0")
-    zero_o(a)
+    if zero:
+        zero_o(a)
 
 
 def kernel(fp8=False):
@@ -2059,26 +2188,21 @@ def kernel(fp8=False):
       f"s_and_b32 {s(S_HBLK)}, s2, s{T}")
     a.label(mapped)
     # ------------------------------------------------ partition map
-    # every sequence weighs its units + SEG_WEIGHT; partition p of P takes the
-    # weighted positions [(p W) >> log2 P, ((p + 1) W) >> log2 P), W the total,
-    # i.e. the units [UA, UB) whose positions fall there
-    seq_units_pass(a, find_first=False)
-    a(f"s_mul_i32 s{T + 3}, {s(S_BATCH)}, {SEG_WEIGHT}",
-      f"s_add_u32 s{T + 3}, s{T + 3}, {s(S_U)}",
-      f"s_mul_i32 s{T}, {s(S_PART)}, s{T + 3}",
-      f"s_mul_hi_u32 s{T + 1}, {s(S_PART)}, s{T + 3}",
-      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 s{T + 10}, s{T}",
-      f"s_add_u32 s{T + 2}, {s(S_PART)}, 1",
-      f"s_mul_i32 s{T}, s{T + 2}, s{T + 3}",
-      f"s_mul_hi_u32 s{T + 1}, s{T + 2}, s{T + 3}",
-      f"s_lshr_b64 s[{T}:{T + 1}], s[{T}:{T + 1}], {s(S_LOG2P)}",
-      f"s_mov_b32 s{T + 11}, s{T}")
-    pages_before_pass(a, T + 10, S_UA)
-    pages_before_pass(a, T + 11, S_UB)
-    a(f"s_cmp_ge_u32 {s(S_UA)}, {s(S_UB)}",
-      "s_cbranch_scc1 .Lkernel_end")
-    seq_units_pass(a, find_first=True)
+    # up to 64 FAST_LENS sequences from lengths held in registers (one load),
+    # larger batches in passes over memory
+    slow, mapdone = a.new_label("mapslow"), a.new_label("mapfound")
+    a(f"s_cmp_gt_u32 {s(S_BATCH)}, {64 * FAST_LENS}",
+      f"s_cbranch_scc1 {slow}")
+    load_lens_fast(a)
+    partition_map(a, fast=True)
+    a(f"s_branch {mapdone}")
+    a.label(slow)
+    partition_map(a, fast=False)
+    a.label(mapdone)
+    # the loader cursor starts at the partition's first sequence
+    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
+      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
+    units_of(a, S_LUNITS, S_LLEN)
     # ------------------------------------------------ this wave's query rows
     a(f"s_lshl_b32 s{T}, {s(S_WAVE)}, 5",
       f"s_sub_u32 s{T + 1}, {s(S_HB)}, 1",
@@ -2101,11 +2225,7 @@ def kernel(fp8=False):
         a.lines += [f".L{KNAME}_end:", f"\t.size {KNAME}, .L{KNAME}_end-{KNAME}", ""]
         a.lines += descriptor()
         return a.text()
-    # ------------------------------------------------ loader cursor, first unit
-    a(f"s_mov_b32 {s(S_LSEQ)}, {s(S_CSEQ)}",
-      f"s_mov_b32 {s(S_LPRE)}, {s(S_CPRE)}")
-    load_len(a, S_LLEN, S_LSEQ)
-    units_of(a, S_LUNITS, S_LLEN)
+    # ------------------------------------------------ first unit
     a(f"s_mov_b32 {s(S_UCUR)}, {s(S_UA)}",
       f"s_mov_b32 {s(S_SLOT)}, 0")
     (issue_unit_fp8 if FP8 else issue_unit)(a, S_UCUR, S_SLOT)

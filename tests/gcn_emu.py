@@ -637,7 +637,7 @@ def _vmov(g, w, i):
 
 
 @op("v_add_u32", "v_sub_u32", "v_and_b32", "v_or_b32", "v_xor_b32", "v_lshlrev_b32", "v_lshrrev_b32",
-    "v_ashrrev_i32", "v_max_i32", "v_min_i32", "v_mul_u32_u24")
+    "v_ashrrev_i32", "v_max_i32", "v_min_i32", "v_min_u32", "v_mul_u32_u24")
 def _vint2(g, w, i):
     a, b = _vu(w, i, 1), _vu(w, i, 2)
     if i.op == "v_add_u32":
@@ -660,6 +660,8 @@ def _vint2(g, w, i):
         r = np.maximum(a.astype(np.uint32).view(np.int32), b.astype(np.uint32).view(np.int32)).view(np.uint32)
     elif i.op == "v_min_i32":
         r = np.minimum(a.astype(np.uint32).view(np.int32), b.astype(np.uint32).view(np.int32)).view(np.uint32)
+    elif i.op == "v_min_u32":
+        r = np.minimum(a, b)
     else:
         r = (a & 0xFFFFFF) * (b & 0xFFFFFF)
     w.vset(i.args[0], (np.asarray(r, np.uint64) & M32).astype(np.uint32))

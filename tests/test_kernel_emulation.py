@@ -86,3 +86,23 @@ def test_bf16_result_independent_of_wave_order():
 @pytest.mark.parametrize("lens,s_q,splits", [([100, 70], 1, 1), ([300, 70, 129, 1], 1, 4), ([200, 65], 2, 2)])
 def test_fp8_cache(lens, s_q, splits):
     _check(_small(lens, s_q=s_q, seed=1, cache="fp8_e4m3"), splits)
+
+
+@pytest.mark.parametrize("fast_chunks", [4, 1])
+def test_bf16_partition_map_over_many_sequences(fast_chunks):
+    # 66 sequences: two chunks of lengths, read from registers by the prologue
+    # (4 chunks held) or in passes over memory (1 chunk held, batch too large)
+    import gen_decode_gfx950 as G
+    lens = [1 + (7 * i) % 5 for i in range(60)] + [70, 3, 130, 5, 64, 2]
+    inp = _small(lens, seed=9)
+    keep = G.FAST_LENS
+    G.FAST_LENS = fast_chunks
+    try:
+        text = G.kernel(False)
+    finally:
+        G.FAST_LENS = keep
+    out, lse, po, pl = ED.emulate_decode(inp, 4, seed=5, text=text)
+    out, lse = ED.merged(inp, 4, out, lse, po, pl, O.merge_partials)
+    ref_out, ref_lse = O.mla_decode(inp)
+    assert np.max(np.abs(out - ref_out)) <= OUT_TOL
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_TOL
