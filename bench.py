@@ -134,7 +134,7 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     # the partition count only changes how the work is cut (the merge is exact): fill the GPU
-    splits = args.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q)
+    splits = args.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q, inp.max_blocks)
 
     # rotate enough copies of cache + queries that the MALL cannot hold them across steps
     footprint = inp.cache.numel() * inp.cache.element_size() + inp.q_absorbed.numel() * 2 + inp.q_rope.numel() * 2

@@ -107,7 +107,7 @@ typedef struct mla_latent_cache {
  *                units of the sequences before it), and partition p takes the
  *                units whose positions lie in [floor(p W / P),
  *                floor((p + 1) W / P)), W = total units + 3 batch.
- *                mla_num_splits_hint() gives a value that fills the GPU.
+ *                mla_num_splits_hint() gives one for the device and the cache size.
  *   partial_out  fp32 [num_splits, 2, s_q, 128 * 512]  may be NULL if num_splits == 1
  *                (layout below)
  *   partial_lse  fp32 [num_splits, 2, s_q, 128]        may be NULL if num_splits == 1
@@ -146,10 +146,14 @@ mla_status mla_combine(const float* partial_out, const float* partial_lse, const
                        hipStream_t stream);
 
 /*
- * A num_splits for mla_decode that gives every compute unit of `device` one
- * work partition (0 on error).  Depends only on the device and s_q.
+ * A num_splits for mla_decode (0 on error): one work partition per compute
+ * unit of `device` (per two with s_q = 2), halved while the cache capacity
+ * the block table allows, batch * max_blocks_per_seq pages plus 3 units per
+ * sequence of fixed cost, would leave fewer than 4 units per partition: short
+ * contexts then stay in few partitions and need little or no merging.
+ * max_blocks_per_seq <= 0 means unknown (no cap).
  */
-int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q);
+int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t max_blocks_per_seq);
 
 /* Bytes of partial_out and partial_lse needed for (num_splits, s_q). */
 size_t mla_partial_out_bytes(int32_t num_splits, int32_t s_q);

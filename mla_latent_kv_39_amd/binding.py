@@ -66,7 +66,7 @@ def _load():
     lib.mla_combine.restype = i32
     lib.mla_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.mla_num_splits_hint.restype = i32
-    lib.mla_num_splits_hint.argtypes = [i32, i32, i32]
+    lib.mla_num_splits_hint.argtypes = [i32, i32, i32, i32]
     lib.mla_partial_out_bytes.restype = sz
     lib.mla_partial_out_bytes.argtypes = [i32, i32]
     lib.mla_partial_lse_bytes.restype = sz
@@ -94,8 +94,8 @@ def mla_version() -> int:
     return int(_lib.mla_version())
 
 
-def mla_num_splits_hint(device: int, batch: int, s_q: int) -> int:
-    return int(_lib.mla_num_splits_hint(int(device), int(batch), int(s_q)))
+def mla_num_splits_hint(device: int, batch: int, s_q: int, max_blocks_per_seq: int = 0) -> int:
+    return int(_lib.mla_num_splits_hint(int(device), int(batch), int(s_q), int(max_blocks_per_seq)))
 
 
 def mla_partial_out_bytes(num_splits: int, s_q: int) -> int:

@@ -715,20 +715,22 @@ def softmax_lean(ss, S=None, P=None, tmp=None):
     set: P = 2^(scale S - m_ref), row sums, bf16 pack.  No max: a lane whose
     8-row sum passes 2^64 (the largest score more than ~64 above m_ref) flags a
     restart, and V_PEAK keeps the largest such sum so that the restart can
-    raise m_ref past it."""
+    raise m_ref past it.
+
+    The two row halves are interleaved so that no two exponentials (quarter
+    rate) sit next to each other: spread between MFMAs, each MFMA then hides
+    at most one of them."""
     if S is None:
         S, P, tmp = V_S[ss], V_P[ss], V_SMT[ss]
     t0, t1 = tmp[0], tmp[1]
-    x = Asm()
+    fma, exp, tail = [], [], []
     for h in range(2):
         regs = [S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
         mref = V_MREF[h]
-        for r in regs:
-            x(f"v_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(mref)}")
-        for r in regs:
-            x(f"v_exp_f32 {vreg(r)}, {vreg(r)}")
-        x("s_nop 0",
-          f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
+        fma.append([f"\tv_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(mref)}" for r in regs])
+        exp.append([f"\tv_exp_f32 {vreg(r)}, {vreg(r)}" for r in regs])
+        x = Asm()
+        x(f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
           f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
           f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
           f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[5])}",
@@ -745,7 +747,16 @@ def softmax_lean(ss, S=None, P=None, tmp=None):
               f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
               f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
               f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
-    return x.lines
+        tail.append(x.lines)
+    # half 0's sums read its exponentials long after they issue, half 1's sums
+    # follow seven other instructions (a transcendental result needs one)
+    out = list(fma[0])
+    for i in range(8):
+        out += [exp[0][i], fma[1][i]]
+    for i in range(8):
+        out += [exp[1][i], tail[0][i]]
+    out += tail[0][8:] + tail[1]
+    return out
 
 
 def merge_filler(ins, groups):
@@ -1412,7 +1423,9 @@ def epi_store_split(a, hb, cb, vv, inv, operands):
         a(f"v_accvgpr_write_b32 a{o + i}, 0")
     for i in range(4):
         a(f"v_mul_f32 {vreg(vv[i])}, {vreg(vv[i])}, {vreg(inv)}")
-    a("global_store_dwordx4 " + operands.format(v=vr(vv[0], 4)))
+    # system scope: written through the L2, which then holds no dirty output
+    # lines for the end of the kernel to write back (the merge reads them next)
+    a("global_store_dwordx4 " + operands.format(v=vr(vv[0], 4)) + " sc0 sc1")
 
 
 def epi_store(a, h, cb, vv, inv, operands):

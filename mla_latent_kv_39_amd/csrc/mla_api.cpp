@@ -7,6 +7,7 @@
 
 #include "../../include/mla.h"
 #include "mla_internal.h"
+#include "mla_schedule.h"
 
 namespace {
 
@@ -107,13 +108,18 @@ mla_status mla_combine(const float* partial_out, const float* partial_lse, const
   return mla::launch_combine(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
-int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q) {
+int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t max_blocks_per_seq) {
   if (batch < 1 || s_q < 1 || s_q > 2) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) return 0;
   int parts = s_q == 1 ? cus : cus / 2;
   int p2 = 1;
   while (p2 * 2 <= parts) p2 *= 2;  // partitions must be a power of two
+  if (max_blocks_per_seq > 0) {
+    // the most weighted units the partition map can see (see mla_schedule.h)
+    const long long most = (long long)batch * (max_blocks_per_seq + mla::kSegWeight);
+    while (p2 > 1 && most < 4LL * p2) p2 /= 2;
+  }
   return p2;
 }
 

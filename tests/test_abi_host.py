@@ -93,5 +93,5 @@ def test_combine_argument_errors(lib):
 
 
 def test_hint_rejects_bad_arguments(lib):
-    assert lib.mla_num_splits_hint(0, 0, 1) == 0
-    assert lib.mla_num_splits_hint(0, 4, 3) == 0
+    assert lib.mla_num_splits_hint(0, 0, 1, 0) == 0
+    assert lib.mla_num_splits_hint(0, 4, 3, 0) == 0

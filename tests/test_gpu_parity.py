@@ -154,3 +154,15 @@ def test_combine_kernel_on_oracle_partials(lens, s_q, splits):
 def _first_unit(inp, b):
     units = [max(1, (int(L) + 63) // 64) for L in inp.seq_lens.tolist()]
     return int(sum(units[:b]))
+
+
+def test_num_splits_hint_follows_the_cache_capacity():
+    import mla_latent_kv_39_amd as mla
+    dev = torch.cuda.current_device()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    full = 1 << (cus.bit_length() - 1)
+    assert mla.mla_num_splits_hint(dev, 32, 1, 0) == full          # capacity unknown
+    assert mla.mla_num_splits_hint(dev, 32, 1, 64) == full         # 32 * 67 units >= 4 per partition
+    assert mla.mla_num_splits_hint(dev, 1, 1, 2) == 1              # 5 units: one partition
+    assert mla.mla_num_splits_hint(dev, 8, 1, 2) == 8              # 40 units: 5 per partition
+    assert mla.mla_num_splits_hint(dev, 128, 2, 128) == full // 2  # two query tokens: two workgroups per partition

@@ -17,7 +17,7 @@ def _num_splits(inp):
     import mla_latent_kv_39_amd as mla
     if inp.num_splits:
         return int(inp.num_splits)
-    return mla.mla_num_splits_hint(torch.cuda.current_device(), inp.batch, inp.s_q)
+    return mla.mla_num_splits_hint(torch.cuda.current_device(), inp.batch, inp.s_q, inp.max_blocks)
 
 
 @pytest.mark.parametrize("name", ["single_b1_l128", "batched_b32_l1k_4k", "paged_b64_l256_32k",
