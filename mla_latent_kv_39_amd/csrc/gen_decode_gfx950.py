@@ -586,7 +586,8 @@ def pv_read(ss, cb):
 
 
 class Frag:
-    """One LDS operand fragment and the two MFMAs that consume it."""
+    """One LDS operand fragment (read into a ring buffer) and the MFMAs that
+    consume it."""
 
     def __init__(self, ring, ring_base, nring, idx, reads, mfmas, deps=None):
         self.ring, self.idx, self.nring = ring, idx, nring
@@ -595,20 +596,6 @@ class Frag:
         self.mfmas = [m.format(buf=vr(buf, 4)) for m in mfmas]
         self.deps = deps or [()] * len(mfmas)   # per MFMA: keys of other LDS reads it waits for
         self.read_ids = []
-
-
-def qk_frags(ss):
-    out = []
-    for i in range(36):
-        ks, tb = divmod(i, 2)
-        mf = []
-        for h in range(2):
-            sreg = V_S[ss] + (2 * tb + h) * 4
-            qreg = V_Q + (2 * ks + h) * 4
-            c = "0" if ks == 0 else vr(sreg, 4)
-            mf.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(sreg, 4)}, {{buf}}, {vr(qreg, 4)}, {c}")
-        out.append(Frag("A", V_A, NA, 36 * ss + i, qk_read(ss, i), mf))
-    return out
 
 
 def pv_frags(ss):
@@ -1064,12 +1051,17 @@ def f8_scale_reads(ss, blk, dst):
 
 def qk_fp8(a, ss):
     """Scores of sub-step ss: k^R part into S, then per latent block
-    T = C8_blk Q_blk (MFMA) and S += T * s_blk (fp32)."""
+    T = C8_blk Q_blk (MFMA) and S += T * s_blk (fp32).  Blocks alternate
+    between two accumulators (F8_T and the output-operand ring, which the
+    scores leave free) so that the fp32 update of block k runs between the
+    MFMAs of block k + 1; only the last block's update is exposed."""
+    TB = (F8_T, V_B)                 # block accumulators of even / odd blocks
+    SCB = (F8_P[0], F8_P[1])         # their scales (rows 4g .. of both row halves)
     order = [(16, tb) for tb in range(2)] + [(17, tb) for tb in range(2)]
     order += [(ks, tb) for ks in range(16) for tb in range(2)]
     frags = []
     for n, (ks, tb) in enumerate(order):
-        acc = F8_S if ks >= 16 else F8_T
+        acc = F8_S if ks >= 16 else TB[(ks // 4) % 2]
         first = ks == 16 or (ks < 16 and ks % 4 == 0)
         mf = []
         for h in range(2):
@@ -1078,18 +1070,35 @@ def qk_fp8(a, ss):
             c = "0" if first else vr(d, 4)
             mf.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(d, 4)}, {{buf}}, {vr(qreg, 4)}, {c}")
         frags.append(Frag("A", V_A, NA, n, qk_read(ss, 2 * ks + tb), mf))
+
+    def update(blk):
+        """S += T_blk * s_blk, 16 fp32 FMAs."""
+        out = []
+        for tb in range(2):
+            for h in range(2):
+                for i in range(4):
+                    r = (2 * tb + h) * 4 + i
+                    out.append(f"\tv_fma_f32 {vreg(F8_S + r)}, {vreg(TB[blk % 2] + r)}, "
+                               f"{vreg(SCB[blk % 2] + 4 * tb + i)}, {vreg(F8_S + r)}")
+        return out
+
     lds = LdsOrder()
     for f in frags[:NA]:
         for r in f.reads:
             f.read_ids.append(lds.issue())
             a.lines.append(r)
-    sc_ids = None
+    sc_ids = {}
+    pending = []                      # the previous block's update, spread over this block's fragments
     for p, f in enumerate(frags):
-        ks = order[p][0]
-        if ks < 16 and ks % 4 == 0 and order[p][1] == 0:      # block start: its scales
-            for r in f8_scale_reads(ss, ks // 4, F8_P[0]):
+        ks, tb = order[p]
+        if ks < 16 and ks % 4 == 0 and tb == 0:      # block start: its scales
+            blk = ks // 4
+            for r in f8_scale_reads(ss, blk, SCB[blk % 2]):
                 a.lines.append(r)
-            sc_ids = lds.issue(), lds.issue()
+            sc_ids[blk] = (lds.issue(), lds.issue())
+            if blk > 0:
+                pending = update(blk - 1)
+                a.lines += lds.wait(sc_ids[blk - 1][1])
         a.lines += lds.wait(max(f.read_ids))
         a.lines += f.mfmas
         if p + NA < len(frags):
@@ -1097,43 +1106,60 @@ def qk_fp8(a, ss):
             for r in g.reads:
                 g.read_ids.append(lds.issue())
                 a.lines.append(r)
-        if ks < 16 and ks % 4 == 3 and order[p][1] == 1:      # block end: S += T * s
-            a.lines += lds.wait(sc_ids[1])
-            a("s_nop 7", "s_nop 7", "s_nop 3")
-            for tb in range(2):
-                for h in range(2):
-                    for i in range(4):
-                        r = (2 * tb + h) * 4 + i
-                        a(f"v_fma_f32 {vreg(F8_S + r)}, {vreg(F8_T + r)}, {vreg(F8_P[0] + 4 * tb + i)}, {vreg(F8_S + r)}")
-    a("s_nop 7", "s_nop 7", "s_nop 3")
+        # the update starts two fragments (four MFMAs) into the next block, past the
+        # last MFMA of its block by more than the MFMA-to-VALU latency
+        if ks < 16 and pending and (ks % 4) * 2 + tb >= 2:
+            a.lines += pending[:3]
+            pending = pending[3:]
+    a.lines += pending
+    a("s_nop 7", "s_nop 7", "s_nop 3")   # last block's MFMAs -> its update
+    a.lines += lds.wait(sc_ids[3][1])
+    a.lines += update(3)
 
 
 def pv_fp8(a, ss):
-    """O^T += C8^T (P * s_blk)^T block by block (8 column blocks of 16 per latent block)."""
+    """O^T += C8^T (P * s_blk)^T block by block (8 column blocks of 16 per
+    latent block).  The scaled probabilities of block blk + 1 are formed between
+    the MFMAs of block blk (the two bf16 buffers alternate)."""
     frags = pv_frags(ss)
     lds = LdsOrder()
     for f in frags[:NB]:
         for r in f.reads:
             f.read_ids.append(lds.issue())
             a.lines.append(r)
-    for blk in range(4):
+
+    def scaled(blk):
+        """P * s_blk -> bf16 buffer F8_P[blk & 1] (24 VALU instructions)."""
         pb = F8_P[blk & 1]
-        for r in f8_scale_reads(ss, blk, F8_T):
-            a.lines.append(r)
-        sid = lds.issue(), lds.issue()
-        a.lines += lds.wait(sid[1])
+        out = []
         for h in range(2):
             regs = [F8_S + (2 * tb + h) * 4 + i for tb in range(2) for i in range(4)]
             prod = [F8_T + 8 + j for j in range(8)]
             for j, r in enumerate(regs):
-                a(f"v_mul_f32 {vreg(prod[j])}, {vreg(r)}, {vreg(F8_T + j)}")
-            p = pb + 4 * h
-            a(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(prod[0])}, {vreg(prod[1])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(prod[2])}, {vreg(prod[3])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(prod[4])}, {vreg(prod[5])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(prod[6])}, {vreg(prod[7])}")
-        a("s_nop 4")   # VALU writes of P -> MFMA reads
-        for cb in range(8 * blk, 8 * blk + 8):
+                out.append(f"\tv_mul_f32 {vreg(prod[j])}, {vreg(r)}, {vreg(F8_T + j)}")
+            q = pb + 4 * h
+            out += [f"\tv_cvt_pk_bf16_f32 {vreg(q)}, {vreg(prod[0])}, {vreg(prod[1])}",
+                    f"\tv_cvt_pk_bf16_f32 {vreg(q + 1)}, {vreg(prod[2])}, {vreg(prod[3])}",
+                    f"\tv_cvt_pk_bf16_f32 {vreg(q + 2)}, {vreg(prod[4])}, {vreg(prod[5])}",
+                    f"\tv_cvt_pk_bf16_f32 {vreg(q + 3)}, {vreg(prod[6])}, {vreg(prod[7])}"]
+        return out
+
+    for r in f8_scale_reads(ss, 0, F8_T):
+        a.lines.append(r)
+    sid = lds.issue(), lds.issue()
+    a.lines += lds.wait(sid[1])
+    a.lines += scaled(0)
+    a("s_nop 4")   # VALU writes of P -> MFMA reads
+    for blk in range(4):
+        pb = F8_P[blk & 1]
+        nxt = []
+        if blk < 3:
+            # scale values of the next block into F8_T (free: this block's products are packed)
+            for r in f8_scale_reads(ss, blk + 1, F8_T):
+                a.lines.append(r)
+            sid = lds.issue(), lds.issue()
+            nxt = scaled(blk + 1)
+        for j, cb in enumerate(range(8 * blk, 8 * blk + 8)):
             f = frags[cb]
             a.lines += lds.wait(max(f.read_ids))
             for h in range(2):
@@ -1145,6 +1171,14 @@ def pv_fp8(a, ss):
                 for r in g.reads:
                     g.read_ids.append(lds.issue())
                     a.lines.append(r)
+            # the next block's products over fragments 1 .. 4 (done three fragments,
+            # six MFMAs, before its first MFMA reads them)
+            if nxt and 1 <= j <= 4:
+                if j == 1:
+                    a.lines += lds.wait(sid[1])
+                k = 6 if j < 4 else len(nxt)
+                a.lines += nxt[:k]
+                nxt = nxt[k:]
 
 
 def substep_fp8(a, ss, lean):
