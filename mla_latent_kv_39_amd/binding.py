@@ -184,7 +184,14 @@ def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, sc
 
 def mla_combine(partial_out, partial_lse, seq_lens, num_splits: int, out_latent, lse, stream=None) -> None:
     """Enqueue mla_combine (see include/mla.h)."""
+    import torch
     B, S = int(out_latent.shape[0]), int(out_latent.shape[1])
+    if int(num_splits) > 1:
+        _need(partial_out, torch.float32, (num_splits, 2, S, NUM_HEADS * LATENT_DIM), "partial_out")
+        _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
+    _need(seq_lens, torch.int32, (B,), "seq_lens")
+    _need(out_latent, torch.float32, (B, S, NUM_HEADS, LATENT_DIM), "out_latent")
+    _need(lse, torch.float32, (B, S, NUM_HEADS), "lse")
     st = _lib.mla_combine(_ptr(partial_out), _ptr(partial_lse), _ptr(seq_lens), B, S, int(num_splits),
                           _ptr(out_latent), _ptr(lse), _stream_handle(stream))
     if st != MLA_OK:

@@ -95,3 +95,21 @@ def test_combine_argument_errors(lib):
 def test_hint_rejects_bad_arguments(lib):
     assert lib.mla_num_splits_hint(0, 0, 1, 0) == 0
     assert lib.mla_num_splits_hint(0, 4, 3, 0) == 0
+
+
+def test_binding_checks_combine_buffers_before_the_library(lib):
+    # shapes, dtypes and placement are checked on the host before any call into libmla
+    import torch
+    out = torch.zeros((2, 1, 128, 512), dtype=torch.float32)
+    lse = torch.zeros((2, 1, 128), dtype=torch.float32)
+    lens = torch.zeros((2,), dtype=torch.int32)
+    po = torch.zeros((4, 2, 1, 128 * 512), dtype=torch.float32)
+    pl = torch.zeros((4, 2, 1, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="partial_out must have shape"):
+        lib.mla_combine(po[:, :, :, :100], pl, lens, 4, out, lse)
+    with pytest.raises(TypeError, match="partial_out must be"):
+        lib.mla_combine(po.double(), pl, lens, 4, out, lse)
+    with pytest.raises(ValueError, match="partial_out must be a device tensor"):
+        lib.mla_combine(po, pl, lens, 4, out, lse)        # host tensors never reach the library
+    with pytest.raises(ValueError, match="seq_lens must have shape"):
+        lib.mla_combine(po, pl, lens[:1], 1, out, lse)    # one partition: no partials to check
