@@ -106,3 +106,34 @@ def test_bf16_partition_map_over_many_sequences(fast_chunks):
     ref_out, ref_lse = O.mla_decode(inp)
     assert np.max(np.abs(out - ref_out)) <= OUT_TOL
     assert np.max(np.abs(lse - ref_lse)) <= LSE_TOL
+
+
+def test_fp8_restart_path():
+    # as the bf16 case: two rows whose (bf16) k^R is 48 times head 0's q^R
+    inp = _small([300], seed=6, cache="fp8_e4m3")
+    for j in (150, 295):
+        page = int(inp.block_table[0, j // 64])
+        inp.cache_rope[page, j % 64] = (inp.q_rope[0, 0, 0].float() * 48.0).to(torch.bfloat16)
+    cmax = float(np.abs(O.sequence_rows(inp, 0, 300)[:, :512]).max())
+    _check(inp, 1, out_tol=2.0 ** -8 * cmax)
+
+
+def test_fp8_empty_sequences_and_nan_tails():
+    inp = _small([0, 1, 33, 70], s_q=2, seed=4, cache="fp8_e4m3")
+    ref = O.mla_decode(inp)
+    # token 1 of the 33-row sequence gives one row 93% of its softmax: the bf16
+    # rounding of P * scale (relative 2^-8) then bounds the output error by
+    # 2^-8 max|c| rather than 1e-2 (the kernel's 0.0123 is exactly what that
+    # rounding gives in numpy)
+    cmax = max(float(np.abs(O.sequence_rows(inp, b, int(inp.seq_lens[b]))[:, :512]).max())
+               for b in range(inp.batch) if int(inp.seq_lens[b]) > 0)
+    tol = max(OUT_TOL, 2.0 ** -8 * cmax)
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        if L % 64:
+            page = int(inp.block_table[b, (L - 1) // 64])
+            inp.cache[page, L % 64:, :] = 0x7F            # e4m3 NaN code
+            inp.cache_scales[page, L % 64:, :] = float("nan")
+            inp.cache_rope[page, L % 64:, :] = float("nan")
+    for splits in (1, 4):
+        _check(inp, splits, out_tol=tol, ref=ref)
