@@ -1648,6 +1648,9 @@ N_PH, N_STEP, N_NVH, N_ROW0, N_MODE, N_DMALDS = 70, 72, 74, 75, 76, 77
 S_LKUP = 3                        # page to look up (the loader items' own; s3 holds nothing else)
 S_EPI = 50                        # 1: the segment follows an epilogue (its Q loads went out before
                                   # the epilogue's 66 stores)
+# The cache rows are read once per launch: their direct-to-LDS loads are
+# nontemporal (streaming), which measured 2-5% faster than the default policy.
+ROW_LOAD_POLICY = " nt"
 DMA_EARLY = 9                     # > 0: the loads of step t + 2 go out over fragments 0..DMA_EARLY
 
 
@@ -1737,7 +1740,7 @@ def dma_groups_hp():
                        f"\ts_addc_u32 s{S_DPAGE + 1}, s{S_PH + 1}, 0",
                        f"\ts_add_u32 m0, {s(S_DMALDS)}, {4096 * k}",
                        "\ts_nop 0",
-                       f"\tglobal_load_lds_dwordx4 {vreg(V_DMAS)}, {sp(S_DPAGE)}"])
+                       f"\tglobal_load_lds_dwordx4 {vreg(V_DMAS)}, {sp(S_DPAGE)}{ROW_LOAD_POLICY}"])
     return groups
 
 
