@@ -108,18 +108,25 @@ typedef struct mla_latent_cache {
  *                units whose positions lie in [floor(p W / P),
  *                floor((p + 1) W / P)), W = total units + 3 batch.
  *                mla_num_splits_hint() gives one for the device and the cache size.
- *   partial_out  fp32 [num_splits, 2, s_q, 128 * 512]  may be NULL if num_splits == 1
- *                (layout below)
+ *   partial_out  workspace of mla_partial_out_bytes(num_splits, s_q) bytes,
+ *                16-byte aligned; may be NULL if num_splits == 1 (layout below)
  *   partial_lse  fp32 [num_splits, 2, s_q, 128]        may be NULL if num_splits == 1
  *   out_latent   fp32 [batch, s_q, 128, 512]
  *   lse          fp32 [batch, s_q, 128]
  *
- * partial_out layout: each (split, slot, token) block of 128 x 512 values is
- * four groups of 32 heads, 16384 values each, in the order the kernel's lanes
- * hold them: the value of head 32 j + 16 a + r (a < 2, r < 16) and latent
- * column 16 c + 4 g + i (c < 32, g < 4, i < 4) is at offset
- * 16384 j + 4 (64 (32 a + c) + 16 g + r) + i of its block.  partial_lse is
- * plain [.., head].
+ * partial_out layout.  First num_splits * 2 * s_q blocks (split, slot, token)
+ * of 128 x 512 fp16 values (131,072 bytes each), then, for the same blocks in
+ * the same order, 512 fp32 descales each (2,048 bytes).  A block is four
+ * groups of 32 heads, 16384 values each, in the order the kernels' lanes hold
+ * them: the value of head 32 j + 16 a + r (a < 2, r < 16) and latent column
+ * 16 c + 4 g + i (c < 32, g < 4, i < 4) sits at index
+ * 16384 j + 8 (64 c + 16 g + r) + 4 a + i of its block, and its descale d at
+ * index 128 (c / 8) + 32 j + 2 r + a of the block's descales.  The partial
+ * output is the fp16 value times d; d is a power of two chosen per (block,
+ * column quarter c / 8, head) so that the largest |value| lies in
+ * [2^14, 2^15) (d no smaller than 2^-90): 11 significant bits for every
+ * element that matters.
+ * partial_lse is plain [.., head] fp32.
  *
  * A sequence whose rows all fall into one partition gets its final out_latent
  * and lse here.  A sequence cut across partitions leaves one normalised partial
@@ -129,7 +136,7 @@ typedef struct mla_latent_cache {
  */
 mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_latent_cache* cache,
                       const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, float* partial_out,
+                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, void* partial_out,
                       float* partial_lse, float* out_latent, float* lse, hipStream_t stream);
 
 /*
@@ -141,7 +148,7 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
  * finished are left untouched.  seq_lens, batch, s_q and num_splits must equal
  * those of the preceding mla_decode (they rebuild the same partition map).
  */
-mla_status mla_combine(const float* partial_out, const float* partial_lse, const int32_t* seq_lens,
+mla_status mla_combine(const void* partial_out, const float* partial_lse, const int32_t* seq_lens,
                        int32_t batch, int32_t s_q, int32_t num_splits, float* out_latent, float* lse,
                        hipStream_t stream);
 

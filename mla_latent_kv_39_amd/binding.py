@@ -172,7 +172,7 @@ def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, sc
             raise ValueError("max_blocks_per_seq is required for a contiguous cache")
         mb = int(max_blocks_per_seq)
     if num_splits > 1:
-        _need(partial_out, torch.float32, (num_splits, 2, S, NUM_HEADS * LATENT_DIM), "partial_out")
+        _need(partial_out, torch.uint8, (mla_partial_out_bytes(num_splits, S),), "partial_out")
         _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
     d = cache.desc()
     st = _lib.mla_decode(_ptr(q_absorbed), _ptr(q_rope), ctypes.byref(d), _ptr(block_table), mb, _ptr(seq_lens),
@@ -187,7 +187,7 @@ def mla_combine(partial_out, partial_lse, seq_lens, num_splits: int, out_latent,
     import torch
     B, S = int(out_latent.shape[0]), int(out_latent.shape[1])
     if int(num_splits) > 1:
-        _need(partial_out, torch.float32, (num_splits, 2, S, NUM_HEADS * LATENT_DIM), "partial_out")
+        _need(partial_out, torch.uint8, (mla_partial_out_bytes(num_splits, S),), "partial_out")
         _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
     _need(seq_lens, torch.int32, (B,), "seq_lens")
     _need(out_latent, torch.float32, (B, S, NUM_HEADS, LATENT_DIM), "out_latent")

@@ -1240,20 +1240,20 @@ def epilogue(a):
       f"s_mul_hi_u32 s{T + 12}, s{T + 1}, 2048",
       f"s_add_u32 s{T + 12 + 2}, s{T + 4}, s{T + 9}",
       f"s_addc_u32 s{T + 12 + 3}, s{T + 5}, s{T + 12}")
-    x = EPI_TEMPS
     obase = sp(T + 14)
+    inv = (16, 17)
     for h in range(2):
-        lt, inv, lse, t0, t1, off = temps(*x[0:6], pool=x)
+        lt, lse, t0, t1 = 18, 19, 20, 21
         a(f"v_mov_b32 {vreg(lt)}, {vreg(V_LRUN[h])}")
         xor_reduce(a, lt, "v_add_f32", t0, t1)
-        a(f"v_rcp_f32 {vreg(inv)}, {vreg(lt)}",
+        a(f"v_rcp_f32 {vreg(inv[h])}, {vreg(lt)}",
           f"v_log_f32 {vreg(lse)}, {vreg(lt)}",
           "s_nop 1",
           f"v_cmp_lt_f32 vcc, 0, {vreg(lt)}",
           f"v_add_f32 {vreg(lse)}, {vreg(V_MREF[h])}, {vreg(lse)}",
           f"v_mul_f32 {vreg(lse)}, {LN2}, {vreg(lse)}",
           "s_nop 1",
-          f"v_cndmask_b32 {vreg(inv)}, 0, {vreg(inv)}, vcc",
+          f"v_cndmask_b32 {vreg(inv[h])}, 0, {vreg(inv[h])}, vcc",
           f"v_cndmask_b32 {vreg(lse)}, {vreg(V_NEGINF)}, {vreg(lse)}, vcc")
         # lse of head 16h + r16 from the lanes with g == 0
         a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
@@ -1261,28 +1261,82 @@ def epilogue(a):
           f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
           f"global_store_dword {vreg(t0)}, {vreg(lse)}, s[{T + 10}:{T + 11}] offset:{64 * h}",
           f"s_mov_b64 exec, {sp(S_EXEC)}")
-        bufs = [x[8:12], x[12:16], x[16:20], x[20:24]]
-        rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
-        a(f"s_cmp_eq_u32 s{T + 3}, 0",
-          f"s_cbranch_scc1 {rowwise}")
-        # partial: lane order, store (h, cb) of lane L at (32h + cb) KB + 16 L of the wave's 64 KB
-        a(f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
-          f"s_add_u32 s{T + 16}, s{T + 14}, {32 * 1024 * h}",
-          f"s_addc_u32 s{T + 17}, s{T + 15}, 0")
-        for cb in range(32):
-            if cb and cb % 4 == 0:
-                a(f"s_add_u32 s{T + 16}, s{T + 16}, 4096", f"s_addc_u32 s{T + 17}, s{T + 17}, 0")
-            epi_store(a, h, cb, bufs[cb % 4], inv, f"{vreg(off)}, {{v}}, s[{T + 16}:{T + 17}] offset:{1024 * (cb % 4)}")
-        a(f"s_branch {stored}")
-        # final result: row layout, lane (g, r16) -> (16h + r16) * 2048 + 16g + 64cb
-        a.label(rowwise)
+    rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
+    a(f"s_cmp_eq_u32 s{T + 3}, 0",
+      f"s_cbranch_scc1 {rowwise}")
+    epi_partial_f16_fp8(a, inv)
+    a(f"s_branch {stored}")
+    # final result: row layout, lane (g, r16) -> (16h + r16) * 2048 + 16g + 64cb
+    a.label(rowwise)
+    x = EPI_TEMPS
+    bufs = [x[8:12], x[12:16], x[16:20], x[20:24]]
+    off, t0 = 18, 19
+    for h in range(2):
         a(f"v_lshlrev_b32 {vreg(t0)}, 4, {vreg(V_G)}",
           f"v_lshl_add_u32 {vreg(off)}, {vreg(V_R16)}, 11, {vreg(t0)}")
         if h:
             a(f"v_add_u32 {vreg(off)}, {16 * 2048}, {vreg(off)}")
         for cb in range(32):
-            epi_store(a, h, cb, bufs[cb % 4], inv, f"{vreg(off)}, {{v}}, {obase} offset:{64 * cb}")
-        a.label(stored)
+            epi_store(a, h, cb, bufs[cb % 4], inv[h], f"{vreg(off)}, {{v}}, {obase} offset:{64 * cb}")
+    a.label(stored)
+
+
+def epi_partial_f16_fp8(a, inv):
+    """e4m3 kernel: this wave's 32 query rows (row index s[T+1]) over all 512
+    columns, normalised, as fp16 partials with their descales (the layout of
+    the bf16 kernel's partials: chunk (column block c, lane) holds heads
+    16a + r16, a < 2, columns 16c + 4g .. +3, at 1 KB c + 16 lane).  Per
+    column quarter the 64 accumulator values of each lane are read, the
+    per-row largest |value| taken (the four lanes g of a row), the descales
+    stored, and the values scaled, packed and stored."""
+    T = S_TMP
+    vals = list(range(32, 96))           # (cb - 8q, a, i) at 32 + 8 (cb - 8q) + 4 a + i
+    invq, m0, m1, t, t0, t1, off, offt = (18, 19), 20, 21, 22, 23, 24, 25, 26
+    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_SQ)}",
+      f"s_lshr_b32 s{T + 7}, s{T + 8}, 14",
+      f"s_lshl_b32 s{T + 6}, s{T + 8}, 18",
+      f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 4}",
+      f"s_addc_u32 s{T + 7}, s{T + 7}, s{T + 5}",
+      # values: out + 1024 row; descales: table + 16 row - 12 (row & 127)
+      f"s_lshl_b32 s{T + 16}, s{T + 1}, 10",
+      f"s_lshr_b32 s{T + 17}, s{T + 1}, 22",
+      f"s_add_u32 s{T + 16}, s{T + 16}, s{T + 4}",
+      f"s_addc_u32 s{T + 17}, s{T + 17}, s{T + 5}",
+      f"s_and_b32 s{T + 8}, s{T + 1}, 127",
+      f"s_mul_i32 s{T + 8}, s{T + 8}, 12",
+      f"s_lshl_b32 s{T + 9}, s{T + 1}, 4",
+      f"s_sub_u32 s{T + 9}, s{T + 9}, s{T + 8}",
+      f"s_add_u32 s{T + 18}, s{T + 6}, s{T + 9}",
+      f"s_addc_u32 s{T + 19}, s{T + 7}, 0",
+      f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
+      f"v_lshlrev_b32 {vreg(offt)}, 3, {vreg(V_R16)}")
+    for q in range(4):
+        for cl in range(8):
+            for h in range(2):
+                for i in range(4):
+                    a(f"v_accvgpr_read_b32 {vreg(vals[8 * cl + 4 * h + i])}, a{(2 * (8 * q + cl) + h) * 4 + i}")
+        for h, m in ((0, m0), (1, m1)):
+            lane_abs_max(a, m, [vals[8 * cl + 4 * h + i] for cl in range(8) for i in range(4)])
+            xor_reduce(a, m, "v_max_f32", t0, t1)
+            a(f"v_mov_b32 {vreg(invq[h])}, {vreg(inv[h])}")
+            f16_scale(a, m, invq[h], t)
+        a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
+          f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
+          f"global_store_dwordx2 {vreg(offt)}, {vr(m0, 2)}, s[{T + 18}:{T + 19}] offset:{512 * q} sc0 sc1",
+          f"s_mov_b64 exec, {sp(S_EXEC)}")
+        for cl in range(8):
+            for h in range(2):
+                for i in range(4):
+                    r = vals[8 * cl + 4 * h + i]
+                    a(f"v_mul_f32 {vreg(r)}, {vreg(r)}, {vreg(invq[h])}")
+        for cl in range(8):
+            v0 = vals[8 * cl]
+            for k in range(4):
+                a(f"v_cvt_pk_f16_f32 {vreg(v0 + k)}, {vreg(v0 + 2 * k)}, {vreg(v0 + 2 * k + 1)}")
+            cb = 8 * q + cl
+            if cb and cb % 4 == 0:
+                a(f"s_add_u32 s{T + 16}, s{T + 16}, 4096", f"s_addc_u32 s{T + 17}, s{T + 17}, 0")
+            a(f"global_store_dwordx4 {vreg(off)}, {vr(v0, 4)}, s[{T + 16}:{T + 17}] offset:{1024 * (cb % 4)} sc0 sc1")
 
 
 def epilogue_split(a):
@@ -1385,58 +1439,49 @@ def epilogue_split(a):
           f"v_cndmask_b32 {vreg(inv[hb])}, 0, {vreg(t1)}, vcc")
     a("s_nop 7", "s_nop 7", "s_nop 3")   # last MFMAs -> accvgpr reads
     # per owner group j (query rows 32j ..): token (32j) >> log2(heads per block), head
-    # (32j & (heads per block - 1)) + head block * heads per block; base pointer s[T+12+2j : +1]
+    # (32j & (heads per block - 1)) + head block * heads per block; its row index
+    # (128 rows per (slot | sequence, token) + head) in s[T+12+j]
     a(f"s_ff1_i32_b32 s{T + 9}, {s(S_HB)}",
       f"s_sub_u32 s{T + 10}, {s(S_HB)}, 1",
       f"s_mul_i32 s{T + 11}, {s(S_HBLK)}, {s(S_HB)}")
     for j in range(4):
-        b = T + 12 + 2 * j
+        b = T + 12 + j
         a(f"s_lshr_b32 s{b}, {32 * j}, s{T + 9}",
           f"s_add_u32 s{b}, s{b}, s{T + 1}",
           f"s_lshl_b32 s{b}, s{b}, 7",
-          f"s_and_b32 s{b + 1}, {32 * j}, s{T + 10}",
-          f"s_add_u32 s{b}, s{b}, s{b + 1}",
-          f"s_add_u32 s{b}, s{b}, s{T + 11}",
-          f"s_mul_hi_u32 s{b + 1}, s{b}, 2048",
-          f"s_mul_i32 s{b}, s{b}, 2048",
-          f"s_add_u32 s{b}, s{b}, s{T + 4}",
-          f"s_addc_u32 s{b + 1}, s{b + 1}, s{T + 5}")
-    bufs = [list(range(32 + 4 * k, 36 + 4 * k)) for k in range(4)]
-    off = 48
+          f"s_and_b32 s{T + 16}, {32 * j}, s{T + 10}",
+          f"s_add_u32 s{b}, s{b}, s{T + 16}",
+          f"s_add_u32 s{b}, s{b}, s{T + 11}")
     rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
     a(f"s_cmp_eq_u32 s{T + 3}, 0",
       f"s_cbranch_scc1 {rowwise}")
-    # partial: lane order, block (hb = 2j + a, column block c = 8w + cb) at (32a + c) KB + 16 L
-    # of group j's 64 KB
-    a(f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
-      f"s_lshl_b32 s{T + 8}, {s(S_WAVE)}, 13")
-    n = 0
-    for j in range(4):
-        b = T + 12 + 2 * j
-        for h in range(2):
-            a(f"s_add_u32 s{T + 6}, s{b}, s{T + 8}",
-              f"s_addc_u32 s{T + 7}, s{b + 1}, 0")
-            if h:
-                a(f"s_add_u32 s{T + 6}, s{T + 6}, 0x8000",
-                  f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
-            for cb in range(8):
-                if cb == 4:
-                    a(f"s_add_u32 s{T + 6}, s{T + 6}, 4096", f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
-                epi_store_split(a, 2 * j + h, cb, bufs[n % 4], inv[2 * j + h],
-                                f"{vreg(off)}, {{v}}, s[{T + 6}:{T + 7}] offset:{1024 * (cb % 4)}")
-                n += 1
-    a(f"s_branch {stored}")
+    # S_EPI tells the next segment's first step how many stores follow its Q
+    # loads (the two lse stores above, then this branch's)
+    n0 = len(a.lines)
+    epi_partial_f16(a, inv)
+    assert 2 + sum(ln.strip().startswith("global_store") for ln in a.lines[n0:]) == EPI_STORES_PARTIAL
+    a(f"s_mov_b32 {s(S_EPI)}, 2",
+      f"s_branch {stored}")
     # final result: row layout, lane (g, r16) of block (hb, cb) -> row head + 16h + r16,
     # columns 128w + 16cb + 4g ..
+    bufs = [list(range(32 + 4 * k, 36 + 4 * k)) for k in range(4)]
+    off = 48
     a.label(rowwise)
     a(f"v_lshlrev_b32 {vreg(t0)}, 4, {vreg(V_G)}",
       f"v_lshl_add_u32 {vreg(off)}, {vreg(V_R16)}, 11, {vreg(t0)}",
       f"s_lshl_b32 s{T + 8}, {s(S_WAVE)}, 9")
+    n = 0
+    n0 = len(a.lines)
     for j in range(4):
-        b = T + 12 + 2 * j
+        b = T + 12 + j
         for h in range(2):
-            a(f"s_add_u32 s{T + 6}, s{b}, s{T + 8}",
-              f"s_addc_u32 s{T + 7}, s{b + 1}, 0")
+            # s[T+6:T+7] = out + 2048 row + 512 w (+ 16 rows for the second half)
+            a(f"s_lshl_b32 s{T + 6}, s{b}, 11",
+              f"s_lshr_b32 s{T + 7}, s{b}, 21",
+              f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 8}",
+              f"s_addc_u32 s{T + 7}, s{T + 7}, 0",
+              f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 4}",
+              f"s_addc_u32 s{T + 7}, s{T + 7}, s{T + 5}")
             if h:
                 a(f"s_add_u32 s{T + 6}, s{T + 6}, 0x8000",
                   f"s_addc_u32 s{T + 7}, s{T + 7}, 0")
@@ -1444,7 +1489,112 @@ def epilogue_split(a):
                 epi_store_split(a, 2 * j + h, cb, bufs[n % 4], inv[2 * j + h],
                                 f"{vreg(off)}, {{v}}, s[{T + 6}:{T + 7}] offset:{64 * cb}")
                 n += 1
+    assert 2 + sum(ln.strip().startswith("global_store") for ln in a.lines[n0:]) == EPI_STORES_ROWS
+    a(f"s_mov_b32 {s(S_EPI)}, 1")
     a.label(stored)
+
+
+# Partial outputs are written as fp16 with a power-of-two descale per (block,
+# column quarter, head): d = 2^(e - 15) for the largest |value| m of the quarter
+# (m in [2^(e-1), 2^e)), so that |value / d| < 2^15 stays inside fp16 and keeps
+# 11 significant bits; d is clamped to 2^-90 for rows that are (nearly) zero.
+F16_DESC_FIELD_MIN = 51    # clamp of the exponent field: scale <= 2^90
+
+
+def f16_scale(a, m, inv, t):
+    """m = this lane's largest |O| of a row (one column quarter), inv its 1/l:
+    inv <- inv * 2^k with (m inv) 2^k in [2^14, 2^15), m <- the descale 2^-k
+    (fp32 bits built from the exponent field of m inv)."""
+    a(f"v_mul_f32 {vreg(m)}, {vreg(m)}, {vreg(inv)}",
+      f"v_bfe_u32 {vreg(m)}, {vreg(m)}, 23, 8",
+      f"v_max_i32 {vreg(m)}, {F16_DESC_FIELD_MIN}, {vreg(m)}",
+      f"v_sub_u32 {vreg(t)}, 268, {vreg(m)}",
+      f"v_lshlrev_b32 {vreg(t)}, 23, {vreg(t)}",
+      f"v_mul_f32 {vreg(inv)}, {vreg(inv)}, {vreg(t)}",
+      f"v_subrev_u32 {vreg(m)}, 14, {vreg(m)}",
+      f"v_lshlrev_b32 {vreg(m)}, 23, {vreg(m)}")
+
+
+def lane_abs_max(a, dst, regs):
+    """dst = max |regs| (v_max3 chain)."""
+    a(f"v_max3_f32 {vreg(dst)}, |{vreg(regs[0])}|, |{vreg(regs[1])}|, |{vreg(regs[2])}|")
+    rest = regs[3:]
+    for k in range(0, len(rest), 2):
+        if k + 1 < len(rest):
+            a(f"v_max3_f32 {vreg(dst)}, {vreg(dst)}, |{vreg(rest[k])}|, |{vreg(rest[k + 1])}|")
+        else:
+            a(f"v_max_f32 {vreg(dst)}, {vreg(dst)}, |{vreg(rest[k])}|")
+
+
+def epi_partial_f16(a, inv):
+    """bf16 kernel: this wave's 128 columns (quarter w) of all 128 query rows,
+    normalised, as fp16 partials with their descales.  Owner group j holds
+    query rows 32j .. (row index s[T+12+j]); per j the 64 accumulator values of
+    each lane are read (and cleared for the next segment), the per-row largest
+    |value| taken over the wave's columns (the four lanes g of a row), the
+    descales stored, and the values scaled, packed and stored: chunk
+    (column block c = 8w + cb, lane) = 16 bytes at 1 KB c + 16 lane of the
+    group's 32 KB."""
+    T = S_TMP
+    vals = list(range(32, 96))           # (cb, a, i) at 32 + 8 cb + 4 a + i
+    off, offt, m0, m1, t, t0, t1 = 20, 21, 22, 23, 18, 16, 17
+    # table of descales after the num_splits * 2 * s_q value blocks of 128 KB
+    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_SQ)}",
+      f"s_lshr_b32 s{T + 7}, s{T + 8}, 14",
+      f"s_lshl_b32 s{T + 6}, s{T + 8}, 18",
+      f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 4}",
+      f"s_addc_u32 s{T + 7}, s{T + 7}, s{T + 5}",
+      f"s_lshl_b32 s{T + 8}, {s(S_WAVE)}, 13",          # 8 KB w: the wave's column blocks
+      f"s_lshl_b32 s{T + 9}, {s(S_WAVE)}, 9",           # 512 B w: the wave's quarter of the table
+      f"v_lshlrev_b32 {vreg(off)}, 4, {vreg(V_LANE)}",
+      f"v_lshlrev_b32 {vreg(offt)}, 3, {vreg(V_R16)}")
+    for j in range(4):
+        b = T + 12 + j
+        # values: out + 1024 row + 8 KB w; descales: table + 16 row - 12 (row & 127) + 512 w
+        a(f"s_lshl_b32 s{T + 16}, s{b}, 10",
+          f"s_lshr_b32 s{T + 17}, s{b}, 22",
+          f"s_add_u32 s{T + 16}, s{T + 16}, s{T + 8}",
+          f"s_addc_u32 s{T + 17}, s{T + 17}, 0",
+          f"s_add_u32 s{T + 16}, s{T + 16}, s{T + 4}",
+          f"s_addc_u32 s{T + 17}, s{T + 17}, s{T + 5}",
+          f"s_and_b32 s{T + 10}, s{b}, 127",
+          f"s_mul_i32 s{T + 10}, s{T + 10}, 12",
+          f"s_lshl_b32 s{T + 11}, s{b}, 4",
+          f"s_sub_u32 s{T + 11}, s{T + 11}, s{T + 10}",
+          f"s_add_u32 s{T + 11}, s{T + 11}, s{T + 9}",
+          f"s_add_u32 s{T + 18}, s{T + 6}, s{T + 11}",
+          f"s_addc_u32 s{T + 19}, s{T + 7}, 0")
+        for cb in range(8):
+            for h in range(2):
+                o = (8 * cb + 2 * j + h) * 4
+                for i in range(4):
+                    a(f"v_accvgpr_read_b32 {vreg(vals[8 * cb + 4 * h + i])}, a{o + i}")
+        for cb in range(8):
+            for h in range(2):
+                o = (8 * cb + 2 * j + h) * 4
+                for i in range(4):
+                    a(f"v_accvgpr_write_b32 a{o + i}, 0")
+        for h, m in ((0, m0), (1, m1)):
+            lane_abs_max(a, m, [vals[8 * cb + 4 * h + i] for cb in range(8) for i in range(4)])
+            xor_reduce(a, m, "v_max_f32", t0, t1)
+            f16_scale(a, m, inv[2 * j + h], t)
+        # descales of rows 32j + r16 (a = 0) and + 16 (a = 1), lanes g == 0
+        a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
+          f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
+          f"global_store_dwordx2 {vreg(offt)}, {vr(m0, 2)}, s[{T + 18}:{T + 19}] sc0 sc1",
+          f"s_mov_b64 exec, {sp(S_EXEC)}")
+        for cb in range(8):
+            for h in range(2):
+                for i in range(4):
+                    r = vals[8 * cb + 4 * h + i]
+                    a(f"v_mul_f32 {vreg(r)}, {vreg(r)}, {vreg(inv[2 * j + h])}")
+        for cb in range(8):
+            v0 = vals[8 * cb]
+            for k in range(4):
+                a(f"v_cvt_pk_f16_f32 {vreg(v0 + k)}, {vreg(v0 + 2 * k)}, {vreg(v0 + 2 * k + 1)}")
+            if cb == 4:
+                a(f"s_add_u32 s{T + 16}, s{T + 16}, 4096", f"s_addc_u32 s{T + 17}, s{T + 17}, 0")
+            a(f"global_store_dwordx4 {vreg(off)}, {vr(v0, 4)}, s[{T + 16}:{T + 17}] offset:{1024 * (cb % 4)} sc0 sc1")
 
 
 def epi_store_split(a, hb, cb, vv, inv, operands):
@@ -1646,8 +1796,9 @@ V_PVM = (V_PV0, 98, 99, 107)      # output-read lane offsets of the four 16-colu
 # steps leave alone; the epilogue does not, so a segment start recomputes them)
 N_PH, N_STEP, N_NVH, N_ROW0, N_MODE, N_DMALDS = 70, 72, 74, 75, 76, 77
 S_LKUP = 3                        # page to look up (the loader items' own; s3 holds nothing else)
-S_EPI = 50                        # 1: the segment follows an epilogue (its Q loads went out before
-                                  # the epilogue's 66 stores)
+S_EPI = 50                        # 1 / 2: the segment follows an epilogue of final rows / of a
+                                  # partial (its Q loads went out before that epilogue's stores)
+EPI_STORES_ROWS, EPI_STORES_PARTIAL = 66, 38
 # The cache rows are read once per launch: their direct-to-LDS loads are
 # nontemporal (streaming), which measured 2-5% faster than the default policy.
 ROW_LOAD_POLICY = " nt"
@@ -1961,13 +2112,18 @@ def step_hp(a):
       s_waitcnt_vm(9),
       f"s_branch {wdone}")
     a.label(w0)
-    # a segment's first step: Q and this step's rows.  After an epilogue at
-    # least 63 stores went out after the Q loads, so at most 63 may stay
-    # outstanding; else none
-    wz = a.new_label("wz")
+    # a segment's first step: Q and this step's rows.  After an epilogue, the
+    # stores that went out after the Q loads may stay outstanding (at most 63
+    # of the 66 of final rows, all 38 of a partial); else nothing
+    wz, wpart = a.new_label("wz"), a.new_label("wpart")
     a(f"s_cmp_eq_u32 {s(S_EPI)}, 0",
       f"s_cbranch_scc1 {wz}",
-      s_waitcnt_vm(63),
+      f"s_cmp_eq_u32 {s(S_EPI)}, 2",
+      f"s_cbranch_scc1 {wpart}",
+      s_waitcnt_vm(min(63, EPI_STORES_ROWS)),
+      f"s_branch {wdone}")
+    a.label(wpart)
+    a(s_waitcnt_vm(EPI_STORES_PARTIAL),
       f"s_branch {wdone}")
     a.label(wz)
     a(s_waitcnt_vm(0))
@@ -2076,8 +2232,7 @@ def kernel_tail_hp(a):
     # end of the segment: every wave past its output reads
     a(s_waitcnt_lgkm(0), "s_barrier")
     epilogue_split(a)
-    a(f"s_mov_b32 {s(S_EPI)}, 1",
-      f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
+    a(f"s_add_u32 {s(S_CPRE)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_add_u32 {s(S_CSEQ)}, {s(S_CSEQ)}, 1",
       f"s_cmp_lt_u32 {s(S_UCUR)}, {s(S_UB)}",
       "s_cbranch_scc1 .Lseg",

@@ -27,12 +27,13 @@ mla_status check_device() {
   return state == 1 ? MLA_OK : MLA_ERR_DEVICE;
 }
 
-mla_status check_common(int32_t batch, int32_t s_q, int32_t num_splits, const float* partial_out,
+mla_status check_common(int32_t batch, int32_t s_q, int32_t num_splits, const void* partial_out,
                         const float* partial_lse) {
   if (batch < 1 || s_q < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SHAPE;
   if ((num_splits & (num_splits - 1)) != 0) return MLA_ERR_SHAPE;  // partitions are cut with shifts
   if (s_q > 2) return MLA_ERR_UNSUPPORTED;
   if (num_splits > 1 && (partial_out == nullptr || partial_lse == nullptr)) return MLA_ERR_NULL;
+  if (num_splits > 1 && ((uintptr_t)partial_out & 15) != 0) return MLA_ERR_SHAPE;  // 16-byte stores
   // every output index must fit the kernels' size_t arithmetic with room to spare
   const double out_elems = (double)batch * s_q * MLA_NUM_HEADS * MLA_LATENT_DIM;
   if (out_elems > 9.0e15) return MLA_ERR_SHAPE;
@@ -45,7 +46,7 @@ extern "C" {
 
 mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_latent_cache* cache,
                       const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, float* partial_out,
+                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, void* partial_out,
                       float* partial_lse, float* out_latent, float* lse, hipStream_t stream) {
   if (!q_absorbed || !q_rope || !cache || !seq_lens || !out_latent || !lse) return MLA_ERR_NULL;
   if (!cache->rows) return MLA_ERR_NULL;
@@ -85,7 +86,7 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
-mla_status mla_combine(const float* partial_out, const float* partial_lse, const int32_t* seq_lens,
+mla_status mla_combine(const void* partial_out, const float* partial_lse, const int32_t* seq_lens,
                        int32_t batch, int32_t s_q, int32_t num_splits, float* out_latent, float* lse,
                        hipStream_t stream) {
   if (!seq_lens || !out_latent || !lse) return MLA_ERR_NULL;
@@ -125,7 +126,7 @@ int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t 
 
 size_t mla_partial_out_bytes(int32_t num_splits, int32_t s_q) {
   if (num_splits < 1 || s_q < 1) return 0;
-  return (size_t)num_splits * 2 * s_q * MLA_NUM_HEADS * MLA_LATENT_DIM * sizeof(float);
+  return (size_t)num_splits * 2 * s_q * (mla::kPartBlockBytes + mla::kPartDescBytes);
 }
 
 size_t mla_partial_lse_bytes(int32_t num_splits, int32_t s_q) {

@@ -5,15 +5,19 @@
 // rows.
 //
 // One workgroup merges one slice of the latent columns (16 CB of them, CB = 8,
-// 4 or 2 column blocks; the host picks the widest slice that still gives
-// the GPU enough workgroups) of one group of 32 heads of one (sequence, query
-// token).  Partials are stored in the decode kernel's lane order (see the
-// partial_out layout in include/mla.h): a slice is two contiguous runs of
-// CB KB (head halves a = 0, 1), so consecutive threads read consecutive
-// 16-byte chunks.  Partitions are taken in chunks whose loads are all issued
-// before any is used, each chunk merged into a running (max, sum, accumulator)
-// triple, so a sequence cut into few partitions costs one memory round trip.
-// The merged slice goes through LDS once to be written back in row order.
+// 4 or 2 column blocks; the host picks the widest slice that still gives the
+// GPU enough workgroups) of one group of 32 heads of one (sequence, query
+// token).  Partials are fp16 in the decode kernels' lane order with one
+// power-of-two descale per (block, column quarter, head) (the partial_out
+// layout in include/mla.h): a slice is one contiguous run of CB KB, 16-byte
+// chunks of two heads (r, r + 16) x four columns, so consecutive threads read
+// consecutive chunks.  Partitions are taken in chunks whose loads are all
+// issued before any is used, each chunk merged into a running (max, sum,
+// accumulator) triple per head, so a sequence cut into few partitions costs
+// one memory round trip.  The merged slice goes through LDS once to be
+// written back in row order.
+#include <hip/hip_fp16.h>
+
 #include "mla_internal.h"
 #include "mla_schedule.h"
 
@@ -23,18 +27,26 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kGroupHeads = 32;
 
-// LDS slot of lane-order chunk c: XOR the head bits with the column phase so
-// that both the lane-order writes and the row-order reads spread over all banks.
+// LDS slot of a (head half, column block, lane) float4 c: XOR the head bits with
+// the column phase so that both the lane-order writes and the row-order reads
+// spread over all banks.
 __device__ __forceinline__ int lds_slot(int c) { return c ^ ((((c >> 6) & 3) << 2) | ((c >> 4) & 3)); }
 
+__device__ __forceinline__ float4 half4(uint2 h) {
+  const __half2 a = *reinterpret_cast<const __half2*>(&h.x);
+  const __half2 b = *reinterpret_cast<const __half2*>(&h.y);
+  return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
+}
+
 template <int CB>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(CombineParams p) {
+  constexpr int kThreads = CB * 64 < 256 ? CB * 64 : 256;
   constexpr int kSlices = 32 / CB;
-  constexpr int kRun = 64 * CB;                // chunks per head half of a slice
-  constexpr int kPerThread = 2 * kRun / 256;   // 4, 2 or 1
-  constexpr int kChunk = 4;                    // partitions whose loads are in flight together
+  constexpr int kRun = 64 * CB;                 // 16-byte chunks of a slice
+  constexpr int kPerThread = kRun / kThreads;   // 2 or 1
+  constexpr int kChunk = 4;                     // partitions whose loads are in flight together
   __shared__ float4 s_tile[2 * kRun];
-  __shared__ int s_red[8];
+  __shared__ int s_red[2 * (kThreads / 64)];
   const int tid = threadIdx.x;
   const int per_tok = (kHeads / kGroupHeads) * kSlices;
   const int b = blockIdx.x / (p.s_q * per_tok);
@@ -44,7 +56,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
   // rebuild the partition map: total units U and the first unit u0 of sequence b
   int cnt = 0, before = 0;
-  for (int i = tid; i < p.batch; i += 256) {
+  for (int i = tid; i < p.batch; i += kThreads) {
     const int n = units_of_len(p.seq_lens[i]);
     cnt += n;
     if (i < b) before += n;
@@ -59,8 +71,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     s_red[2 * (tid >> 6) + 1] = before;
   }
   __syncthreads();
-  const int total_units = s_red[0] + s_red[2] + s_red[4] + s_red[6];
-  const int u0 = s_red[1] + s_red[3] + s_red[5] + s_red[7];
+  int total_units = 0, u0 = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    total_units += s_red[2 * w];
+    u0 += s_red[2 * w + 1];
+  }
   const int nb = units_of_len(p.seq_lens[b]);
   const int weight = total_units + p.batch * kSegWeight;
   // weighted positions of the sequence's first and last units
@@ -73,83 +89,105 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   // slot 1) iff that sequence's last unit lies at or past its start
   const int slot0 = (b > 0 && u0 - 1 + b * kSegWeight >= part_start(p0, weight, p.log2_parts)) ? 1 : 0;
 
-  // chunk k of this thread: slice-local index t + 256 k, head half a, lane-order offset in the group
-  int head[kPerThread], coff[kPerThread];
+  // chunk k of this thread: slice-local index tid + kThreads k = 64 cl + 16 g + r,
+  // heads grp * 32 + r and + 16, column quarter of the slice
+  const int quarter = (CB * slice) >> 3;
+  int cidx[kPerThread], r16[kPerThread];
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
-    const int lc = tid + 256 * k;
-    const int a = lc / kRun;
-    head[k] = grp * kGroupHeads + 16 * a + (tid & 15);
-    coff[k] = 2048 * a + kRun * slice + lc % kRun;
+    const int lc = tid + kThreads * k;
+    r16[k] = lc & 15;
+    cidx[k] = kRun * slice + lc;
   }
-  float m[kPerThread], wsum[kPerThread];
-  float4 acc[kPerThread];
+  const size_t nblocks = (size_t)p.num_parts * 2 * p.s_q;
+  const char* vals = static_cast<const char*>(p.part_out);
+  const float* desc = reinterpret_cast<const float*>(vals + nblocks * kPartBlockBytes);
+  float m[kPerThread][2], wsum[kPerThread][2];
+  float4 acc[kPerThread][2];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    m[k] = kNegInf;
-    wsum[k] = 0.f;
-    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int k = 0; k < kPerThread; ++k)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      m[k][a] = kNegInf;
+      wsum[k][a] = 0.f;
+      acc[k][a] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   // partitions in chunks of kChunk: all loads of a chunk go out before any is
   // used (one memory round trip per chunk), then the chunk is merged into the
   // running (m, wsum, acc) with a rescale when its largest lse is new
   for (int qb = p0; qb <= p1; qb += kChunk) {
-    float l[kChunk][kPerThread];
-    float4 v[kChunk][kPerThread];
+    float l[kChunk][kPerThread][2];
+    float2 d[kChunk][kPerThread];
+    uint4 v[kChunk][kPerThread];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const int q = qb + i;
       // a partition past the sequence or without units holds no share
       const bool live = q <= p1 && part_start(q, weight, p.log2_parts) != part_start(q + 1, weight, p.log2_parts);
-      const size_t row = ((size_t)(q * 2 + (q == p0 ? slot0 : 0)) * p.s_q + s) * kHeads;
-      const float4* src = (const float4*)(p.part_out + (row + grp * kGroupHeads) * kLatent);
+      const size_t blk = (size_t)(q * 2 + (q == p0 ? slot0 : 0)) * p.s_q + s;
+      const uint4* src = reinterpret_cast<const uint4*>(vals + blk * kPartBlockBytes) + grp * 2048;
+      const float2* dsc = reinterpret_cast<const float2*>(desc + blk * 512 + 128 * quarter + 32 * grp);
+      const float* lsrc = p.part_lse + blk * kHeads + grp * kGroupHeads;
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
-        l[i][k] = kNegInf;
-        v[i][k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        l[i][k][0] = l[i][k][1] = kNegInf;
+        d[i][k] = make_float2(0.f, 0.f);
+        v[i][k] = make_uint4(0, 0, 0, 0);
         if (live) {
-          l[i][k] = p.part_lse[row + head[k]];     // -inf: the share saw no row of this token
-          v[i][k] = src[coff[k]];
+          l[i][k][0] = lsrc[r16[k]];             // -inf: the share saw no row of this token
+          l[i][k][1] = lsrc[r16[k] + 16];
+          d[i][k] = dsc[r16[k]];
+          v[i][k] = src[cidx[k]];
         }
       }
     }
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      float mc = m[k];
+    for (int k = 0; k < kPerThread; ++k)
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) mc = fmaxf(mc, l[i][k]);
-      if (mc == kNegInf) continue;          // nothing seen yet
-      const float r = __expf(m[k] - mc);    // 0 while m is -inf
-      wsum[k] *= r;
-      acc[k].x *= r; acc[k].y *= r; acc[k].z *= r; acc[k].w *= r;
-      m[k] = mc;
+      for (int a = 0; a < 2; ++a) {
+        float mc = m[k][a];
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        const float w = __expf(l[i][k] - mc);   // 0 for -inf
-        wsum[k] += w;
-        acc[k].x += w * v[i][k].x; acc[k].y += w * v[i][k].y; acc[k].z += w * v[i][k].z; acc[k].w += w * v[i][k].w;
+        for (int i = 0; i < kChunk; ++i) mc = fmaxf(mc, l[i][k][a]);
+        if (mc == kNegInf) continue;          // nothing seen yet
+        const float r = __expf(m[k][a] - mc);  // 0 while m is -inf
+        wsum[k][a] *= r;
+        acc[k][a].x *= r; acc[k][a].y *= r; acc[k][a].z *= r; acc[k][a].w *= r;
+        m[k][a] = mc;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+          const float w = __expf(l[i][k][a] - mc);   // 0 for -inf
+          wsum[k][a] += w;
+          const float wd = w * (a ? d[i][k].y : d[i][k].x);
+          const float4 x = half4(a ? make_uint2(v[i][k].z, v[i][k].w) : make_uint2(v[i][k].x, v[i][k].y));
+          acc[k][a].x += wd * x.x; acc[k][a].y += wd * x.y; acc[k][a].z += wd * x.z; acc[k][a].w += wd * x.w;
+        }
       }
-    }
   }
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const float ik = wsum[k] > 0.f ? 1.f / wsum[k] : 0.f;
-    s_tile[lds_slot(tid + 256 * k)] = make_float4(acc[k].x * ik, acc[k].y * ik, acc[k].z * ik, acc[k].w * ik);
-  }
+  for (int k = 0; k < kPerThread; ++k)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float ik = wsum[k][a] > 0.f ? 1.f / wsum[k][a] : 0.f;
+      s_tile[lds_slot(kRun * a + tid + kThreads * k)] =
+          make_float4(acc[k][a].x * ik, acc[k][a].y * ik, acc[k][a].z * ik, acc[k][a].w * ik);
+    }
   const size_t orow = ((size_t)b * p.s_q + s) * kHeads + grp * kGroupHeads;
   if (slice == 0) {
-    // lse of the group's heads: the threads whose chunk k sits in column block 0, g == 0
+    // lse of the group's heads: the threads whose chunk sits in column block 0, g == 0
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-      const int lc = tid + 256 * k;
-      if ((lc % kRun) < 16) p.lse[head[k]  - grp * kGroupHeads + orow] = wsum[k] > 0.f ? m[k] + __logf(wsum[k]) : kNegInf;
+      const int lc = tid + kThreads * k;
+      if (lc < 16)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          p.lse[orow + 16 * a + r16[k]] = wsum[k][a] > 0.f ? m[k][a] + __logf(wsum[k][a]) : kNegInf;
     }
   }
   __syncthreads();
-  // row order: chunk e of the slice is head e / (4 CB), columns 16 CB slice + 4 (e % (4 CB)) .. +3
+  // row order: float4 e of the slice is head e / (4 CB), columns 16 CB slice + 4 (e % (4 CB)) .. +3
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int e = tid + 256 * k;
+  for (int k = 0; k < 2 * kPerThread; ++k) {
+    const int e = tid + kThreads * k;
     const int hl = e / (4 * CB), cc = e % (4 * CB);
     const int c = kRun * (hl >> 4) + 64 * (cc >> 2) + 16 * (cc & 3) + (hl & 15);
     float4* dst = (float4*)(p.out + (orow + hl) * kLatent + 16 * CB * slice) + cc;
@@ -169,7 +207,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   } else if (base * 8 >= want) {
     combine_kernel<4><<<dim3((unsigned)(base * 8)), dim3(256), 0, stream>>>(p);
   } else {
-    combine_kernel<2><<<dim3((unsigned)(base * 16)), dim3(256), 0, stream>>>(p);
+    combine_kernel<2><<<dim3((unsigned)(base * 16)), dim3(128), 0, stream>>>(p);
   }
   return hipGetLastError();
 }

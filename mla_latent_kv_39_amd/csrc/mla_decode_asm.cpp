@@ -18,7 +18,7 @@ struct AsmArgs {
   const void* rows;
   const void* table;
   const int32_t* seq_lens;
-  float* part_out;
+  void* part_out;
   float* part_lse;
   float* out;
   float* lse;

@@ -11,6 +11,10 @@ constexpr int kRope = 64;
 constexpr int kRow = 576;
 constexpr int kPage = 64;          // rows per cache page = rows per work unit
 constexpr int kRowBytesBf16 = kRow * 2;  // 1152
+// A partial block (split, slot, query token): 128 x 512 fp16 values; after all
+// blocks, 4 x 128 fp32 descales per block (column quarter, head).
+constexpr size_t kPartBlockBytes = (size_t)kHeads * kLatent * 2;
+constexpr size_t kPartDescBytes = (size_t)4 * kHeads * 4;
 
 // Everything one decode launch needs; all pointers are device pointers.
 struct DecodeParams {
@@ -21,7 +25,7 @@ struct DecodeParams {
   const __bf16* fp8_rope;    // [NB, 64, 64]
   const int32_t* block_table;  // [B, max_blocks] or nullptr (contiguous)
   const int32_t* seq_lens;   // [B]
-  float* part_out;           // [P, 2, S_q, 128, 512]
+  void* part_out;            // P * 2 * S_q blocks of 128 x 512 fp16, then their descales
   float* part_lse;           // [P, 2, S_q, 128]
   float* out;                // [B, S_q, 128, 512]
   float* lse;                // [B, S_q, 128]
@@ -32,7 +36,7 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-  const float* part_out;
+  const void* part_out;
   const float* part_lse;
   const int32_t* seq_lens;
   float* out;

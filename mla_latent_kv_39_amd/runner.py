@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import torch
 
-from .binding import LATENT_DIM, NUM_HEADS, mla_combine, mla_decode
+from .binding import LATENT_DIM, NUM_HEADS, mla_combine, mla_decode, mla_partial_out_bytes
 
 
 class DecodeWorkspace:
@@ -19,7 +19,9 @@ class DecodeWorkspace:
         self.out = torch.empty((batch, s_q, NUM_HEADS, LATENT_DIM), dtype=f32, device=device)
         self.lse = torch.empty((batch, s_q, NUM_HEADS), dtype=f32, device=device)
         if num_splits > 1:
-            self.partial_out = torch.empty((num_splits, 2, s_q, NUM_HEADS * LATENT_DIM), dtype=f32, device=device)
+            # fp16 partial blocks and their descales (layout in include/mla.h)
+            self.partial_out = torch.empty((mla_partial_out_bytes(num_splits, s_q),), dtype=torch.uint8,
+                                           device=device)
             self.partial_lse = torch.empty((num_splits, 2, s_q, NUM_HEADS), dtype=f32, device=device)
         else:
             self.partial_out = self.partial_lse = None

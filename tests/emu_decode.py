@@ -14,21 +14,13 @@ import sys
 import numpy as np
 
 import gcn_emu as E
+from partial_format import partial_bytes, unpack
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.join(HERE, "..", "mla_latent_kv_39_amd", "csrc"))
 import gen_decode_gfx950 as G  # noqa: E402
 
 N_HEADS, D_C = 128, 512
-
-
-def unpack_partial(flat, s_q):
-    """partial_out [splits, 2, s_q, 128 * 512] in the library's lane order ->
-    [splits, 2, s_q, 128, 512]: the value of head 32j + 16a + r, column
-    16c + 4g + i sits at 16384 j + 4 (64 (32a + c) + 16g + r) + i."""
-    n = flat.shape[0]
-    v = flat.reshape(n, 2, s_q, 4, 2, 32, 4, 16, 4)                # j, a, c, g, r, i
-    return v.transpose(0, 1, 2, 3, 4, 7, 5, 6, 8).reshape(n, 2, s_q, N_HEADS, D_C)
 
 
 def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
@@ -47,7 +39,7 @@ def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
     rows = mem.add(inp.cache.contiguous().view(torch.uint8).numpy())
     table = 0 if inp.block_table is None else mem.add(inp.block_table.numpy().astype(np.int32))
     lens = mem.add(inp.seq_lens.numpy().astype(np.int32))
-    pout = mem.add(np.full(num_splits * 2 * S * N_HEADS * D_C, np.nan, np.float32))
+    pout = mem.add(np.full(partial_bytes(num_splits, S), 0xFF, np.uint8))      # NaN until written
     plse = mem.add(np.full(num_splits * 2 * S * N_HEADS, np.nan, np.float32))
     out = mem.add(np.full(B * S * N_HEADS * D_C, np.nan, np.float32))
     lse = mem.add(np.full(B * S * N_HEADS, np.nan, np.float32))
@@ -64,7 +56,7 @@ def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
     E.run_kernel(text, kname, lds, mem, karg, num_splits * (N_HEADS // hpb), seed=seed, hook=hook)
     f = lambda base, shape: mem.buffer(base).view(np.float32).reshape(shape).astype(np.float64)
     return (f(out, (B, S, N_HEADS, D_C)), f(lse, (B, S, N_HEADS)),
-            unpack_partial(mem.buffer(pout).view(np.float32).reshape(num_splits, 2, S, N_HEADS * D_C), S).astype(np.float64),
+            unpack(mem.buffer(pout), num_splits, S),
             f(plse, (num_splits, 2, S, N_HEADS)))
 
 

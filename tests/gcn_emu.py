@@ -96,10 +96,10 @@ _REG = re.compile(r"^(-?)([sva])(\d+)$|^(-?)([sva])\[(\d+):(\d+)\]$")
 
 
 class Opd:
-    __slots__ = ("kind", "idx", "n", "neg", "val")
+    __slots__ = ("kind", "idx", "n", "neg", "val", "abs")
 
-    def __init__(self, kind, idx=0, n=1, neg=False, val=0):
-        self.kind, self.idx, self.n, self.neg, self.val = kind, idx, n, neg, val
+    def __init__(self, kind, idx=0, n=1, neg=False, val=0, abs_=False):
+        self.kind, self.idx, self.n, self.neg, self.val, self.abs = kind, idx, n, neg, val, abs_
 
 
 def _float_bits(x):
@@ -107,6 +107,10 @@ def _float_bits(x):
 
 
 def parse_operand(tok):
+    if len(tok) > 2 and tok[0] == "|" and tok[-1] == "|":     # |x|: absolute value (VOP3 float source)
+        o = parse_operand(tok[1:-1])
+        o.abs = True
+        return o
     m = _REG.match(tok)
     if m:
         if m.group(2):
@@ -234,6 +238,7 @@ class Wave:
         self.state = "run"
         self.steps = 0
         self._em_bits, self._em = None, None
+        self.store_data = None     # VGPRs a store of more than 64 bits read in the instruction before
 
     # --- scalar operands
     def sget(self, o, width=32):
@@ -287,6 +292,8 @@ class Wave:
 
     def fget(self, o, k=0):
         x = f32(self.vget(o, k)).copy()
+        if o.abs:
+            x = np.abs(x)
         return -x if o.neg else x
 
     def execmask(self):
@@ -379,6 +386,19 @@ class Workgroup:
             fn = OPS.get(ins.op)
             if fn is None:
                 raise Fault(f"instruction not emulated: {ins.text}")
+            # GCN store-data hazard: a VALU write of a VGPR that the previous
+            # instruction, a store of more than 64 bits, reads as data needs one
+            # wait state in between (the store may otherwise send the new value)
+            if w.store_data is not None and ins.op.startswith("v_") and ins.args and ins.args[0].kind == "v":
+                d = ins.args[0]
+                lo, hi = w.store_data
+                if d.idx <= hi and d.idx + d.n - 1 >= lo:
+                    raise Fault(f"wave {w.wid} pc {w.pc - 1} '{ins.text}': writes v{d.idx} right after a store "
+                                f"reading v[{lo}:{hi}] (store-data hazard)")
+            w.store_data = None
+            if ins.op.startswith(("global_store", "buffer_store")) and len(ins.args) > 1 and ins.args[1].kind == "v" \
+                    and ins.args[1].n > 2:
+                w.store_data = (ins.args[1].idx, ins.args[1].idx + ins.args[1].n - 1)
             try:
                 fn(self, w, ins)
             except Fault as e:
@@ -637,13 +657,15 @@ def _vmov(g, w, i):
 
 
 @op("v_add_u32", "v_sub_u32", "v_and_b32", "v_or_b32", "v_xor_b32", "v_lshlrev_b32", "v_lshrrev_b32",
-    "v_ashrrev_i32", "v_max_i32", "v_min_i32", "v_min_u32", "v_mul_u32_u24")
+    "v_ashrrev_i32", "v_max_i32", "v_min_i32", "v_min_u32", "v_mul_u32_u24", "v_subrev_u32")
 def _vint2(g, w, i):
     a, b = _vu(w, i, 1), _vu(w, i, 2)
     if i.op == "v_add_u32":
         r = a + b
     elif i.op == "v_sub_u32":
         r = a - b
+    elif i.op == "v_subrev_u32":
+        r = b - a
     elif i.op == "v_and_b32":
         r = a & b
     elif i.op == "v_or_b32":
@@ -781,6 +803,15 @@ def _vtrans(g, w, i):
             r = 1.0 / a.astype(np.float64)
         r = r.astype(np.float32)
     _fset(w, i, r)
+
+
+@op("v_cvt_pk_f16_f32")
+def _vcvtpkf16(g, w, i):
+    """Two fp32 -> two fp16 (round to nearest even, IEEE overflow to inf), packed."""
+    with np.errstate(all="ignore"):
+        lo = w.fget(i.args[1]).astype(np.float16).view(np.uint16).astype(np.uint32)
+        hi = w.fget(i.args[2]).astype(np.float16).view(np.uint16).astype(np.uint32)
+    w.vset(i.args[0], (lo | (hi << 16)).astype(np.uint32))
 
 
 @op("v_cvt_pk_bf16_f32")

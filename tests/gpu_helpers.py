@@ -49,9 +49,9 @@ def compare(out, lse, ref_out, ref_lse, what="", out_tol=OUT_TOL):
 
 def pack_partial_out(po):
     """[splits, 2, s_q, 128, 512] partials in head/column order -> the library's
-    partial_out layout [splits, 2, s_q, 128 * 512]: per group of 32 heads, the
-    value of head 32j + 16a + r and column 16c + 4g + i at 16384 j + 4 (64 (32a + c) + 16g + r) + i."""
-    n, k, s = po.shape[:3]
-    v = po.reshape(n, k, s, 4, 2, 16, 32, 4, 4)          # j, a, r, c, g, i
-    return v.permute(0, 1, 2, 3, 4, 6, 7, 5, 8).contiguous().reshape(n, k, s, 128 * 512)   # j, a, c, g, r, i
+    partial_out bytes (fp16 values in lane order and their descales, the layout
+    of include/mla.h) as a uint8 tensor."""
+    import torch
+    from partial_format import pack
+    return torch.from_numpy(pack(po.double().numpy() if hasattr(po, "double") else po))
 

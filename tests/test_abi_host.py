@@ -34,7 +34,8 @@ def test_status_strings_and_version(lib):
         assert isinstance(lib.status_string(code), str) and lib.status_string(code)
     assert lib.status_string(99) == "unknown status"
     assert lib.mla_version() >= 100
-    assert lib.mla_partial_out_bytes(3, 2) == 3 * 2 * 2 * 128 * 512 * 4
+    # fp16 values (128 KB) and 512 fp32 descales per (split, slot, token) block
+    assert lib.mla_partial_out_bytes(3, 2) == 3 * 2 * 2 * (128 * 512 * 2 + 4 * 128 * 4)
     assert lib.mla_partial_lse_bytes(3, 1) == 3 * 2 * 128 * 4
     assert lib.mla_partial_out_bytes(0, 1) == 0
 
@@ -103,12 +104,12 @@ def test_binding_checks_combine_buffers_before_the_library(lib):
     out = torch.zeros((2, 1, 128, 512), dtype=torch.float32)
     lse = torch.zeros((2, 1, 128), dtype=torch.float32)
     lens = torch.zeros((2,), dtype=torch.int32)
-    po = torch.zeros((4, 2, 1, 128 * 512), dtype=torch.float32)
+    po = torch.zeros((lib.mla_partial_out_bytes(4, 1),), dtype=torch.uint8)
     pl = torch.zeros((4, 2, 1, 128), dtype=torch.float32)
     with pytest.raises(ValueError, match="partial_out must have shape"):
-        lib.mla_combine(po[:, :, :, :100], pl, lens, 4, out, lse)
+        lib.mla_combine(po[:100], pl, lens, 4, out, lse)
     with pytest.raises(TypeError, match="partial_out must be"):
-        lib.mla_combine(po.double(), pl, lens, 4, out, lse)
+        lib.mla_combine(po.float(), pl, lens, 4, out, lse)
     with pytest.raises(ValueError, match="partial_out must be a device tensor"):
         lib.mla_combine(po, pl, lens, 4, out, lse)        # host tensors never reach the library
     with pytest.raises(ValueError, match="seq_lens must have shape"):

@@ -30,7 +30,14 @@ def _check(inp, splits, what, out_tol=None):
 
 @pytest.mark.parametrize("splits", [1, 4, 16])
 def test_fp8_paged_ragged(splits):
-    _check(_fp8([1, 63, 64, 65, 130, 700, 257], seed=21), splits, f"fp8 ragged splits={splits}")
+    # head 102 of the 130-row sequence puts most of its weight on one row whose
+    # |c| is 2.8: the bf16 rounding of P * scale alone moves out by ~1e-2 there
+    # (the CPU emulation of the kernel gives the same 0.0106), so the bound
+    # derived from the arithmetic applies where it exceeds 1e-2
+    from gpu_helpers import OUT_TOL
+    from partial_format import concentrated_bound
+    inp = _fp8([1, 63, 64, 65, 130, 700, 257], seed=21)
+    _check(inp, splits, f"fp8 ragged splits={splits}", out_tol=max(OUT_TOL, concentrated_bound(inp, O)))
 
 
 @pytest.mark.parametrize("splits", [1, 8])
@@ -74,6 +81,6 @@ def test_fp8_large_spread_restart_path(factor):
         for j in (L - 5, L // 2):
             page = int(inp.block_table[b, j // 64])
             inp.cache_rope[page, j % 64] = (inp.q_rope[b, 0, 0].float() * factor).to(torch.bfloat16)
-    cmax = max(float(np.abs(O.sequence_rows(inp, b, int(inp.seq_lens[b]))[:, :512]).max()) for b in range(2))
+    from partial_format import concentrated_bound
     for splits in (1, 4):
-        _check(inp, splits, f"fp8 large spread x{factor:g} splits={splits}", out_tol=2.0 ** -8 * cmax)
+        _check(inp, splits, f"fp8 large spread x{factor:g} splits={splits}", out_tol=concentrated_bound(inp, O))

@@ -17,6 +17,7 @@ from mla_inputs import make_inputs
 from oracle import mla_oracle as O
 
 import emu_decode as ED
+from partial_format import concentrated_bound
 
 OUT_TOL, LSE_TOL = 1e-2, 1e-3
 
@@ -59,8 +60,7 @@ def test_bf16_restart_path():
     for j in (150, 295):
         page = int(inp.block_table[0, j // 64])
         inp.cache[page, j % 64, 512:] = (inp.q_rope[0, 0, 0].float() * 48.0).to(torch.bfloat16)
-    cmax = float(np.abs(O.sequence_rows(inp, 0, 300)[:, :512]).max())
-    _check(inp, 1, out_tol=2.0 ** -8 * cmax)
+    _check(inp, 1, out_tol=concentrated_bound(inp, O))
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
@@ -114,8 +114,7 @@ def test_fp8_restart_path():
     for j in (150, 295):
         page = int(inp.block_table[0, j // 64])
         inp.cache_rope[page, j % 64] = (inp.q_rope[0, 0, 0].float() * 48.0).to(torch.bfloat16)
-    cmax = float(np.abs(O.sequence_rows(inp, 0, 300)[:, :512]).max())
-    _check(inp, 1, out_tol=2.0 ** -8 * cmax)
+    _check(inp, 1, out_tol=concentrated_bound(inp, O))
 
 
 def test_fp8_empty_sequences_and_nan_tails():
@@ -125,9 +124,7 @@ def test_fp8_empty_sequences_and_nan_tails():
     # rounding of P * scale (relative 2^-8) then bounds the output error by
     # 2^-8 max|c| rather than 1e-2 (the kernel's 0.0123 is exactly what that
     # rounding gives in numpy)
-    cmax = max(float(np.abs(O.sequence_rows(inp, b, int(inp.seq_lens[b]))[:, :512]).max())
-               for b in range(inp.batch) if int(inp.seq_lens[b]) > 0)
-    tol = max(OUT_TOL, 2.0 ** -8 * cmax)
+    tol = max(OUT_TOL, concentrated_bound(inp, O))
     for b in range(inp.batch):
         L = int(inp.seq_lens[b])
         if L % 64:
@@ -137,3 +134,25 @@ def test_fp8_empty_sequences_and_nan_tails():
             inp.cache_rope[page, L % 64:, :] = float("nan")
     for splits in (1, 4):
         _check(inp, splits, out_tol=tol, ref=ref)
+
+
+def test_emulator_flags_the_store_data_hazard():
+    """A VALU write of a register that the instruction before, a 16-byte
+    store, sends as data must fault in the emulator (the hardware needs a wait
+    state there); with one instruction in between it must not."""
+    import gcn_emu as E
+
+    def run(body):
+        text = "k:\n" + "\n".join("\t" + ln for ln in [
+            "s_load_dwordx2 s[4:5], s[0:1], 0x0", "s_waitcnt lgkmcnt(0)",
+            "v_lshlrev_b32 v1, 4, v0", "v_mov_b32 v4, 1", "v_mov_b32 v5, 2", "v_mov_b32 v6, 3",
+            "v_mov_b32 v7, 4", "global_store_dwordx4 v1, v[4:7], s[4:5]"] + body + ["s_waitcnt vmcnt(0)", "s_endpgm"])
+        mem = E.Memory()
+        buf = mem.add(np.zeros(64 * 16 * 4, np.uint8))
+        E.run_kernel(text, "k", 0, mem, np.array([buf], np.uint64).tobytes(), 1)
+        return mem.buffer(buf).view(np.uint32)
+
+    with pytest.raises(E.Fault, match="store-data hazard"):
+        run(["v_mov_b32 v5, 9"])
+    out = run(["s_nop 0", "v_mov_b32 v5, 9"])
+    assert list(out[:4]) == [1, 2, 3, 4]

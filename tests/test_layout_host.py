@@ -1,28 +1,51 @@
-"""Host-side checks of the partial_out layout helper the GPU tests use to feed
-mla_combine: it must place each value where include/mla.h says."""
+"""Host-side checks of the partial_out format helpers the tests use to feed
+mla_combine and to read the emulated kernels' partials: values and descales
+must sit where include/mla.h says, and the round trip keeps 11 bits."""
 import numpy as np
 import torch
 
 from gpu_helpers import pack_partial_out
+from partial_format import BLOCK_BYTES, partial_bytes, unpack
+
+
+def _partials(seed, shape=(2, 2, 2)):
+    rng = np.random.default_rng(seed)
+    po = rng.standard_normal(shape + (128, 512)) * np.exp(3 * rng.standard_normal(shape + (128, 1)))
+    po[0, 0, 0, 7] = 0.0                       # a row that saw nothing
+    po[0, 1, 0, 9, :128] *= 1e-30              # a quarter far below the others
+    return po
 
 
 def test_pack_partial_out_matches_documented_offsets():
     rng = np.random.default_rng(3)
-    po = torch.from_numpy(rng.standard_normal((2, 2, 2, 128, 512)).astype(np.float32))
-    packed = pack_partial_out(po)
-    assert packed.shape == (2, 2, 2, 128 * 512)
-    for _ in range(2000):
-        n, k, s = (int(x) for x in rng.integers(0, 2, 3))
+    po = _partials(3)
+    packed = pack_partial_out(torch.from_numpy(po)).numpy()
+    assert packed.dtype == np.uint8 and packed.size == partial_bytes(2, 2)
+    nb = 8
+    vals = packed[:nb * BLOCK_BYTES].view(np.float16)
+    desc = packed[nb * BLOCK_BYTES:].view(np.float32)
+    flat = po.reshape(nb, 128, 512)
+    for _ in range(3000):
+        blk = int(rng.integers(nb))
         j, a, r = int(rng.integers(4)), int(rng.integers(2)), int(rng.integers(16))
         c, g, i = int(rng.integers(32)), int(rng.integers(4)), int(rng.integers(4))
-        off = 16384 * j + 4 * (64 * (32 * a + c) + 16 * g + r) + i
-        assert packed[n, k, s, off] == po[n, k, s, 32 * j + 16 * a + r, 16 * c + 4 * g + i]
+        head, col, q = 32 * j + 16 * a + r, 16 * c + 4 * g + i, c // 8
+        d = float(desc[512 * blk + 128 * q + 32 * j + 2 * r + a])
+        x = float(vals[65536 * blk + 16384 * j + 8 * (64 * c + 16 * g + r) + 4 * a + i]) * d
+        m = np.abs(flat[blk, head, 128 * q:128 * q + 128]).max()
+        assert d == 2.0 ** np.round(np.log2(d))                          # a power of two
+        # largest |value| in [2^14, 2^15) d, d no smaller than 2^-90 (rows of (nearly) zeros)
+        assert (2.0 ** 14 <= m / d < 2.0 ** 15) if m >= 2.0 ** -76 else (d == 2.0 ** -90)
+        assert abs(x - flat[blk, head, col]) <= 2.0 ** -11 * m
 
 
-def test_pack_partial_out_is_a_permutation():
-    po = torch.arange(128 * 512, dtype=torch.float32).reshape(1, 1, 1, 128, 512)
-    packed = pack_partial_out(po).flatten()
-    assert torch.equal(torch.sort(packed).values, po.flatten())
+def test_partial_round_trip_keeps_eleven_bits():
+    po = _partials(4)
+    back = unpack(pack_partial_out(torch.from_numpy(po)).numpy(), 2, 2)
+    m = np.abs(po).reshape(2, 2, 2, 128, 4, 128).max(axis=5, keepdims=True)
+    err = np.abs(back - po).reshape(2, 2, 2, 128, 4, 128)
+    assert np.all(err <= 2.0 ** -11 * m)
+    assert np.all(back[0, 0, 0, 7] == 0)
 
 
 # ------------------------------------------------------- partition map
