@@ -113,10 +113,11 @@ def _combine_lens(n):
 
 
 # (lens, s_q, partitions): the third cuts one sequence into about thirty
-# shares; the last two give the launcher enough workgroups to pick its wider
-# column slices (4 and 8 column blocks)
+# shares; the fourth averages 16 partitions or more per sequence, so the
+# launcher merges 16 partitions per round trip; the last two give it enough
+# workgroups to pick its wider column slices (4 and 8 column blocks)
 @pytest.mark.parametrize("lens,s_q,splits", [([1, 64, 65, 300, 129], 1, 8), ([1, 64, 65, 300, 129], 2, 8),
-                                             ([3, 2000, 70], 1, 32),
+                                             ([3, 2000, 70], 1, 32), ([3, 2000, 70], 2, 64),
                                              (_combine_lens(32), 2, 32), (_combine_lens(64), 2, 64)])
 def test_combine_kernel_on_oracle_partials(lens, s_q, splits):
     """mla_combine alone, fed partials the oracle computed over the partition map."""
