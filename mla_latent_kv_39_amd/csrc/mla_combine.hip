@@ -11,11 +11,11 @@
 // power-of-two descale per (block, column quarter, head) (the partial_out
 // layout in include/mla.h): a slice is one contiguous run of CB KB, 16-byte
 // chunks of two heads (r, r + 16) x four columns, so consecutive threads read
-// consecutive chunks.  Partitions are taken in chunks whose loads are all
-// issued before any is used, each chunk merged into a running (max, sum,
-// accumulator) triple per head, so a sequence cut into few partitions costs
-// one memory round trip.  The merged slice goes through LDS once to be
-// written back in row order.
+// consecutive chunks.  Partitions are taken in chunks (4, or 8-16 when
+// sequences are cut into many) whose loads are all issued before any is
+// used, each chunk merged into a running (max, sum, accumulator) triple per
+// head, so a sequence cut into few partitions costs one memory round trip.
+// The merged slice goes through LDS once to be written back in row order.
 #include <hip/hip_fp16.h>
 
 #include "mla_internal.h"
@@ -38,13 +38,13 @@ __device__ __forceinline__ float4 half4(uint2 h) {
   return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
 }
 
-template <int CB>
+template <int CB, int KC>
 __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(CombineParams p) {
   constexpr int kThreads = CB * 64 < 256 ? CB * 64 : 256;
   constexpr int kSlices = 32 / CB;
   constexpr int kRun = 64 * CB;                 // 16-byte chunks of a slice
   constexpr int kPerThread = kRun / kThreads;   // 2 or 1
-  constexpr int kChunk = 4;                     // partitions whose loads are in flight together
+  constexpr int kChunk = KC;                    // partitions whose loads are in flight together
   __shared__ float4 s_tile[2 * kRun];
   __shared__ int s_red[2 * (kThreads / 64)];
   const int tid = threadIdx.x;
@@ -197,17 +197,31 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  // widest column slice that still gives about eight workgroups per compute
-  // unit: the shares of short and long sequences then mix on every unit
-  const long long base = (long long)p.batch * p.s_q * (kHeads / kGroupHeads);
+template <int KC4, int KC8>
+void launch_slices(const CombineParams& p, long long base, hipStream_t stream) {
   const long long want = 2048;
   if (base * 4 >= want) {
-    combine_kernel<8><<<dim3((unsigned)(base * 4)), dim3(256), 0, stream>>>(p);
+    combine_kernel<8, KC8><<<dim3((unsigned)(base * 4)), dim3(256), 0, stream>>>(p);
   } else if (base * 8 >= want) {
-    combine_kernel<4><<<dim3((unsigned)(base * 8)), dim3(256), 0, stream>>>(p);
+    combine_kernel<4, KC4><<<dim3((unsigned)(base * 8)), dim3(256), 0, stream>>>(p);
   } else {
-    combine_kernel<2><<<dim3((unsigned)(base * 16)), dim3(128), 0, stream>>>(p);
+    combine_kernel<2, KC4><<<dim3((unsigned)(base * 16)), dim3(128), 0, stream>>>(p);
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+  // widest column slice that still gives about eight workgroups per compute
+  // unit: the shares of short and long sequences then mix on every unit.
+  // Partitions merged per memory round trip: 4, or, when sequences average
+  // 16 partitions or more (a few long sequences), 16 (8 with two chunks a
+  // thread).  Measured with rocprofv3: 17.2 -> 14.5 us on 4 x 128k rows; on
+  // 32 x 1k-4k and the paged mix the wider chunk would cost 18% and 52%
+  // (fewer resident waves, merges of partitions that are not there).
+  const long long base = (long long)p.batch * p.s_q * (kHeads / kGroupHeads);
+  if ((long long)p.num_parts >= 16LL * p.batch) {
+    launch_slices<16, 8>(p, base, stream);
+  } else {
+    launch_slices<4, 4>(p, base, stream);
   }
   return hipGetLastError();
 }
