@@ -239,6 +239,7 @@ class Wave:
         self.steps = 0
         self._em_bits, self._em = None, None
         self.store_data = None     # VGPRs a store of more than 64 bits read in the instruction before
+        self.hist = deque(maxlen=6)  # (wait states it provides, VALU SGPR writes, VALU VGPR writes, M0 write, trans)
 
     # --- scalar operands
     def sget(self, o, width=32):
@@ -340,6 +341,65 @@ def _mask_to_bits(mask):
     return int.from_bytes(np.packbits(np.asarray(mask, bool), bitorder="little").tobytes(), "little")
 
 
+_TRANS = ("v_exp_f32", "v_log_f32", "v_rcp_f32", "v_rsq_f32", "v_sqrt_f32", "v_sin_f32", "v_cos_f32")
+
+
+def _regs(o):
+    return set(range(o.idx, o.idx + o.n))
+
+
+def check_wait_states(w, ins):
+    """Wait states the hardware does not insert (software must, with s_nop or
+    independent instructions; s_nop k gives k + 1):
+      a VALU write of an SGPR read by a memory instruction as its address: 5;
+      an SALU write of M0 read by a direct-to-LDS load as its LDS address: 1;
+      a VALU write of a VGPR read by a DPP instruction: 2;
+      a transcendental VALU result read by the next VALU: 1.
+    Raises Fault on a violation, then records the instruction."""
+    op = ins.op
+    def since(pred, limit):
+        ws = 0
+        for rec in reversed(w.hist):
+            if ws >= limit:
+                return False
+            if pred(rec):
+                return True
+            ws += rec[0]
+        return False
+    if op.startswith(("global_", "buffer_")):
+        for o in ins.args:
+            if o.kind == "s":
+                r = _regs(o)
+                if since(lambda rec: rec[1] & r, 5):
+                    raise Fault(f"s{o.idx} written by a VALU fewer than 5 wait states before its use as an address")
+        if "_lds_" in op and since(lambda rec: rec[3], 1):
+            raise Fault("M0 written by the instruction right before a direct-to-LDS load")
+    if op.startswith("v_"):
+        srcs = set()
+        for o in ins.args[1:]:
+            if o.kind == "v":
+                srcs |= _regs(o)
+        if op.endswith("_dpp") and since(lambda rec: rec[2] & srcs, 2):
+            raise Fault("VGPR written by a VALU fewer than 2 wait states before a DPP read")
+        if not op.startswith(_TRANS) and since(lambda rec: rec[4] and rec[2] & srcs, 1):
+            raise Fault("transcendental result read by the next VALU (1 wait state needed)")
+    # record
+    nop = int(ins.args[0].val) + 1 if op == "s_nop" else 1
+    sw, vw, m0, trans = set(), set(), False, False
+    if op.startswith("v_") and ins.args:
+        d = ins.args[0]
+        if d.kind == "s":
+            sw = _regs(d)
+        elif d.kind == "vcc":
+            sw = {106, 107}
+        elif d.kind == "v":
+            vw = _regs(d)
+        trans = op.startswith(_TRANS)
+    elif op.startswith("s_") and ins.args and ins.args[0].kind == "m0":
+        m0 = True
+    w.hist.append((nop, sw, vw, m0, trans))
+
+
 class Workgroup:
     def __init__(self, prog, mem, lds_bytes, wg_id, kernarg, nwaves=4, seed=0, max_steps=5_000_000, hook=None):
         self.prog, self.mem, self.hook = prog, mem, hook
@@ -399,6 +459,7 @@ class Workgroup:
             if ins.op.startswith(("global_store", "buffer_store")) and len(ins.args) > 1 and ins.args[1].kind == "v" \
                     and ins.args[1].n > 2:
                 w.store_data = (ins.args[1].idx, ins.args[1].idx + ins.args[1].n - 1)
+            check_wait_states(w, ins)
             try:
                 fn(self, w, ins)
             except Fault as e:

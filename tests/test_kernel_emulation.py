@@ -136,23 +136,40 @@ def test_fp8_empty_sequences_and_nan_tails():
         _check(inp, splits, out_tol=tol, ref=ref)
 
 
-def test_emulator_flags_the_store_data_hazard():
-    """A VALU write of a register that the instruction before, a 16-byte
-    store, sends as data must fault in the emulator (the hardware needs a wait
-    state there); with one instruction in between it must not."""
+def _run_tiny(body, lds=0):
+    """A one-wave kernel: s[4:5] = a 4 KB buffer, v1 = 16 lane, v4..v7 = 1..4,
+    then `body`."""
     import gcn_emu as E
+    text = "k:\n" + "\n".join("\t" + ln for ln in [
+        "s_load_dwordx2 s[4:5], s[0:1], 0x0", "s_waitcnt lgkmcnt(0)",
+        "v_lshlrev_b32 v1, 4, v0", "v_mov_b32 v4, 1", "v_mov_b32 v5, 2", "v_mov_b32 v6, 3",
+        "v_mov_b32 v7, 4", "s_nop 4"] + body + ["s_waitcnt vmcnt(0)", "s_endpgm"])
+    mem = E.Memory()
+    buf = mem.add(np.zeros(64 * 16 * 4, np.uint8))
+    E.run_kernel(text, "k", lds, mem, np.array([buf], np.uint64).tobytes(), 1, nwaves=1)
+    return mem.buffer(buf).view(np.uint32)
 
-    def run(body):
-        text = "k:\n" + "\n".join("\t" + ln for ln in [
-            "s_load_dwordx2 s[4:5], s[0:1], 0x0", "s_waitcnt lgkmcnt(0)",
-            "v_lshlrev_b32 v1, 4, v0", "v_mov_b32 v4, 1", "v_mov_b32 v5, 2", "v_mov_b32 v6, 3",
-            "v_mov_b32 v7, 4", "global_store_dwordx4 v1, v[4:7], s[4:5]"] + body + ["s_waitcnt vmcnt(0)", "s_endpgm"])
-        mem = E.Memory()
-        buf = mem.add(np.zeros(64 * 16 * 4, np.uint8))
-        E.run_kernel(text, "k", 0, mem, np.array([buf], np.uint64).tobytes(), 1)
-        return mem.buffer(buf).view(np.uint32)
 
-    with pytest.raises(E.Fault, match="store-data hazard"):
-        run(["v_mov_b32 v5, 9"])
-    out = run(["s_nop 0", "v_mov_b32 v5, 9"])
-    assert list(out[:4]) == [1, 2, 3, 4]
+@pytest.mark.parametrize("case", ["store data", "sgpr address", "m0", "dpp", "trans"])
+def test_emulator_flags_missing_wait_states(case):
+    """Each wait-state rule the emulator checks faults when the wait is
+    missing and passes with it: the kernels above are checked against them."""
+    import gcn_emu as E
+    bad, good, match = {
+        "store data": (["global_store_dwordx4 v1, v[4:7], s[4:5]", "v_mov_b32 v5, 9"],
+                       ["global_store_dwordx4 v1, v[4:7], s[4:5]", "s_nop 0", "v_mov_b32 v5, 9"], "store-data"),
+        "sgpr address": (["v_mov_b32 v8, s4", "v_readfirstlane_b32 s6, v8", "s_mov_b32 s7, s5", "s_nop 2",
+                          "global_store_dword v1, v5, s[6:7]"],
+                         ["v_mov_b32 v8, s4", "v_readfirstlane_b32 s6, v8", "s_mov_b32 s7, s5", "s_nop 3",
+                          "global_store_dword v1, v5, s[6:7]"], "as an address"),
+        "m0": (["s_mov_b32 m0, 0", "global_load_lds_dwordx4 v1, s[4:5]"],
+               ["s_mov_b32 m0, 0", "s_nop 0", "global_load_lds_dwordx4 v1, s[4:5]"], "M0"),
+        "dpp": (["v_mov_b32 v2, 5", "s_nop 0", "v_add_u32_dpp v3, v2, v2 row_shr:1 row_mask:0xf bank_mask:0xf"],
+                ["v_mov_b32 v2, 5", "s_nop 1", "v_add_u32_dpp v3, v2, v2 row_shr:1 row_mask:0xf bank_mask:0xf"],
+                "DPP"),
+        "trans": (["v_exp_f32 v2, v4", "v_add_f32 v3, v2, v2"],
+                  ["v_exp_f32 v2, v4", "s_nop 0", "v_add_f32 v3, v2, v2"], "transcendental"),
+    }[case]
+    with pytest.raises(E.Fault, match=match):
+        _run_tiny(bad, lds=16384)
+    _run_tiny(good, lds=16384)
