@@ -947,11 +947,12 @@ def issue_unit_fp8(a, u_sgpr, slot_sgpr):
     dma_fp8(a, slot_sgpr)
 
 
-def dequant_fp8(a):
+def dequant_fp8(a, masked=True):
     """Rows 16w .. 16w+15 of the current unit: staging slot S_SLOT -> bf16
     tile (codes widened exactly, rows at or past S_CURVALID zeroed), rope
     copied, scales transposed to [block][row].  Ends with the LDS writes in
-    flight."""
+    flight.  masked=False: every row holds data (S_CURVALID >= 64), no
+    zeroing."""
     T = S_TMP
     lds = LdsOrder()
     lds.issue()                                 # the restart-flag read issued before
@@ -988,9 +989,10 @@ def dequant_fp8(a):
         d, o = 16 + 2 * n, 48 + 4 * (n % 4)
         m = f"s[{mk[rsel]}:{mk[rsel] + 1}]"
         a.lines += lds.wait(rid[n])
-        a(f"v_cndmask_b32 {vreg(d)}, 0, {vreg(d)}, {m}",
-          f"v_cndmask_b32 {vreg(d + 1)}, 0, {vreg(d + 1)}, {m}",
-          f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o)}, {vreg(d)}, 1.0",
+        if masked:
+            a(f"v_cndmask_b32 {vreg(d)}, 0, {vreg(d)}, {m}",
+              f"v_cndmask_b32 {vreg(d + 1)}, 0, {vreg(d + 1)}, {m}")
+        a(f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o)}, {vreg(d)}, 1.0",
           f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 1)}, {vreg(d)}, 1.0 op_sel:[1,0,0]",
           f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 2)}, {vreg(d + 1)}, 1.0",
           f"v_cvt_scalef32_pk_bf16_fp8 {vreg(o + 3)}, {vreg(d + 1)}, 1.0 op_sel:[1,0,0]",
@@ -1012,7 +1014,7 @@ def dequant_fp8(a):
         d = 64 + 8 + 4 * rsel
         m = f"s[{mk[rsel]}:{mk[rsel] + 1}]"
         a.lines += lds.wait(rr[rsel])
-        for q in range(4):
+        for q in range(4 if masked else 0):
             a(f"v_cndmask_b32 {vreg(d + q)}, 0, {vreg(d + q)}, {m}")
         a(f"v_add_u32 {vreg(t0)}, 0x10000, {vreg(w1 if rsel else w0)}",
           "s_nop 1",
@@ -1035,7 +1037,7 @@ def dequant_fp8(a):
       f"v_lshlrev_b32 {vreg(sa)}, 2, {vreg(st)}",
       f"v_add_u32 {vreg(sa)}, {F8_SCL}, {vreg(sa)}")
     a.lines += lds.wait(r)
-    for q in range(4):
+    for q in range(4 if masked else 0):
         a(f"v_cndmask_b32 {vreg(sc + q)}, 0, {vreg(sc + q)}, vcc")
     a("s_nop 1")
     for q in range(4):
@@ -1730,7 +1732,14 @@ def unit_body_fp8(a):
     dma_fp8(a, T + 21)
     a(f"s_add_u32 s{T + 19}, {s(S_UCUR)}, 1")
     prefetch_next(a, T + 19)
-    dequant_fp8(a)
+    dqfull, dqdone = a.new_label("dqfull"), a.new_label("dqdone")
+    a(f"s_cmp_ge_i32 {s(S_CURVALID)}, 64",
+      f"s_cbranch_scc1 {dqfull}")
+    dequant_fp8(a, masked=True)
+    a(f"s_branch {dqdone}")
+    a.label(dqfull)
+    dequant_fp8(a, masked=False)
+    a.label(dqdone)
     a(s_waitcnt_lgkm(0), "s_barrier",
       "s_nop 1",
       f"v_readfirstlane_b32 s{T}, {vreg(V_T)}",
