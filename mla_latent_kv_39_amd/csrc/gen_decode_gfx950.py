@@ -1,33 +1,42 @@
 #!/usr/bin/env python3
-"""Emit the gfx950 assembly of the bf16 split-KV MLA decode kernel.
+"""Emit the gfx950 assembly of the split-KV MLA decode kernels (bf16 and
+e4m3 latent caches).
 
-The kernel is written here as a program that prints GCN assembly, so that the
-register file can be laid out by hand: one wave per SIMD holds its 32 heads of
-Q (144 VGPRs) and its 32 x 512 fp32 output accumulator (all 256 AGPRs) for a
-whole sequence segment, which a compiler's register allocator does not manage
-without spilling.  Everything else (page walk, tile ring, softmax, epilogue)
-is spelled out below with the same structure as the description in
-include/mla.h:
+The kernels are written here as a program that prints GCN assembly, so that
+the register file can be laid out by hand: one wave per SIMD holds 32 query
+rows of Q (144 VGPRs) and a 128 x 128 (bf16) or 32 x 512 (e4m3) fp32 block of
+the output accumulator (all 256 AGPRs) for a whole sequence segment, which a
+compiler's register allocator does not manage without spilling.  Everything
+else is spelled out below:
 
   * work partition: units of 64 rows (one cache page), sequence after
-    sequence; partition p of P (a power of two) owns units
-    [(pU) >> log2 P, ((p+1)U) >> log2 P);
-  * tile ring: two LDS slots of one page each (72 KB), filled one unit ahead
-    with direct-to-LDS loads.  A slot is 9 x 8 blocks of 8 rows x 8 chunks
-    (chunk = 16 bytes); one load instruction moves one block, eight whole
-    128-byte lines of the page, and an XOR swizzle of the chunk slot inside
-    a block keeps the 16-row score reads and the transposed output reads
-    free of bank conflicts (lane_constants below);
-  * per 32-row sub-step: scores S^T = C Q^T (72 MFMA 16x16x32 bf16),
-    softmax against a per-segment reference m_ref (first max + 30, log2
-    units), output O += P C (64 MFMAs, B operand read with ds_read_b64_tr_b16);
-  * a max that passes m_ref + 64 raises the reference and restarts the
-    segment (LDS flag, all waves together).
+    sequence; every sequence also weighs SEG_WEIGHT units (its fixed cost),
+    so unit j of sequence b sits at position u0_b + SEG_WEIGHT (b + 1) + j,
+    and partition p of P (a power of two) takes the units whose positions lie
+    in [(pW) >> log2 P, ((p+1)W) >> log2 P), W the total weight;
+  * bf16 kernel, steps of 32 rows (half a page): four LDS tiles of a half
+    page filled two steps ahead with direct-to-LDS loads (one load moves
+    eight whole 128-byte lines; an XOR swizzle keeps the 16-row score reads
+    and the transposed output reads free of bank conflicts); in step t the
+    score MFMAs of step t (S^T = C Q^T) run interleaved with the output MFMAs
+    of step t - 1 (O += P C, B operand read with ds_read_b64_tr_b16), the
+    softmax of step t beside the last of them, one barrier per step;
+  * e4m3 kernel, units of 64 rows: raw pages (codes, 1x128 scales, bf16 k^R)
+    staged one unit ahead, widened exactly to bf16 in LDS, scores per 128-wide
+    block scaled in fp32 after the block's MFMAs, P * scale rounded to bf16
+    for the output;
+  * softmax against a per-segment reference m_ref (first max + 30, log2
+    units) instead of a running max; sums that overflow, or a max far past
+    the reference, restart the segment with an exact reference;
+  * epilogue: final rows in fp32 for a sequence wholly inside the partition,
+    else an fp16 partial with one power-of-two descale per (column quarter,
+    head) and its lse (the partial_out layout of include/mla.h).
 
 Score/softmax/output follow DeepSeek-V3 architecture notes (deepseek.csdn.net)
 §2.1.1-§2.1.3: one shared latent row per token serves as key (with the
 decoupled RoPE part) and, its first 512 values, as value; scores are scaled by
-1/sqrt(d_h + d_h^R).
+1/sqrt(d_h + d_h^R).  The e4m3 cache and its 1x128 scales follow DeepSeek-V3
+详解 (yudonglee.me) §4.2.
 
 Usage: gen_decode_gfx950.py OUT.s
 """
