@@ -147,6 +147,6 @@ const char* mla_status_string(mla_status status) {
   return "unknown status";
 }
 
-int32_t mla_version(void) { return 100; }
+int32_t mla_version(void) { return 200; }  // 0.2.0: fp16 partials with descales
 
 }  // extern "C"
