@@ -65,6 +65,7 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, out=None) == E.MLA_ERR_NULL
     assert _decode(lib, lse=None) == E.MLA_ERR_NULL
     assert _decode(lib, po=None) == E.MLA_ERR_NULL              # partials needed when splits > 1
+    assert _decode(lib, po=FAKE + 8) == E.MLA_ERR_SHAPE         # partial_out: 16-byte aligned
     assert _decode(lib, batch=0) == E.MLA_ERR_SHAPE
     assert _decode(lib, s_q=0) == E.MLA_ERR_SHAPE
     assert _decode(lib, s_q=3) == E.MLA_ERR_UNSUPPORTED
