@@ -102,7 +102,8 @@ V_LDA, V_LDB, V_LCA, V_LCB = 104, 105, 106, 107   # loader lane constants
 V_LIM = 15               # visible-row limit of the current sub-step (mask; a temporary outside the phases)
 V_ENT = 108              # block-table entry of the unit after next (vector load, one unit ahead)
 V_NEGINF = 109
-V_PEAK = (110, 111)      # largest 8-row probability sum seen per lane in this segment (lean softmax)
+V_PEAK = (110, 111)      # e4m3: largest 8-row probability sum seen per lane in this segment (lean
+                         # softmax); bf16: the lane's exact fp32 probability sum, for lse
 V_Q = 112                # Q[ks][h] at 112 + (2*ks + h)*4, 144 regs
 # source offsets of the next unit's loads (row groups 2w, 2w+1): live through the phases
 V_DMA = (V_T + 1, V_T + 2)
@@ -144,7 +145,8 @@ S_MODE = S_TMP + 13      # bf16: kind of the current unit (0 none, 1 half, 2 cla
 S_PFOFF = S_TMP + 14     # bf16: block-table byte offset of the page prefetch to issue
 # loads of the next unit issued in phases 1, 2, 3 of a full unit
 DMA_SPLIT = (8, 6, 4)
-S_MAX = 98
+S_ONES = 98              # bf16 pair (1.0, 1.0): sums of packed probabilities by v_dot2
+S_MAX = 99
 
 
 def temps(*regs, pool):
@@ -688,22 +690,46 @@ def softmax_code(ss, S=None, P=None, tmp=None):
             x(f"v_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(ref)}")
         for r in regs:
             x(f"v_exp_f32 {vreg(r)}, {vreg(r)}")
-        x("s_nop 0",
-          f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[5])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[6])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}",
-          f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}")
+        x("s_nop 0", *exact_sum(regs, t0, t1))
         if P is not None:
-            p = P + 4 * h
-            x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
+            # bf16: the exact sum goes to lse (V_PEAK), the sum of the rounded
+            # probabilities to the normalisation (V_LRUN)
+            x(f"v_add_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
+              *pack_and_sum(regs, P + 4 * h, t1),
+              f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t1)}")
+        else:
+            x(f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}")
     return x.lines
+
+
+def exact_sum(regs, t0, t1):
+    """t0 = the fp32 sum of the eight probabilities regs (t1 scratch)."""
+    return [f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
+            f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+            f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
+            f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[5])}",
+            f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[6])}",
+            f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
+            f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}"]
+
+
+def pack_and_sum(regs, p, t):
+    """The eight fp32 probabilities regs -> four bf16 pairs at p .. p + 3 (the
+    output MFMAs' operand), and t = the sum of the rounded values (v_dot2
+    against (1.0, 1.0): exact products, fp32 accumulation; a DOT result read
+    by another VALU instruction needs three wait states).  Normalising the
+    output by this sum makes it an exact convex combination of the rows with
+    the rounded weights: when one row takes nearly all of a softmax its weight
+    rounds to nearly 1 and the output to nearly that row."""
+    return [f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
+            f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
+            f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
+            f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}",
+            f"v_dot2_f32_bf16 {vreg(t)}, {vreg(p)}, {s(S_ONES)}, 0",
+            f"v_dot2_f32_bf16 {vreg(t)}, {vreg(p + 1)}, {s(S_ONES)}, {vreg(t)}",
+            f"v_dot2_f32_bf16 {vreg(t)}, {vreg(p + 2)}, {s(S_ONES)}, {vreg(t)}",
+            f"v_dot2_f32_bf16 {vreg(t)}, {vreg(p + 3)}, {s(S_ONES)}, {vreg(t)}",
+            "s_nop 2"]
 
 
 def softmax_lean(ss, S=None, P=None, tmp=None):
@@ -726,23 +752,18 @@ def softmax_lean(ss, S=None, P=None, tmp=None):
         fma.append([f"\tv_fma_f32 {vreg(r)}, {vreg(r)}, {s(S_SCALE)}, -{vreg(mref)}" for r in regs])
         exp.append([f"\tv_exp_f32 {vreg(r)}, {vreg(r)}" for r in regs])
         x = Asm()
-        x(f"v_add_f32 {vreg(t0)}, {vreg(regs[0])}, {vreg(regs[1])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[4])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[5])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(regs[6])}",
-          f"v_add_f32 {vreg(t1)}, {vreg(t1)}, {vreg(regs[7])}",
-          f"v_add_f32 {vreg(t0)}, {vreg(t0)}, {vreg(t1)}",
-          f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}",
-          f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(t0)}",
-          f"v_max_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
-          f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc")
+        x(*exact_sum(regs, t0, t1),
+          f"v_cmp_lt_f32 vcc, {OVF_SUM}, {vreg(t0)}")
         if P is not None:
-            p = P + 4 * h
-            x(f"v_cvt_pk_bf16_f32 {vreg(p)}, {vreg(regs[0])}, {vreg(regs[1])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 1)}, {vreg(regs[2])}, {vreg(regs[3])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 2)}, {vreg(regs[4])}, {vreg(regs[5])}",
-              f"v_cvt_pk_bf16_f32 {vreg(p + 3)}, {vreg(regs[6])}, {vreg(regs[7])}")
+            # bf16: exact sum for lse, rounded sum for the normalisation (softmax_code)
+            x(f"v_add_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
+              f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc",
+              *pack_and_sum(regs, P + 4 * h, t1),
+              f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t1)}")
+        else:
+            x(f"v_add_f32 {vreg(V_LRUN[h])}, {vreg(V_LRUN[h])}, {vreg(t0)}",
+              f"v_max_f32 {vreg(V_PEAK[h])}, {vreg(V_PEAK[h])}, {vreg(t0)}",
+              f"s_or_b64 {sp(S_OVF)}, {sp(S_OVF)}, vcc")
         tail.append(x.lines)
     # half 0's sums read its exponentials long after they issue, half 1's sums
     # follow seven other instructions (a transcendental result needs one)
@@ -1359,9 +1380,12 @@ def epilogue_split(a):
     the wave's own rows."""
     T = S_TMP
     L, t0, t1 = (16, 17), 18, 19
+    LX = (32, 33)                         # exact sums of this wave's rows, for lse
     for h in range(2):
-        a(f"v_mov_b32 {vreg(L[h])}, {vreg(V_LRUN[h])}")
+        a(f"v_mov_b32 {vreg(L[h])}, {vreg(V_LRUN[h])}",
+          f"v_mov_b32 {vreg(LX[h])}, {vreg(V_PEAK[h])}")
         xor_reduce(a, L[h], "v_add_f32", t0, t1)
+        xor_reduce(a, LX[h], "v_add_f32", t0, t1)
     # row sum of query row 32w + 16h + r16 at P_BASE + 4 (32w + 16h + r16); request at P_BASE + 512 + 4w
     a(f"s_lshl_b32 s{T}, {s(S_WAVE)}, 7",
       f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
@@ -1430,9 +1454,9 @@ def epilogue_split(a):
       f"s_addc_u32 s{T + 11}, s{T + 7}, 0")
     for h in range(2):
         lse = t1
-        a(f"v_log_f32 {vreg(lse)}, {vreg(L[h])}",
+        a(f"v_log_f32 {vreg(lse)}, {vreg(LX[h])}",
           "s_nop 1",
-          f"v_cmp_lt_f32 vcc, 0, {vreg(L[h])}",
+          f"v_cmp_lt_f32 vcc, 0, {vreg(LX[h])}",
           f"v_add_f32 {vreg(lse)}, {vreg(V_MREF[h])}, {vreg(lse)}",
           f"v_mul_f32 {vreg(lse)}, {LN2}, {vreg(lse)}",
           "s_nop 1",
@@ -2384,6 +2408,7 @@ def kernel(fp8=False):
       f"s_load_dwordx8 s[{S_LSE}:{S_LSE + 7}], s[0:1], 0x40",
       f"s_load_dwordx2 s[{S_NHB}:{S_NHB + 1}], s[0:1], 0x60",
       *([f"s_load_dwordx4 s[{S_FSC}:{S_FSC + 3}], s[0:1], 0x68"] if FP8 else []),
+      f"s_mov_b32 {s(S_ONES)}, 0x3f803f80",
       f"v_and_b32 {vreg(V_LANE)}, 63, {vreg(V_TID)}",
       f"v_lshrrev_b32 {vreg(V_G)}, 4, {vreg(V_LANE)}",
       f"v_and_b32 {vreg(V_R16)}, 15, {vreg(V_LANE)}",

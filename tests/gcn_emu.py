@@ -354,7 +354,8 @@ def check_wait_states(w, ins):
       a VALU write of an SGPR read by a memory instruction as its address: 5;
       an SALU write of M0 read by a direct-to-LDS load as its LDS address: 1;
       a VALU write of a VGPR read by a DPP instruction: 2;
-      a transcendental VALU result read by the next VALU: 1.
+      a transcendental VALU result read by the next VALU: 1;
+      a DOT result read by another VALU (not as a DOT's accumulator): 3.
     Raises Fault on a violation, then records the instruction."""
     op = ins.op
     def since(pred, limit):
@@ -383,9 +384,15 @@ def check_wait_states(w, ins):
             raise Fault("VGPR written by a VALU fewer than 2 wait states before a DPP read")
         if not op.startswith(_TRANS) and since(lambda rec: rec[4] and rec[2] & srcs, 1):
             raise Fault("transcendental result read by the next VALU (1 wait state needed)")
+        # a DOT result read by another VALU instruction (a DOT of the same kind may
+        # take it as its accumulator, srcC, at once)
+        acc = _regs(ins.args[3]) if op.startswith("v_dot") and len(ins.args) > 3 and ins.args[3].kind == "v" \
+            else set()
+        if since(lambda rec: rec[5] and rec[2] & (srcs - acc), 3):
+            raise Fault("DOT result read by another VALU fewer than 3 wait states later")
     # record
     nop = int(ins.args[0].val) + 1 if op == "s_nop" else 1
-    sw, vw, m0, trans = set(), set(), False, False
+    sw, vw, m0, trans, dot = set(), set(), False, False, op.startswith("v_dot")
     if op.startswith("v_") and ins.args:
         d = ins.args[0]
         if d.kind == "s":
@@ -397,7 +404,7 @@ def check_wait_states(w, ins):
         trans = op.startswith(_TRANS)
     elif op.startswith("s_") and ins.args and ins.args[0].kind == "m0":
         m0 = True
-    w.hist.append((nop, sw, vw, m0, trans))
+    w.hist.append((nop, sw, vw, m0, trans, dot))
 
 
 class Workgroup:
@@ -864,6 +871,18 @@ def _vtrans(g, w, i):
             r = 1.0 / a.astype(np.float64)
         r = r.astype(np.float32)
     _fset(w, i, r)
+
+
+@op("v_dot2_f32_bf16")
+def _vdot2bf16(g, w, i):
+    """D = a.lo * b.lo + a.hi * b.hi + c, a and b bf16 pairs, c fp32; computed
+    exactly and rounded once to fp32."""
+    a, b = w.vget(i.args[1]), w.vget(i.args[2])
+    c = w.fget(i.args[3]).astype(np.float64)
+    bf = lambda x: ((x & 0xFFFF) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    with np.errstate(all="ignore"):
+        r = bf(a) * bf(b) + bf(a >> 16) * bf(b >> 16) + c
+    _fset(w, i, r.astype(np.float32))
 
 
 @op("v_cvt_pk_f16_f32")

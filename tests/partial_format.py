@@ -54,11 +54,14 @@ def unpack(buf, num_splits, s_q):
 
 
 def concentrated_bound(inp, oracle):
-    """Largest output error the arithmetic allows when one cache row takes
-    (nearly) all of a softmax: the probabilities (times the e4m3 scale) enter
-    the output MFMAs as bf16, 8 significant bits, so a weight is off by up to
-    2^-8 of itself; a split partial adds the fp16 rounding of its values,
-    2^-11 of the largest.  Both scale with the largest |c| of the rows."""
+    """Largest output error the arithmetic allows for the e4m3 cache when one
+    cache row takes (nearly) all of a softmax: the probabilities times the
+    per-block scale enter the output MFMAs as bf16, 8 significant bits, so a
+    weight is off by up to 2^-8 of itself (the row sum cannot follow four
+    differently scaled roundings); a split partial adds the fp16 rounding of
+    its values, 2^-11 of the largest.  Both scale with the largest |c| of the
+    rows.  (The bf16 kernel normalises by the sum of its rounded
+    probabilities and stays within 1e-2.)"""
     cmax = 0.0
     for b in range(inp.batch):
         n = int(inp.seq_lens[b])

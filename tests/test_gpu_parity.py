@@ -93,12 +93,11 @@ def test_scores_with_large_spread_restart_path(factor):
         for j in (L - 5, L // 2):
             page = int(inp.block_table[b, j // 64])
             inp.cache[page, j % 64, 512:] = (inp.q_rope[b, 0, 0].float() * factor).to(torch.bfloat16)
-    # With the softmax concentrated on two rows, rounding P to bf16 (8
-    # significant bits: relative 2^-8 per weight) moves out by up to 2^-8 max|c|,
-    # and an fp16 partial by 2^-11 max|c| more.
-    from partial_format import concentrated_bound
+    # The softmax concentrates on two rows: the kernel normalises by the sum of
+    # the bf16-rounded probabilities it multiplies with, so the output stays a
+    # convex combination of the rows and within 1e-2 (measured <= 5.7e-3)
     for splits in (1, 4):
-        _run_and_check(inp, splits, f"large spread x{factor:g} splits={splits}", out_tol=concentrated_bound(inp, O))
+        _run_and_check(inp, splits, f"large spread x{factor:g} splits={splits}")
 
 
 @pytest.mark.parametrize("s_q,splits", [(1, 256), (2, 128), (1, 4096)])
@@ -106,15 +105,10 @@ def test_many_short_sequences(s_q, splits):
     # 300 sequences (more than the 256 whose lengths the prologue keeps in
     # registers: the partition map scans seq_lens in passes), lengths 1..150,
     # and in the last case more partitions than 64-row units.  Sequences of a
-    # few rows put one row in charge of a softmax, where the bf16 rounding of
-    # P bounds the error by (2^-8 + 2^-11) max|c| rather than 1e-2 (600 such
-    # sequences with two query tokens measured 1.03e-2)
-    from gpu_helpers import OUT_TOL
-    from partial_format import concentrated_bound
+    # few rows put one row in charge of a softmax (measured <= 4.5e-3)
     lens = [int(x) for x in np.random.default_rng(11).integers(1, 151, size=300)]
     inp = _small(lens, s_q=s_q, seed=12)
-    _run_and_check(inp, splits, f"300 short sequences s_q={s_q} splits={splits}",
-                   out_tol=max(OUT_TOL, concentrated_bound(inp, O)))
+    _run_and_check(inp, splits, f"300 short sequences s_q={s_q} splits={splits}")
 
 
 def _partition_map(lens, num_splits):
