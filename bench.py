@@ -54,19 +54,29 @@ def algorithmic_work(inp):
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE and
     WRITE_SIZE passes (profiles/decode_traffic.json, scaled by the copy
-    calibration), or None when they were taken on another version of the
-    kernel generator or not for this workload."""
-    import hashlib
+    calibration), or None when they were taken on other kernels (the SHA-256
+    of both kernels' generated assembly differs) or not for this workload."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    gen = os.path.join(ROOT, "mla_latent_kv_39_amd", "csrc", "gen_decode_gfx950.py")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(gen, "rb").read()).hexdigest()
+        sha = kernels_sha256()
     except (OSError, ValueError):
         return None
-    if rec.get("generator_sha256") != sha or workload not in rec.get("workloads", {}):
+    if rec.get("kernel_sha256") != sha or workload not in rec.get("workloads", {}):
         return None
     return rec["workloads"][workload]["bytes"]
+
+
+def kernels_sha256() -> str:
+    """SHA-256 of the assembly the generator emits for the bf16 and the e4m3
+    decode kernels (what the library embeds)."""
+    import hashlib
+    import importlib.util
+    gen = os.path.join(ROOT, "mla_latent_kv_39_amd", "csrc", "gen_decode_gfx950.py")
+    spec = importlib.util.spec_from_file_location("_gen_decode_for_sha", gen)
+    g = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(g)
+    return hashlib.sha256((g.kernel(False) + g.kernel(True)).encode()).hexdigest()
 
 
 def cpu_baseline(inp, budget_s: float):

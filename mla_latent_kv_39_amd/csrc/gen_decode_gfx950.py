@@ -27,7 +27,9 @@ else is spelled out below:
     for the output;
   * softmax against a per-segment reference m_ref (first max + 30, log2
     units) instead of a running max; sums that overflow, or a max far past
-    the reference, restart the segment with an exact reference;
+    the reference, restart the segment with an exact reference; the bf16
+    kernel normalises the output by the sum of the bf16-rounded
+    probabilities its MFMAs use and takes lse from the exact fp32 sum;
   * epilogue: final rows in fp32 for a sequence wholly inside the partition,
     else an fp16 partial with one power-of-two descale per (column quarter,
     head) and its lse (the partial_out layout of include/mla.h).
