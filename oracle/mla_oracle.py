@@ -94,15 +94,6 @@ def dequantize_latent(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------- paging
-def page_rows(cache_pages: np.ndarray, pages: list, n: int, block_size: int) -> np.ndarray:
-    """Rows 0..n-1 of one sequence: row j is slot j % block_size of page pages[j // block_size]."""
-    if n == 0:
-        return cache_pages[:0, 0]
-    need = (n + block_size - 1) // block_size
-    stacked = np.concatenate([cache_pages[p] for p in pages[:need]], axis=0)
-    return stacked[:n]
-
-
 def sequence_pages(b: int, block_table, max_blocks: int) -> list:
     """Page ids of sequence b; without a table, page b*max_blocks + u holds rows 64u..64u+63."""
     if block_table is None:
