@@ -63,12 +63,17 @@ LDS_BYTES = P_BASE + P_BYTES
 PAGE_BYTES = SLOT_BYTES         # global bytes of one page of the row array
 
 # fp8 kernel: one bf16 tile, two staging slots of raw pages (e4m3 codes, bf16
-# rope, fp32 scales), the current unit's scales as [block][row], the flag
+# rope, fp32 scales), the current unit's scales as [block][row], their
+# reciprocals as bf16 (hi, lo) pairs, the flag
 F8_CODES, F8_ROPE, F8_SCALES = 64 * 512, 64 * 128, 64 * 16
 F8_RAW = F8_CODES + F8_ROPE + F8_SCALES          # 41984
 F8_RAW0 = SLOT_BYTES
 F8_SCL = F8_RAW0 + 2 * F8_RAW                    # 157696
-F8_FLAG = F8_SCL + 1024
+# 1/scale of row r, block q, split into bf16 hi + lo (hi = bf16(1/s), lo =
+# bf16(1/s - hi)): the 16 bytes at F8_INV + 256 q + 16 (r / 4) hold
+# [hi(r0, r1), lo(r0, r1), hi(r2, r3), lo(r2, r3)] for rows r0 = 4 (r / 4) ..
+F8_INV = F8_SCL + 1024
+F8_FLAG = F8_INV + 1024
 
 
 def configure(fp8):
@@ -107,6 +112,9 @@ V_NEGINF = 109
 V_PEAK = (110, 111)      # e4m3: largest 8-row probability sum seen per lane in this segment (lean
                          # softmax); bf16: the lane's exact fp32 probability sum, for lse
 V_Q = 112                # Q[ks][h] at 112 + (2*ks + h)*4, 144 regs
+V_LBLK = (0, 7)          # e4m3: lane (g, r16): running sum over the segment of the rounded
+                         # weights of latent block g, bf16(P s_g) / s_g, head 16h + r16 (v0 and v7
+                         # serve only the prologue and the bf16 loader)
 # source offsets of the next unit's loads (row groups 2w, 2w+1): live through the phases
 V_DMA = (V_T + 1, V_T + 2)
 # softmax scratch: sub-step 0 borrows P[1], sub-step 1 borrows S[0] (both free at that time)
@@ -1074,6 +1082,51 @@ def dequant_fp8(a, masked=True):
     a("s_nop 1")
     for q in range(4):
         a(f"ds_write_b32 {vreg(sa)}, {vreg(sc + q)} offset:{256 * q}")
+    # reciprocal scales, for the per-block normalisation of the output: lane
+    # L < 32 takes rows 16w + 2p, + 1 (p = L & 7) of block q = L >> 3, and
+    # writes 1/s as bf16 hi + lo pairs (0 for a row past the sequence or a
+    # scale that is not positive)
+    ia, r0, r1, i0, i1, t, hi, lo, pp, qq = range(16, 26)      # the code reads are consumed (hi even)
+    mk0, mk1 = T + 16, T + 18
+    a("s_mov_b64 exec, 0xffffffff",
+      f"v_and_b32 {vreg(pp)}, 7, {vreg(V_LANE)}",
+      f"v_lshrrev_b32 {vreg(qq)}, 3, {vreg(V_LANE)}",
+      f"v_lshlrev_b32 {vreg(ia)}, 5, {vreg(pp)}",
+      f"v_lshl_add_u32 {vreg(ia)}, {vreg(qq)}, 2, {vreg(ia)}",
+      f"v_add_u32 {vreg(ia)}, s{T + 13}, {vreg(ia)}",           # staged scales: 16 B per row
+      f"ds_read_b32 {vreg(r0)}, {vreg(ia)}",
+      f"ds_read_b32 {vreg(r1)}, {vreg(ia)} offset:16")
+    rr = lds.issue(), lds.issue()
+    a(f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 4",
+      f"v_lshl_add_u32 {vreg(t)}, {vreg(pp)}, 1, s{T + 15}",   # row 16w + 2p
+      f"v_cmp_gt_i32 s[{mk0}:{mk0 + 1}], {s(S_CURVALID)}, {vreg(t)}",
+      f"v_add_u32 {vreg(t)}, 1, {vreg(t)}",
+      f"v_cmp_gt_i32 s[{mk1}:{mk1 + 1}], {s(S_CURVALID)}, {vreg(t)}",
+      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 6",
+      f"s_add_u32 s{T + 15}, s{T + 15}, {F8_INV}",
+      f"v_lshlrev_b32 {vreg(t)}, 3, {vreg(pp)}",
+      f"v_lshl_add_u32 {vreg(t)}, {vreg(qq)}, 8, {vreg(t)}",
+      f"v_add_u32 {vreg(ia)}, s{T + 15}, {vreg(t)}")            # F8_INV + 256 q + 64 w + 8 p
+    a.lines += lds.wait(rr[1])
+    if masked:
+        a(f"v_cndmask_b32 {vreg(r0)}, 0, {vreg(r0)}, s[{mk0}:{mk0 + 1}]",
+          f"v_cndmask_b32 {vreg(r1)}, 0, {vreg(r1)}, s[{mk1}:{mk1 + 1}]")
+    a(f"v_rcp_f32 {vreg(i0)}, {vreg(r0)}",
+      f"v_rcp_f32 {vreg(i1)}, {vreg(r1)}",
+      f"v_cmp_lt_f32 vcc, 0, {vreg(r0)}",
+      "s_nop 1",
+      f"v_cndmask_b32 {vreg(i0)}, 0, {vreg(i0)}, vcc",
+      f"v_cmp_lt_f32 vcc, 0, {vreg(r1)}",
+      "s_nop 1",
+      f"v_cndmask_b32 {vreg(i1)}, 0, {vreg(i1)}, vcc",
+      f"v_cvt_pk_bf16_f32 {vreg(hi)}, {vreg(i0)}, {vreg(i1)}",
+      f"v_lshlrev_b32 {vreg(t)}, 16, {vreg(hi)}",
+      f"v_sub_f32 {vreg(t)}, {vreg(i0)}, {vreg(t)}",              # exact: 1/s - hi
+      f"v_and_b32 {vreg(lo)}, 0xffff0000, {vreg(hi)}",
+      f"v_sub_f32 {vreg(lo)}, {vreg(i1)}, {vreg(lo)}",
+      f"v_cvt_pk_bf16_f32 {vreg(lo)}, {vreg(t)}, {vreg(lo)}",
+      f"ds_write_b64 {vreg(ia)}, {vr(hi, 2)}")
+    lds.issue()
     a("s_mov_b64 exec, -1")
 
 
@@ -1151,10 +1204,67 @@ def qk_fp8(a, ss):
     a.lines += update(3)
 
 
+PV_PART = 48    # e4m3 output phase: this sub-step's rounded-weight sums, (h, blk) at 48 + 4h + blk
+PV_INV = 56     # the current block's reciprocal-scale pairs of rows 32ss + 16tb + 4g .. +3 at 56 + 4tb
+
+
+def f8_inv_reads(ss, blk):
+    """bf16 (hi, lo) pairs of 1/s of rows 32ss + 16tb + 4g .. +3, block blk ->
+    PV_INV + 4tb: [hi(i0, i1), lo(i0, i1), hi(i2, i3), lo(i2, i3)]."""
+    return [f"\tds_read_b128 {vr(PV_INV + 4 * tb, 4)}, {vreg(V_SCLB)} "
+            f"offset:{F8_INV - F8_SCL + 256 * blk + 128 * ss + 64 * tb}" for tb in range(2)]
+
+
+def block_weight_sums(blk):
+    """PV_PART[h][blk] = sum over this lane's 8 rows of bf16(P s) / s for
+    block blk: each packed pair of rounded weights dotted with the (hi, lo)
+    pairs of the rows' reciprocal scales, exact products accumulated in fp32.
+    The two heads' chains alternate (a DOT may take a DOT result as its
+    accumulator at once)."""
+    pb = F8_P[blk & 1]
+    out = []
+    for k in range(4):
+        tb, half = divmod(k, 2)
+        for part in range(2):
+            for h in range(2):
+                acc = PV_PART + 4 * h + blk
+                c = "0" if k == 0 and part == 0 else vreg(acc)
+                out.append(f"\tv_dot2_f32_bf16 {vreg(acc)}, {vreg(pb + 4 * h + k)}, "
+                           f"{vreg(PV_INV + 4 * tb + 2 * half + part)}, {c}")
+    return out
+
+
+def block_sums_reduce():
+    """Reduce-scatter of PV_PART over the four lanes g of a head: lane g keeps
+    block g's sum (permlane swaps), added to the segment's V_LBLK."""
+    out = ["\ts_nop 2"]            # DOT results -> another VALU
+    for h in range(2):
+        v = [PV_PART + 4 * h + k for k in range(4)]
+        out += [f"\tv_permlane16_swap_b32 {vreg(v[0])}, {vreg(v[1])}",
+                f"\tv_permlane16_swap_b32 {vreg(v[2])}, {vreg(v[3])}"]
+    out.append("\ts_nop 1")
+    for h in range(2):
+        v = [PV_PART + 4 * h + k for k in range(4)]
+        out += [f"\tv_add_f32 {vreg(v[0])}, {vreg(v[0])}, {vreg(v[1])}",
+                f"\tv_add_f32 {vreg(v[2])}, {vreg(v[2])}, {vreg(v[3])}"]
+    out.append("\ts_nop 1")
+    for h in range(2):
+        v = [PV_PART + 4 * h + k for k in range(4)]
+        out.append(f"\tv_permlane32_swap_b32 {vreg(v[0])}, {vreg(v[2])}")
+    out.append("\ts_nop 1")
+    for h in range(2):
+        v = [PV_PART + 4 * h + k for k in range(4)]
+        out += [f"\tv_add_f32 {vreg(v[0])}, {vreg(v[0])}, {vreg(v[2])}",
+                f"\tv_add_f32 {vreg(V_LBLK[h])}, {vreg(V_LBLK[h])}, {vreg(v[0])}"]
+    return out
+
+
 def pv_fp8(a, ss):
     """O^T += C8^T (P * s_blk)^T block by block (8 column blocks of 16 per
     latent block).  The scaled probabilities of block blk + 1 are formed between
-    the MFMAs of block blk (the two bf16 buffers alternate)."""
+    the MFMAs of block blk (the two bf16 buffers alternate).  Each block's
+    rounded weights are also summed divided by their scales, so that the
+    epilogue can normalise block blk by the weights its MFMAs actually used."""
     frags = pv_frags(ss)
     lds = LdsOrder()
     for f in frags[:NB]:
@@ -1193,6 +1303,11 @@ def pv_fp8(a, ss):
                 a.lines.append(r)
             sid = lds.issue(), lds.issue()
             nxt = scaled(blk + 1)
+        # this block's reciprocal scales (the previous block's sums are done with them)
+        for r in f8_inv_reads(ss, blk):
+            a.lines.append(r)
+        iid = lds.issue(), lds.issue()
+        sums = block_weight_sums(blk)
         for j, cb in enumerate(range(8 * blk, 8 * blk + 8)):
             f = frags[cb]
             a.lines += lds.wait(max(f.read_ids))
@@ -1213,6 +1328,14 @@ def pv_fp8(a, ss):
                 k = 6 if j < 4 else len(nxt)
                 a.lines += nxt[:k]
                 nxt = nxt[k:]
+            # the block's weight sums over fragments 5 .. 7
+            if j >= 5:
+                if j == 5:
+                    a.lines += lds.wait(iid[1])
+                k = 6 if j < 7 else len(sums)
+                a.lines += sums[:k]
+                sums = sums[k:]
+    a.lines += block_sums_reduce()
 
 
 def substep_fp8(a, ss, lean):
@@ -1275,19 +1398,18 @@ def epilogue(a):
       f"s_add_u32 s{T + 12 + 2}, s{T + 4}, s{T + 9}",
       f"s_addc_u32 s{T + 12 + 3}, s{T + 5}, s{T + 12}")
     obase = sp(T + 14)
-    inv = (16, 17)
+    # lse from the exact fp32 sums; the output is normalised per latent block
+    # by the sums of the rounded weights (block_inverses)
     for h in range(2):
         lt, lse, t0, t1 = 18, 19, 20, 21
         a(f"v_mov_b32 {vreg(lt)}, {vreg(V_LRUN[h])}")
         xor_reduce(a, lt, "v_add_f32", t0, t1)
-        a(f"v_rcp_f32 {vreg(inv[h])}, {vreg(lt)}",
-          f"v_log_f32 {vreg(lse)}, {vreg(lt)}",
+        a(f"v_log_f32 {vreg(lse)}, {vreg(lt)}",
           "s_nop 1",
           f"v_cmp_lt_f32 vcc, 0, {vreg(lt)}",
           f"v_add_f32 {vreg(lse)}, {vreg(V_MREF[h])}, {vreg(lse)}",
           f"v_mul_f32 {vreg(lse)}, {LN2}, {vreg(lse)}",
           "s_nop 1",
-          f"v_cndmask_b32 {vreg(inv[h])}, 0, {vreg(inv[h])}, vcc",
           f"v_cndmask_b32 {vreg(lse)}, {vreg(V_NEGINF)}, {vreg(lse)}, vcc")
         # lse of head 16h + r16 from the lanes with g == 0
         a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
@@ -1295,6 +1417,7 @@ def epilogue(a):
           f"v_lshlrev_b32 {vreg(t0)}, 2, {vreg(V_R16)}",
           f"global_store_dword {vreg(t0)}, {vreg(lse)}, s[{T + 10}:{T + 11}] offset:{64 * h}",
           f"s_mov_b64 exec, {sp(S_EXEC)}")
+    inv = block_inverses(a)
     rowwise, stored = a.new_label("rowwise"), a.new_label("stored")
     a(f"s_cmp_eq_u32 s{T + 3}, 0",
       f"s_cbranch_scc1 {rowwise}")
@@ -1311,8 +1434,36 @@ def epilogue(a):
         if h:
             a(f"v_add_u32 {vreg(off)}, {16 * 2048}, {vreg(off)}")
         for cb in range(32):
-            epi_store(a, h, cb, bufs[cb % 4], inv[h], f"{vreg(off)}, {{v}}, {obase} offset:{64 * cb}")
+            epi_store(a, h, cb, bufs[cb % 4], inv[h][cb // 8], f"{vreg(off)}, {{v}}, {obase} offset:{64 * cb}")
     a.label(stored)
+
+
+def block_inverses(a):
+    """e4m3 epilogue: 1 / (sum of block k's rounded weights) of both heads of
+    this lane, for k = 0..3, in v96 + 4h + k (the unit's read bases, free
+    between units); 0 where the sum is not positive.  Lane (g, r16) holds
+    block g's sum (V_LBLK); permlane swaps spread all four to every lane."""
+    t = 27
+    inv = [[96 + 4 * h + k for k in range(4)] for h in range(2)]
+    for h in range(2):
+        r = inv[h]
+        a(f"v_mov_b32 {vreg(r[0])}, {vreg(V_LBLK[h])}",
+          f"v_mov_b32 {vreg(r[1])}, {vreg(V_LBLK[h])}",
+          "s_nop 1",
+          f"v_permlane16_swap_b32 {vreg(r[0])}, {vreg(r[1])}",     # rows: L0 L0 L2 L2 / L1 L1 L3 L3
+          "s_nop 1",
+          f"v_mov_b32 {vreg(r[2])}, {vreg(r[0])}",
+          f"v_mov_b32 {vreg(r[3])}, {vreg(r[1])}",
+          "s_nop 1",
+          f"v_permlane32_swap_b32 {vreg(r[0])}, {vreg(r[2])}",
+          f"v_permlane32_swap_b32 {vreg(r[1])}, {vreg(r[3])}",
+          "s_nop 1")
+        for k in range(4):
+            a(f"v_rcp_f32 {vreg(t)}, {vreg(r[k])}",
+              f"v_cmp_lt_f32 vcc, 0, {vreg(r[k])}",
+              "s_nop 1",
+              f"v_cndmask_b32 {vreg(r[k])}, 0, {vreg(t)}, vcc")
+    return inv
 
 
 def epi_partial_f16_fp8(a, inv):
@@ -1352,7 +1503,7 @@ def epi_partial_f16_fp8(a, inv):
         for h, m in ((0, m0), (1, m1)):
             lane_abs_max(a, m, [vals[8 * cl + 4 * h + i] for cl in range(8) for i in range(4)])
             xor_reduce(a, m, "v_max_f32", t0, t1)
-            a(f"v_mov_b32 {vreg(invq[h])}, {vreg(inv[h])}")
+            a(f"v_mov_b32 {vreg(invq[h])}, {vreg(inv[h][q])}")
             f16_scale(a, m, invq[h], t)
         a(f"v_cmp_eq_u32 vcc, 0, {vreg(V_G)}",
           f"s_and_saveexec_b64 {sp(S_EXEC)}, vcc",
@@ -2390,6 +2541,9 @@ def segment_setup(a, with_q=True, zero=True):
       f"v_mov_b32 {vreg(V_PEAK[0])}, 0",
       f"v_mov_b32 {vreg(V_PEAK[1])}, 0",
       f"s_mov_b32 {s(S_EXACT)}, 0")
+    if FP8:
+        a(f"v_mov_b32 {vreg(V_LBLK[0])}, 0",
+          f"v_mov_b32 {vreg(V_LBLK[1])}, 0")
     if zero:
         zero_o(a)
 
@@ -2548,6 +2702,9 @@ def kernel(fp8=False):
       f"s_mov_b32 {s(S_LLEN)}, {s(S_CLEN)}",
       f"v_mov_b32 {vreg(V_LRUN[0])}, 0",
       f"v_mov_b32 {vreg(V_LRUN[1])}, 0")
+    if FP8:
+        a(f"v_mov_b32 {vreg(V_LBLK[0])}, 0",
+          f"v_mov_b32 {vreg(V_LBLK[1])}, 0")
     zero_o(a)
     a(f"s_sub_u32 {s(S_SLOT)}, {s(S_UCUR)}, {s(S_UA)}",
       f"s_and_b32 {s(S_SLOT)}, {s(S_SLOT)}, 1")

@@ -1021,11 +1021,11 @@ def _dsread(g, w, i):
     w.lgkm.append(land)
 
 
-@op("ds_write_b32", "ds_write_b128")
+@op("ds_write_b32", "ds_write_b64", "ds_write_b128")
 def _dswrite(g, w, i):
     mask = w.execmask()
     addr = _lds_addr(w, i)
-    n = 4 if i.op == "ds_write_b32" else 16
+    n = {"ds_write_b32": 4, "ds_write_b64": 8, "ds_write_b128": 16}[i.op]
     g.lds_check(addr[mask], n)
     src = i.args[1]
     data = np.stack([w.vget(src, k) for k in range(n // 4)], axis=1).copy().view(np.uint8)   # [64, n]

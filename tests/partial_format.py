@@ -51,20 +51,3 @@ def unpack(buf, num_splits, s_q):
     d = dsc.transpose(0, 2, 4, 3, 1).reshape(nb, N_HEADS, 4)             # head (j a r), q
     v = v * d.repeat(8, axis=2)[:, :, :, None]                            # c -> quarter c / 8
     return v.reshape(num_splits, 2, s_q, N_HEADS, D_C)
-
-
-def concentrated_bound(inp, oracle):
-    """Largest output error the arithmetic allows for the e4m3 cache when one
-    cache row takes (nearly) all of a softmax: the probabilities times the
-    per-block scale enter the output MFMAs as bf16, 8 significant bits, so a
-    weight is off by up to 2^-8 of itself (the row sum cannot follow four
-    differently scaled roundings); a split partial adds the fp16 rounding of
-    its values, 2^-11 of the largest.  Both scale with the largest |c| of the
-    rows.  (The bf16 kernel normalises by the sum of its rounded
-    probabilities and stays within 1e-2.)"""
-    cmax = 0.0
-    for b in range(inp.batch):
-        n = int(inp.seq_lens[b])
-        if n > 0:
-            cmax = max(cmax, float(np.abs(oracle.sequence_rows(inp, b, n)[:, :512]).max()))
-    return (2.0 ** -8 + 2.0 ** -11) * cmax

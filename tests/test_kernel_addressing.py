@@ -99,8 +99,13 @@ class Wave:
                  "v_add_u32": lambda: V(1) + V(2), "v_mul_u32_u24": lambda: V(1) * V(2),
                  "v_lshl_add_u32": lambda: (V(1) << V(2)) + V(3), "v_lshl_or_b32": lambda: (V(1) << V(2)) | V(3),
                  "v_bfe_u32": lambda: (V(1) >> V(2)) & ((1 << V(3)) - 1), "v_mov_b32": lambda: V(1)}
-        if op in arith:
+        if op in arith and all(isinstance(V(k), (int, float)) for k in range(1, len(a))):
             self.v[(dst(), L)] = arith[op]()
+        elif op in arith or op in ("v_rcp_f32", "v_sub_f32", "v_cvt_pk_bf16_f32"):
+            # arithmetic on loaded data: kept symbolic, with its operands
+            self.v[(dst(), L)] = ("op", op) + tuple(V(k) for k in range(1, len(a)))
+        elif op == "v_cmp_lt_f32":
+            self.vcc[L] = True          # data-dependent (scale > 0): both outcomes keep the sources
         elif op == "v_cmp_gt_i32":
             if a[0] == "vcc":
                 self.vcc[L] = V(1) > V(2)
@@ -116,24 +121,25 @@ class Wave:
             src = V(1)
             pair = src[2:4] if "op_sel:[1,0,0]" in " ".join(a) else src[0:2]
             self.v[(dst(), L)] = ("bf16",) + tuple(pair)
-        elif op in ("ds_read_b64", "ds_read_b128", "ds_read_b64_tr_b16"):
+        elif op in ("ds_read_b32", "ds_read_b64", "ds_read_b128", "ds_read_b64_tr_b16"):
             base, _, off = a[1].partition(" offset:")
             addr = self.val(base, L) + int(off or 0)
             self.reads.append((op, addr, L))
             if op != "ds_read_b64_tr_b16":
-                n = 8 if op == "ds_read_b64" else 16
-                d0 = int(re.match(r"v\[(\d+):", a[0]).group(1))
+                n = {"ds_read_b32": 4, "ds_read_b64": 8, "ds_read_b128": 16}[op]
+                m = re.match(r"v\[(\d+):", a[0]) or re.fullmatch(r"v(\d+)", a[0])
+                d0 = int(m.group(1))
                 byts = [self.lds.get(addr + b, ("undef",)) for b in range(n)]
                 for q in range(n // 4):
                     self.v[(d0 + q, L)] = tuple(byts[4 * q:4 * q + 4])
-        elif op in ("ds_write_b128", "ds_write_b32"):
+        elif op in ("ds_write_b128", "ds_write_b64", "ds_write_b32"):
             src, _, off = a[1].partition(" offset:")
             addr = self.val(a[0], L) + int(off or 0)
             if op == "ds_write_b32":
                 self.writes[addr] = self.val(src, L)
             else:
                 d0 = int(re.match(r"v\[(\d+):", src).group(1))
-                for q in range(4):
+                for q in range(4 if op == "ds_write_b128" else 2):
                     self.writes[addr + 4 * q] = self.v[(d0 + q, L)]
         elif op == "global_load_lds_dwordx4":
             src = V(0) + self.sval(a[1])
@@ -143,6 +149,20 @@ class Wave:
                 self.lds[dst_addr + b] = ("g", src + b)
         else:
             raise AssertionError(f"instruction not modelled: {op}")
+
+
+def _leaves(x):
+    """The symbolic source bytes (("g", address) or ZERO) a value derives from."""
+    if isinstance(x, tuple) and x and x[0] == "g":
+        return {x}
+    if x == ZERO:
+        return {ZERO}
+    out = set()
+    if isinstance(x, (tuple, list)) or hasattr(x, "__iter__") and not isinstance(x, str):
+        for y in x:
+            if isinstance(y, (tuple, list)) or hasattr(y, "__iter__") and not isinstance(y, str):
+                out |= _leaves(y)
+    return out
 
 
 def lines_of(fn, *args):
@@ -295,7 +315,7 @@ def test_fp8_staging_and_dequant(fp8_mode, valid):
         m.s[G.S_SLOT], m.s[G.S_CURVALID] = 1, valid
         m.run(lines_of(G.dequant_fp8))
     for addr in tile:
-        assert 0 <= addr < G.SLOT_BYTES or G.F8_SCL <= addr < G.F8_SCL + 1024
+        assert 0 <= addr < G.SLOT_BYTES or G.F8_SCL <= addr < G.F8_INV + 1024
     for r in range(64):
         for c in range(72):
             for q in range(4):
@@ -313,3 +333,18 @@ def test_fp8_staging_and_dequant(fp8_mode, valid):
         for r in range(64):
             want = (ZERO,) * 4 if r >= valid else tuple(("g", SCALES + r * 16 + blk * 4 + i) for i in range(4))
             assert tile.get(G.F8_SCL + blk * 256 + r * 4) == want
+    # reciprocal scales: rows r, r + 1 (r even) of block blk as bf16 (hi, lo)
+    # pairs at F8_INV + 256 blk + 16 (r / 4) + 8 ((r % 4) / 2): the hi pair is
+    # formed from the two rows' own scales (zeroed past the valid rows), the
+    # lo pair from the same scales and the hi pair
+    for blk in range(4):
+        for r in range(0, 64, 2):
+            at = G.F8_INV + blk * 256 + 16 * (r // 4) + 8 * ((r % 4) // 2)
+            hi, lo = tile.get(at), tile.get(at + 4)
+            assert hi is not None and lo is not None, (blk, r)
+            assert hi[:2] == ("op", "v_cvt_pk_bf16_f32") and lo[:2] == ("op", "v_cvt_pk_bf16_f32")
+            for k, row in enumerate((r, r + 1)):
+                want = _leaves(("g", SCALES + row * 16 + blk * 4 + i) for i in range(4)) if row < valid \
+                    else {ZERO}
+                assert _leaves(hi[2 + k]) == want, (blk, row, hi)
+                assert want <= _leaves(lo[2 + k]), (blk, row, lo)

@@ -17,7 +17,6 @@ from mla_inputs import make_inputs
 from oracle import mla_oracle as O
 
 import emu_decode as ED
-from partial_format import concentrated_bound
 
 OUT_TOL, LSE_TOL = 1e-2, 1e-3
 
@@ -34,9 +33,12 @@ def _check(inp, splits, out_tol=OUT_TOL, seed=3, ref=None):
     assert np.all(np.isfinite(out))
     neg = np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(lse), neg)
-    assert np.max(np.abs(out - ref_out)) <= out_tol
-    if (~neg).any():
-        assert np.max(np.abs(lse[~neg] - ref_lse[~neg])) <= LSE_TOL
+    e_out = np.max(np.abs(out - ref_out))
+    e_lse = np.max(np.abs(lse[~neg] - ref_lse[~neg])) if (~neg).any() else 0.0
+    print(f"[emu] {inp.cache_dtype} B={inp.batch} S_q={inp.s_q} splits={splits}: "
+          f"max err out {e_out:.2e} lse {e_lse:.2e}")
+    assert e_out <= out_tol
+    assert e_lse <= LSE_TOL
 
 
 @pytest.mark.parametrize("splits", [1, 4])
@@ -114,17 +116,16 @@ def test_fp8_restart_path():
     for j in (150, 295):
         page = int(inp.block_table[0, j // 64])
         inp.cache_rope[page, j % 64] = (inp.q_rope[0, 0, 0].float() * 48.0).to(torch.bfloat16)
-    _check(inp, 1, out_tol=concentrated_bound(inp, O))
+    _check(inp, 1)
 
 
 def test_fp8_empty_sequences_and_nan_tails():
+    # token 1 of the 33-row sequence gives one row 93% of its softmax: each
+    # latent block is normalised by its own rounded weights, so the rounding of
+    # P * scale to bf16 cannot move that row's share (0.0123 when the kernel
+    # divided by the exact sum)
     inp = _small([0, 1, 33, 70], s_q=2, seed=4, cache="fp8_e4m3")
     ref = O.mla_decode(inp)
-    # token 1 of the 33-row sequence gives one row 93% of its softmax: the bf16
-    # rounding of P * scale (relative 2^-8) then bounds the output error by
-    # 2^-8 max|c| rather than 1e-2 (the kernel's 0.0123 is exactly what that
-    # rounding gives in numpy)
-    tol = max(OUT_TOL, concentrated_bound(inp, O))
     for b in range(inp.batch):
         L = int(inp.seq_lens[b])
         if L % 64:
@@ -133,7 +134,7 @@ def test_fp8_empty_sequences_and_nan_tails():
             inp.cache_scales[page, L % 64:, :] = float("nan")
             inp.cache_rope[page, L % 64:, :] = float("nan")
     for splits in (1, 4):
-        _check(inp, splits, out_tol=tol, ref=ref)
+        _check(inp, splits, ref=ref)
 
 
 def _run_tiny(body, lds=0):
