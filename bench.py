@@ -8,6 +8,11 @@ synthetic and already resident in HBM when the timed region starts; the
 latent cache and queries are rotated over enough copies that the 256 MB
 Infinity Cache cannot serve them from one step to the next.
 
+The headline workload (default: the MTP batch, B=128 with two query tokens
+over 4096..8192 cached rows, the largest of the five) gives `value`; every
+other workload is timed the same way in the same run and reported under
+config.workloads, so that one run measures all five.
+
 Prints one JSON line (see --help).  --gpus above 1 is refused: this build
 runs on one GPU.
 """
@@ -20,8 +25,6 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -29,7 +32,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
 FLOP_PER_QROW_ROW = 2 * 128 * 576 + 2 * 128 * 512   # scores + output per (query token, cache row)
-DEFAULT_WORKLOAD = "batched_b32_l1k_4k"
+DEFAULT_WORKLOAD = "mtp_b128_sq2_l4k_8k"
+ALL_WORKLOADS = ("single_b1_l128", "batched_b32_l1k_4k", "paged_b64_l256_32k", "mtp_b128_sq2_l4k_8k",
+                 "fp8_b4_l128k")
 
 
 def row_bytes(cache_dtype: str) -> int:
@@ -39,7 +44,8 @@ def row_bytes(cache_dtype: str) -> int:
 
 def algorithmic_work(inp):
     """Bytes the method must move and MFMA flops it must do for one step."""
-    lens = inp.seq_lens.to(dtype=__import__("torch").int64)
+    import torch
+    lens = inp.seq_lens.to(dtype=torch.int64)
     rows = int(lens.sum())
     qrows = inp.batch * inp.s_q * 128
     nbytes = rows * row_bytes(inp.cache_dtype) + qrows * 576 * 2 + qrows * (512 + 1) * 4
@@ -49,6 +55,17 @@ def algorithmic_work(inp):
         vis += int((lens - inp.s_q + s + 1).clamp(min=0).sum())
     flops = vis * FLOP_PER_QROW_ROW
     return rows, nbytes, flops
+
+
+def binding_bound(nbytes, flops):
+    intensity = flops / nbytes
+    return "hbm" if intensity < (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+
+def roofline_frac(bound, nbytes, flops, seconds):
+    if bound == "hbm":
+        return nbytes / seconds / 1e9 / HBM_PEAK_GBS
+    return flops / seconds / 1e12 / MFMA_BF16_PEAK_TFLOPS
 
 
 def measured_traffic(workload: str):
@@ -79,6 +96,17 @@ def kernels_sha256() -> str:
     return hashlib.sha256((g.kernel(False) + g.kernel(True)).encode()).hexdigest()
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(inp, budget_s: float):
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences in order (repeating the batch if it ends first) until about
@@ -102,58 +130,35 @@ def cpu_baseline(inp, budget_s: float):
     dt = time.perf_counter() - t0
     passes = f", {done / inp.batch:.1f} passes over the batch" if done > inp.batch else ""
     return {"value": rows / dt, "unit": "cache-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{min(done, inp.batch)} of {inp.batch} sequences{passes} ({rows} cache rows, all heads "
                       f"and query tokens), {dt:.1f} s, numpy fp64 on the host"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--num-splits", type=int, default=0, help="0: the library's hint")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (20 times), to scale HBM counters")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
-              "described, not built", file=sys.stderr)
-        return 2
-
+def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: int = 0):
+    """Time `steps` decode steps (decode + combine) and `steps` decode
+    launches alone on one stream with HIP events; returns a dict."""
     import torch
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(20):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}))
-        return 0
+
     import mla_latent_kv_39_amd as mla
     from mla_latent_kv_39_amd.runner import DecodeWorkspace
     from mla_inputs import make_inputs
 
-    print(f"[bench] generating {args.workload} (seed {args.seed})", file=sys.stderr, flush=True)
-    inp = make_inputs(args.workload, seed=args.seed)
+    print(f"[bench] generating {workload} (seed {seed})", file=sys.stderr, flush=True)
+    inp = make_inputs(workload, seed=seed)
     rows, nbytes, flops = algorithmic_work(inp)
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    # the partition count only changes how the work is cut (the merge is exact): fill the GPU
-    splits = args.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q, inp.max_blocks)
+    # the partition count only changes how the work is cut (the merge is exact):
+    # the workload's own, else the library's hint that fills the GPU
+    splits = num_splits or inp.num_splits or mla.mla_num_splits_hint(0, inp.batch, inp.s_q, inp.max_blocks)
 
     # rotate enough copies of cache + queries that the MALL cannot hold them across steps
     footprint = inp.cache.numel() * inp.cache.element_size() + inp.q_absorbed.numel() * 2 + inp.q_rope.numel() * 2
     if inp.cache_scales is not None:
         footprint += inp.cache_scales.numel() * 4 + inp.cache_rope.numel() * 2
     copies = 1 if footprint > 2 * MALL_BYTES else int(math.ceil((1 << 30) / footprint)) + 1
-    print(f"[bench] rows={rows} bytes={nbytes/1e6:.1f}MB flops={flops/1e9:.1f}G splits={splits} copies={copies}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {workload}: rows={rows} bytes={nbytes/1e6:.1f}MB flops={flops/1e9:.1f}G splits={splits} "
+          f"copies={copies}", file=sys.stderr, flush=True)
     sets = []
     for _ in range(copies):
         if inp.cache_dtype == "bf16":
@@ -176,53 +181,118 @@ def main(argv=None):
         decode(i)
         mla.mla_combine(ws.partial_out, ws.partial_lse, seq_lens, splits, ws.out, ws.lse, stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # whole steps
+    # whole steps; the events are recorded on the stream the kernels run on
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = e0.elapsed_time(e1) / steps
     # the dominant kernel alone, same launches back to back
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         decode(i)
     k1.record(stream)
     torch.cuda.synchronize()
-    ms_decode = k0.elapsed_time(k1) / args.steps
-    print(f"[bench] step {ms_step*1e3:.1f} us, decode kernel {ms_decode*1e3:.1f} us", file=sys.stderr, flush=True)
+    ms_decode = k0.elapsed_time(k1) / steps
+    del sets, ws
+    torch.cuda.empty_cache()
+    bound = binding_bound(nbytes, flops)
+    res = {"workload": workload, "inp": inp, "rows": rows, "bytes": nbytes, "flops": flops, "splits": splits,
+           "copies": copies, "ms_step": ms_step, "ms_decode": ms_decode, "bound": bound,
+           "frac_decode": roofline_frac(bound, nbytes, flops, ms_decode * 1e-3),
+           "frac_step": roofline_frac(bound, nbytes, flops, ms_step * 1e-3)}
+    print(f"[bench] {workload}: step {ms_step*1e3:.1f} us, decode kernel {ms_decode*1e3:.1f} us, "
+          f"{bound}-bound fraction {res['frac_decode']:.3f} (decode) {res['frac_step']:.3f} (step)",
+          file=sys.stderr, flush=True)
+    return res
 
-    value = rows / (ms_step * 1e-3)
-    intensity = flops / nbytes
-    bound = "hbm" if intensity < (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
-    if bound == "hbm":
+
+def summary(r):
+    """The per-workload record of config.workloads."""
+    s = r["ms_step"] * 1e-3
+    return {"step_us": round(r["ms_step"] * 1e3, 2), "decode_us": round(r["ms_decode"] * 1e3, 2),
+            "combine_us_est": round((r["ms_step"] - r["ms_decode"]) * 1e3, 2),
+            "cache_tokens_per_s": round(r["rows"] / s, 1), "step_gbs": round(r["bytes"] / s / 1e9, 1),
+            "step_tflops": round(r["flops"] / s / 1e12, 1), "bound": r["bound"],
+            "frac_decode": round(r["frac_decode"], 4), "frac_step": round(r["frac_step"], 4),
+            "num_splits": r["splits"], "cache_dtype": r["inp"].cache_dtype, "rows": r["rows"],
+            "algorithmic_bytes": r["bytes"], "mfma_flops": r["flops"],
+            "decode_traffic_bytes": measured_traffic(r["workload"])}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="the headline workload")
+    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--num-splits", type=int, default=0, help="0: the workload's, else the library's hint")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (20 times), to scale HBM counters")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
+              "described, not built", file=sys.stderr)
+        return 2
+
+    import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}))
+        return 0
+    torch.cuda.set_device(0)
+
+    head = measure(args.workload, args.steps, args.warmup, args.num_splits, args.seed)
+    others = {}
+    if not args.only:
+        for w in ALL_WORKLOADS:
+            if w != args.workload:
+                others[w] = summary(measure(w, args.steps, args.warmup, 0, args.seed))
+    inp = head["inp"]
+    ms_step, ms_decode = head["ms_step"], head["ms_decode"]
+    nbytes, flops = head["bytes"], head["flops"]
+    if head["bound"] == "hbm":
         achieved = nbytes / (ms_decode * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         achieved = flops / (ms_decode * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(head["frac_decode"], 4)
     roof["traffic"] = measured_traffic(args.workload)
+    roof["step_frac"] = round(head["frac_step"], 4)
+    workloads = {args.workload: summary(head), **others}
     result = {
         "metric": "MLA decode cache-tokens/s and achieved HBM GB/s (% of roofline), 1 MI355X",
-        "value": round(value, 1), "unit": "cache-tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "value": round(head["rows"] / (ms_step * 1e-3), 1), "unit": "cache-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        # the arithmetic: bf16 MFMA with fp32 accumulation; an e4m3 cache is widened exactly to bf16
+        "dtype": "bf16" if inp.cache_dtype == "bf16" else "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": inp.batch, "s_q": inp.s_q, "cache_rows": rows,
+        "config": {"workload": args.workload, "batch": inp.batch, "s_q": inp.s_q, "cache_rows": head["rows"],
                    "layout": "contiguous" if inp.block_table is None else "paged64",
-                   "cache_dtype": inp.cache_dtype, "num_splits": splits, "rotated_copies": copies,
+                   "cache_dtype": inp.cache_dtype, "num_splits": head["splits"], "rotated_copies": head["copies"],
                    "step_gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+                   "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
+                   "query_row_pairs_per_s": round(flops / FLOP_PER_QROW_ROW / (ms_step * 1e-3), 1),
                    "decode_kernel_us": round(ms_decode * 1e3, 2),
-                   "algorithmic_bytes": nbytes, "mfma_flops": flops},
+                   "algorithmic_bytes": nbytes, "mfma_flops": flops, "workloads": workloads},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

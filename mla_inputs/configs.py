@@ -13,6 +13,9 @@ import math
 # inclusive bounds, or ("loguniform", lo, hi): L = floor(exp(U(ln lo, ln hi)))
 # clamped to [lo, hi].  "layout" is "contiguous" ([B, cap, row] with no block
 # table), "paged_shuffled" (a randomly permuted page pool) or "paged_sequential".
+# "num_splits" is the number of work partitions of the whole batch (None: the
+# library's hint for the GPU); the long-context workload's 64 splits per
+# sequence are 4 x 64 = 256 partitions.
 WORKLOADS = {
     "single_b1_l128": dict(
         batch=1, s_q=1, lens=("fixed", 128), layout="contiguous", q_std=1.0,
@@ -32,8 +35,9 @@ WORKLOADS = {
         doc="Two causal query tokens per sequence, B=128, L~U{4096..8192}, paged"),
     "fp8_b4_l128k": dict(
         batch=4, s_q=1, lens=("fixed", 131072), layout="paged_sequential", q_std=1.0,
-        cache="fp8_e4m3", num_splits=64, unabsorbed=False,
-        doc="Long-context decode, B=4, L=131072, e4m3 latent with 1x128 fp32 scales, bf16 RoPE part, 64 splits"),
+        cache="fp8_e4m3", num_splits=256, unabsorbed=False,
+        doc="Long-context decode, B=4, L=131072, e4m3 latent with 1x128 fp32 scales, bf16 RoPE part, "
+            "64 splits of ~2048 rows per sequence (256 work partitions) + LSE combine"),
 }
 
 BLOCK_SIZE = 64          # rows per cache page

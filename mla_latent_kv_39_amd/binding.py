@@ -53,7 +53,7 @@ class LatentCacheDesc(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmla.so is not built at {LIB_PATH}; run __graft_entry__.build() "
-                          "or python -m mla_latent_kv_39_amd.build_lib")
+                          "or python mla_latent_kv_39_amd/build_lib.py")
     # torch first: its HIP runtime is then the one libmla.so binds to.  Loaded
     # the other way round the process holds two HIP runtimes, and the tensors
     # of one are not valid in the other.

@@ -1,6 +1,6 @@
 """Build libmla.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m mla_latent_kv_39_amd.build_lib   (or call build()).
+Usage: python mla_latent_kv_39_amd/build_lib.py   (or __graft_entry__.build()).
 """
 from __future__ import annotations
 
