@@ -174,12 +174,12 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: i
 
     def decode(i):
         qa, qr, cache = sets[i % copies]
-        mla.mla_decode(qa, qr, cache, table, seq_lens, inp.scale, splits, ws.partial_out, ws.partial_lse,
-                       ws.out, ws.lse, max_blocks_per_seq=inp.max_blocks, stream=stream)
+        mla.mla_decode(qa, qr, cache, table, seq_lens, inp.scale, ws.out, ws.lse, ws.partial_out, ws.partial_lse,
+                       stream=stream)
 
     def step(i):
         decode(i)
-        mla.mla_combine(ws.partial_out, ws.partial_lse, seq_lens, splits, ws.out, ws.lse, stream=stream)
+        mla.mla_combine(ws.partial_out, ws.partial_lse, seq_lens, ws.out, ws.lse, stream=stream)
 
     for i in range(warmup):
         step(i)

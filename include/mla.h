@@ -17,20 +17,27 @@
  *     out      = sum_j exp(z_j - lse) c^KV_j              (512 values)
  *     n        = seq_len[b] - S_q + s + 1
  *
- * scale is normally 1/sqrt(d_h + d_h^R) = 1/sqrt(192) (§2.1.3(D)).  With two
- * query tokens (MTP speculative decoding, DeepSeek-V3 详解 §3.3) seq_len counts
- * both new rows and token 0 does not see token 1's row.
+ * scale is normally 1/sqrt(d_h + d_h^R) = 1/sqrt(192) (§2.1.3(D)).  With
+ * several query tokens (MTP speculative decoding, DeepSeek-V3 详解 §3.3)
+ * seq_len counts every new row and token s does not see the rows of the
+ * tokens after it.
  *
  * Conventions for every entry point:
- *   - Tensor arguments are device pointers to densely packed row-major arrays;
- *     the caller allocates and owns them.  Nothing is allocated, freed or
- *     synchronised inside the library; all work is enqueued on `stream`.
- *   - Arguments are validated on the host before any launch; a failed check
- *     returns an error status and enqueues nothing.  The contents of device
- *     arrays (seq_lens, block_table) are the caller's contract and are not
- *     read on the host.
+ *   - Tensors are passed as mla_tensor descriptors (device pointer, dtype,
+ *     rank, shape, strides in elements).  They must be densely packed
+ *     row-major; the caller allocates and owns them.  Nothing is allocated,
+ *     freed or synchronised inside the calls; all work is enqueued on `stream`.
+ *   - Every descriptor is validated on the host before any launch: dtypes
+ *     (MLA_ERR_DTYPE), ranks, shapes, strides, the head count 128 and the
+ *     widths 512 / 64 / 576 (MLA_ERR_SHAPE), missing pointers (MLA_ERR_NULL).
+ *     A failed check returns its status and enqueues nothing.  The contents
+ *     of device arrays (seq_lens, block_table) are the caller's contract and
+ *     are not read on the host; mla_check_indices checks them on the device.
  *   - Calls on different streams may run concurrently as long as their output
- *     and partial buffers do not overlap.
+ *     and workspace buffers do not overlap.
+ *   - State: the library keeps, per device, the handle of its code object
+ *     (loaded by mla_init or on the first call on that device, never
+ *     unloaded, read-only afterwards) and whether the device is a gfx950.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -50,94 +57,113 @@ extern "C" {
 #define MLA_BLOCK_SIZE 64   /* rows per cache page */
 #define MLA_FP8_GROUP 128   /* latent values per fp8 scale */
 #define MLA_MAX_SPLITS 65536
+#define MLA_MAX_RANK 5
 
 typedef enum mla_status {
   MLA_OK = 0,
-  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
-  MLA_ERR_DTYPE = 2,       /* unsupported cache dtype */
-  MLA_ERR_SHAPE = 3,       /* inconsistent or out-of-range sizes */
-  MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q > 2) */
+  MLA_ERR_NULL = 1,        /* a required descriptor or its data pointer is NULL */
+  MLA_ERR_DTYPE = 2,       /* a tensor has the wrong element type */
+  MLA_ERR_SHAPE = 3,       /* rank, shape or strides inconsistent; H != 128; widths != 512/64/576 */
+  MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q = 3, block size 32) */
   MLA_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
   MLA_ERR_DEVICE = 6       /* the current device is not gfx950 or cannot be queried */
 } mla_status;
 
-typedef enum mla_cache_dtype {
-  MLA_CACHE_BF16 = 0,     /* rows: bf16 [num_blocks, 64, 576]                        */
-  MLA_CACHE_FP8_E4M3 = 1  /* rows: OCP e4m3 bytes [num_blocks, 64, 512];
-                             scales: fp32 [num_blocks, 64, 4], one per 128 latent values;
-                             rope: bf16 [num_blocks, 64, 64]                            */
-} mla_cache_dtype;
+typedef enum mla_dtype {
+  MLA_DTYPE_BF16 = 0,
+  MLA_DTYPE_FP32 = 1,
+  MLA_DTYPE_INT32 = 2,
+  MLA_DTYPE_FP8_E4M3 = 3,  /* OCP E4M3 (e4m3fn) bytes: no infinity, 0x7F / 0xFF are NaN, max 448 */
+  MLA_DTYPE_UINT8 = 4      /* raw bytes (the partial_out workspace) */
+} mla_dtype;
+
+/* A device tensor: element (i0, i1, ..) sits at data + sum_k i_k * strides[k]
+ * elements.  Only densely packed row-major tensors are accepted (the stride
+ * of a dimension of size 1 is not checked). */
+typedef struct mla_tensor {
+  void* data;
+  int32_t dtype;                 /* mla_dtype */
+  int32_t rank;                  /* 1 .. MLA_MAX_RANK */
+  int64_t shape[MLA_MAX_RANK];
+  int64_t strides[MLA_MAX_RANK]; /* in elements */
+} mla_tensor;
 
 /*
- * The latent cache.  Row j of sequence b is slot (j % 64) of page
- * block_table[b * max_blocks_per_seq + j / 64].  Without a block table the cache
- * is contiguous: [batch, max_blocks_per_seq * 64, .], i.e. page b *
- * max_blocks_per_seq + j / 64.  fp8 rows dequantize as e4m3(byte) * scale
- * (fine-grained 1x128 scaling, DeepSeek-V3 详解 §4.2; E4M3 range about 448,
- * 拆解DeepSeek V3, kongchang.com, "MLA 与 FP8").  Page slots past a sequence's
- * end are never read into the result: they may hold any bits, NaN included.
+ * The latent cache, in 64-row pages.  Row j of sequence b is slot (j % 64) of
+ * page block_table[b][j / 64].  Without a block table the cache is
+ * contiguous: page b * max_blocks + j / 64, where max_blocks = NB / B; rows
+ * given as [B, L_cap, .] with L_cap a multiple of 64 are read the same way.
+ *
+ *   bf16 cache:  rows   bf16 [NB, 64, 576]   (c^KV then k^R), scales / rope data NULL
+ *   e4m3 cache:  rows   e4m3 [NB, 64, 512]   (c^KV codes)
+ *                scales fp32 [NB, 64, 4]     one per 128 latent values
+ *                rope   bf16 [NB, 64, 64]    k^R
+ *
+ * e4m3 rows dequantize as e4m3(byte) * scale (fine-grained 1x128 scaling,
+ * DeepSeek-V3 详解 §4.2; E4M3 range about 448, 拆解DeepSeek V3,
+ * kongchang.com, "MLA 与 FP8"); scales must be positive normal numbers.
+ * Page slots past a sequence's end are never read into the result: they may
+ * hold any bits, NaN included.
  */
 typedef struct mla_latent_cache {
-  int32_t dtype;        /* mla_cache_dtype */
-  int32_t block_size;   /* must be MLA_BLOCK_SIZE */
-  int64_t num_blocks;   /* pages in the pool (for bounds on the host side) */
-  const void* rows;     /* see mla_cache_dtype */
-  const float* scales;  /* fp8 only, else NULL */
-  const void* rope;     /* fp8 only, else NULL */
+  mla_tensor rows;
+  mla_tensor scales;
+  mla_tensor rope;
 } mla_latent_cache;
 
 /*
  * mla_decode: the split-KV decode kernel.
  *
- *   q_absorbed   bf16  [batch, s_q, 128, 512]   W^UK^T q^C per head
- *   q_rope       bf16  [batch, s_q, 128, 64]    rotated q^R per head
- *   cache        host pointer to the cache descriptor above
- *   block_table  int32 [batch, max_blocks_per_seq], device; NULL = contiguous
- *   seq_lens     int32 [batch], device; requires s_q <= seq_len <= max_blocks_per_seq*64
- *   scale        score scale (1/sqrt(192) for DeepSeek-V3)
- *   num_splits   number of work partitions the rows of the whole batch are cut
- *                into: a power of two P, 1 .. MLA_MAX_SPLITS.  The rows of all
- *                sequences, in 64-row pages (units; a sequence owns
- *                max(1, ceil(seq_len / 64)) of them), are dealt out in order,
- *                so one partition can cover the tail of one sequence, whole
- *                sequences and the head of another.  The shares are equal in
- *                cost rather than in units: every sequence also weighs 3
- *                units (its fixed cost), placed before its pages, so unit j of
- *                sequence b sits at position u0(b) + 3 (b + 1) + j (u0(b): the
- *                units of the sequences before it), and partition p takes the
- *                units whose positions lie in [floor(p W / P),
- *                floor((p + 1) W / P)), W = total units + 3 batch.
- *                mla_num_splits_hint() gives one for the device and the cache size.
- *   partial_out  workspace of mla_partial_out_bytes(num_splits, s_q) bytes,
- *                16-byte aligned; may be NULL if num_splits == 1 (layout below)
- *   partial_lse  fp32 [num_splits, 2, s_q, 128]        may be NULL if num_splits == 1
- *   out_latent   fp32 [batch, s_q, 128, 512]
- *   lse          fp32 [batch, s_q, 128]
+ *   q_absorbed   bf16  [B, S_q, 128, 512]   W^UK^T q^C per head
+ *   q_rope       bf16  [B, S_q, 128, 64]    rotated q^R per head
+ *   cache        the latent cache above (host pointer to the descriptors)
+ *   block_table  int32 [B, max_blocks]; NULL (or data NULL) = contiguous cache
+ *   seq_lens     int32 [B]; requires 0 <= seq_len <= max_blocks * 64
+ *   scale        score scale (1/sqrt(192) for DeepSeek-V3), finite
+ *   out_latent   fp32  [B, S_q, 128, 512]
+ *   lse          fp32  [B, S_q, 128]
+ *   partial_out  uint8 [mla_partial_out_bytes(P, S_q)] (or larger), 16-byte aligned
+ *   partial_lse  fp32  [P, 2, S_q, 128]
  *
- * partial_out layout.  First num_splits * 2 * s_q blocks (split, slot, token)
- * of 128 x 512 fp16 values (131,072 bytes each), then, for the same blocks in
- * the same order, 512 fp32 descales each (2,048 bytes).  A block is four
- * groups of 32 heads, 16384 values each, in the order the kernels' lanes hold
- * them: the value of head 32 j + 16 a + r (a < 2, r < 16) and latent column
+ * S_q is 1, 2 or 4 (MLA_ERR_UNSUPPORTED otherwise).  The split count P is the
+ * leading dimension of partial_lse (P = 1 when partial_lse is NULL): a power
+ * of two, 1 .. MLA_MAX_SPLITS, the number of work partitions the rows of the
+ * whole batch are cut into.  The rows of all sequences, in 64-row pages
+ * (units; a sequence owns max(1, ceil(seq_len / 64)) of them), are dealt out
+ * in order, so one partition can cover the tail of one sequence, whole
+ * sequences and the head of another.  The shares are equal in cost rather
+ * than in units: every sequence also weighs 3 units (its fixed cost), placed
+ * before its pages, so unit j of sequence b sits at position
+ * u0(b) + 3 (b + 1) + j (u0(b): the units of the sequences before it), and
+ * partition p takes the units whose positions lie in [floor(p W / P),
+ * floor((p + 1) W / P)), W = total units + 3 B.  mla_num_splits_hint() gives
+ * a P for the device and the cache size.
+ *
+ * partial_out layout (a workspace: fp16 halves the bytes of fp32 partials
+ * at a rounding of 2^-11 of the largest value, under the 2^-8 of the bf16
+ * probabilities).  First P * 2 * S_q blocks (split, slot, token) of 128 x 512
+ * fp16 values (131,072 bytes each), then, for the same blocks in the same
+ * order, 512 fp32 descales each (2,048 bytes).  A block is four groups of 32
+ * heads, 16384 values each, in the order the kernels' lanes hold them: the
+ * value of head 32 j + 16 a + r (a < 2, r < 16) and latent column
  * 16 c + 4 g + i (c < 32, g < 4, i < 4) sits at index
  * 16384 j + 8 (64 c + 16 g + r) + 4 a + i of its block, and its descale d at
  * index 128 (c / 8) + 32 j + 2 r + a of the block's descales.  The partial
  * output is the fp16 value times d; d is a power of two chosen per (block,
  * column quarter c / 8, head) so that the largest |value| lies in
  * [2^14, 2^15) (d no smaller than 2^-90): 11 significant bits for every
- * element that matters.
- * partial_lse is plain [.., head] fp32.
+ * element that matters.  partial_lse is plain [split, slot, token, head].
  *
  * A sequence whose rows all fall into one partition gets its final out_latent
  * and lse here.  A sequence cut across partitions leaves one normalised partial
  * (out_s, lse_s) per partition it touches; mla_combine then writes its final
- * result.  Always call mla_combine with the same arguments after mla_decode.
- * A query that sees no row (seq_len < s_q) gets out = 0 and lse = -inf.
+ * result.  Always call mla_combine with the same partials after mla_decode.
+ * A query that sees no row (seq_len < S_q) gets out = 0 and lse = -inf.
  */
-mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_latent_cache* cache,
-                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, void* partial_out,
-                      float* partial_lse, float* out_latent, float* lse, hipStream_t stream);
+mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                      const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                      const mla_tensor* out_latent, const mla_tensor* lse, const mla_tensor* partial_out,
+                      const mla_tensor* partial_lse, hipStream_t stream);
 
 /*
  * mla_combine: merge the per-partition partials of every sequence that
@@ -145,26 +171,48 @@ mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_late
  *     LSE = log sum_s exp(lse_s),   out = sum_s exp(lse_s - LSE) out_s,
  * an exact identity of the softmax over the union of the partitions' rows.
  * A partial with lse_s = -inf has weight 0.  Sequences that mla_decode already
- * finished are left untouched.  seq_lens, batch, s_q and num_splits must equal
- * those of the preceding mla_decode (they rebuild the same partition map).
+ * finished are left untouched.  The split count is partial_lse's leading
+ * dimension; seq_lens and the partials must be those of the preceding
+ * mla_decode (they rebuild the same partition map).  With P = 1 there is
+ * nothing to merge: no launch, partials may be NULL.
  */
-mla_status mla_combine(const void* partial_out, const float* partial_lse, const int32_t* seq_lens,
-                       int32_t batch, int32_t s_q, int32_t num_splits, float* out_latent, float* lse,
-                       hipStream_t stream);
+mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_lse, const mla_tensor* seq_lens,
+                       const mla_tensor* out_latent, const mla_tensor* lse, hipStream_t stream);
 
 /*
- * A num_splits for mla_decode (0 on error): one work partition per compute
- * unit of `device` (per two with s_q = 2), halved while the cache capacity
- * the block table allows, batch * max_blocks_per_seq pages plus 3 units per
- * sequence of fixed cost, would leave fewer than 4 units per partition: short
- * contexts then stay in few partitions and need little or no merging.
- * max_blocks_per_seq <= 0 means unknown (no cap).
+ * A split count P for mla_decode (0 on error): one work partition per compute
+ * unit of `device` (per two with s_q = 2, per four with s_q = 4), halved while
+ * the cache capacity the block table allows, batch * max_blocks_per_seq pages
+ * plus 3 units per sequence of fixed cost, would leave fewer than 4 units per
+ * partition: short contexts then stay in few partitions and need little or no
+ * merging.  max_blocks_per_seq <= 0 means unknown (no cap).
  */
 int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t max_blocks_per_seq);
 
-/* Bytes of partial_out and partial_lse needed for (num_splits, s_q). */
+/* Bytes of partial_out and partial_lse needed for (split count, s_q). */
 size_t mla_partial_out_bytes(int32_t num_splits, int32_t s_q);
 size_t mla_partial_lse_bytes(int32_t num_splits, int32_t s_q);
+
+/*
+ * mla_check_indices: the device-side contract of mla_decode, checked on the
+ * device (the host never reads seq_lens or block_table).  Enqueues one small
+ * kernel on `stream` that writes into counts (int32 [2], device):
+ *   counts[0] = sequences with seq_len < 0 or seq_len > max_blocks * 64,
+ *   counts[1] = block-table entries of pages a sequence uses (j < ceil(seq_len/64))
+ *               that are not in [0, NB).
+ * Both zero means mla_decode reads only inside the cache.  Same descriptors
+ * as mla_decode (only their shapes are used, plus the table and lengths).
+ */
+mla_status mla_check_indices(const mla_latent_cache* cache, const mla_tensor* block_table,
+                             const mla_tensor* seq_lens, const mla_tensor* counts, hipStream_t stream);
+
+/*
+ * mla_init: load the library's code object on `device` now (otherwise the
+ * first call on the device does it).  Idempotent and thread-safe.  A caller
+ * that must not see the load inside a later call (graph capture, a serving
+ * loop) calls it once at set-up.
+ */
+mla_status mla_init(int32_t device);
 
 /* Static text for a status code. */
 const char* mla_status_string(mla_status status);

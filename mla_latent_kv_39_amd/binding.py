@@ -1,9 +1,11 @@
 """ctypes binding of libmla (include/mla.h): argument marshalling only.
 
 Every step of the decode runs in the HIP kernels of libmla.so; this module
-turns torch tensors into the pointers and sizes of the C ABI and raises
-MlaError on a non-OK status.  Importing it fails loudly when the library has
-not been built.
+turns torch tensors into the mla_tensor descriptors of the C ABI and raises
+MlaError on a non-OK status.  Shapes, dtypes and strides are checked by the
+library itself; the binding only makes sure that what it hands over is device
+memory (a host pointer would reach the GPU).  Importing it fails loudly when
+the library has not been built.
 """
 from __future__ import annotations
 
@@ -24,6 +26,14 @@ MLA_ERR_UNSUPPORTED = 4
 MLA_ERR_LAUNCH = 5
 MLA_ERR_DEVICE = 6
 
+# element types (mla_dtype)
+MLA_DTYPE_BF16 = 0
+MLA_DTYPE_FP32 = 1
+MLA_DTYPE_INT32 = 2
+MLA_DTYPE_FP8_E4M3 = 3
+MLA_DTYPE_UINT8 = 4
+
+# latent cache kinds of LatentCache
 MLA_CACHE_BF16 = 0
 MLA_CACHE_FP8_E4M3 = 1
 
@@ -32,10 +42,11 @@ LATENT_DIM = 512
 ROPE_DIM = 64
 ROW_DIM = 576
 BLOCK_SIZE = 64
+MAX_RANK = 5
 
 # every symbol include/mla.h declares
 EXPORTED_SYMBOLS = ("mla_decode", "mla_combine", "mla_num_splits_hint", "mla_partial_out_bytes",
-                    "mla_partial_lse_bytes", "mla_status_string", "mla_version")
+                    "mla_partial_lse_bytes", "mla_check_indices", "mla_init", "mla_status_string", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -44,10 +55,15 @@ class MlaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)} (status {status})")
 
 
-class LatentCacheDesc(ctypes.Structure):
+class MlaTensor(ctypes.Structure):
+    """Mirror of struct mla_tensor."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * MAX_RANK), ("strides", ctypes.c_int64 * MAX_RANK)]
+
+
+class MlaLatentCache(ctypes.Structure):
     """Mirror of struct mla_latent_cache."""
-    _fields_ = [("dtype", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
-                ("rows", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rope", ctypes.c_void_p)]
+    _fields_ = [("rows", MlaTensor), ("scales", MlaTensor), ("rope", MlaTensor)]
 
 
 def _load():
@@ -60,11 +76,15 @@ def _load():
     import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    T, C = ctypes.POINTER(MlaTensor), ctypes.POINTER(MlaLatentCache)
     lib.mla_decode.restype = i32
-    lib.mla_decode.argtypes = [vp, vp, ctypes.POINTER(LatentCacheDesc), vp, i32, vp, i32, i32, f32, i32,
-                               vp, vp, vp, vp, vp]
+    lib.mla_decode.argtypes = [T, T, C, T, T, f32, T, T, T, T, vp]
     lib.mla_combine.restype = i32
-    lib.mla_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.mla_combine.argtypes = [T, T, T, T, T, vp]
+    lib.mla_check_indices.restype = i32
+    lib.mla_check_indices.argtypes = [C, T, T, T, vp]
+    lib.mla_init.restype = i32
+    lib.mla_init.argtypes = [i32]
     lib.mla_num_splits_hint.restype = i32
     lib.mla_num_splits_hint.argtypes = [i32, i32, i32, i32]
     lib.mla_partial_out_bytes.restype = sz
@@ -106,9 +126,41 @@ def mla_partial_lse_bytes(num_splits: int, s_q: int) -> int:
     return int(_lib.mla_partial_lse_bytes(int(num_splits), int(s_q)))
 
 
+def mla_init(device: int = 0) -> None:
+    """Load the library's code object on `device` now (see include/mla.h)."""
+    st = _lib.mla_init(int(device))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_init")
+
+
 # ------------------------------------------------------------------ tensors
-def _ptr(t) -> Optional[int]:
-    return None if t is None else int(t.data_ptr())
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: MLA_DTYPE_BF16, torch.float32: MLA_DTYPE_FP32, torch.int32: MLA_DTYPE_INT32,
+             torch.uint8: MLA_DTYPE_UINT8}
+    if hasattr(torch, "float8_e4m3fn"):
+        codes[torch.float8_e4m3fn] = MLA_DTYPE_FP8_E4M3
+    # any other element type goes through with a code the library rejects (MLA_ERR_DTYPE)
+    return codes.get(t.dtype, 255)
+
+
+def tensor(t, dtype: Optional[int] = None, device_only: bool = True) -> MlaTensor:
+    """The mla_tensor of a torch tensor (None -> an empty descriptor).  dtype
+    overrides the element type code (e4m3 codes held in a uint8 tensor)."""
+    d = MlaTensor()
+    if t is None:
+        return d
+    if device_only and t.device.type != "cuda":
+        raise ValueError(f"tensor on {t.device} passed to libmla: device tensors only")
+    if t.dim() > MAX_RANK:
+        raise ValueError(f"rank {t.dim()} above {MAX_RANK}")
+    d.data = int(t.data_ptr()) or None
+    d.dtype = _dtype_code(t) if dtype is None else int(dtype)
+    d.rank = t.dim()
+    for k in range(t.dim()):
+        d.shape[k] = int(t.shape[k])
+        d.strides[k] = int(t.stride(k))
+    return d
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -120,25 +172,16 @@ def _stream_handle(stream) -> Optional[int]:
     return int(stream.cuda_stream) or None
 
 
-def _need(t, dtype, shape, name):
-    import torch
-    if t is None:
-        raise ValueError(f"{name} is required")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
-    return t
+def _ref(d: MlaTensor):
+    return None if d.data is None and d.rank == 0 else ctypes.byref(d)
 
 
 @dataclass
 class LatentCache:
-    """Device-resident latent cache: bf16 rows [NB, 64, 576], or the fp8 bundle
-    (e4m3 bytes [NB, 64, 512] as uint8, fp32 scales [NB, 64, 4], bf16 rope [NB, 64, 64])."""
+    """Device-resident latent cache: bf16 rows [NB, 64, 576], or the e4m3
+    bundle (codes [NB, 64, 512] as uint8 or float8_e4m3fn, fp32 scales
+    [NB, 64, 4], bf16 rope [NB, 64, 64]).  A contiguous cache (no block table)
+    is [B * max_blocks, 64, .] or [B, L_cap, .]."""
     dtype: int
     rows: object
     scales: object = None
@@ -148,51 +191,43 @@ class LatentCache:
     def num_blocks(self) -> int:
         return int(self.rows.shape[0])
 
-    def desc(self) -> LatentCacheDesc:
-        return LatentCacheDesc(int(self.dtype), int(self.rows.shape[1]), self.num_blocks, _ptr(self.rows),
-                               _ptr(self.scales), _ptr(self.rope))
+    def desc(self) -> MlaLatentCache:
+        c = MlaLatentCache()
+        fp8 = self.dtype == MLA_CACHE_FP8_E4M3
+        c.rows = tensor(self.rows, MLA_DTYPE_FP8_E4M3 if fp8 else None)
+        c.scales = tensor(self.scales)
+        c.rope = tensor(self.rope)
+        return c
 
 
-def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, scale: float, num_splits: int,
-               partial_out, partial_lse, out_latent, lse, max_blocks_per_seq: Optional[int] = None,
-               stream=None) -> None:
-    """Enqueue mla_decode (see include/mla.h) on `stream` (default: torch's current stream)."""
-    import torch
-    B, S = int(q_absorbed.shape[0]), int(q_absorbed.shape[1])
-    _need(q_absorbed, torch.bfloat16, (B, S, NUM_HEADS, LATENT_DIM), "q_absorbed")
-    _need(q_rope, torch.bfloat16, (B, S, NUM_HEADS, ROPE_DIM), "q_rope")
-    _need(seq_lens, torch.int32, (B,), "seq_lens")
-    _need(out_latent, torch.float32, (B, S, NUM_HEADS, LATENT_DIM), "out_latent")
-    _need(lse, torch.float32, (B, S, NUM_HEADS), "lse")
-    if block_table is not None:
-        _need(block_table, torch.int32, tuple(block_table.shape), "block_table")
-        mb = int(block_table.shape[1])
-    else:
-        if max_blocks_per_seq is None:
-            raise ValueError("max_blocks_per_seq is required for a contiguous cache")
-        mb = int(max_blocks_per_seq)
-    if num_splits > 1:
-        _need(partial_out, torch.uint8, (mla_partial_out_bytes(num_splits, S),), "partial_out")
-        _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
-    d = cache.desc()
-    st = _lib.mla_decode(_ptr(q_absorbed), _ptr(q_rope), ctypes.byref(d), _ptr(block_table), mb, _ptr(seq_lens),
-                         B, S, float(scale), int(num_splits), _ptr(partial_out), _ptr(partial_lse),
-                         _ptr(out_latent), _ptr(lse), _stream_handle(stream))
+def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, scale: float, out_latent, lse,
+               partial_out=None, partial_lse=None, stream=None) -> None:
+    """Enqueue mla_decode (see include/mla.h) on `stream` (default: torch's
+    current stream).  The split count is partial_lse's leading dimension (1
+    without partials)."""
+    c = cache.desc()
+    args = [tensor(q_absorbed), tensor(q_rope), c, tensor(block_table), tensor(seq_lens), tensor(out_latent),
+            tensor(lse), tensor(partial_out), tensor(partial_lse)]
+    st = _lib.mla_decode(_ref(args[0]), _ref(args[1]), ctypes.byref(c), _ref(args[3]), _ref(args[4]),
+                         float(scale), _ref(args[5]), _ref(args[6]), _ref(args[7]), _ref(args[8]),
+                         _stream_handle(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode")
 
 
-def mla_combine(partial_out, partial_lse, seq_lens, num_splits: int, out_latent, lse, stream=None) -> None:
+def mla_combine(partial_out, partial_lse, seq_lens, out_latent, lse, stream=None) -> None:
     """Enqueue mla_combine (see include/mla.h)."""
-    import torch
-    B, S = int(out_latent.shape[0]), int(out_latent.shape[1])
-    if int(num_splits) > 1:
-        _need(partial_out, torch.uint8, (mla_partial_out_bytes(num_splits, S),), "partial_out")
-        _need(partial_lse, torch.float32, (num_splits, 2, S, NUM_HEADS), "partial_lse")
-    _need(seq_lens, torch.int32, (B,), "seq_lens")
-    _need(out_latent, torch.float32, (B, S, NUM_HEADS, LATENT_DIM), "out_latent")
-    _need(lse, torch.float32, (B, S, NUM_HEADS), "lse")
-    st = _lib.mla_combine(_ptr(partial_out), _ptr(partial_lse), _ptr(seq_lens), B, S, int(num_splits),
-                          _ptr(out_latent), _ptr(lse), _stream_handle(stream))
+    args = [tensor(partial_out), tensor(partial_lse), tensor(seq_lens), tensor(out_latent), tensor(lse)]
+    st = _lib.mla_combine(*[_ref(a) for a in args], _stream_handle(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_combine")
+
+
+def mla_check_indices(cache: LatentCache, block_table, seq_lens, counts, stream=None) -> None:
+    """Enqueue mla_check_indices: counts (int32 [2], device) <- bad lengths,
+    bad block-table entries."""
+    c = cache.desc()
+    args = [tensor(block_table), tensor(seq_lens), tensor(counts)]
+    st = _lib.mla_check_indices(ctypes.byref(c), *[_ref(a) for a in args], _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_check_indices")

@@ -2574,7 +2574,9 @@ def kernel(fp8=False):
       s_waitcnt_lgkm(0))
     # ------------------------------------------------ workgroup -> (partition, head block)
     plain, mapped = a.new_label("mapplain"), a.new_label("mapdone")
+    # head blocks per partition: a power of two (mask s[T], shift s[T+4])
     a(f"s_sub_u32 s{T}, {s(S_NHB)}, 1",
+      f"s_ff1_i32_b32 s{T + 4}, {s(S_NHB)}",
       f"s_and_b32 s{T + 1}, {s(S_NPART)}, 7",
       f"s_cmp_eq_u32 s{T + 1}, 0",
       f"s_cbranch_scc0 {plain}",
@@ -2583,12 +2585,12 @@ def kernel(fp8=False):
       f"s_and_b32 s{T + 2}, s2, 7",
       f"s_lshr_b32 s{T + 3}, {s(S_NPART)}, 3",
       f"s_mul_i32 s{T + 2}, s{T + 2}, s{T + 3}",
-      f"s_lshr_b32 {s(S_PART)}, s{T + 1}, s{T}",
+      f"s_lshr_b32 {s(S_PART)}, s{T + 1}, s{T + 4}",
       f"s_add_u32 {s(S_PART)}, {s(S_PART)}, s{T + 2}",
       f"s_and_b32 {s(S_HBLK)}, s{T + 1}, s{T}",
       f"s_branch {mapped}")
     a.label(plain)
-    a(f"s_lshr_b32 {s(S_PART)}, s2, s{T}",
+    a(f"s_lshr_b32 {s(S_PART)}, s2, s{T + 4}",
       f"s_and_b32 {s(S_HBLK)}, s2, s{T}")
     a.label(mapped)
     # ------------------------------------------------ partition map

@@ -1,5 +1,5 @@
-// The C ABI of libmla: argument checks on the host, then kernel launches on the
-// caller's stream.  Nothing is allocated, freed or synchronised here.
+// The C ABI of libmla: descriptor checks on the host, then kernel launches on
+// the caller's stream.  Nothing is allocated, freed or synchronised here.
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -14,9 +14,8 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
-mla_status check_device() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+mla_status check_device_id(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
   int state = g_device_ok[dev].load(std::memory_order_relaxed);
   if (state == 0) {
     hipDeviceProp_t prop;
@@ -27,16 +26,120 @@ mla_status check_device() {
   return state == 1 ? MLA_OK : MLA_ERR_DEVICE;
 }
 
-mla_status check_common(int32_t batch, int32_t s_q, int32_t num_splits, const void* partial_out,
-                        const float* partial_lse) {
-  if (batch < 1 || s_q < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SHAPE;
-  if ((num_splits & (num_splits - 1)) != 0) return MLA_ERR_SHAPE;  // partitions are cut with shifts
-  if (s_q > 2) return MLA_ERR_UNSUPPORTED;
-  if (num_splits > 1 && (partial_out == nullptr || partial_lse == nullptr)) return MLA_ERR_NULL;
-  if (num_splits > 1 && ((uintptr_t)partial_out & 15) != 0) return MLA_ERR_SHAPE;  // 16-byte stores
-  // every output index must fit the kernels' size_t arithmetic with room to spare
-  const double out_elems = (double)batch * s_q * MLA_NUM_HEADS * MLA_LATENT_DIM;
-  if (out_elems > 9.0e15) return MLA_ERR_SHAPE;
+mla_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  return check_device_id(dev);
+}
+
+bool present(const mla_tensor* t) { return t != nullptr && t->data != nullptr; }
+
+// dtype, then rank and shape (want[k] < 0: any size >= 1), then dense row-major strides
+mla_status check_tensor(const mla_tensor* t, mla_dtype dtype, int rank, const int64_t* want) {
+  if (!present(t)) return MLA_ERR_NULL;
+  if (t->dtype != dtype) return MLA_ERR_DTYPE;
+  if (t->rank != rank) return MLA_ERR_SHAPE;
+  int64_t expect = 1;
+  for (int k = rank - 1; k >= 0; --k) {
+    const int64_t n = t->shape[k];
+    if (n < 1 || (want[k] >= 0 && n != want[k])) return MLA_ERR_SHAPE;
+    if (n != 1 && t->strides[k] != expect) return MLA_ERR_SHAPE;
+    if (expect > ((int64_t)1 << 52) / n) return MLA_ERR_SHAPE;   // sizes far past any device memory
+    expect *= n;
+  }
+  return MLA_OK;
+}
+
+#define MLA_TRY(x)                    \
+  do {                                \
+    const mla_status st_ = (x);       \
+    if (st_ != MLA_OK) return st_;    \
+  } while (0)
+
+bool supported_tokens(int64_t s_q) { return s_q == 1 || s_q == 2 || s_q == 4; }
+
+// The cache descriptors: kind (bf16 / e4m3), pages NB, and for a contiguous
+// cache the pages per sequence.
+struct CacheView {
+  bool fp8 = false;
+  int64_t num_blocks = 0;     // pages of 64 rows
+  int64_t contig_blocks = 0;  // contiguous layout: pages per sequence
+};
+
+mla_status check_cache(const mla_latent_cache* c, bool paged, int64_t batch, CacheView* v) {
+  if (c == nullptr || !present(&c->rows)) return MLA_ERR_NULL;
+  const mla_tensor& r = c->rows;
+  if (r.dtype == MLA_DTYPE_BF16) {
+    v->fp8 = false;
+  } else if (r.dtype == MLA_DTYPE_FP8_E4M3) {
+    v->fp8 = true;
+  } else {
+    return MLA_ERR_DTYPE;
+  }
+  if (r.rank != 3) return MLA_ERR_SHAPE;
+  const int64_t width = v->fp8 ? MLA_LATENT_DIM : MLA_ROW_DIM;
+  const int64_t lead = r.shape[0], rows = r.shape[1];
+  // page size: 64 rows; a contiguous cache may also come as [B, L_cap, .]
+  if (paged && rows != MLA_BLOCK_SIZE) {
+    return (rows > 0 && (rows & (rows - 1)) == 0) ? MLA_ERR_UNSUPPORTED : MLA_ERR_SHAPE;
+  }
+  if (!paged && (rows < 1 || rows % MLA_BLOCK_SIZE != 0)) return MLA_ERR_SHAPE;
+  const int64_t want[3] = {-1, rows, width};
+  MLA_TRY(check_tensor(&r, (mla_dtype)r.dtype, 3, want));
+  v->num_blocks = lead * (rows / MLA_BLOCK_SIZE);
+  if (!paged) {
+    if (rows == MLA_BLOCK_SIZE) {
+      if (lead % batch != 0) return MLA_ERR_SHAPE;    // [B * max_blocks, 64, .]
+      v->contig_blocks = lead / batch;
+    } else {
+      if (lead != batch) return MLA_ERR_SHAPE;         // [B, L_cap, .]
+      v->contig_blocks = rows / MLA_BLOCK_SIZE;
+    }
+  }
+  if (v->fp8) {
+    const int64_t ws[3] = {lead, rows, MLA_LATENT_DIM / MLA_FP8_GROUP};
+    const int64_t wr[3] = {lead, rows, MLA_ROPE_DIM};
+    MLA_TRY(check_tensor(&c->scales, MLA_DTYPE_FP32, 3, ws));
+    MLA_TRY(check_tensor(&c->rope, MLA_DTYPE_BF16, 3, wr));
+  }
+  return MLA_OK;
+}
+
+// Split count from partial_lse (leading dimension), with both partial buffers checked.
+mla_status check_partials(const mla_tensor* partial_out, const mla_tensor* partial_lse, int64_t s_q,
+                          int32_t* parts) {
+  if (!present(partial_lse)) {
+    *parts = 1;
+    return MLA_OK;    // one partition: every sequence is finished by the decode
+  }
+  const int64_t wl[4] = {-1, 2, s_q, MLA_NUM_HEADS};
+  MLA_TRY(check_tensor(partial_lse, MLA_DTYPE_FP32, 4, wl));
+  const int64_t p = partial_lse->shape[0];
+  if (p > MLA_MAX_SPLITS || (p & (p - 1)) != 0) return MLA_ERR_SHAPE;   // partitions are cut with shifts
+  *parts = (int32_t)p;
+  if (p == 1) return MLA_OK;
+  const int64_t wo[1] = {-1};
+  MLA_TRY(check_tensor(partial_out, MLA_DTYPE_UINT8, 1, wo));
+  if ((size_t)partial_out->shape[0] < mla_partial_out_bytes((int32_t)p, (int32_t)s_q)) return MLA_ERR_SHAPE;
+  if (((uintptr_t)partial_out->data & 15) != 0) return MLA_ERR_SHAPE;  // 16-byte stores
+  return MLA_OK;
+}
+
+// Batch and query tokens from out_latent, with out_latent and lse checked.
+mla_status check_outputs(const mla_tensor* out_latent, const mla_tensor* lse, int64_t* batch, int64_t* s_q) {
+  if (!present(out_latent) || !present(lse)) return MLA_ERR_NULL;
+  if (out_latent->dtype != MLA_DTYPE_FP32) return MLA_ERR_DTYPE;
+  if (out_latent->rank != 4) return MLA_ERR_SHAPE;
+  const int64_t b = out_latent->shape[0], s = out_latent->shape[1];
+  if (b < 1 || s < 1) return MLA_ERR_SHAPE;
+  const int64_t wo[4] = {b, s, MLA_NUM_HEADS, MLA_LATENT_DIM};
+  const int64_t wl[3] = {b, s, MLA_NUM_HEADS};
+  MLA_TRY(check_tensor(out_latent, MLA_DTYPE_FP32, 4, wo));
+  MLA_TRY(check_tensor(lse, MLA_DTYPE_FP32, 3, wl));
+  if (b > INT_MAX / 4) return MLA_ERR_SHAPE;
+  if (!supported_tokens(s)) return MLA_ERR_UNSUPPORTED;
+  *batch = b;
+  *s_q = s;
   return MLA_OK;
 }
 
@@ -44,76 +147,127 @@ mla_status check_common(int32_t batch, int32_t s_q, int32_t num_splits, const vo
 
 extern "C" {
 
-mla_status mla_decode(const void* q_absorbed, const void* q_rope, const mla_latent_cache* cache,
-                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                      int32_t batch, int32_t s_q, float scale, int32_t num_splits, void* partial_out,
-                      float* partial_lse, float* out_latent, float* lse, hipStream_t stream) {
-  if (!q_absorbed || !q_rope || !cache || !seq_lens || !out_latent || !lse) return MLA_ERR_NULL;
-  if (!cache->rows) return MLA_ERR_NULL;
-  mla_status st = check_common(batch, s_q, num_splits, partial_out, partial_lse);
-  if (st != MLA_OK) return st;
-  if (cache->dtype != MLA_CACHE_BF16 && cache->dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_DTYPE;
-  if (cache->dtype == MLA_CACHE_FP8_E4M3 && (!cache->scales || !cache->rope)) return MLA_ERR_NULL;
-  if (cache->block_size != MLA_BLOCK_SIZE) {
-    const int bs = cache->block_size;
-    return (bs > 0 && (bs & (bs - 1)) == 0) ? MLA_ERR_UNSUPPORTED : MLA_ERR_SHAPE;
+mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                      const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                      const mla_tensor* out_latent, const mla_tensor* lse, const mla_tensor* partial_out,
+                      const mla_tensor* partial_lse, hipStream_t stream) {
+  int64_t B = 0, S = 0;
+  MLA_TRY(check_outputs(out_latent, lse, &B, &S));
+  const int64_t wq[4] = {B, S, MLA_NUM_HEADS, MLA_LATENT_DIM};
+  const int64_t wr[4] = {B, S, MLA_NUM_HEADS, MLA_ROPE_DIM};
+  const int64_t wl[1] = {B};
+  MLA_TRY(check_tensor(q_absorbed, MLA_DTYPE_BF16, 4, wq));
+  MLA_TRY(check_tensor(q_rope, MLA_DTYPE_BF16, 4, wr));
+  MLA_TRY(check_tensor(seq_lens, MLA_DTYPE_INT32, 1, wl));
+  const bool paged = present(block_table);
+  int64_t max_blocks = 0;
+  if (paged) {
+    const int64_t wt[2] = {B, -1};
+    MLA_TRY(check_tensor(block_table, MLA_DTYPE_INT32, 2, wt));
+    max_blocks = block_table->shape[1];
   }
-  if (max_blocks_per_seq < 1 || cache->num_blocks < 1) return MLA_ERR_SHAPE;
-  // all units of the batch are counted in int32 inside the kernels
-  if ((int64_t)batch * max_blocks_per_seq > (int64_t)INT_MAX / 2) return MLA_ERR_SHAPE;
-  if (block_table == nullptr && cache->num_blocks < (int64_t)batch * max_blocks_per_seq) return MLA_ERR_SHAPE;
+  CacheView cv;
+  MLA_TRY(check_cache(cache, paged, B, &cv));
+  if (!paged) max_blocks = cv.contig_blocks;
+  int32_t parts = 1;
+  MLA_TRY(check_partials(partial_out, partial_lse, S, &parts));
   if (!std::isfinite(scale)) return MLA_ERR_SHAPE;
-  st = check_device();
-  if (st != MLA_OK) return st;
+  // all units of the batch are counted in int32 inside the kernels
+  if (max_blocks > INT_MAX / 2 || B * (max_blocks + mla::kSegWeight) > (int64_t)INT_MAX / 2) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
 
   mla::DecodeParams p;
-  p.q_abs = static_cast<const __bf16*>(q_absorbed);
-  p.q_rope = static_cast<const __bf16*>(q_rope);
-  p.rows = static_cast<const char*>(cache->rows);
-  p.fp8_scales = cache->scales;
-  p.fp8_rope = static_cast<const __bf16*>(cache->rope);
-  p.block_table = block_table;
-  p.seq_lens = seq_lens;
-  p.part_out = partial_out;
-  p.part_lse = partial_lse;
-  p.out = out_latent;
-  p.lse = lse;
+  p.q_abs = static_cast<const __bf16*>(q_absorbed->data);
+  p.q_rope = static_cast<const __bf16*>(q_rope->data);
+  p.rows = static_cast<const char*>(cache->rows.data);
+  p.fp8_scales = cv.fp8 ? static_cast<const float*>(cache->scales.data) : nullptr;
+  p.fp8_rope = cv.fp8 ? static_cast<const __bf16*>(cache->rope.data) : nullptr;
+  p.block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
+  p.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  p.part_out = parts > 1 ? partial_out->data : nullptr;
+  p.part_lse = parts > 1 ? static_cast<float*>(partial_lse->data) : nullptr;
+  p.out = static_cast<float*>(out_latent->data);
+  p.lse = static_cast<float*>(lse->data);
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.max_blocks = max_blocks_per_seq;
-  p.batch = batch;
-  p.num_parts = num_splits;
-  const hipError_t err = mla::launch_decode(p, s_q, cache->dtype == MLA_CACHE_FP8_E4M3, stream);
+  p.max_blocks = (int32_t)max_blocks;
+  p.batch = (int32_t)B;
+  p.num_parts = parts;
+  const hipError_t err = mla::launch_decode(p, (int)S, cv.fp8, stream);
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
-mla_status mla_combine(const void* partial_out, const float* partial_lse, const int32_t* seq_lens,
-                       int32_t batch, int32_t s_q, int32_t num_splits, float* out_latent, float* lse,
-                       hipStream_t stream) {
-  if (!seq_lens || !out_latent || !lse) return MLA_ERR_NULL;
-  mla_status st = check_common(batch, s_q, num_splits, partial_out, partial_lse);
-  if (st != MLA_OK) return st;
-  if (num_splits == 1) return MLA_OK;  // a single partition holds every sequence whole
-  st = check_device();
-  if (st != MLA_OK) return st;
+mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_lse, const mla_tensor* seq_lens,
+                       const mla_tensor* out_latent, const mla_tensor* lse, hipStream_t stream) {
+  int64_t B = 0, S = 0;
+  MLA_TRY(check_outputs(out_latent, lse, &B, &S));
+  const int64_t wl[1] = {B};
+  MLA_TRY(check_tensor(seq_lens, MLA_DTYPE_INT32, 1, wl));
+  int32_t parts = 1;
+  MLA_TRY(check_partials(partial_out, partial_lse, S, &parts));
+  if (parts == 1) return MLA_OK;  // a single partition holds every sequence whole
+  MLA_TRY(check_device());
   mla::CombineParams p;
-  p.part_out = partial_out;
-  p.part_lse = partial_lse;
-  p.seq_lens = seq_lens;
-  p.out = out_latent;
-  p.lse = lse;
-  p.batch = batch;
-  p.s_q = s_q;
-  p.num_parts = num_splits;
+  p.part_out = partial_out->data;
+  p.part_lse = static_cast<const float*>(partial_lse->data);
+  p.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  p.out = static_cast<float*>(out_latent->data);
+  p.lse = static_cast<float*>(lse->data);
+  p.batch = (int32_t)B;
+  p.s_q = (int32_t)S;
+  p.num_parts = parts;
   p.log2_parts = 0;
-  while ((1 << p.log2_parts) < num_splits) ++p.log2_parts;
+  while ((1 << p.log2_parts) < parts) ++p.log2_parts;
   return mla::launch_combine(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+mla_status mla_check_indices(const mla_latent_cache* cache, const mla_tensor* block_table,
+                             const mla_tensor* seq_lens, const mla_tensor* counts, hipStream_t stream) {
+  if (!present(seq_lens)) return MLA_ERR_NULL;
+  if (seq_lens->dtype != MLA_DTYPE_INT32) return MLA_ERR_DTYPE;
+  if (seq_lens->rank != 1) return MLA_ERR_SHAPE;
+  const int64_t B = seq_lens->shape[0];
+  const int64_t wl[1] = {B};
+  MLA_TRY(check_tensor(seq_lens, MLA_DTYPE_INT32, 1, wl));
+  if (B > INT_MAX / 4) return MLA_ERR_SHAPE;
+  const bool paged = present(block_table);
+  int64_t max_blocks = 0;
+  if (paged) {
+    const int64_t wt[2] = {B, -1};
+    MLA_TRY(check_tensor(block_table, MLA_DTYPE_INT32, 2, wt));
+    max_blocks = block_table->shape[1];
+  }
+  CacheView cv;
+  MLA_TRY(check_cache(cache, paged, B, &cv));
+  if (!paged) max_blocks = cv.contig_blocks;
+  if (max_blocks > INT_MAX / 128) return MLA_ERR_SHAPE;
+  const int64_t wc[1] = {2};
+  MLA_TRY(check_tensor(counts, MLA_DTYPE_INT32, 1, wc));
+  MLA_TRY(check_device());
+  mla::CheckParams p;
+  p.block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
+  p.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  p.counts = static_cast<int32_t*>(counts->data);
+  p.num_blocks = cv.num_blocks;
+  p.max_blocks = (int32_t)max_blocks;
+  p.batch = (int32_t)B;
+  return mla::launch_check_indices(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_init(int32_t device) {
+  MLA_TRY(check_device_id(device));
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_DEVICE;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return MLA_ERR_DEVICE;
+  const hipError_t err = mla::load_decode_module();
+  if (prev != device) (void)hipSetDevice(prev);
+  return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t max_blocks_per_seq) {
-  if (batch < 1 || s_q < 1 || s_q > 2) return 0;
+  if (batch < 1 || !supported_tokens(s_q)) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) return 0;
-  int parts = s_q == 1 ? cus : cus / 2;
+  const int parts = cus / s_q;   // a partition takes s_q workgroups (128 query rows each)
   int p2 = 1;
   while (p2 * 2 <= parts) p2 *= 2;  // partitions must be a power of two
   if (max_blocks_per_seq > 0) {
@@ -137,9 +291,9 @@ size_t mla_partial_lse_bytes(int32_t num_splits, int32_t s_q) {
 const char* mla_status_string(mla_status status) {
   switch (status) {
     case MLA_OK: return "ok";
-    case MLA_ERR_NULL: return "a required pointer is NULL";
-    case MLA_ERR_DTYPE: return "unsupported cache dtype";
-    case MLA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case MLA_ERR_NULL: return "a required tensor or its data pointer is NULL";
+    case MLA_ERR_DTYPE: return "a tensor has the wrong element type";
+    case MLA_ERR_SHAPE: return "inconsistent or out-of-range shapes or strides";
     case MLA_ERR_UNSUPPORTED: return "valid request not implemented by this build";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
     case MLA_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
@@ -147,6 +301,6 @@ const char* mla_status_string(mla_status status) {
   return "unknown status";
 }
 
-int32_t mla_version(void) { return 200; }  // 0.2.0: fp16 partials with descales
+int32_t mla_version(void) { return 30000; }  // 3.0.0: tensor descriptors, S_q = 4, index check, init
 
 }  // extern "C"

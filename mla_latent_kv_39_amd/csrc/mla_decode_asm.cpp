@@ -1,6 +1,6 @@
 // Host launcher of the assembly decode kernels (bf16 and fp8 cache), generated
 // by gen_decode_gfx950.py and assembled into one code object that is embedded
-// in libmla.so and loaded once per device on first use.
+// in libmla.so and loaded once per device (by mla_init or on first use).
 #include <mutex>
 
 #include "mla_internal.h"
@@ -46,6 +46,7 @@ hipError_t decode_function(bool fp8, hipFunction_t* fn) {
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
+  // the code object is loaded once per device and kept until the process ends
   if (!g_mod[dev]) {
     hipModule_t mod;
     err = hipModuleLoadData(&mod, mla_decode_gfx950_co);
@@ -63,6 +64,11 @@ hipError_t decode_function(bool fp8, hipFunction_t* fn) {
 }
 
 }  // namespace
+
+hipError_t load_decode_module() {
+  hipFunction_t fn;
+  return decode_function(false, &fn);
+}
 
 hipError_t launch_decode(const DecodeParams& p, int s_q, bool fp8, hipStream_t stream) {
   hipFunction_t fn;

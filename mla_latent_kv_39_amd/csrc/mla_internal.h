@@ -47,12 +47,28 @@ struct CombineParams {
   int32_t log2_parts;        // num_parts is a power of two
 };
 
-// Heads handled by one workgroup for a given number of query tokens.
-inline int heads_per_block(int s_q) { return s_q == 1 ? 128 : 64; }
+// Heads handled by one workgroup for a given number of query tokens (1, 2 or
+// 4): a workgroup always holds 128 query rows, four waves of 32 rows of one
+// token each.
+inline int heads_per_block(int s_q) { return kHeads / s_q; }
 
 // Kernel launchers (defined next to the kernels).  They return the HIP error
 // of the launch.
 hipError_t launch_decode(const DecodeParams& p, int s_q, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+// Index contract of the decode (seq_lens and block_table contents).
+struct CheckParams {
+  const int32_t* block_table;  // [B, max_blocks] or nullptr (contiguous)
+  const int32_t* seq_lens;     // [B]
+  int32_t* counts;             // [2]: bad lengths, bad table entries
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t batch;
+};
+hipError_t launch_check_indices(const CheckParams& p, hipStream_t stream);
+
+// Load the decode code object on the current device (idempotent).
+hipError_t load_decode_module();
 
 }  // namespace mla

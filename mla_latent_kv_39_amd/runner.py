@@ -27,10 +27,9 @@ class DecodeWorkspace:
             self.partial_out = self.partial_lse = None
 
 
-def decode_step(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws: DecodeWorkspace,
-                max_blocks_per_seq=None, stream=None):
+def decode_step(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws: DecodeWorkspace, stream=None):
     """Enqueue decode + combine; returns (out_latent, lse) views of the workspace."""
-    mla_decode(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws.num_splits, ws.partial_out,
-               ws.partial_lse, ws.out, ws.lse, max_blocks_per_seq=max_blocks_per_seq, stream=stream)
-    mla_combine(ws.partial_out, ws.partial_lse, seq_lens, ws.num_splits, ws.out, ws.lse, stream=stream)
+    mla_decode(q_absorbed, q_rope, cache, block_table, seq_lens, scale, ws.out, ws.lse, ws.partial_out,
+               ws.partial_lse, stream=stream)
+    mla_combine(ws.partial_out, ws.partial_lse, seq_lens, ws.out, ws.lse, stream=stream)
     return ws.out, ws.lse

@@ -45,7 +45,7 @@ def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
     lse = mem.add(np.full(B * S * N_HEADS, np.nan, np.float32))
     fsc = mem.add(inp.cache_scales.numpy()) if fp8 else 0
     fro = mem.add(inp.cache_rope.contiguous().view(torch.uint8).numpy()) if fp8 else 0
-    hpb = 128 if S == 1 else 64
+    hpb = 128 // S
     lg = 0
     while (1 << lg) < num_splits:
         lg += 1

@@ -29,7 +29,7 @@ class DeviceInputs:
         if ws is None:
             ws = DecodeWorkspace(inp.batch, inp.s_q, num_splits)
         out, lse = decode_step(self.q_absorbed, self.q_rope, self.cache, self.block_table, self.seq_lens,
-                               inp.scale, ws, max_blocks_per_seq=inp.max_blocks)
+                               inp.scale, ws)
         torch.cuda.synchronize()
         return out.cpu().double().numpy(), lse.cpu().double().numpy()
 

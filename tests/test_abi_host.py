@@ -1,5 +1,9 @@
 """The C-ABI library on the host: it loads, exports every symbol include/mla.h
-declares, and rejects bad arguments before any launch (no GPU needed)."""
+declares, and rejects bad descriptors before any launch (no GPU needed).
+
+Every call below goes straight through ctypes to libmla with raw mla_tensor
+descriptors whose data pointers are never dereferenced: the library's own
+host-side checks must reject each one (no Python check in between)."""
 import ctypes
 import os
 import re
@@ -7,6 +11,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000   # 16-byte aligned, never dereferenced
 
 
 @pytest.fixture(scope="module")
@@ -33,65 +38,177 @@ def test_status_strings_and_version(lib):
     for code in range(7):
         assert isinstance(lib.status_string(code), str) and lib.status_string(code)
     assert lib.status_string(99) == "unknown status"
-    assert lib.mla_version() >= 200        # 0.2: the fp16 partial_out format
+    assert lib.mla_version() >= 30000      # 3.0: tensor descriptors
     # fp16 values (128 KB) and 512 fp32 descales per (split, slot, token) block
     assert lib.mla_partial_out_bytes(3, 2) == 3 * 2 * 2 * (128 * 512 * 2 + 4 * 128 * 4)
     assert lib.mla_partial_lse_bytes(3, 1) == 3 * 2 * 128 * 4
     assert lib.mla_partial_out_bytes(0, 1) == 0
 
 
-FAKE = 0x10000  # never dereferenced: every call below fails validation first
+def desc(lib, shape, dtype, data=FAKE, strides=None):
+    """A raw mla_tensor: densely packed row-major unless strides are given."""
+    d = lib.MlaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.rank = len(shape)
+    st, acc = [], 1
+    for n in reversed(shape):
+        st.insert(0, acc)
+        acc *= n
+    for k, n in enumerate(shape):
+        d.shape[k] = n
+        d.strides[k] = (strides or st)[k]
+    return d
 
 
-def _decode(lib, **kw):
-    args = dict(q=FAKE, qr=FAKE, dtype=0, bs=64, nb=10, rows=FAKE, scales=None, rope=None, table=FAKE, mb=4,
-                lens=FAKE, batch=2, s_q=1, scale=0.072, splits=4, po=FAKE, pl=FAKE, out=FAKE, lse=FAKE,
-                cache_null=False)
-    args.update(kw)
-    desc = lib.LatentCacheDesc(args["dtype"], args["bs"], args["nb"], args["rows"], args["scales"], args["rope"])
-    c = lib.library()
-    return c.mla_decode(args["q"], args["qr"], None if args["cache_null"] else ctypes.byref(desc), args["table"],
-                        args["mb"], args["lens"], args["batch"], args["s_q"], args["scale"], args["splits"],
-                        args["po"], args["pl"], args["out"], args["lse"], None)
+def _args(lib, B=2, S=1, H=128, NB=10, MB=4, P=4, fp8=False):
+    """A consistent set of decode descriptors (fake device pointers)."""
+    bf, f32, i32, u8, e4 = (lib.MLA_DTYPE_BF16, lib.MLA_DTYPE_FP32, lib.MLA_DTYPE_INT32, lib.MLA_DTYPE_UINT8,
+                            lib.MLA_DTYPE_FP8_E4M3)
+    cache = lib.MlaLatentCache()
+    if fp8:
+        cache.rows = desc(lib, (NB, 64, 512), e4)
+        cache.scales = desc(lib, (NB, 64, 4), f32)
+        cache.rope = desc(lib, (NB, 64, 64), bf)
+    else:
+        cache.rows = desc(lib, (NB, 64, 576), bf)
+    return dict(q=desc(lib, (B, S, H, 512), bf), qr=desc(lib, (B, S, H, 64), bf), cache=cache,
+                table=desc(lib, (B, MB), i32), lens=desc(lib, (B,), i32), scale=0.072,
+                out=desc(lib, (B, S, H, 512), f32), lse=desc(lib, (B, S, H), f32),
+                po=desc(lib, (lib.mla_partial_out_bytes(P, S),), u8), pl=desc(lib, (P, 2, S, H), f32))
 
 
-def test_decode_argument_errors(lib):
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def _decode(lib, a):
+    return lib.library().mla_decode(_ref(a["q"]), _ref(a["qr"]), _ref(a["cache"]), _ref(a["table"]),
+                                    _ref(a["lens"]), a["scale"], _ref(a["out"]), _ref(a["lse"]), _ref(a["po"]),
+                                    _ref(a["pl"]), None)
+
+
+def _with(lib, **changes):
+    kw = {k: changes.pop(k) for k in ("B", "S", "H", "NB", "MB", "P", "fp8") if k in changes}
+    a = _args(lib, **kw)
+    for k, v in changes.items():
+        if callable(v):
+            v(a)
+        else:
+            a[k] = v
+    return _decode(lib, a)
+
+
+def test_decode_rejects_bad_descriptors(lib):
     E = lib
-    assert _decode(lib, q=None) == E.MLA_ERR_NULL
-    assert _decode(lib, qr=None) == E.MLA_ERR_NULL
-    assert _decode(lib, cache_null=True) == E.MLA_ERR_NULL
-    assert _decode(lib, rows=None) == E.MLA_ERR_NULL
-    assert _decode(lib, lens=None) == E.MLA_ERR_NULL
-    assert _decode(lib, out=None) == E.MLA_ERR_NULL
-    assert _decode(lib, lse=None) == E.MLA_ERR_NULL
-    assert _decode(lib, po=None) == E.MLA_ERR_NULL              # partials needed when splits > 1
-    assert _decode(lib, po=FAKE + 8) == E.MLA_ERR_SHAPE         # partial_out: 16-byte aligned
-    assert _decode(lib, batch=0) == E.MLA_ERR_SHAPE
-    assert _decode(lib, s_q=0) == E.MLA_ERR_SHAPE
-    assert _decode(lib, s_q=3) == E.MLA_ERR_UNSUPPORTED
-    assert _decode(lib, splits=0) == E.MLA_ERR_SHAPE
-    assert _decode(lib, splits=65537) == E.MLA_ERR_SHAPE
-    assert _decode(lib, splits=6) == E.MLA_ERR_SHAPE            # partitions: a power of two
-    assert _decode(lib, dtype=7) == E.MLA_ERR_DTYPE
-    assert _decode(lib, dtype=1) == E.MLA_ERR_NULL              # fp8 needs scales and rope
-    assert _decode(lib, bs=32) == E.MLA_ERR_UNSUPPORTED
-    assert _decode(lib, bs=48) == E.MLA_ERR_SHAPE
-    assert _decode(lib, mb=0) == E.MLA_ERR_SHAPE
-    assert _decode(lib, nb=0) == E.MLA_ERR_SHAPE
-    assert _decode(lib, table=None, nb=7) == E.MLA_ERR_SHAPE    # contiguous cache smaller than batch * mb
-    assert _decode(lib, scale=float("nan")) == E.MLA_ERR_SHAPE
-    assert _decode(lib, batch=1 << 30, mb=4) == E.MLA_ERR_SHAPE
+    bf, f32, i32 = lib.MLA_DTYPE_BF16, lib.MLA_DTYPE_FP32, lib.MLA_DTYPE_INT32
+    # missing tensors
+    for k in ("q", "qr", "lens", "out", "lse", "cache"):
+        assert _with(lib, **{k: None}) == E.MLA_ERR_NULL, k
+    assert _with(lib, q=desc(lib, (2, 1, 128, 512), bf, data=None)) == E.MLA_ERR_NULL
+    # head count and widths (the library, not the binding, knows H = 128, 512 and 64)
+    assert _with(lib, H=64) == E.MLA_ERR_SHAPE
+    assert _with(lib, q=desc(lib, (2, 1, 64, 512), bf)) == E.MLA_ERR_SHAPE
+    assert _with(lib, q=desc(lib, (2, 1, 128, 500), bf)) == E.MLA_ERR_SHAPE
+    assert _with(lib, qr=desc(lib, (2, 1, 128, 32), bf)) == E.MLA_ERR_SHAPE
+    assert _with(lib, qr=desc(lib, (3, 1, 128, 64), bf)) == E.MLA_ERR_SHAPE
+    assert _with(lib, lse=desc(lib, (2, 1, 64), f32)) == E.MLA_ERR_SHAPE
+    assert _with(lib, q=desc(lib, (2, 1, 128, 512, 1), bf)) == E.MLA_ERR_SHAPE      # rank
+    # dtypes
+    assert _with(lib, q=desc(lib, (2, 1, 128, 512), f32)) == E.MLA_ERR_DTYPE
+    assert _with(lib, out=desc(lib, (2, 1, 128, 512), bf)) == E.MLA_ERR_DTYPE
+    assert _with(lib, lens=desc(lib, (2,), f32)) == E.MLA_ERR_DTYPE
+    assert _with(lib, table=desc(lib, (2, 4), f32)) == E.MLA_ERR_DTYPE
+    # strides: only densely packed row-major tensors
+    assert _with(lib, q=desc(lib, (2, 1, 128, 512), bf, strides=(65536, 65536, 1, 128))) == E.MLA_ERR_SHAPE
+    assert _with(lib, out=desc(lib, (2, 1, 128, 512), f32, strides=(131072, 65536, 512, 1))) == E.MLA_ERR_SHAPE
+    # query tokens
+    assert _with(lib, S=3) == E.MLA_ERR_UNSUPPORTED
+    assert _with(lib, S=8) == E.MLA_ERR_UNSUPPORTED
+    # sequence lengths and block table
+    assert _with(lib, lens=desc(lib, (3,), i32)) == E.MLA_ERR_SHAPE
+    assert _with(lib, table=desc(lib, (2,), i32)) == E.MLA_ERR_SHAPE
+    assert _with(lib, table=desc(lib, (3, 4), i32)) == E.MLA_ERR_SHAPE
+    # cache
+    def rows(shape, dtype=bf):
+        return lambda a: setattr(a["cache"], "rows", desc(lib, shape, dtype))
+    assert _with(lib, cache=lambda a: rows((10, 64, 512))(a)) == E.MLA_ERR_SHAPE          # bf16 rows are 576 wide
+    assert _with(lib, cache=lambda a: rows((10, 64, 576), f32)(a)) == E.MLA_ERR_DTYPE
+    assert _with(lib, cache=lambda a: rows((10, 32, 576))(a)) == E.MLA_ERR_UNSUPPORTED    # pages of 32 rows
+    assert _with(lib, cache=lambda a: rows((10, 48, 576))(a)) == E.MLA_ERR_SHAPE
+    # e4m3 bundle
+    assert _with(lib, fp8=True, cache=lambda a: setattr(a["cache"], "scales", lib.MlaTensor())) == E.MLA_ERR_NULL
+    assert _with(lib, fp8=True, cache=lambda a: setattr(a["cache"], "scales", desc(lib, (10, 64, 8), f32))) \
+        == E.MLA_ERR_SHAPE
+    assert _with(lib, fp8=True, cache=lambda a: setattr(a["cache"], "rope", desc(lib, (10, 64, 64), f32))) \
+        == E.MLA_ERR_DTYPE
+    assert _with(lib, fp8=True, cache=lambda a: setattr(a["cache"], "rope", desc(lib, (9, 64, 64), bf))) \
+        == E.MLA_ERR_SHAPE
+    # contiguous cache: NB must be a multiple of B, or [B, L_cap, .] with L_cap a multiple of 64
+    assert _with(lib, table=None, NB=7) == E.MLA_ERR_SHAPE
+    assert _with(lib, table=None, cache=lambda a: rows((2, 100, 576))(a)) == E.MLA_ERR_SHAPE
+    assert _with(lib, table=None, cache=lambda a: rows((3, 128, 576))(a)) == E.MLA_ERR_SHAPE
+    # partials: the split count is partial_lse's leading dimension, a power of two
+    assert _with(lib, P=6) == E.MLA_ERR_SHAPE
+    assert _with(lib, pl=desc(lib, (4, 2, 1, 64), f32)) == E.MLA_ERR_SHAPE
+    assert _with(lib, pl=desc(lib, (4, 1, 1, 128), f32)) == E.MLA_ERR_SHAPE
+    assert _with(lib, po=None) == E.MLA_ERR_NULL
+    assert _with(lib, po=desc(lib, (1000,), lib.MLA_DTYPE_UINT8)) == E.MLA_ERR_SHAPE   # too small
+    assert _with(lib, po=desc(lib, (lib.mla_partial_out_bytes(4, 1),), lib.MLA_DTYPE_UINT8, data=FAKE + 8)) \
+        == E.MLA_ERR_SHAPE                                                               # 16-byte stores
+    assert _with(lib, po=desc(lib, (lib.mla_partial_out_bytes(4, 1),), f32)) == E.MLA_ERR_DTYPE
+    # scale
+    assert _with(lib, scale=float("nan")) == E.MLA_ERR_SHAPE
+    assert _with(lib, scale=float("inf")) == E.MLA_ERR_SHAPE
+    # sizes far beyond any device
+    assert _with(lib, B=1 << 30, MB=4) == E.MLA_ERR_SHAPE
 
 
-def test_combine_argument_errors(lib):
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="a GPU would run the launch")
+def test_a_valid_call_gets_past_every_host_check(lib):
+    # no GPU here: the only thing left to fail is the device
+    assert _decode(lib, _args(lib)) == lib.MLA_ERR_DEVICE
+    assert _decode(lib, _args(lib, fp8=True, S=4)) == lib.MLA_ERR_DEVICE
+    a = _args(lib)
+    a["table"] = None                                  # contiguous: [B * 5, 64, 576]
+    a["cache"].rows = desc(lib, (10, 64, 576), lib.MLA_DTYPE_BF16)
+    assert _decode(lib, a) == lib.MLA_ERR_DEVICE
+
+
+def test_combine_rejects_bad_descriptors(lib):
+    E = lib
     c = lib.library()
-    assert c.mla_combine(FAKE, FAKE, None, 2, 1, 4, FAKE, FAKE, None) == lib.MLA_ERR_NULL
-    assert c.mla_combine(FAKE, FAKE, FAKE, 2, 1, 4, None, FAKE, None) == lib.MLA_ERR_NULL
-    assert c.mla_combine(None, FAKE, FAKE, 2, 1, 4, FAKE, FAKE, None) == lib.MLA_ERR_NULL
-    assert c.mla_combine(FAKE, FAKE, FAKE, 0, 1, 4, FAKE, FAKE, None) == lib.MLA_ERR_SHAPE
-    assert c.mla_combine(FAKE, FAKE, FAKE, 2, 3, 4, FAKE, FAKE, None) == lib.MLA_ERR_UNSUPPORTED
+    a = _args(lib)
+
+    def comb(po="po", pl="pl", lens="lens", out="out", lse="lse"):
+        v = lambda k: a.get(k) if isinstance(k, str) else k
+        return c.mla_combine(_ref(v(po)), _ref(v(pl)), _ref(v(lens)), _ref(v(out)), _ref(v(lse)), None)
+
+    assert comb(lens=None) == E.MLA_ERR_NULL
+    assert comb(out=None) == E.MLA_ERR_NULL
+    assert comb(po=None) == E.MLA_ERR_NULL
+    assert comb(lens=desc(lib, (3,), lib.MLA_DTYPE_INT32)) == E.MLA_ERR_SHAPE
+    assert comb(pl=desc(lib, (4, 2, 2, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_SHAPE     # S_q differs
+    assert comb(out=desc(lib, (2, 3, 128, 512), lib.MLA_DTYPE_FP32),
+                lse=desc(lib, (2, 3, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_UNSUPPORTED
+    assert comb(out=desc(lib, (2, 1, 96, 512), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_SHAPE
     # one partition: nothing to merge, no launch
-    assert c.mla_combine(None, None, FAKE, 2, 1, 1, FAKE, FAKE, None) == lib.MLA_OK
+    assert comb(po=None, pl=None) == E.MLA_OK
+    assert comb(po=None, pl=desc(lib, (1, 2, 1, 128), lib.MLA_DTYPE_FP32)) == E.MLA_OK
+
+
+def test_check_indices_rejects_bad_descriptors(lib):
+    E = lib
+    c = lib.library()
+    a = _args(lib)
+    i32 = lib.MLA_DTYPE_INT32
+    counts = desc(lib, (2,), i32)
+    assert c.mla_check_indices(_ref(a["cache"]), _ref(a["table"]), _ref(a["lens"]), None, None) == E.MLA_ERR_NULL
+    assert c.mla_check_indices(_ref(a["cache"]), _ref(a["table"]), _ref(a["lens"]), _ref(desc(lib, (3,), i32)),
+                               None) == E.MLA_ERR_SHAPE
+    assert c.mla_check_indices(_ref(a["cache"]), _ref(desc(lib, (3, 4), i32)), _ref(a["lens"]), _ref(counts),
+                               None) == E.MLA_ERR_SHAPE
+    assert c.mla_check_indices(None, _ref(a["table"]), _ref(a["lens"]), _ref(counts), None) == E.MLA_ERR_NULL
 
 
 def test_hint_rejects_bad_arguments(lib):
@@ -99,19 +216,22 @@ def test_hint_rejects_bad_arguments(lib):
     assert lib.mla_num_splits_hint(0, 4, 3, 0) == 0
 
 
-def test_binding_checks_combine_buffers_before_the_library(lib):
-    # shapes, dtypes and placement are checked on the host before any call into libmla
+def test_binding_passes_only_device_memory(lib):
+    # the library cannot tell host from device pointers: the binding refuses host tensors
     import torch
     out = torch.zeros((2, 1, 128, 512), dtype=torch.float32)
     lse = torch.zeros((2, 1, 128), dtype=torch.float32)
     lens = torch.zeros((2,), dtype=torch.int32)
-    po = torch.zeros((lib.mla_partial_out_bytes(4, 1),), dtype=torch.uint8)
-    pl = torch.zeros((4, 2, 1, 128), dtype=torch.float32)
-    with pytest.raises(ValueError, match="partial_out must have shape"):
-        lib.mla_combine(po[:100], pl, lens, 4, out, lse)
-    with pytest.raises(TypeError, match="partial_out must be"):
-        lib.mla_combine(po.float(), pl, lens, 4, out, lse)
-    with pytest.raises(ValueError, match="partial_out must be a device tensor"):
-        lib.mla_combine(po, pl, lens, 4, out, lse)        # host tensors never reach the library
-    with pytest.raises(ValueError, match="seq_lens must have shape"):
-        lib.mla_combine(po, pl, lens[:1], 1, out, lse)    # one partition: no partials to check
+    with pytest.raises(ValueError, match="device tensors only"):
+        lib.mla_combine(None, None, lens, out, lse)
+
+
+def test_descriptor_of_a_tensor(lib):
+    import torch
+    t = torch.zeros((3, 4, 5), dtype=torch.bfloat16)
+    d = lib.tensor(t, device_only=False)
+    assert (d.dtype, d.rank) == (lib.MLA_DTYPE_BF16, 3)
+    assert list(d.shape)[:3] == [3, 4, 5] and list(d.strides)[:3] == [20, 5, 1]
+    v = lib.tensor(t.transpose(0, 1), device_only=False)
+    assert list(v.strides)[:3] == [5, 20, 1]
+    assert lib.tensor(None).data is None

@@ -55,6 +55,48 @@ def test_two_query_tokens_causal(num_splits):
     _run_and_check(inp, num_splits, f"mtp splits={num_splits}")
 
 
+@pytest.mark.parametrize("num_splits", [1, 4, 8, 64])
+def test_four_query_tokens_causal(num_splits):
+    # MTP with three draft tokens: token s sees seq_len - 4 + s + 1 rows
+    inp = _small([3, 4, 64, 65, 67, 131, 500, 1000], s_q=4, seed=13)
+    _run_and_check(inp, num_splits, f"s_q=4 splits={num_splits}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 16])
+def test_four_query_tokens_e4m3(num_splits):
+    inp = _small([3, 66, 129, 700], s_q=4, seed=14, cache="fp8_e4m3")
+    _run_and_check(inp, num_splits, f"s_q=4 e4m3 splits={num_splits}")
+
+
+def test_check_indices_counts_contract_violations():
+    """mla_check_indices: zero on the generated inputs; a length past the
+    table's capacity and a table entry outside the cache are counted."""
+    import mla_latent_kv_39_amd as mla
+    from gpu_helpers import DeviceInputs
+    inp = _small([1, 63, 65, 130, 700], seed=15)
+    dev = DeviceInputs(inp)
+    counts = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    mla.mla_check_indices(dev.cache, dev.block_table, dev.seq_lens, counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
+    lens = dev.seq_lens.clone()
+    lens[1] = inp.max_blocks * 64 + 1
+    lens[2] = -3
+    table = dev.block_table.clone()
+    table[3, 1] = dev.cache.num_blocks          # page 1 of a 130-row sequence: used
+    table[4, 0] = -1
+    table[0, 2] = 10 ** 6                       # page 2 of a 1-row sequence: unused, not counted
+    mla.mla_check_indices(dev.cache, table, lens, counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [2, 2]
+    # contiguous layout: the identity table is always inside the cache
+    cinp = _small([100, 1000, 37], layout="contiguous", seed=16)
+    cdev = DeviceInputs(cinp)
+    mla.mla_check_indices(cdev.cache, None, cdev.seq_lens, counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
+
+
 def test_nan_in_page_tails_never_reaches_output():
     from gpu_helpers import DeviceInputs, compare
     inp = _small([1, 63, 65, 130, 200], seed=4)
@@ -157,7 +199,7 @@ def test_combine_kernel_on_oracle_partials(lens, s_q, splits):
     d = lambda t: t.cuda()
     out_d, lse_d = d(out), d(lse)
     from gpu_helpers import pack_partial_out
-    mla.mla_combine(d(pack_partial_out(po)), d(pl), d(inp.seq_lens), splits, out_d, lse_d)
+    mla.mla_combine(d(pack_partial_out(po)), d(pl), d(inp.seq_lens), out_d, lse_d)
     torch.cuda.synchronize()
     from gpu_helpers import compare
     compare(out_d.cpu().double().numpy(), lse_d.cpu().double().numpy(), ref_out, ref_lse, f"combine s_q={s_q}")
@@ -178,3 +220,4 @@ def test_num_splits_hint_follows_the_cache_capacity():
     assert mla.mla_num_splits_hint(dev, 1, 1, 2) == 1              # 5 units: one partition
     assert mla.mla_num_splits_hint(dev, 8, 1, 2) == 8              # 40 units: 5 per partition
     assert mla.mla_num_splits_hint(dev, 128, 2, 128) == full // 2  # two query tokens: two workgroups per partition
+    assert mla.mla_num_splits_hint(dev, 128, 4, 128) == full // 4  # four tokens: four workgroups per partition

@@ -77,6 +77,15 @@ def test_bf16_empty_sequences_and_nan_tails(s_q):
         _check(inp, splits, ref=ref)
 
 
+@pytest.mark.parametrize("cache,lens,splits", [("bf16", [4, 5, 66, 130], 1), ("bf16", [3, 70, 129, 200, 9], 8),
+                                               ("fp8_e4m3", [3, 70, 129, 200], 4)])
+def test_four_query_tokens(cache, lens, splits):
+    # 128 heads x 4 tokens: four workgroups of 32 heads per partition (eight
+    # partitions: the XCD-grouped workgroup order); the 3-row sequence leaves
+    # token 0 with no row
+    _check(_small(lens, s_q=4, seed=5, cache=cache), splits)
+
+
 def test_bf16_result_independent_of_wave_order():
     inp = _small([65, 130, 200], seed=7)
     a = ED.emulate_decode(inp, 4, seed=1)
