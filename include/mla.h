@@ -37,7 +37,8 @@
  *     and workspace buffers do not overlap.
  *   - State: the library keeps, per device, the handle of its code object
  *     (loaded by mla_init or on the first call on that device, never
- *     unloaded, read-only afterwards) and whether the device is a gfx950.
+ *     unloaded, read-only afterwards), whether the device is a gfx950, and
+ *     the address of mla_decode_noalloc's static scratch.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -66,7 +67,8 @@ typedef enum mla_status {
   MLA_ERR_SHAPE = 3,       /* rank, shape or strides inconsistent; H != 128; widths != 512/64/576 */
   MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q = 3, block size 32) */
   MLA_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
-  MLA_ERR_DEVICE = 6       /* the current device is not gfx950 or cannot be queried */
+  MLA_ERR_DEVICE = 6,      /* the current device is not gfx950 or cannot be queried */
+  MLA_ERR_SCRATCH = 7      /* mla_decode_noalloc: num_splits * S_q above MLA_NOALLOC_MAX_SPLIT_TOKENS */
 } mla_status;
 
 typedef enum mla_dtype {
@@ -178,6 +180,30 @@ mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, co
  */
 mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_lse, const mla_tensor* seq_lens,
                        const mla_tensor* out_latent, const mla_tensor* lse, hipStream_t stream);
+
+/*
+ * mla_decode_noalloc: mla_decode followed by mla_combine, with the split
+ * partials in the library's own static device scratch instead of a caller's
+ * workspace.  For callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * call allocates and frees nothing.  Arguments as mla_decode, except the
+ * split count, given as num_splits (a power of two) with
+ * num_splits * S_q <= MLA_NOALLOC_MAX_SPLIT_TOKENS (MLA_ERR_SCRATCH above):
+ * the scratch holds MLA_NOALLOC_SCRATCH_BYTES (65.25 MiB) per device, taken
+ * once by the device's code object and held until the process ends.  Its
+ * address is looked up by mla_init (or by the first call on the device, which
+ * then also loads the code object: call mla_init at set-up to keep that out
+ * of the call).  Every call on a device shares that device's scratch and it
+ * keeps the last call's partials (each call writes every partial it reads, so
+ * nothing needs clearing): calls that overlap in time on one device, on any
+ * streams, race and must be serialised by the caller.
+ */
+#define MLA_NOALLOC_MAX_SPLIT_TOKENS 256
+#define MLA_NOALLOC_SCRATCH_BYTES 68419584  /* 256 x 2 x (131,072 + 2,048 + 512) */
+mla_status mla_decode_noalloc(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                              const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                              const mla_tensor* out_latent, const mla_tensor* lse, int32_t num_splits,
+                              hipStream_t stream);
 
 /*
  * A split count P for mla_decode (0 on error): one work partition per compute

@@ -25,6 +25,8 @@ MLA_ERR_SHAPE = 3
 MLA_ERR_UNSUPPORTED = 4
 MLA_ERR_LAUNCH = 5
 MLA_ERR_DEVICE = 6
+MLA_ERR_SCRATCH = 7
+NOALLOC_MAX_SPLIT_TOKENS = 256
 
 # element types (mla_dtype)
 MLA_DTYPE_BF16 = 0
@@ -45,8 +47,9 @@ BLOCK_SIZE = 64
 MAX_RANK = 5
 
 # every symbol include/mla.h declares
-EXPORTED_SYMBOLS = ("mla_decode", "mla_combine", "mla_num_splits_hint", "mla_partial_out_bytes",
-                    "mla_partial_lse_bytes", "mla_check_indices", "mla_init", "mla_status_string", "mla_version")
+EXPORTED_SYMBOLS = ("mla_decode", "mla_combine", "mla_decode_noalloc", "mla_num_splits_hint",
+                    "mla_partial_out_bytes", "mla_partial_lse_bytes", "mla_check_indices", "mla_init",
+                    "mla_status_string", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -81,6 +84,8 @@ def _load():
     lib.mla_decode.argtypes = [T, T, C, T, T, f32, T, T, T, T, vp]
     lib.mla_combine.restype = i32
     lib.mla_combine.argtypes = [T, T, T, T, T, vp]
+    lib.mla_decode_noalloc.restype = i32
+    lib.mla_decode_noalloc.argtypes = [T, T, C, T, T, f32, T, T, i32, vp]
     lib.mla_check_indices.restype = i32
     lib.mla_check_indices.argtypes = [C, T, T, T, vp]
     lib.mla_init.restype = i32
@@ -213,6 +218,20 @@ def mla_decode(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, sc
                          _stream_handle(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_decode")
+
+
+def mla_decode_noalloc(q_absorbed, q_rope, cache: LatentCache, block_table, seq_lens, scale: float, out_latent,
+                       lse, num_splits: int, stream=None) -> None:
+    """Enqueue mla_decode_noalloc (decode + combine with the library's static
+    scratch for the partials; see include/mla.h)."""
+    c = cache.desc()
+    args = [tensor(q_absorbed), tensor(q_rope), c, tensor(block_table), tensor(seq_lens), tensor(out_latent),
+            tensor(lse)]
+    st = _lib.mla_decode_noalloc(_ref(args[0]), _ref(args[1]), ctypes.byref(c), _ref(args[3]), _ref(args[4]),
+                                 float(scale), _ref(args[5]), _ref(args[6]), int(num_splits),
+                                 _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_decode_noalloc")
 
 
 def mla_combine(partial_out, partial_lse, seq_lens, out_latent, lse, stream=None) -> None:

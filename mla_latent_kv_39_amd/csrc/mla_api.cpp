@@ -143,14 +143,12 @@ mla_status check_outputs(const mla_tensor* out_latent, const mla_tensor* lse, in
   return MLA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
-                      const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
-                      const mla_tensor* out_latent, const mla_tensor* lse, const mla_tensor* partial_out,
-                      const mla_tensor* partial_lse, hipStream_t stream) {
+// Everything mla_decode checks except the partials; fills p (partials unset)
+// and returns S_q and the cache kind.
+mla_status prepare_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                          const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                          const mla_tensor* out_latent, const mla_tensor* lse, mla::DecodeParams* p,
+                          int64_t* s_q, bool* fp8) {
   int64_t B = 0, S = 0;
   MLA_TRY(check_outputs(out_latent, lse, &B, &S));
   const int64_t wq[4] = {B, S, MLA_NUM_HEADS, MLA_LATENT_DIM};
@@ -169,31 +167,85 @@ mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, co
   CacheView cv;
   MLA_TRY(check_cache(cache, paged, B, &cv));
   if (!paged) max_blocks = cv.contig_blocks;
-  int32_t parts = 1;
-  MLA_TRY(check_partials(partial_out, partial_lse, S, &parts));
   if (!std::isfinite(scale)) return MLA_ERR_SHAPE;
   // all units of the batch are counted in int32 inside the kernels
   if (max_blocks > INT_MAX / 2 || B * (max_blocks + mla::kSegWeight) > (int64_t)INT_MAX / 2) return MLA_ERR_SHAPE;
-  MLA_TRY(check_device());
+  p->q_abs = static_cast<const __bf16*>(q_absorbed->data);
+  p->q_rope = static_cast<const __bf16*>(q_rope->data);
+  p->rows = static_cast<const char*>(cache->rows.data);
+  p->fp8_scales = cv.fp8 ? static_cast<const float*>(cache->scales.data) : nullptr;
+  p->fp8_rope = cv.fp8 ? static_cast<const __bf16*>(cache->rope.data) : nullptr;
+  p->block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
+  p->seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  p->out = static_cast<float*>(out_latent->data);
+  p->lse = static_cast<float*>(lse->data);
+  p->scale_log2 = scale * 1.4426950408889634f;
+  p->max_blocks = (int32_t)max_blocks;
+  p->batch = (int32_t)B;
+  *s_q = S;
+  *fp8 = cv.fp8;
+  return MLA_OK;
+}
 
+mla::CombineParams combine_params(const mla::DecodeParams& d, int s_q) {
+  mla::CombineParams p;
+  p.part_out = d.part_out;
+  p.part_lse = d.part_lse;
+  p.seq_lens = d.seq_lens;
+  p.out = d.out;
+  p.lse = d.lse;
+  p.batch = d.batch;
+  p.s_q = s_q;
+  p.num_parts = d.num_parts;
+  p.log2_parts = 0;
+  while ((1 << p.log2_parts) < d.num_parts) ++p.log2_parts;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                      const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                      const mla_tensor* out_latent, const mla_tensor* lse, const mla_tensor* partial_out,
+                      const mla_tensor* partial_lse, hipStream_t stream) {
   mla::DecodeParams p;
-  p.q_abs = static_cast<const __bf16*>(q_absorbed->data);
-  p.q_rope = static_cast<const __bf16*>(q_rope->data);
-  p.rows = static_cast<const char*>(cache->rows.data);
-  p.fp8_scales = cv.fp8 ? static_cast<const float*>(cache->scales.data) : nullptr;
-  p.fp8_rope = cv.fp8 ? static_cast<const __bf16*>(cache->rope.data) : nullptr;
-  p.block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
-  p.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  int64_t S = 0;
+  bool fp8 = false;
+  MLA_TRY(prepare_decode(q_absorbed, q_rope, cache, block_table, seq_lens, scale, out_latent, lse, &p, &S, &fp8));
+  int32_t parts = 1;
+  MLA_TRY(check_partials(partial_out, partial_lse, S, &parts));
+  MLA_TRY(check_device());
   p.part_out = parts > 1 ? partial_out->data : nullptr;
   p.part_lse = parts > 1 ? static_cast<float*>(partial_lse->data) : nullptr;
-  p.out = static_cast<float*>(out_latent->data);
-  p.lse = static_cast<float*>(lse->data);
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.max_blocks = (int32_t)max_blocks;
-  p.batch = (int32_t)B;
   p.num_parts = parts;
-  const hipError_t err = mla::launch_decode(p, (int)S, cv.fp8, stream);
+  const hipError_t err = mla::launch_decode(p, (int)S, fp8, stream);
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_decode_noalloc(const mla_tensor* q_absorbed, const mla_tensor* q_rope, const mla_latent_cache* cache,
+                              const mla_tensor* block_table, const mla_tensor* seq_lens, float scale,
+                              const mla_tensor* out_latent, const mla_tensor* lse, int32_t num_splits,
+                              hipStream_t stream) {
+  mla::DecodeParams p;
+  int64_t S = 0;
+  bool fp8 = false;
+  MLA_TRY(prepare_decode(q_absorbed, q_rope, cache, block_table, seq_lens, scale, out_latent, lse, &p, &S, &fp8));
+  if (num_splits < 1 || num_splits > MLA_MAX_SPLITS || (num_splits & (num_splits - 1)) != 0) return MLA_ERR_SHAPE;
+  if ((int64_t)num_splits * S > mla::kNoallocMaxSplitTokens) return MLA_ERR_SCRATCH;
+  MLA_TRY(check_device());
+  void* scratch = nullptr;
+  if (num_splits > 1 && mla::noalloc_scratch(&scratch) != hipSuccess) return MLA_ERR_DEVICE;
+  // partial blocks and descales from the start of the scratch, partial_lse at a
+  // fixed offset; every partial the combine reads is written by this decode
+  p.part_out = num_splits > 1 ? scratch : nullptr;
+  p.part_lse = num_splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(scratch) + mla::kNoallocLseOffset)
+                              : nullptr;
+  p.num_parts = num_splits;
+  if (mla::launch_decode(p, (int)S, fp8, stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (num_splits == 1) return MLA_OK;
+  return mla::launch_combine(combine_params(p, (int)S), stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_lse, const mla_tensor* seq_lens,
@@ -258,7 +310,11 @@ mla_status mla_init(int32_t device) {
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_DEVICE;
   if (prev != device && hipSetDevice(device) != hipSuccess) return MLA_ERR_DEVICE;
-  const hipError_t err = mla::load_decode_module();
+  // with `device` current: the decode code object and the address of the
+  // static scratch of mla_decode_noalloc on this device
+  hipError_t err = mla::load_decode_module();
+  void* scratch = nullptr;
+  if (err == hipSuccess) err = mla::noalloc_scratch(&scratch);
   if (prev != device) (void)hipSetDevice(prev);
   return err == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
@@ -297,10 +353,11 @@ const char* mla_status_string(mla_status status) {
     case MLA_ERR_UNSUPPORTED: return "valid request not implemented by this build";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
     case MLA_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
+    case MLA_ERR_SCRATCH: return "num_splits * s_q exceeds the static scratch of mla_decode_noalloc (256)";
   }
   return "unknown status";
 }
 
-int32_t mla_version(void) { return 30000; }  // 3.0.0: tensor descriptors, S_q = 4, index check, init
+int32_t mla_version(void) { return 30100; }  // 3.1.0: + mla_decode_noalloc
 
 }  // extern "C"

@@ -71,4 +71,13 @@ hipError_t launch_check_indices(const CheckParams& p, hipStream_t stream);
 // Load the decode code object on the current device (idempotent).
 hipError_t load_decode_module();
 
+// mla_decode_noalloc: the largest num_splits * s_q its static scratch holds,
+// and the scratch bytes (partial_out blocks and descales, then partial_lse).
+constexpr int kNoallocMaxSplitTokens = 256;
+constexpr size_t kNoallocLseOffset = (size_t)kNoallocMaxSplitTokens * 2 * (kPartBlockBytes + kPartDescBytes);
+constexpr size_t kNoallocScratchBytes = kNoallocLseOffset + (size_t)kNoallocMaxSplitTokens * 2 * kHeads * 4;
+static_assert(kNoallocScratchBytes == 68419584, "MLA_NOALLOC_SCRATCH_BYTES");
+// The current device's address of the static scratch (taken once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace mla

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         assert isinstance(lib.status_string(code), str) and lib.status_string(code)
     assert lib.status_string(99) == "unknown status"
     assert lib.mla_version() >= 30000      # 3.0: tensor descriptors
@@ -173,6 +173,22 @@ def test_a_valid_call_gets_past_every_host_check(lib):
     a["table"] = None                                  # contiguous: [B * 5, 64, 576]
     a["cache"].rows = desc(lib, (10, 64, 576), lib.MLA_DTYPE_BF16)
     assert _decode(lib, a) == lib.MLA_ERR_DEVICE
+
+
+def test_noalloc_rejects_bad_requests_before_any_launch(lib):
+    E = lib
+    c = lib.library()
+
+    def call(a, splits):
+        return c.mla_decode_noalloc(_ref(a["q"]), _ref(a["qr"]), _ref(a["cache"]), _ref(a["table"]),
+                                    _ref(a["lens"]), a["scale"], _ref(a["out"]), _ref(a["lse"]), splits, None)
+
+    assert call(_args(lib, S=2), 256) == E.MLA_ERR_SCRATCH            # 512 split-tokens > 256
+    assert call(_args(lib, S=4), 128) == E.MLA_ERR_SCRATCH
+    assert call(_args(lib), 6) == E.MLA_ERR_SHAPE                       # not a power of two
+    assert call(_args(lib), 0) == E.MLA_ERR_SHAPE
+    assert call(_args(lib, H=64), 4) == E.MLA_ERR_SHAPE                 # the decode's own checks first
+    assert "static scratch" in lib.status_string(E.MLA_ERR_SCRATCH)
 
 
 def test_combine_rejects_bad_descriptors(lib):
