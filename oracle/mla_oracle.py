@@ -239,3 +239,164 @@ def absorb_query(q_c: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
 def apply_output_absorption(out_latent: np.ndarray, W_UV: np.ndarray) -> np.ndarray:
     """o_h = W^UV_h out_latent_h: the per-head value output recovered from latent space."""
     return np.einsum("hdc,hc->hd", W_UV, out_latent)
+
+
+# =============================================== around the decode: the next rows
+# The steps that feed the decode and consume its output in one MLA attention
+# layer ([P2] §2.1.2, §2.1.3(B), (D)): the absorbed query with its rotated
+# RoPE part, the latent-space output mapped back to per-head values, and the
+# cache row of a new token (its projection, its RoPE key, its fp8 encoding).
+#
+# Readings where the pages are silent (each also listed in the design notes):
+#  * RoPE ([P2] §2.1.3(A): a position-dependent rotation of q and k, LLaMA
+#    style) rotates consecutive pairs (x_{2i}, x_{2i+1}) of a d-wide vector by
+#    the angle pos * base^(-2i/d), base 10000, with no long-context frequency
+#    scaling; both the query's q^R and the cached k^R use it.
+#  * k^R of token t is RoPE(W^KR h_t, t) with W^KR of shape [d_h^R, d] and
+#    c^KV_t = W^DKV h_t ([P2] §2.1.2), d = 7168 ([P2] §3).
+#  * The position of query token s of sequence b is seq_len[b] - S_q + s (the
+#    count of rows before it, the same reading as visible_rows).
+#  * The fp8 encoding of a new row: per 128-wide block, amax = max |x|, scale =
+#    amax / 448 rounded to fp32 (1 for an all-zero block), code = the e4m3
+#    value nearest to x / scale (fp32 quotient), ties to the even code,
+#    saturated to +-448 ([P1] §4.2; [P5] "MLA 与 FP8"); the quantizer works in
+#    fp32 because that is where the kernel decides the codes.
+ROPE_BASE = 10000.0
+
+
+def rope(x, pos, base: float = ROPE_BASE) -> np.ndarray:
+    """RoPE(x, pos): pairs (x_{2i}, x_{2i+1}) of the last dim rotated by
+    pos * base^(-2i/d) ([P2] §2.1.3(A), (D)).  pos broadcasts over x's
+    leading dims.  fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    theta = base ** (-2.0 * np.arange(d // 2) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)))
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def token_positions(seq_lens, s_q: int) -> np.ndarray:
+    """[B, S_q] positions of the query tokens: seq_len - S_q + s."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    return lens[:, None] - s_q + np.arange(s_q)[None, :]
+
+
+def query_side(q_c, q_r, W_UK, seq_lens, base: float = ROPE_BASE):
+    """The decode's query inputs from the per-head query parts.
+
+    q_c [B, S, H, d_h], q_r [B, S, H, d_h^R] (before rotation), W_UK [H, d_h, d_c].
+    q_absorbed = W^UK_h^T q^C_h ([P2] §2.1.3(B)), q_rope = RoPE(q^R, position)
+    ([P2] §2.1.3(D)).  Returns fp64 (q_absorbed [B, S, H, d_c], q_rope [B, S, H, d_h^R])."""
+    q_c = np.asarray(q_c, dtype=np.float64)
+    B, S = q_c.shape[:2]
+    q_abs = np.einsum("hdc,bshd->bshc", np.asarray(W_UK, dtype=np.float64), q_c)
+    pos = token_positions(seq_lens, S)
+    q_rot = rope(q_r, pos[:, :, None])
+    return q_abs, q_rot
+
+
+def output_side(out_latent, W_UV) -> np.ndarray:
+    """o_h = W^UV_h out_latent_h for every token ([P2] §2.1.2, §2.1.3(B)):
+    out_latent [B, S, H, d_c], W_UV [H, d_h, d_c] -> [B, S, H, d_h], fp64."""
+    return np.einsum("hdc,bshc->bshd", np.asarray(W_UV, dtype=np.float64), np.asarray(out_latent, dtype=np.float64))
+
+
+def kv_project(h, W_DKV, W_KR) -> np.ndarray:
+    """The cache row of each token before its RoPE: [c^KV ; W^KR h] with
+    c^KV = W^DKV h ([P2] §2.1.2).  h [T, d], W_DKV [d_c, d], W_KR [d_h^R, d]
+    -> [T, d_c + d_h^R], fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    return np.concatenate([h @ np.asarray(W_DKV, dtype=np.float64).T, h @ np.asarray(W_KR, dtype=np.float64).T],
+                          axis=-1)
+
+
+_E4M3_FINITE = None
+
+
+def _e4m3_table():
+    """(values, codes) of the 127 non-negative finite e4m3 values, ascending."""
+    global _E4M3_FINITE
+    if _E4M3_FINITE is None:
+        codes = np.arange(128)
+        vals = e4m3_decode(codes)
+        keep = np.isfinite(vals)
+        _E4M3_FINITE = (vals[keep], codes[keep])
+    return _E4M3_FINITE
+
+
+def e4m3_nearest(v) -> np.ndarray:
+    """OCP E4M3 code of the value nearest to each fp32 v (ties: the even
+    code), saturated to +-448; NaN maps to 0x7F."""
+    v = np.asarray(v, dtype=np.float64)
+    vals, codes = _e4m3_table()
+    a = np.minimum(np.abs(v), 448.0).reshape(-1, 1)
+    dist = np.abs(vals[None, :] - a)                          # distance to every candidate
+    best = dist == dist.min(axis=1, keepdims=True)
+    # the nearest value; of two equally near ones, the one with the even code
+    rank = np.where(best, np.where(codes[None, :] % 2 == 0, 0, 1), 2)
+    out = codes[np.argmin(rank, axis=1)].astype(np.uint8).reshape(v.shape)
+    out = np.where(np.isnan(v), np.uint8(0x7F), out)
+    sign = (np.signbit(v) & ~np.isnan(v)).astype(np.uint8) << 7
+    return (out | sign).astype(np.uint8)
+
+
+def e4m3_quantize(x, block: int = FP8_BLOCK):
+    """fp32 x [..., n] -> (codes uint8 [..., n], scales fp32 [..., n/block]):
+    scale = fl32(amax / 448) (1 for an all-zero block), code =
+    e4m3_nearest(fl32(x / scale)) ([P1] §4.2 1x128 scaling; [P5] range 448)."""
+    x = np.asarray(x, dtype=np.float32)
+    shp = x.shape
+    xb = x.reshape(*shp[:-1], shp[-1] // block, block)
+    amax = np.abs(xb).max(axis=-1)
+    scales = np.where(amax > 0, np.float32(amax) / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (xb / scales[..., None]).astype(np.float32)
+    return e4m3_nearest(q).reshape(shp), scales
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """fp32 x -> bf16 bit patterns, round to nearest even (NaN stays NaN)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, np.uint16(0x7FC0), r)
+
+
+def cache_append(kv, seq_lens, block_table, max_blocks: int, cache, base: float = ROPE_BASE):
+    """Write the rows of the S_q new tokens of every sequence into the cache.
+
+    kv [B, S_q, d_c + d_h^R] fp32: [c^KV ; W^KR h] of each new token (before
+    RoPE).  Token s of sequence b is row p = seq_len - S_q + s: page
+    block_table[b][p // 64] (contiguous: b * max_blocks + p // 64), slot p % 64.
+    The stored row is [c^KV ; RoPE(W^KR h, p)].  cache: a dict of numpy arrays
+    (modified copies are returned): {"rows": bf16 bits uint16 [NB, 64, 576]} or
+    the e4m3 bundle {"rows": uint8 [NB, 64, 512], "scales": fp32 [NB, 64, 4],
+    "rope": bf16 bits [NB, 64, 64]}.  bf16 values are round-to-nearest-even of
+    the fp32 c^KV and of the fp64 rotated key; e4m3 rows through e4m3_quantize."""
+    kv = np.asarray(kv, dtype=np.float32)
+    B, S = kv.shape[:2]
+    out = {k: np.array(v, copy=True) for k, v in cache.items()}
+    fp8 = "scales" in out
+    pos = token_positions(seq_lens, S)
+    for b in range(B):
+        for s in range(S):
+            p = int(pos[b, s])
+            if p < 0:
+                continue
+            page = (b * max_blocks + p // 64) if block_table is None else int(block_table[b][p // 64])
+            slot = p % 64
+            lat = kv[b, s, :D_C]
+            k_r = rope(kv[b, s, D_C:].astype(np.float64), p).astype(np.float32)
+            if fp8:
+                codes, sc = e4m3_quantize(lat)
+                out["rows"][page, slot] = codes
+                out["scales"][page, slot] = sc
+                out["rope"][page, slot] = to_bf16_bits(k_r)
+            else:
+                out["rows"][page, slot, :D_C] = to_bf16_bits(lat)
+                out["rows"][page, slot, D_C:] = to_bf16_bits(k_r)
+    return out

@@ -310,7 +310,13 @@ def _mutant_checks():
                      ("split", test_split_merge_identity),
                      ("mtp", test_mtp_tokens_match_single_token_decode),
                      ("e4m3", test_e4m3_decoder_matches_torch_all_codes),
-                     ("fp8rows", test_fp8_oracle_uses_dequantized_rows)]:
+                     ("fp8rows", test_fp8_oracle_uses_dequantized_rows),
+                     ("rope", test_rope_closed_forms),
+                     ("query", test_query_side_absorbs_and_rotates),
+                     ("output", test_output_side_recovers_unabsorbed_values),
+                     ("kvproj", test_kv_project_special_cases),
+                     ("quant", test_e4m3_quantize_against_torch_and_edge_cases),
+                     ("append", test_cache_append_writes_each_new_row_where_the_decode_reads_it)]:
         try:
             fn()
         except AssertionError:
@@ -348,8 +354,46 @@ def _bad_e4m3(codes):
     return _orig_e4m3(codes) * 2.0
 
 
+def _bad_rope_halves(x, pos, base=10000.0):
+    # pairs (i, i + d/2) instead of (2i, 2i + 1)
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    perm = np.stack([np.arange(d // 2), np.arange(d // 2) + d // 2], axis=1).reshape(-1)
+    inv = np.argsort(perm)
+    return _orig_rope(x[..., perm], pos, base)[..., inv]
+
+
+def _bad_rope_sign(x, pos, base=10000.0):
+    return _orig_rope(x, -np.asarray(pos), base)
+
+
+def _bad_positions(seq_lens, s_q):
+    return _orig_positions(seq_lens, s_q) + 1
+
+
+def _bad_nearest_truncate(v):
+    v = np.asarray(v, dtype=np.float64)
+    vals, codes = O._e4m3_table()
+    a = np.minimum(np.abs(v), 448.0)
+    idx = np.searchsorted(vals, a, side="right") - 1
+    out = codes[np.clip(idx, 0, len(codes) - 1)].astype(np.uint8)
+    return (out | ((np.signbit(v)).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def _bad_kv_swap(h, W_DKV, W_KR):
+    kv = _orig_kv(h, W_DKV, W_KR)
+    return np.concatenate([kv[..., 64:576], kv[..., :64]], axis=-1)
+
+
+def _bad_output_transpose(out_latent, W_UV):
+    return np.einsum("hdc,bshc->bshd", np.asarray(W_UV)[::-1], np.asarray(out_latent, dtype=np.float64))
+
+
 _orig_attend = O.attend_latent
 _orig_e4m3 = O.e4m3_decode
+_orig_rope = O.rope
+_orig_positions = O.token_positions
+_orig_kv = O.kv_project
 
 
 @pytest.mark.parametrize("target,mutant", [
@@ -359,6 +403,12 @@ _orig_e4m3 = O.e4m3_decode
     ("visible_rows", _bad_visible),
     ("merge_partials", _bad_merge),
     ("e4m3_decode", _bad_e4m3),
+    ("rope", _bad_rope_halves),
+    ("rope", _bad_rope_sign),
+    ("token_positions", _bad_positions),
+    ("e4m3_nearest", _bad_nearest_truncate),
+    ("kv_project", _bad_kv_swap),
+    ("output_side", _bad_output_transpose),
 ])
 def test_pins_catch_planted_oracle_mistakes(monkeypatch, target, mutant):
     monkeypatch.setattr(O, target, mutant)
@@ -372,3 +422,174 @@ def test_input_generator_rejects_unknown_cache_type():
     with pytest.raises(ValueError):
         make_inputs(dict(batch=1, s_q=1, lens=("explicit", [8]), layout="paged_shuffled", q_std=1.0,
                          cache="fp8", num_splits=None, unabsorbed=False, name="bad"), seed=0)
+
+
+# ====================================== the next rows: absorption, RoPE, cache append
+def test_rope_closed_forms():
+    """RoPE of unit vectors gives cos/sin of pos * 10000^(-2i/64) in the pair
+    (2i, 2i+1); position 0 is the identity; each pair keeps its length;
+    rotations compose; scores depend only on the distance of the positions."""
+    d = 64
+    for i, p in ((0, 1), (1, 1), (5, 7), (31, 1000)):
+        e = np.zeros(d)
+        e[2 * i] = 1.0
+        r = O.rope(e, p)
+        th = 10000.0 ** (-2.0 * i / d)
+        want = np.zeros(d)
+        want[2 * i], want[2 * i + 1] = math.cos(p * th), math.sin(p * th)
+        np.testing.assert_allclose(r, want, atol=1e-12)
+        e2 = np.zeros(d)
+        e2[2 * i + 1] = 1.0
+        r2 = O.rope(e2, p)
+        assert abs(r2[2 * i] + math.sin(p * th)) < 1e-12 and abs(r2[2 * i + 1] - math.cos(p * th)) < 1e-12
+    rng = np.random.default_rng(0)
+    x, k = rng.standard_normal(d), rng.standard_normal(d)
+    np.testing.assert_array_equal(O.rope(x, 0), x)
+    r = O.rope(x, 12345)
+    np.testing.assert_allclose(r[0::2] ** 2 + r[1::2] ** 2, x[0::2] ** 2 + x[1::2] ** 2, rtol=1e-12)
+    np.testing.assert_allclose(O.rope(O.rope(x, 300), 77), O.rope(x, 377), atol=1e-11)
+    for t, j in ((10, 3), (5000, 4990), (7, 0)):
+        np.testing.assert_allclose(O.rope(x, t) @ O.rope(k, j), O.rope(x, t - j) @ k, rtol=1e-10, atol=1e-10)
+    # positions broadcast over leading dims
+    xs = rng.standard_normal((3, 2, d))
+    pos = np.array([[1, 2], [3, 4], [5, 6]])
+    out = O.rope(xs, pos)
+    np.testing.assert_allclose(out[2, 1], O.rope(xs[2, 1], 6), atol=1e-13)
+
+
+def test_query_side_absorbs_and_rotates():
+    """q_absorbed . c^KV equals the unabsorbed q^C . (W^UK c^KV) for every head
+    ([P2] §2.1.3(B)); q_rope is q^R rotated to position seq_len - S_q + s, so
+    its score against a key rotated to row j depends only on the distance."""
+    rng = np.random.default_rng(1)
+    B, S, H, dh, dc = 2, 2, 4, 128, 512
+    q_c = rng.standard_normal((B, S, H, dh))
+    q_r = rng.standard_normal((B, S, H, 64))
+    W_UK = rng.standard_normal((H, dh, dc)) / math.sqrt(dc)
+    lens = np.array([9, 300])
+    q_abs, q_rot = O.query_side(q_c, q_r, W_UK, lens)
+    c = rng.standard_normal(dc)
+    for b in range(B):
+        for s in range(S):
+            for h in range(H):
+                np.testing.assert_allclose(q_abs[b, s, h] @ c, q_c[b, s, h] @ (W_UK[h] @ c), rtol=1e-11, atol=1e-11)
+    np.testing.assert_array_equal(O.token_positions(lens, S), [[7, 8], [298, 299]])
+    k = rng.standard_normal(64)
+    for b in range(B):
+        for s in range(S):
+            p = int(lens[b]) - S + s
+            for j in (0, p // 2, p):
+                np.testing.assert_allclose(q_rot[b, s, 1] @ O.rope(k, j), O.rope(q_r[b, s, 1], p - j) @ k,
+                                           rtol=1e-10, atol=1e-10)
+
+
+def test_output_side_recovers_unabsorbed_values():
+    """o = W^UV_h out_latent equals the unabsorbed attention's per-head value
+    output ([P2] §2.1.2): associativity on the output side."""
+    inp = make_inputs("single_b1_l128", seed=0)
+    q_c = inp.extra["q_c"][0, 0].numpy()
+    W_UK, W_UV = inp.extra["W_UK"].numpy(), inp.extra["W_UV"].numpy()
+    rows = O.sequence_rows(inp, 0, int(inp.seq_lens[0]))
+    q_r = inp.q_rope[0, 0].double().numpy()
+    q_abs = O.absorb_query(q_c, W_UK)
+    out_lat, _ = O.attend_latent(np.concatenate([q_abs, q_r], axis=1), rows, inp.scale)
+    o = O.output_side(out_lat[None, None], W_UV)[0, 0]
+    o_ref, _, _ = O.unabsorbed_attention(q_c, q_r, rows[:, :512], rows[:, 512:], W_UK, W_UV, inp.scale)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_kv_project_special_cases():
+    """Selection matrices pick the hidden state's own coordinates; the result
+    equals torch's fp64 linear layers."""
+    rng = np.random.default_rng(2)
+    T, d = 5, 700
+    h = rng.standard_normal((T, d))
+    W_DKV = np.zeros((512, d))
+    W_DKV[np.arange(512), np.arange(512)] = 1.0
+    W_KR = np.zeros((64, d))
+    W_KR[np.arange(64), 600 + np.arange(64)] = 1.0
+    kv = O.kv_project(h, W_DKV, W_KR)
+    np.testing.assert_array_equal(kv[:, :512], h[:, :512])
+    np.testing.assert_array_equal(kv[:, 512:], h[:, 600:664])
+    A, Bm = rng.standard_normal((512, d)), rng.standard_normal((64, d))
+    kv = O.kv_project(h, A, Bm)
+    ht = torch.from_numpy(h)
+    ref = torch.cat([torch.nn.functional.linear(ht, torch.from_numpy(A)),
+                     torch.nn.functional.linear(ht, torch.from_numpy(Bm))], dim=-1).numpy()
+    np.testing.assert_allclose(kv, ref, rtol=1e-12, atol=1e-10)
+
+
+def test_e4m3_quantize_against_torch_and_edge_cases():
+    """Codes equal torch's float8_e4m3fn cast of the fp32 quotient (round to
+    nearest even) wherever it is within range; every finite code is its own
+    nearest value; midpoints go to the even code; values past 448 saturate;
+    an all-zero block gets scale 1; the block's largest value maps to +-448."""
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn((16, 512), generator=g) * torch.logspace(-3, 3, 16)[:, None]).float()
+    x[2, :128] = 0.0
+    codes, scales = O.e4m3_quantize(x.numpy())
+    q = (x.reshape(16, 4, 128) / torch.from_numpy(scales)[..., None]).float()
+    ref = q.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).reshape(16, 512).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    assert scales[2, 0] == 1.0 and np.all(codes[2, :128] == 0)
+    amax = np.abs(x.numpy()).reshape(16, 4, 128).max(-1)
+    np.testing.assert_array_equal(scales, np.where(amax > 0, amax / np.float32(448), 1.0).astype(np.float32))
+    amax_idx = np.abs(x.numpy()).reshape(16, 4, 128).argmax(-1)
+    for r in (0, 7, 15):
+        for blk in range(4):
+            assert O.e4m3_decode(codes[r, blk * 128 + amax_idx[r, blk]]) in (448.0, -448.0)
+    # every finite code value is its own nearest; midpoints round to the even code
+    all_codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_decode(all_codes)
+    fin = np.isfinite(vals) & ~((all_codes == 0x80))          # -0 maps back to +0's twin below
+    np.testing.assert_array_equal(O.e4m3_nearest(vals[fin]), all_codes[fin])
+    assert O.e4m3_nearest(np.array([-0.0]))[0] == 0x80
+    pos_vals = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    mids = (pos_vals[:-1] + pos_vals[1:]) / 2
+    got = O.e4m3_nearest(mids)
+    assert np.all(got % 2 == 0)
+    assert np.all(O.e4m3_nearest(np.array([449.0, 470.0, 1e9, -1e9])) == [0x7E, 0x7E, 0x7E, 0xFE])
+
+
+def test_bf16_bits_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e38, 1e-40], dtype=np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    np.testing.assert_array_equal(O.to_bf16_bits(x), ref)
+
+
+def test_cache_append_writes_each_new_row_where_the_decode_reads_it():
+    """After cache_append the oracle's own row gather returns, at rows
+    seq_len - S_q + s, [c^KV ; RoPE(k, row)] (bf16) or its e4m3 encoding;
+    every other row is unchanged."""
+    for cache_kind in ("bf16", "fp8_e4m3"):
+        inp = small_inputs([70, 5, 130], s_q=2, cache=cache_kind, seed=4)
+        rng = np.random.default_rng(5)
+        kv = rng.standard_normal((3, 2, 576)).astype(np.float32)
+        if cache_kind == "bf16":
+            cache = {"rows": inp.cache.view(torch.int16).numpy().astype(np.uint16)}
+        else:
+            cache = {"rows": inp.cache.numpy(), "scales": inp.cache_scales.numpy(),
+                     "rope": inp.cache_rope.view(torch.int16).numpy().astype(np.uint16)}
+        before = [O.sequence_rows(inp, b, int(inp.seq_lens[b])) for b in range(3)]
+        new = O.cache_append(kv, inp.seq_lens.numpy(), inp.block_table.numpy(), inp.max_blocks, cache)
+        if cache_kind == "bf16":
+            inp.cache = torch.from_numpy(new["rows"].astype(np.int16)).view(torch.bfloat16)
+        else:
+            inp.cache = torch.from_numpy(new["rows"])
+            inp.cache_scales = torch.from_numpy(new["scales"])
+            inp.cache_rope = torch.from_numpy(new["rope"].astype(np.int16)).view(torch.bfloat16)
+        for b in range(3):
+            L = int(inp.seq_lens[b])
+            after = O.sequence_rows(inp, b, L)
+            np.testing.assert_array_equal(after[:L - 2], before[b][:L - 2])
+            for s in range(2):
+                row = after[L - 2 + s]
+                kr = O.rope(kv[b, s, 512:].astype(np.float64), L - 2 + s)
+                np.testing.assert_allclose(row[512:], kr, rtol=2 ** -8, atol=1e-30)
+                if cache_kind == "bf16":
+                    np.testing.assert_allclose(row[:512], kv[b, s, :512], rtol=2 ** -8)
+                else:
+                    sc = np.abs(kv[b, s, :512]).reshape(4, 128).max(1) / 448
+                    err = np.abs(row[:512] - kv[b, s, :512])
+                    assert np.all(err <= np.maximum(2 ** -4 * np.abs(kv[b, s, :512]), np.repeat(sc, 128) * 2 ** -10)
+                                  + 1e-12)
