@@ -213,6 +213,91 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: i
     return res
 
 
+def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int = 7168, seed: int = 0):
+    """Time the steps around the decode for one decode step of `batch`
+    sequences x `s_q` tokens (query absorption + RoPE, output absorption,
+    KV projection of the new tokens, cache append), each alone with HIP events
+    on the launch stream, inputs rotated past the Infinity Cache.  All four
+    are bound by HBM bytes (intensity well under the ridge)."""
+    import torch
+
+    import mla_latent_kv_39_amd as mla
+    from mla_latent_kv_39_amd.runner import DecodeWorkspace  # noqa: F401
+    g = torch.Generator().manual_seed(seed)
+    dev = torch.device("cuda", 0)
+    T = batch * s_q
+    stream = torch.cuda.current_stream()
+    lens = torch.randint(4096, 8193, (batch,), generator=g, dtype=torch.int32)
+    mb = 8192 // 64
+    table = torch.randperm(batch * mb, generator=g).to(torch.int32).reshape(batch, mb)
+
+    def rnd(*shape, dtype=torch.bfloat16, scale=1.0):
+        return (torch.randn(shape, generator=g) * scale).to(dtype).to(dev)
+
+    def timed(fn, nbytes, flops, name):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) / steps * 1e-3
+        rec = {"us": round(s * 1e6, 2), "algorithmic_bytes": nbytes, "mfma_flops": flops,
+               "gbs": round(nbytes / s / 1e9, 1), "bound": binding_bound(nbytes, max(flops, 1)),
+               "frac": round(roofline_frac(binding_bound(nbytes, max(flops, 1)), nbytes, flops, s), 4)}
+        print(f"[bench] {name}: {rec['us']} us, {rec['gbs']} GB/s, {rec['bound']} fraction {rec['frac']}",
+              file=sys.stderr, flush=True)
+        return rec
+
+    def copies_for(nbytes):
+        return max(1, min(16, int(math.ceil((1 << 30) / max(nbytes, 1))) + 1))
+
+    out = {"tokens": T, "hidden": hidden}
+    # query side
+    w_uk_t = rnd(128, 512, 128, scale=512 ** -0.5)
+    qb = T * 128 * (128 + 64) * 2
+    n = copies_for(qb + T * 128 * 576 * 2)
+    qs = [(rnd(batch, s_q, 128, 128), rnd(batch, s_q, 128, 64)) for _ in range(n)]
+    qa = torch.empty((batch, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
+    qr = torch.empty((batch, s_q, 128, 64), dtype=torch.bfloat16, device=dev)
+    lens_d = lens.to(dev)
+    out["absorb_query"] = timed(lambda i: mla.mla_absorb_query(qs[i % n][0], qs[i % n][1], w_uk_t, lens_d, qa, qr,
+                                                               stream=stream),
+                                qb + w_uk_t.numel() * 2 + T * 128 * 576 * 2 + batch * 4,
+                                2 * T * 128 * 128 * 512, "absorb_query")
+    del qs
+    # output side
+    w_uv = rnd(128, 128, 512, scale=512 ** -0.5)
+    ob = T * 128 * 512 * 4
+    n = copies_for(ob)
+    ols = [rnd(batch, s_q, 128, 512, dtype=torch.float32, scale=0.3) for _ in range(n)]
+    vals = torch.empty((batch, s_q, 128, 128), device=dev)
+    out["absorb_output"] = timed(lambda i: mla.mla_absorb_output(ols[i % n], w_uv, vals, stream=stream),
+                                 ob + w_uv.numel() * 2 + T * 128 * 128 * 4, 2 * T * 128 * 512 * 128, "absorb_output")
+    del ols
+    # KV projection of the new tokens
+    w_kv = rnd(576, hidden, scale=hidden ** -0.5)
+    hb = T * hidden * 2
+    n = copies_for(hb + w_kv.numel() * 2)
+    hs = [rnd(T, hidden) for _ in range(n)]
+    w_kvs = [w_kv] + [w_kv.clone() for _ in range(n - 1)]
+    kv = torch.empty((T, 576), device=dev)
+    out["kv_project"] = timed(lambda i: mla.mla_kv_project(hs[i % n], w_kvs[i % n], kv, stream=stream),
+                              hb + w_kv.numel() * 2 + T * 576 * 4, 2 * T * hidden * 576, "kv_project")
+    del hs, w_kvs
+    # cache append into a bf16 paged cache of the same batch shape
+    rows = torch.zeros((batch * mb, 64, 576), dtype=torch.bfloat16, device=dev)
+    cache = mla.LatentCache(mla.MLA_CACHE_BF16, rows)
+    table_d = table.to(dev)
+    kv3 = kv.view(batch, s_q, 576)
+    out["cache_append"] = timed(lambda i: mla.mla_cache_append(kv3, lens_d, table_d, cache, stream=stream),
+                                T * 576 * 4 + T * 1152 + batch * 4 + T * 4, 0, "cache_append")
+    return out
+
+
 def summary(r):
     """The per-workload record of config.workloads."""
     s = r["ms_step"] * 1e-3
@@ -265,6 +350,7 @@ def main(argv=None):
             if w != args.workload:
                 others[w] = summary(measure(w, args.steps, args.warmup, 0, args.seed))
     inp = head["inp"]
+    next_rows = None if args.only else measure_next_rows(inp.batch, inp.s_q, args.steps, args.warmup)
     ms_step, ms_decode = head["ms_step"], head["ms_decode"]
     nbytes, flops = head["bytes"], head["flops"]
     if head["bound"] == "hbm":
@@ -292,7 +378,8 @@ def main(argv=None):
                    "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
                    "query_row_pairs_per_s": round(flops / FLOP_PER_QROW_ROW / (ms_step * 1e-3), 1),
                    "decode_kernel_us": round(ms_decode * 1e3, 2),
-                   "algorithmic_bytes": nbytes, "mfma_flops": flops, "workloads": workloads},
+                   "algorithmic_bytes": nbytes, "mfma_flops": flops, "workloads": workloads,
+                   "around_the_decode": next_rows},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -54,6 +54,7 @@ extern "C" {
 #define MLA_NUM_HEADS 128   /* n_h */
 #define MLA_LATENT_DIM 512  /* d_c */
 #define MLA_ROPE_DIM 64     /* d_h^R */
+#define MLA_HEAD_DIM 128    /* d_h, per-head width of the unabsorbed query and value */
 #define MLA_ROW_DIM 576     /* d_c + d_h^R values cached per token */
 #define MLA_BLOCK_SIZE 64   /* rows per cache page */
 #define MLA_FP8_GROUP 128   /* latent values per fp8 scale */
@@ -218,6 +219,79 @@ int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t 
 /* Bytes of partial_out and partial_lse needed for (split count, s_q). */
 size_t mla_partial_out_bytes(int32_t num_splits, int32_t s_q);
 size_t mla_partial_lse_bytes(int32_t num_splits, int32_t s_q);
+
+/*
+ * The steps around the decode in one MLA attention layer.  RoPE (DeepSeek-V3
+ * architecture notes §2.1.3(A), (D); the pages give no formula: this library
+ * rotates consecutive pairs (x_{2i}, x_{2i+1}) of a 64-wide vector by the
+ * angle pos * rope_base^(-2i/64), computed in fp64) acts on q^R and on the
+ * cached k^R.  The position of query token s of sequence b, and of the cache
+ * row it appends, is seq_len[b] - S_q + s.
+ */
+
+/*
+ * mla_absorb_query: the decode's query inputs (§2.1.3(B): q^T W^UK c =
+ * (W^UK^T q)^T c; §2.1.3(D)).
+ *   q_c         bf16 [B, S_q, 128, 128]   q^C per head
+ *   q_r         bf16 [B, S_q, 128, 64]    q^R per head, before RoPE
+ *   w_uk_t      bf16 [128, 512, 128]      W^UK_h^T per head (W^UK_h is d_h x d_c; stored transposed,
+ *                                          so each output feature's 128 weights are contiguous)
+ *   seq_lens    int32 [B]                 positions seq_len - S_q + s
+ *   rope_base   the RoPE base (10000), finite and positive
+ *   q_absorbed  bf16 [B, S_q, 128, 512]   = W^UK_h^T q^C_h (fp32 accumulation, rounded once)
+ *   q_rope      bf16 [B, S_q, 128, 64]    = RoPE(q^R, position); may be q_r itself (in place)
+ * bf16 MFMA GEMM per head, then a RoPE kernel; any S_q >= 1.  Data pointers
+ * of q_c, w_uk_t and q_absorbed 16-byte aligned.
+ */
+mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const mla_tensor* w_uk_t,
+                            const mla_tensor* seq_lens, float rope_base, const mla_tensor* q_absorbed,
+                            const mla_tensor* q_rope, hipStream_t stream);
+
+/*
+ * mla_absorb_output: per-head values from the decode's latent-space output
+ * (§2.1.2: v^C = W^UV c^KV, moved past the softmax by associativity,
+ * §2.1.3(B)).
+ *   out_latent  fp32 [B, S_q, 128, 512]   mla_decode's output
+ *   w_uv        bf16 [128, 128, 512]      W^UV_h per head (d_h x d_c)
+ *   out_values  fp32 [B, S_q, 128, 128]   = W^UV_h out_latent_h
+ * bf16 MFMA GEMM per head (out_latent rounded to bf16 on load, fp32
+ * accumulation).  Data pointers of out_latent, w_uv and out_values 16-byte
+ * aligned.
+ */
+mla_status mla_absorb_output(const mla_tensor* out_latent, const mla_tensor* w_uv, const mla_tensor* out_values,
+                             hipStream_t stream);
+
+/*
+ * mla_kv_project: the cache row of each new token before its RoPE (§2.1.2:
+ * c^KV = W^DKV h; the decoupled key k = W^KR h of §2.1.3(D)).
+ *   hidden  bf16 [T, d]     d a multiple of 128 (7168 for DeepSeek-V3, §3)
+ *   w_kv    bf16 [576, d]   rows 0..511 W^DKV, rows 512..575 W^KR
+ *   kv      fp32 [T, 576]   = [W^DKV h ; W^KR h]
+ * bf16 MFMA GEMM with fp32 accumulation, K split over four waves.  hidden,
+ * w_kv and kv 16-byte aligned.
+ */
+mla_status mla_kv_project(const mla_tensor* hidden, const mla_tensor* w_kv, const mla_tensor* kv,
+                          hipStream_t stream);
+
+/*
+ * mla_cache_append: write each new token's row into its page slot, the rows
+ * mla_decode then reads (DeepSeek-V3 详解 §2.1: 576 values per token; §4.2:
+ * fine-grained 1x128 fp8 scaling).
+ *   kv           fp32 [B, S_q, 576]   [c^KV ; k] of the S_q new tokens (mla_kv_project)
+ *   seq_lens     int32 [B]            lengths that already count the new tokens
+ *   block_table  int32 [B, max_blocks], or NULL for a contiguous cache
+ *   cache        the latent cache (bf16 or e4m3 bundle), written in place
+ *   rope_base    the RoPE base (10000)
+ * Row p = seq_len - S_q + s of sequence b gets [c^KV ; RoPE(k, p)]: bf16
+ * (round to nearest even), or for an e4m3 cache, per 128-wide block,
+ * scale = amax / 448 in fp32 (1 for an all-zero block), code = the e4m3 value
+ * nearest to x / scale (fp32 quotient, ties to the even code, saturated at
+ * +-448), and k^R in bf16.  A row whose position falls outside the block
+ * table or whose page lies outside the cache is not written.  kv and the
+ * cache rows 16-byte aligned.
+ */
+mla_status mla_cache_append(const mla_tensor* kv, const mla_tensor* seq_lens, const mla_tensor* block_table,
+                            const mla_latent_cache* cache, float rope_base, hipStream_t stream);
 
 /*
  * mla_check_indices: the device-side contract of mla_decode, checked on the

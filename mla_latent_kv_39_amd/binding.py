@@ -48,8 +48,10 @@ MAX_RANK = 5
 
 # every symbol include/mla.h declares
 EXPORTED_SYMBOLS = ("mla_decode", "mla_combine", "mla_decode_noalloc", "mla_num_splits_hint",
-                    "mla_partial_out_bytes", "mla_partial_lse_bytes", "mla_check_indices", "mla_init",
+                    "mla_partial_out_bytes", "mla_partial_lse_bytes", "mla_absorb_query", "mla_absorb_output",
+                    "mla_kv_project", "mla_cache_append", "mla_check_indices", "mla_init",
                     "mla_status_string", "mla_version")
+ROPE_BASE = 10000.0
 
 
 class MlaError(RuntimeError):
@@ -86,6 +88,14 @@ def _load():
     lib.mla_combine.argtypes = [T, T, T, T, T, vp]
     lib.mla_decode_noalloc.restype = i32
     lib.mla_decode_noalloc.argtypes = [T, T, C, T, T, f32, T, T, i32, vp]
+    lib.mla_absorb_query.restype = i32
+    lib.mla_absorb_query.argtypes = [T, T, T, T, f32, T, T, vp]
+    lib.mla_absorb_output.restype = i32
+    lib.mla_absorb_output.argtypes = [T, T, T, vp]
+    lib.mla_kv_project.restype = i32
+    lib.mla_kv_project.argtypes = [T, T, T, vp]
+    lib.mla_cache_append.restype = i32
+    lib.mla_cache_append.argtypes = [T, T, T, C, f32, vp]
     lib.mla_check_indices.restype = i32
     lib.mla_check_indices.argtypes = [C, T, T, T, vp]
     lib.mla_init.restype = i32
@@ -250,3 +260,39 @@ def mla_check_indices(cache: LatentCache, block_table, seq_lens, counts, stream=
     st = _lib.mla_check_indices(ctypes.byref(c), *[_ref(a) for a in args], _stream_handle(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_check_indices")
+
+
+def mla_absorb_query(q_c, q_r, w_uk_t, seq_lens, q_absorbed, q_rope, rope_base: float = ROPE_BASE,
+                     stream=None) -> None:
+    """Enqueue mla_absorb_query: q_absorbed = W^UK_h^T q^C_h, q_rope = RoPE(q^R, position)."""
+    args = [tensor(x) for x in (q_c, q_r, w_uk_t, seq_lens)] + [tensor(q_absorbed), tensor(q_rope)]
+    st = _lib.mla_absorb_query(*[_ref(a) for a in args[:4]], float(rope_base), _ref(args[4]), _ref(args[5]),
+                               _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_absorb_query")
+
+
+def mla_absorb_output(out_latent, w_uv, out_values, stream=None) -> None:
+    """Enqueue mla_absorb_output: out_values = W^UV_h out_latent_h per head."""
+    args = [tensor(out_latent), tensor(w_uv), tensor(out_values)]
+    st = _lib.mla_absorb_output(*[_ref(a) for a in args], _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_absorb_output")
+
+
+def mla_kv_project(hidden, w_kv, kv, stream=None) -> None:
+    """Enqueue mla_kv_project: kv = [W^DKV ; W^KR] hidden (fp32)."""
+    args = [tensor(hidden), tensor(w_kv), tensor(kv)]
+    st = _lib.mla_kv_project(*[_ref(a) for a in args], _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_kv_project")
+
+
+def mla_cache_append(kv, seq_lens, block_table, cache: LatentCache, rope_base: float = ROPE_BASE,
+                     stream=None) -> None:
+    """Enqueue mla_cache_append: each new token's row into its page slot (bf16 or e4m3)."""
+    c = cache.desc()
+    args = [tensor(kv), tensor(seq_lens), tensor(block_table)]
+    st = _lib.mla_cache_append(*[_ref(a) for a in args], ctypes.byref(c), float(rope_base), _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_cache_append")

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode_asm.cpp", "mla_combine.hip", "mla_check.hip", "mla_noalloc.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode_asm.cpp", "mla_combine.hip", "mla_check.hip", "mla_noalloc.hip",
+           "mla_proj.hip"]
 ARCH = "gfx950"
 
 

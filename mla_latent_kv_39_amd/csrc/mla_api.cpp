@@ -34,6 +34,8 @@ mla_status check_device() {
 
 bool present(const mla_tensor* t) { return t != nullptr && t->data != nullptr; }
 
+bool aligned16(const mla_tensor* t) { return ((uintptr_t)t->data & 15) == 0; }
+
 // dtype, then rank and shape (want[k] < 0: any size >= 1), then dense row-major strides
 mla_status check_tensor(const mla_tensor* t, mla_dtype dtype, int rank, const int64_t* want) {
   if (!present(t)) return MLA_ERR_NULL;
@@ -272,6 +274,151 @@ mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_
   return mla::launch_combine(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const mla_tensor* w_uk_t,
+                            const mla_tensor* seq_lens, float rope_base, const mla_tensor* q_absorbed,
+                            const mla_tensor* q_rope, hipStream_t stream) {
+  if (!present(q_c)) return MLA_ERR_NULL;
+  if (q_c->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
+  if (q_c->rank != 4) return MLA_ERR_SHAPE;
+  const int64_t B = q_c->shape[0], S = q_c->shape[1];
+  const int64_t wc[4] = {B, S, MLA_NUM_HEADS, MLA_HEAD_DIM};
+  const int64_t wr[4] = {B, S, MLA_NUM_HEADS, MLA_ROPE_DIM};
+  const int64_t ww[3] = {MLA_NUM_HEADS, MLA_LATENT_DIM, MLA_HEAD_DIM};
+  const int64_t wa[4] = {B, S, MLA_NUM_HEADS, MLA_LATENT_DIM};
+  const int64_t wl[1] = {B};
+  MLA_TRY(check_tensor(q_c, MLA_DTYPE_BF16, 4, wc));
+  MLA_TRY(check_tensor(q_r, MLA_DTYPE_BF16, 4, wr));
+  MLA_TRY(check_tensor(w_uk_t, MLA_DTYPE_BF16, 3, ww));
+  MLA_TRY(check_tensor(seq_lens, MLA_DTYPE_INT32, 1, wl));
+  MLA_TRY(check_tensor(q_absorbed, MLA_DTYPE_BF16, 4, wa));
+  MLA_TRY(check_tensor(q_rope, MLA_DTYPE_BF16, 4, wr));
+  if (!(std::isfinite(rope_base) && rope_base > 0.f)) return MLA_ERR_SHAPE;
+  if (B * S > INT_MAX / (MLA_NUM_HEADS * MLA_LATENT_DIM)) return MLA_ERR_SHAPE;
+  if (!aligned16(q_c) || !aligned16(w_uk_t) || !aligned16(q_absorbed)) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
+  mla::GemmParams g;
+  g.a = q_c->data;
+  g.w = static_cast<const __bf16*>(w_uk_t->data);
+  g.c = q_absorbed->data;
+  g.a_batch = MLA_HEAD_DIM;                    // head h of a token row
+  g.a_row = (int64_t)MLA_NUM_HEADS * MLA_HEAD_DIM;
+  g.w_batch = (int64_t)MLA_LATENT_DIM * MLA_HEAD_DIM;
+  g.c_batch = MLA_LATENT_DIM;
+  g.c_row = (int64_t)MLA_NUM_HEADS * MLA_LATENT_DIM;
+  g.m_len = (int32_t)(B * S);
+  g.n_len = MLA_LATENT_DIM;
+  g.k_len = MLA_HEAD_DIM;
+  if (mla::launch_gemm_nt(g, MLA_NUM_HEADS, mla::GemmKind::kBf16ToBf16Wide, stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  mla::RopeParams r;
+  r.src = static_cast<const __bf16*>(q_r->data);
+  r.dst = static_cast<__bf16*>(q_rope->data);
+  r.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  r.tokens = (int32_t)(B * S);
+  r.s_q = (int32_t)S;
+  r.base = rope_base;
+  return mla::launch_query_rope(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_absorb_output(const mla_tensor* out_latent, const mla_tensor* w_uv, const mla_tensor* out_values,
+                             hipStream_t stream) {
+  if (!present(out_latent)) return MLA_ERR_NULL;
+  if (out_latent->dtype != MLA_DTYPE_FP32) return MLA_ERR_DTYPE;
+  if (out_latent->rank != 4) return MLA_ERR_SHAPE;
+  const int64_t B = out_latent->shape[0], S = out_latent->shape[1];
+  const int64_t wo[4] = {B, S, MLA_NUM_HEADS, MLA_LATENT_DIM};
+  const int64_t ww[3] = {MLA_NUM_HEADS, MLA_HEAD_DIM, MLA_LATENT_DIM};
+  const int64_t wv[4] = {B, S, MLA_NUM_HEADS, MLA_HEAD_DIM};
+  MLA_TRY(check_tensor(out_latent, MLA_DTYPE_FP32, 4, wo));
+  MLA_TRY(check_tensor(w_uv, MLA_DTYPE_BF16, 3, ww));
+  MLA_TRY(check_tensor(out_values, MLA_DTYPE_FP32, 4, wv));
+  if (B * S > INT_MAX / (MLA_NUM_HEADS * MLA_LATENT_DIM)) return MLA_ERR_SHAPE;
+  if (!aligned16(out_latent) || !aligned16(w_uv) || !aligned16(out_values)) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
+  mla::GemmParams g;
+  g.a = out_latent->data;
+  g.w = static_cast<const __bf16*>(w_uv->data);
+  g.c = out_values->data;
+  g.a_batch = MLA_LATENT_DIM;
+  g.a_row = (int64_t)MLA_NUM_HEADS * MLA_LATENT_DIM;
+  g.w_batch = (int64_t)MLA_HEAD_DIM * MLA_LATENT_DIM;
+  g.c_batch = MLA_HEAD_DIM;
+  g.c_row = (int64_t)MLA_NUM_HEADS * MLA_HEAD_DIM;
+  g.m_len = (int32_t)(B * S);
+  g.n_len = MLA_HEAD_DIM;
+  g.k_len = MLA_LATENT_DIM;
+  return mla::launch_gemm_nt(g, MLA_NUM_HEADS, mla::GemmKind::kF32ToF32Wide, stream) == hipSuccess
+             ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_kv_project(const mla_tensor* hidden, const mla_tensor* w_kv, const mla_tensor* kv,
+                          hipStream_t stream) {
+  if (!present(hidden)) return MLA_ERR_NULL;
+  if (hidden->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
+  if (hidden->rank != 2) return MLA_ERR_SHAPE;
+  const int64_t T = hidden->shape[0], D = hidden->shape[1];
+  const int64_t wh[2] = {T, D};
+  const int64_t ww[2] = {MLA_ROW_DIM, D};
+  const int64_t wk[2] = {T, MLA_ROW_DIM};
+  MLA_TRY(check_tensor(hidden, MLA_DTYPE_BF16, 2, wh));
+  MLA_TRY(check_tensor(w_kv, MLA_DTYPE_BF16, 2, ww));
+  MLA_TRY(check_tensor(kv, MLA_DTYPE_FP32, 2, wk));
+  if (D % 128 != 0 || D > (1 << 20) || T > INT_MAX / MLA_ROW_DIM) return MLA_ERR_SHAPE;
+  if (!aligned16(hidden) || !aligned16(w_kv) || !aligned16(kv)) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
+  mla::GemmParams g;
+  g.a = hidden->data;
+  g.w = static_cast<const __bf16*>(w_kv->data);
+  g.c = kv->data;
+  g.a_batch = g.w_batch = g.c_batch = 0;
+  g.a_row = D;
+  g.c_row = MLA_ROW_DIM;
+  g.m_len = (int32_t)T;
+  g.n_len = MLA_ROW_DIM;
+  g.k_len = (int32_t)D;
+  return mla::launch_gemm_nt(g, 1, mla::GemmKind::kBf16ToF32SplitK, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_cache_append(const mla_tensor* kv, const mla_tensor* seq_lens, const mla_tensor* block_table,
+                            const mla_latent_cache* cache, float rope_base, hipStream_t stream) {
+  if (!present(kv)) return MLA_ERR_NULL;
+  if (kv->dtype != MLA_DTYPE_FP32) return MLA_ERR_DTYPE;
+  if (kv->rank != 3) return MLA_ERR_SHAPE;
+  const int64_t B = kv->shape[0], S = kv->shape[1];
+  const int64_t wk[3] = {B, S, MLA_ROW_DIM};
+  const int64_t wl[1] = {B};
+  MLA_TRY(check_tensor(kv, MLA_DTYPE_FP32, 3, wk));
+  MLA_TRY(check_tensor(seq_lens, MLA_DTYPE_INT32, 1, wl));
+  const bool paged = present(block_table);
+  int64_t max_blocks = 0;
+  if (paged) {
+    const int64_t wt[2] = {B, -1};
+    MLA_TRY(check_tensor(block_table, MLA_DTYPE_INT32, 2, wt));
+    max_blocks = block_table->shape[1];
+  }
+  CacheView cv;
+  MLA_TRY(check_cache(cache, paged, B, &cv));
+  if (!paged) max_blocks = cv.contig_blocks;
+  if (!(std::isfinite(rope_base) && rope_base > 0.f)) return MLA_ERR_SHAPE;
+  if (B * S > INT_MAX || max_blocks > INT_MAX / 128) return MLA_ERR_SHAPE;
+  if (!aligned16(kv) || !aligned16(&cache->rows)) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
+  mla::AppendParams p;
+  p.kv = static_cast<const float*>(kv->data);
+  p.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  p.block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
+  p.rows = cache->rows.data;
+  p.scales = cv.fp8 ? static_cast<float*>(cache->scales.data) : nullptr;
+  p.rope = cv.fp8 ? static_cast<__bf16*>(cache->rope.data) : nullptr;
+  p.num_blocks = cv.num_blocks;
+  p.max_blocks = (int32_t)max_blocks;
+  p.batch = (int32_t)B;
+  p.s_q = (int32_t)S;
+  p.fp8 = cv.fp8 ? 1 : 0;
+  p.base = rope_base;
+  return mla::launch_cache_append(p, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 mla_status mla_check_indices(const mla_latent_cache* cache, const mla_tensor* block_table,
                              const mla_tensor* seq_lens, const mla_tensor* counts, hipStream_t stream) {
   if (!present(seq_lens)) return MLA_ERR_NULL;
@@ -358,6 +505,6 @@ const char* mla_status_string(mla_status status) {
   return "unknown status";
 }
 
-int32_t mla_version(void) { return 30100; }  // 3.1.0: + mla_decode_noalloc
+int32_t mla_version(void) { return 30200; }  // 3.2.0: + absorption, KV projection and cache append
 
 }  // extern "C"

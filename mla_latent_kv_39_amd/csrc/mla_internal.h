@@ -68,6 +68,55 @@ struct CheckParams {
 };
 hipError_t launch_check_indices(const CheckParams& p, hipStream_t stream);
 
+// C[M x N] = A[M x K] W[N x K]^T per batch (mla_proj.hip): element offsets
+// A (m, k) = z a_batch + m a_row + k, W (n, k) = z w_batch + n k_len + k,
+// C (m, n) = z c_batch + m c_row + n.  k_len % 128 == 0; n_len a multiple of
+// the kind's tile width (128 for the wide kinds, 32 for the split-K kind);
+// 16-byte aligned A, W and C rows.
+struct GemmParams {
+  const void* a;
+  const __bf16* w;
+  void* c;
+  int64_t a_batch, a_row, w_batch, c_batch, c_row;
+  int32_t m_len, n_len, k_len;
+};
+enum class GemmKind {
+  kF32ToF32Wide,    // fp32 A (rounded to bf16 on load), fp32 C, 64 x 128 tiles
+  kBf16ToBf16Wide,  // bf16 A, bf16 C, 64 x 128 tiles
+  kBf16ToF32SplitK  // bf16 A, fp32 C, 16 x 32 tiles, K split over the four waves
+};
+hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream);
+
+// RoPE of the query's q^R: [tokens = B S_q, 128, 64] bf16 -> bf16, position
+// seq_len[b] - S_q + s of token b S_q + s.
+struct RopeParams {
+  const __bf16* src;
+  __bf16* dst;
+  const int32_t* seq_lens;
+  int32_t tokens;
+  int32_t s_q;
+  double base;
+};
+hipError_t launch_query_rope(const RopeParams& p, hipStream_t stream);
+
+// New cache rows: kv [B S_q, 576] fp32 ([c^KV ; k^R before RoPE]) -> the page
+// slot of position seq_len[b] - S_q + s, bf16 rows or the e4m3 bundle.
+struct AppendParams {
+  const float* kv;
+  const int32_t* seq_lens;
+  const int32_t* block_table;   // [B, max_blocks] or nullptr (contiguous)
+  void* rows;                   // bf16 [NB, 64, 576] or e4m3 [NB, 64, 512]
+  float* scales;                // e4m3: [NB, 64, 4]
+  __bf16* rope;                 // e4m3: [NB, 64, 64]
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t s_q;
+  int32_t fp8;
+  double base;
+};
+hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream);
+
 // Load the decode code object on the current device (idempotent).
 hipError_t load_decode_module();
 

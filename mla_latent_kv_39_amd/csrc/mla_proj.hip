@@ -1,0 +1,289 @@
+// The steps around the decode in one MLA attention layer (DeepSeek-V3
+// architecture notes, deepseek.csdn.net, §2.1.2 and §2.1.3(B), (D)):
+//
+//   absorbed query   q_absorbed_h = W^UK_h^T q^C_h         (per head, 128 -> 512)
+//   query RoPE       q_rope = RoPE(q^R, position)
+//   output values    o_h = W^UV_h out_latent_h              (per head, 512 -> 128)
+//   KV projection    [c^KV ; k] = [W^DKV ; W^KR] h          (d -> 512 + 64)
+//   cache append     row = [c^KV ; RoPE(k, position)] into its page slot,
+//                    bf16, or e4m3 with one fp32 scale per 128 values
+//                    (DeepSeek-V3 详解, yudonglee.me, §4.2)
+//
+// The three projections are one kernel: C[M x N] = A[M x K] W[N x K]^T on
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, batched over
+// heads.  M is the number of tokens of a decode step (a few hundred): every
+// weight is read once per 64-token tile, so the kernels are bound by the
+// weight and activation bytes, and operands go straight from global memory
+// into MFMA registers (16-byte loads); only the finished tile passes through
+// LDS, to be written in 16-byte row chunks.
+#include <hip/hip_bf16.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// A fragment of the MFMA's A or B operand: 8 consecutive K values of one row.
+__device__ __forceinline__ bf16x8 frag_bf16(const __bf16* p, bool ok) {
+  uint4 u = make_uint4(0, 0, 0, 0);
+  if (ok) u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 frag_f32(const float* p, bool ok) {
+  float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+  if (ok) {
+    lo = reinterpret_cast<const float4*>(p)[0];
+    hi = reinterpret_cast<const float4*>(p)[1];
+  }
+  bf16x8 r;   // round to nearest even
+  r[0] = (__bf16)lo.x;
+  r[1] = (__bf16)lo.y;
+  r[2] = (__bf16)lo.z;
+  r[3] = (__bf16)lo.w;
+  r[4] = (__bf16)hi.x;
+  r[5] = (__bf16)hi.y;
+  r[6] = (__bf16)hi.z;
+  r[7] = (__bf16)hi.w;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 frag(const __bf16* p, bool ok) { return frag_bf16(p, ok); }
+__device__ __forceinline__ bf16x8 frag(const float* p, bool ok) { return frag_f32(p, ok); }
+
+// four consecutive outputs: one 16-byte (fp32) or 8-byte (bf16) store
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(__bf16* p, const float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 h;
+  h[0] = (__bf16)v[0];
+  h[1] = (__bf16)v[1];
+  h[2] = (__bf16)v[2];
+  h[3] = (__bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = h;
+}
+
+// C (m, n) = sum_k A (m, k) W (n, k), batch z:
+//   A (m, k) at a + z a_batch + m a_row + k,  W (n, k) at w + z w_batch + n k_len + k,
+//   C (m, n) at c + z c_batch + m c_row + n.
+// KW = 1: the four waves form a 2 x 2 grid, each owning (16 WM) x (16 WN)
+// outputs over all of K; KW = 4: all four own the same (16 WM) x (16 WN)
+// outputs, each over a quarter of K (for long K and few outputs), and the
+// quarters are summed in LDS in a fixed order.  Loads run four K-steps (128)
+// ahead of their MFMAs.  The tile goes through LDS so that C is written in
+// 16-byte row chunks.  Requires k_len % (32 KW) == 0 and n_len a multiple of
+// the tile width; rows m >= m_len are neither read nor written.
+template <typename TA, typename TC, int WM, int WN, int KW>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
+  constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
+  constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
+  constexpr int PITCH = TN + 4;                  // floats per LDS row
+  constexpr int COPIES = KW == 1 ? 1 : 4;
+  __shared__ float s_tile[COPIES * TM * PITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int wm0 = KW == 1 ? (wave & 1) * (16 * WM) : 0;     // this wave's block inside the tile
+  const int wn0 = KW == 1 ? (wave >> 1) * (16 * WN) : 0;
+  const int m0 = blockIdx.y * TM + wm0;
+  const int n0 = blockIdx.x * TN + wn0;
+  const int kq = g.k_len / KW;
+  const int kbeg = KW == 1 ? 0 : wave * kq;
+  const int64_t z = blockIdx.z;
+  const TA* A = static_cast<const TA*>(g.a) + z * g.a_batch;
+  const __bf16* W = g.w + z * g.w_batch;
+  const TA* arow[WM];
+  bool aok[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int m = m0 + 16 * i + r16;
+    aok[i] = m < g.m_len;
+    arow[i] = A + (int64_t)(aok[i] ? m : 0) * g.a_row + kbeg + 8 * kg;
+  }
+  const __bf16* wrow[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) wrow[j] = W + (int64_t)(n0 + 16 * j + r16) * g.k_len + kbeg + 8 * kg;
+  floatx4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  int k = 0;
+  for (; k + 32 * U <= kq; k += 32 * U) {
+    bf16x8 a[U][WM], b[U][WN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i) a[u][i] = frag(arow[i] + k + 32 * u, aok[i]);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) b[u][j] = frag_bf16(wrow[j] + k + 32 * u, true);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+  }
+  for (; k < kq; k += 32) {
+    bf16x8 a[WM], b[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) a[i] = frag(arow[i] + k, aok[i]);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) b[j] = frag_bf16(wrow[j] + k, true);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  // lane (r16, kg) holds rows 4 kg .. 4 kg + 3 of column r16 of each 16 x 16 block
+  float* mine = s_tile + (KW == 1 ? 0 : wave * TM * PITCH);
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine[(wm0 + 16 * i + 4 * kg + q) * PITCH + wn0 + 16 * j + r16] = acc[i][j][q];
+  __syncthreads();
+  // the tile, row by row, four columns per thread
+  TC* C = static_cast<TC*>(g.c) + z * g.c_batch;
+  const int mt = blockIdx.y * TM, nt = blockIdx.x * TN;
+  for (int e = threadIdx.x; e < TM * (TN / 4); e += 256) {
+    const int r = e / (TN / 4), c4 = (e % (TN / 4)) * 4;
+    if (mt + r >= g.m_len) continue;
+    float v[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      v[x] = s_tile[r * PITCH + c4 + x];
+#pragma unroll
+      for (int w = 1; w < COPIES; ++w) v[x] += s_tile[(w * TM + r) * PITCH + c4 + x];
+    }
+    TC* dst = C + (int64_t)(mt + r) * g.c_row + nt + c4;
+    store4(dst, v);
+  }
+}
+
+template <typename TA, typename TC, int WM, int WN, int KW>
+hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
+  constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
+  constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
+  const dim3 grid((unsigned)(g.n_len / TN), (unsigned)((g.m_len + TM - 1) / TM), (unsigned)batches);
+  hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW>), grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+// RoPE of one pair at `pos`: angle pos * base^(-2i/d) in fp64 (positions run
+// to 1e5 and more, where an fp32 angle would be off by 1e-2 rad).
+__device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, int d, double base, float* y0,
+                                          float* y1) {
+  const double theta = pow(base, -2.0 * (double)i / (double)d);
+  double sn, cs;
+  sincos((double)pos * theta, &sn, &cs);
+  *y0 = (float)((double)x0 * cs - (double)x1 * sn);
+  *y1 = (float)((double)x0 * sn + (double)x1 * cs);
+}
+
+// q_rope of query token t = b S_q + s, head h, pair i: position seq_len[b] - S_q + s.
+__global__ __launch_bounds__(256) void query_rope_kernel(RopeParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pairs = (int64_t)p.tokens * kHeads * (kRope / 2);
+  if (idx >= pairs) return;
+  const int i = (int)(idx % (kRope / 2));
+  const int64_t t = idx / ((int64_t)kHeads * (kRope / 2));
+  const int b = (int)(t / p.s_q), s = (int)(t % p.s_q);
+  const int pos = p.seq_lens[b] - p.s_q + s;
+  const __bf16* x = p.src + idx * 2;
+  float y0, y1;
+  rope_pair((float)x[0], (float)x[1], pos, i, kRope, p.base, &y0, &y1);
+  p.dst[idx * 2] = (__bf16)y0;
+  p.dst[idx * 2 + 1] = (__bf16)y1;
+}
+
+// OCP E4M3 code of the value nearest to v (ties to the even code), saturated
+// to +-448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);   // subnormal steps of 2^-9 (8 = 2^-6)
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;  // 2^e <= a < 2^(e+1), -6 <= e <= 8
+  const int m = (int)rintf(ldexpf(a, 3 - e));                    // 8 .. 16
+  const int code = ((e + 7) << 3) + m - 8;                       // m = 16 carries into the exponent
+  return sign | (uint32_t)(code > 0x7E ? 0x7E : code);
+}
+
+// One new row per workgroup (token t = b S_q + s, position seq_len - S_q + s):
+// 128 threads, thread k holds latent values 4k .. 4k + 3 (block k / 32),
+// threads 0..31 the RoPE pairs.  A position outside the block table's
+// capacity or a page outside the cache is skipped (nothing is written).
+__global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
+  const int t = blockIdx.x;
+  const int b = t / p.s_q, s = t % p.s_q;
+  const int pos = p.seq_lens[b] - p.s_q + s;
+  if (pos < 0 || pos >= p.max_blocks * kPage) return;
+  const int64_t entry = (int64_t)b * p.max_blocks + pos / kPage;
+  const int64_t page = p.block_table ? (int64_t)p.block_table[entry] : entry;
+  if (page < 0 || page >= p.num_blocks) return;
+  const int64_t slot = page * kPage + (pos % kPage);
+  const int tid = threadIdx.x;
+  const float* row = p.kv + (int64_t)t * kRow;
+  const float4 v = reinterpret_cast<const float4*>(row)[tid];
+  float k0 = 0.f, k1 = 0.f;
+  if (tid < kRope / 2) rope_pair(row[kLatent + 2 * tid], row[kLatent + 2 * tid + 1], pos, tid, kRope, p.base, &k0, &k1);
+  if (!p.fp8) {
+    __bf16* dst = static_cast<__bf16*>(p.rows) + slot * kRow;
+    dst[4 * tid] = (__bf16)v.x;
+    dst[4 * tid + 1] = (__bf16)v.y;
+    dst[4 * tid + 2] = (__bf16)v.z;
+    dst[4 * tid + 3] = (__bf16)v.w;
+    if (tid < kRope / 2) {
+      dst[kLatent + 2 * tid] = (__bf16)k0;
+      dst[kLatent + 2 * tid + 1] = (__bf16)k1;
+    }
+    return;
+  }
+  // e4m3: block amax over the 32 threads of the block (lanes 0..31 / 32..63 of a wave)
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  const uint32_t code = e4m3_encode(__fdiv_rn(v.x, sc)) | (e4m3_encode(__fdiv_rn(v.y, sc)) << 8) |
+                        (e4m3_encode(__fdiv_rn(v.z, sc)) << 16) | (e4m3_encode(__fdiv_rn(v.w, sc)) << 24);
+  reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.rows) + slot * kLatent)[tid] = code;
+  if ((tid & 31) == 0) p.scales[slot * 4 + tid / 32] = sc;
+  if (tid < kRope / 2) {
+    p.rope[slot * kRope + 2 * tid] = (__bf16)k0;
+    p.rope[slot * kRope + 2 * tid + 1] = (__bf16)k1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream) {
+  switch (kind) {
+    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 2, 4, 1>(g, batches, stream);
+    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 2, 4, 1>(g, batches, stream);
+    case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 1, 2, 4>(g, batches, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_query_rope(const RopeParams& p, hipStream_t stream) {
+  const int64_t pairs = (int64_t)p.tokens * kHeads * (kRope / 2);
+  hipLaunchKernelGGL(query_rope_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(cache_append_kernel, dim3((unsigned)(p.batch * p.s_q)), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

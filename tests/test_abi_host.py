@@ -251,3 +251,47 @@ def test_descriptor_of_a_tensor(lib):
     v = lib.tensor(t.transpose(0, 1), device_only=False)
     assert list(v.strides)[:3] == [5, 20, 1]
     assert lib.tensor(None).data is None
+
+
+def test_next_rows_reject_bad_descriptors(lib):
+    E = lib
+    c = lib.library()
+    bf, f32, i32 = lib.MLA_DTYPE_BF16, lib.MLA_DTYPE_FP32, lib.MLA_DTYPE_INT32
+    B, S = 3, 2
+    qc, qr = desc(lib, (B, S, 128, 128), bf), desc(lib, (B, S, 128, 64), bf)
+    wuk, lens = desc(lib, (128, 512, 128), bf), desc(lib, (B,), i32)
+    qa, qo = desc(lib, (B, S, 128, 512), bf), desc(lib, (B, S, 128, 64), bf)
+
+    def aq(**kw):
+        a = dict(qc=qc, qr=qr, wuk=wuk, lens=lens, base=10000.0, qa=qa, qo=qo)
+        a.update(kw)
+        return c.mla_absorb_query(_ref(a["qc"]), _ref(a["qr"]), _ref(a["wuk"]), _ref(a["lens"]), a["base"],
+                                  _ref(a["qa"]), _ref(a["qo"]), None)
+    assert aq(qc=None) == E.MLA_ERR_NULL
+    assert aq(qc=desc(lib, (B, S, 64, 128), bf)) == E.MLA_ERR_SHAPE                # H = 128
+    assert aq(wuk=desc(lib, (128, 128, 512), bf)) == E.MLA_ERR_SHAPE               # W^UK_h^T is [512, 128]
+    assert aq(qa=desc(lib, (B, S, 128, 512), f32)) == E.MLA_ERR_DTYPE
+    assert aq(base=float("nan")) == E.MLA_ERR_SHAPE
+    assert aq(base=-1.0) == E.MLA_ERR_SHAPE
+    assert aq(qc=desc(lib, (B, S, 128, 128), bf, data=FAKE + 8)) == E.MLA_ERR_SHAPE   # 16-byte loads
+
+    ol, wuv, ov = desc(lib, (B, S, 128, 512), f32), desc(lib, (128, 128, 512), bf), desc(lib, (B, S, 128, 128), f32)
+    assert c.mla_absorb_output(_ref(ol), _ref(desc(lib, (128, 512, 128), bf)), _ref(ov), None) == E.MLA_ERR_SHAPE
+    assert c.mla_absorb_output(_ref(desc(lib, (B, S, 128, 512), bf)), _ref(wuv), _ref(ov), None) == E.MLA_ERR_DTYPE
+    assert c.mla_absorb_output(_ref(ol), _ref(wuv), _ref(desc(lib, (B, S, 128, 64), f32)), None) == E.MLA_ERR_SHAPE
+
+    h, w, kv = desc(lib, (7, 7168), bf), desc(lib, (576, 7168), bf), desc(lib, (7, 576), f32)
+    assert c.mla_kv_project(_ref(desc(lib, (7, 7072), bf)), _ref(desc(lib, (576, 7072), bf)),
+                            _ref(kv), None) == E.MLA_ERR_SHAPE                             # d % 128
+    assert c.mla_kv_project(_ref(h), _ref(desc(lib, (512, 7168), bf)), _ref(kv), None) == E.MLA_ERR_SHAPE
+    assert c.mla_kv_project(_ref(h), _ref(w), _ref(desc(lib, (7, 576), bf)), None) == E.MLA_ERR_DTYPE
+
+    a = _args(lib, B=B, S=S)
+    kvb = desc(lib, (B, S, 576), f32)
+    assert c.mla_cache_append(_ref(desc(lib, (B, S, 512), f32)), _ref(a["lens"]), _ref(a["table"]),
+                              _ref(a["cache"]), 10000.0, None) == E.MLA_ERR_SHAPE
+    assert c.mla_cache_append(_ref(kvb), _ref(desc(lib, (B + 1,), i32)), _ref(a["table"]), _ref(a["cache"]),
+                              10000.0, None) == E.MLA_ERR_SHAPE
+    assert c.mla_cache_append(_ref(kvb), _ref(a["lens"]), _ref(a["table"]), None, 10000.0, None) == E.MLA_ERR_NULL
+    assert c.mla_cache_append(_ref(kvb), _ref(a["lens"]), _ref(a["table"]), _ref(a["cache"]), float("inf"),
+                              None) == E.MLA_ERR_SHAPE
