@@ -66,7 +66,7 @@ typedef enum mla_status {
   MLA_ERR_NULL = 1,        /* a required descriptor or its data pointer is NULL */
   MLA_ERR_DTYPE = 2,       /* a tensor has the wrong element type */
   MLA_ERR_SHAPE = 3,       /* rank, shape or strides inconsistent; H != 128; widths != 512/64/576 */
-  MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q = 3, block size 32) */
+  MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q > 64, block size 32) */
   MLA_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
   MLA_ERR_DEVICE = 6,      /* the current device is not gfx950 or cannot be queried */
   MLA_ERR_SCRATCH = 7      /* mla_decode_noalloc: num_splits * S_q above MLA_NOALLOC_MAX_SPLIT_TOKENS */
@@ -128,7 +128,9 @@ typedef struct mla_latent_cache {
  *   partial_out  uint8 [mla_partial_out_bytes(P, S_q)] (or larger), 16-byte aligned
  *   partial_lse  fp32  [P, 2, S_q, 128]
  *
- * S_q is 1, 2 or 4 (MLA_ERR_UNSUPPORTED otherwise).  The split count P is the
+ * S_q is 1 .. 64 (MLA_ERR_UNSUPPORTED above): the tokens run in groups of 4,
+ * 2 and 1, one kernel launch each, and every group reads the rows again (the
+ * decode of a few draft tokens, not a long prefill chunk).  The split count P is the
  * leading dimension of partial_lse (P = 1 when partial_lse is NULL): a power
  * of two, 1 .. MLA_MAX_SPLITS, the number of work partitions the rows of the
  * whole batch are cut into.  The rows of all sequences, in 64-row pages
@@ -208,7 +210,7 @@ mla_status mla_decode_noalloc(const mla_tensor* q_absorbed, const mla_tensor* q_
 
 /*
  * A split count P for mla_decode (0 on error): one work partition per compute
- * unit of `device` (per two with s_q = 2, per four with s_q = 4), halved while
+ * unit of `device` (per two with s_q = 2 or 3, per four with s_q >= 4), halved while
  * the cache capacity the block table allows, batch * max_blocks_per_seq pages
  * plus 3 units per sequence of fixed cost, would leave fewer than 4 units per
  * partition: short contexts then stay in few partitions and need little or no

@@ -47,7 +47,7 @@ from __future__ import annotations
 import sys
 
 SLOT_BYTES = 64 * 1152          # one page of bf16 rows = one LDS tile
-KARG_BYTES = 120                # kernel argument block (both kernels)
+KARG_BYTES = 128                # kernel argument block (both kernels)
 
 # bf16 kernel: two tile slots, then the probability exchange buffer (16 KB):
 # the bf16 probabilities of all 128 query rows for the two 32-row sub-steps of
@@ -156,7 +156,11 @@ S_PFOFF = S_TMP + 14     # bf16: block-table byte offset of the page prefetch to
 # loads of the next unit issued in phases 1, 2, 3 of a full unit
 DMA_SPLIT = (8, 6, 4)
 S_ONES = 98              # bf16 pair (1.0, 1.0): sums of packed probabilities by v_dot2
-S_MAX = 99
+# query tokens are launched in groups of 1, 2 or 4: S_SQ is the group's size,
+# S_STRIDE the tokens per sequence in the query, output and partial arrays,
+# S_TOK0 the group's first token
+S_STRIDE, S_TOK0 = 100, 101
+S_MAX = 102
 
 
 def temps(*regs, pool):
@@ -1365,8 +1369,9 @@ def epilogue(a):
       f"s_add_u32 s{T}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_cmp_gt_u32 s{T}, {s(S_UB)}",
       f"s_cbranch_scc1 {whole_no}",
-      # whole: row_base = (c_seq * s_q + s_tok) * 128
-      f"s_mul_i32 s{T + 1}, {s(S_CSEQ)}, {s(S_SQ)}",
+      # whole: row_base = (c_seq * stride + tok0 + s_tok) * 128
+      f"s_mul_i32 s{T + 1}, {s(S_CSEQ)}, {s(S_STRIDE)}",
+      f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_TOK0)}",
       f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_STOK)}",
       f"s_lshl_b32 s{T + 1}, s{T + 1}, 7",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_OUT)}",
@@ -1381,7 +1386,8 @@ def epilogue(a):
     a.label(pslot1)
     a(f"s_lshl_b32 s{T + 1}, {s(S_PART)}, 1",
       f"s_add_u32 s{T + 1}, s{T + 1}, s{T + 2}",
-      f"s_mul_i32 s{T + 1}, s{T + 1}, {s(S_SQ)}",
+      f"s_mul_i32 s{T + 1}, s{T + 1}, {s(S_STRIDE)}",
+      f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_TOK0)}",
       f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_STOK)}",
       f"s_lshl_b32 s{T + 1}, s{T + 1}, 7",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_POUT)}",
@@ -1477,7 +1483,7 @@ def epi_partial_f16_fp8(a, inv):
     T = S_TMP
     vals = list(range(32, 96))           # (cb - 8q, a, i) at 32 + 8 (cb - 8q) + 4 a + i
     invq, m0, m1, t, t0, t1, off, offt = (18, 19), 20, 21, 22, 23, 24, 25, 26
-    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_SQ)}",
+    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_STRIDE)}",
       f"s_lshr_b32 s{T + 7}, s{T + 8}, 14",
       f"s_lshl_b32 s{T + 6}, s{T + 8}, 18",
       f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 4}",
@@ -1580,7 +1586,8 @@ def epilogue_split(a):
       f"s_add_u32 s{T}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_cmp_gt_u32 s{T}, {s(S_UB)}",
       f"s_cbranch_scc1 {whole_no}",
-      f"s_mul_i32 s{T + 1}, {s(S_CSEQ)}, {s(S_SQ)}",
+      f"s_mul_i32 s{T + 1}, {s(S_CSEQ)}, {s(S_STRIDE)}",
+      f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_TOK0)}",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_OUT)}",
       f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_LSE)}",
       f"s_mov_b32 s{T + 3}, 0",
@@ -1593,7 +1600,8 @@ def epilogue_split(a):
     a.label(pslot1)
     a(f"s_lshl_b32 s{T + 1}, {s(S_PART)}, 1",
       f"s_add_u32 s{T + 1}, s{T + 1}, s{T + 2}",
-      f"s_mul_i32 s{T + 1}, s{T + 1}, {s(S_SQ)}",
+      f"s_mul_i32 s{T + 1}, s{T + 1}, {s(S_STRIDE)}",
+      f"s_add_u32 s{T + 1}, s{T + 1}, {s(S_TOK0)}",
       f"s_mov_b64 s[{T + 4}:{T + 5}], {sp(S_POUT)}",
       f"s_mov_b64 s[{T + 6}:{T + 7}], {sp(S_PLSE)}",
       f"s_mov_b32 s{T + 3}, 1")
@@ -1727,7 +1735,7 @@ def epi_partial_f16(a, inv):
     vals = list(range(32, 96))           # (cb, a, i) at 32 + 8 cb + 4 a + i
     off, offt, m0, m1, t, t0, t1 = 20, 21, 22, 23, 18, 16, 17
     # table of descales after the num_splits * 2 * s_q value blocks of 128 KB
-    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_SQ)}",
+    a(f"s_mul_i32 s{T + 8}, {s(S_NPART)}, {s(S_STRIDE)}",
       f"s_lshr_b32 s{T + 7}, s{T + 8}, 14",
       f"s_lshl_b32 s{T + 6}, s{T + 8}, 18",
       f"s_add_u32 s{T + 6}, s{T + 6}, s{T + 4}",
@@ -2474,7 +2482,8 @@ def load_q(a, seq_sgpr):
     loads): row (seq * s_q + s_tok) * 128 + head0 .. + 31, latent then rope."""
     T = S_TMP
     t = V_T
-    a(f"s_mul_i32 s{T}, s{seq_sgpr}, {s(S_SQ)}",
+    a(f"s_mul_i32 s{T}, s{seq_sgpr}, {s(S_STRIDE)}",
+      f"s_add_u32 s{T}, s{T}, {s(S_TOK0)}",
       f"s_add_u32 s{T}, s{T}, {s(S_STOK)}",
       f"s_lshl_b32 s{T}, s{T}, 7",
       f"s_add_u32 s{T}, s{T}, {s(S_HEAD0)}",
@@ -2523,7 +2532,8 @@ def segment_setup(a, with_q=True, zero=True):
     units_of(a, S_CUNITS, S_CLEN)
     a(f"s_add_u32 {s(S_SEGEND)}, {s(S_CPRE)}, {s(S_CUNITS)}",
       f"s_min_u32 {s(S_SEGEND)}, {s(S_SEGEND)}, {s(S_UB)}",
-      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_SQ)}",
+      f"s_sub_i32 {s(S_NVIS)}, {s(S_CLEN)}, {s(S_STRIDE)}",
+      f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_TOK0)}",
       f"s_add_i32 {s(S_NVLO)}, {s(S_NVIS)}, 1",
       f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, {s(S_STOK)}",
       f"s_add_i32 {s(S_NVIS)}, {s(S_NVIS)}, 1",
@@ -2564,6 +2574,7 @@ def kernel(fp8=False):
       f"s_load_dwordx8 s[{S_LSE}:{S_LSE + 7}], s[0:1], 0x40",
       f"s_load_dwordx2 s[{S_NHB}:{S_NHB + 1}], s[0:1], 0x60",
       *([f"s_load_dwordx4 s[{S_FSC}:{S_FSC + 3}], s[0:1], 0x68"] if FP8 else []),
+      f"s_load_dwordx2 s[{S_STRIDE}:{S_TOK0}], s[0:1], 0x78",
       f"s_mov_b32 {s(S_ONES)}, 0x3f803f80",
       f"v_and_b32 {vreg(V_LANE)}, 63, {vreg(V_TID)}",
       f"v_lshrrev_b32 {vreg(V_G)}, 4, {vreg(V_LANE)}",
@@ -2746,7 +2757,7 @@ def descriptor():
 
 def metadata(kernels):
     """Code-object metadata for the given (name, lds_bytes) kernels, which all
-    take the same argument block: 11 pointers, then 8 scalars."""
+    take the same argument block: 9 pointers, 8 scalars, 2 pointers, 2 scalars."""
     lines = ["\t.amdgpu_metadata", "---", "amdhsa.kernels:"]
     for name, lds in kernels:
         lines += [f"  - .agpr_count:     256", "    .args:"]
@@ -2756,6 +2767,8 @@ def metadata(kernels):
             lines.append(f"      - {{ .offset: {72 + 4 * k}, .size: 4, .value_kind: by_value }}")
         for k in range(2):
             lines.append(f"      - {{ .address_space: global, .offset: {104 + 8 * k}, .size: 8, .value_kind: global_buffer }}")
+        for k in range(2):
+            lines.append(f"      - {{ .offset: {120 + 4 * k}, .size: 4, .value_kind: by_value }}")
         lines += [f"    .group_segment_fixed_size: {lds}",
                   "    .kernarg_segment_align: 8",
                   f"    .kernarg_segment_size: {KARG_BYTES}",

@@ -58,7 +58,7 @@ mla_status check_tensor(const mla_tensor* t, mla_dtype dtype, int rank, const in
     if (st_ != MLA_OK) return st_;    \
   } while (0)
 
-bool supported_tokens(int64_t s_q) { return s_q == 1 || s_q == 2 || s_q == 4; }
+bool supported_tokens(int64_t s_q) { return s_q >= 1 && s_q <= mla::kMaxTokens; }
 
 // The cache descriptors: kind (bf16 / e4m3), pages NB, and for a contiguous
 // cache the pages per sequence.
@@ -470,7 +470,8 @@ int32_t mla_num_splits_hint(int32_t device, int32_t batch, int32_t s_q, int32_t 
   if (batch < 1 || !supported_tokens(s_q)) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) return 0;
-  const int parts = cus / s_q;   // a partition takes s_q workgroups (128 query rows each)
+  // a partition takes as many workgroups (128 query rows each) as its largest token group
+  const int parts = cus / mla::token_group(s_q);
   int p2 = 1;
   while (p2 * 2 <= parts) p2 *= 2;  // partitions must be a power of two
   if (max_blocks_per_seq > 0) {

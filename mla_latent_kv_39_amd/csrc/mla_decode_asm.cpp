@@ -32,8 +32,10 @@ struct AsmArgs {
   int32_t log2_parts;
   const float* fp8_scales;  // fp8 cache only
   const void* fp8_rope;     // fp8 cache only
+  int32_t tok_stride;       // query tokens per sequence in q, out, lse and the partials
+  int32_t tok0;             // the first token of this launch's group
 };
-static_assert(sizeof(AsmArgs) == 120, "kernel argument layout");
+static_assert(sizeof(AsmArgs) == 128, "kernel argument layout");
 
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
@@ -74,32 +76,44 @@ hipError_t launch_decode(const DecodeParams& p, int s_q, bool fp8, hipStream_t s
   hipFunction_t fn;
   hipError_t err = decode_function(fp8, &fn);
   if (err != hipSuccess) return err;
-  AsmArgs a;
-  a.q_abs = p.q_abs;
-  a.q_rope = p.q_rope;
-  a.rows = p.rows;
-  a.table = p.block_table;
-  a.seq_lens = p.seq_lens;
-  a.part_out = p.part_out;
-  a.part_lse = p.part_lse;
-  a.out = p.out;
-  a.lse = p.lse;
-  a.scale_log2 = p.scale_log2;
-  a.max_blocks = p.max_blocks;
-  a.batch = p.batch;
-  a.num_parts = p.num_parts;
-  a.s_q = s_q;
-  a.heads_per_block = heads_per_block(s_q);
-  a.head_blocks = kHeads / a.heads_per_block;
   int lg = 0;
   while ((1 << lg) < p.num_parts) ++lg;
-  a.log2_parts = lg;
-  a.fp8_scales = p.fp8_scales;
-  a.fp8_rope = p.fp8_rope;
-  size_t size = sizeof(a);
-  void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size, HIP_LAUNCH_PARAM_END};
-  return hipModuleLaunchKernel(fn, (unsigned)(p.num_parts * a.head_blocks), 1, 1, 256, 1, 1, 0, stream, nullptr,
-                               config);
+  // a workgroup holds 128 query rows, four waves of 32 heads of one token: the
+  // tokens go out in groups of 4, 2 and 1, each group one launch over the same
+  // partitions (the partition map depends on the lengths only)
+  for (int tok0 = 0; tok0 < s_q;) {
+    const int group = token_group(s_q - tok0);
+    AsmArgs a;
+    a.q_abs = p.q_abs;
+    a.q_rope = p.q_rope;
+    a.rows = p.rows;
+    a.table = p.block_table;
+    a.seq_lens = p.seq_lens;
+    a.part_out = p.part_out;
+    a.part_lse = p.part_lse;
+    a.out = p.out;
+    a.lse = p.lse;
+    a.scale_log2 = p.scale_log2;
+    a.max_blocks = p.max_blocks;
+    a.batch = p.batch;
+    a.num_parts = p.num_parts;
+    a.s_q = group;
+    a.heads_per_block = heads_per_block(group);
+    a.head_blocks = kHeads / a.heads_per_block;
+    a.log2_parts = lg;
+    a.fp8_scales = p.fp8_scales;
+    a.fp8_rope = p.fp8_rope;
+    a.tok_stride = s_q;
+    a.tok0 = tok0;
+    size_t size = sizeof(a);
+    void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
+                      HIP_LAUNCH_PARAM_END};
+    err = hipModuleLaunchKernel(fn, (unsigned)(p.num_parts * a.head_blocks), 1, 1, 256, 1, 1, 0, stream, nullptr,
+                                config);
+    if (err != hipSuccess) return err;
+    tok0 += group;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mla

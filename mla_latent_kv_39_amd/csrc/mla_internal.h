@@ -47,10 +47,17 @@ struct CombineParams {
   int32_t log2_parts;        // num_parts is a power of two
 };
 
-// Heads handled by one workgroup for a given number of query tokens (1, 2 or
-// 4): a workgroup always holds 128 query rows, four waves of 32 rows of one
-// token each.
-inline int heads_per_block(int s_q) { return kHeads / s_q; }
+// Heads handled by one workgroup for a group of 1, 2 or 4 query tokens: a
+// workgroup always holds 128 query rows, four waves of 32 rows of one token
+// each.
+inline int heads_per_block(int group) { return kHeads / group; }
+
+// The size of the next token group when `left` tokens remain: 4, 2 or 1.
+inline int token_group(int left) { return left >= 4 ? 4 : (left >= 2 ? 2 : 1); }
+
+// Most query tokens per sequence a decode call takes (several draft tokens of
+// speculative decoding; every group of up to four re-reads the rows).
+constexpr int kMaxTokens = 64;
 
 // Kernel launchers (defined next to the kernels).  They return the HIP error
 // of the launch.

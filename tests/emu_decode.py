@@ -45,15 +45,20 @@ def emulate_decode(inp, num_splits, seed=0, text=None, fp8=None, hook=None):
     lse = mem.add(np.full(B * S * N_HEADS, np.nan, np.float32))
     fsc = mem.add(inp.cache_scales.numpy()) if fp8 else 0
     fro = mem.add(inp.cache_rope.contiguous().view(torch.uint8).numpy()) if fp8 else 0
-    hpb = 128 // S
     lg = 0
     while (1 << lg) < num_splits:
         lg += 1
     scale_log2 = float(np.float32(inp.scale) * np.float32(1.4426950408889634))
-    karg = struct.pack("<9Qf7i2Q", q_abs, q_rope, rows, table, lens, pout, plse, out, lse,
-                       scale_log2, inp.max_blocks, B, num_splits, S, hpb, N_HEADS // hpb, lg, fsc, fro)
-    assert len(karg) == G.KARG_BYTES
-    E.run_kernel(text, kname, lds, mem, karg, num_splits * (N_HEADS // hpb), seed=seed, hook=hook)
+    tok0 = 0
+    while tok0 < S:   # token groups of 4, 2 and 1, one launch each (as the library's launcher)
+        group = 4 if S - tok0 >= 4 else (2 if S - tok0 >= 2 else 1)
+        hpb = 128 // group
+        karg = struct.pack("<9Qf7i2Q2i", q_abs, q_rope, rows, table, lens, pout, plse, out, lse,
+                           scale_log2, inp.max_blocks, B, num_splits, group, hpb, N_HEADS // hpb, lg, fsc, fro,
+                           S, tok0)
+        assert len(karg) == G.KARG_BYTES
+        E.run_kernel(text, kname, lds, mem, karg, num_splits * (N_HEADS // hpb), seed=seed, hook=hook)
+        tok0 += group
     f = lambda base, shape: mem.buffer(base).view(np.float32).reshape(shape).astype(np.float64)
     return (f(out, (B, S, N_HEADS, D_C)), f(lse, (B, S, N_HEADS)),
             unpack(mem.buffer(pout), num_splits, S),

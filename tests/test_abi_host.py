@@ -123,8 +123,7 @@ def test_decode_rejects_bad_descriptors(lib):
     assert _with(lib, q=desc(lib, (2, 1, 128, 512), bf, strides=(65536, 65536, 1, 128))) == E.MLA_ERR_SHAPE
     assert _with(lib, out=desc(lib, (2, 1, 128, 512), f32, strides=(131072, 65536, 512, 1))) == E.MLA_ERR_SHAPE
     # query tokens
-    assert _with(lib, S=3) == E.MLA_ERR_UNSUPPORTED
-    assert _with(lib, S=8) == E.MLA_ERR_UNSUPPORTED
+    assert _with(lib, S=65) == E.MLA_ERR_UNSUPPORTED                 # at most 64 query tokens
     # sequence lengths and block table
     assert _with(lib, lens=desc(lib, (3,), i32)) == E.MLA_ERR_SHAPE
     assert _with(lib, table=desc(lib, (2,), i32)) == E.MLA_ERR_SHAPE
@@ -169,6 +168,7 @@ def test_a_valid_call_gets_past_every_host_check(lib):
     # no GPU here: the only thing left to fail is the device
     assert _decode(lib, _args(lib)) == lib.MLA_ERR_DEVICE
     assert _decode(lib, _args(lib, fp8=True, S=4)) == lib.MLA_ERR_DEVICE
+    assert _decode(lib, _args(lib, S=7)) == lib.MLA_ERR_DEVICE
     a = _args(lib)
     a["table"] = None                                  # contiguous: [B * 5, 64, 576]
     a["cache"].rows = desc(lib, (10, 64, 576), lib.MLA_DTYPE_BF16)
@@ -205,8 +205,8 @@ def test_combine_rejects_bad_descriptors(lib):
     assert comb(po=None) == E.MLA_ERR_NULL
     assert comb(lens=desc(lib, (3,), lib.MLA_DTYPE_INT32)) == E.MLA_ERR_SHAPE
     assert comb(pl=desc(lib, (4, 2, 2, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_SHAPE     # S_q differs
-    assert comb(out=desc(lib, (2, 3, 128, 512), lib.MLA_DTYPE_FP32),
-                lse=desc(lib, (2, 3, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_UNSUPPORTED
+    assert comb(out=desc(lib, (2, 65, 128, 512), lib.MLA_DTYPE_FP32),
+                lse=desc(lib, (2, 65, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_UNSUPPORTED
     assert comb(out=desc(lib, (2, 1, 96, 512), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_SHAPE
     # one partition: nothing to merge, no launch
     assert comb(po=None, pl=None) == E.MLA_OK
@@ -229,7 +229,7 @@ def test_check_indices_rejects_bad_descriptors(lib):
 
 def test_hint_rejects_bad_arguments(lib):
     assert lib.mla_num_splits_hint(0, 0, 1, 0) == 0
-    assert lib.mla_num_splits_hint(0, 4, 3, 0) == 0
+    assert lib.mla_num_splits_hint(0, 4, 65, 0) == 0
 
 
 def test_binding_passes_only_device_memory(lib):

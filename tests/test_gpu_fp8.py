@@ -49,6 +49,11 @@ def test_fp8_two_query_tokens(splits):
     _check(_fp8([2, 3, 65, 129, 500], s_q=2, seed=23), splits, f"fp8 mtp splits={splits}")
 
 
+@pytest.mark.parametrize("s_q,splits", [(3, 4), (6, 1)])
+def test_fp8_token_groups(s_q, splits):
+    _check(_fp8([s_q, 66, 129, 500], s_q=s_q, seed=27 + s_q), splits, f"fp8 s_q={s_q} splits={splits}")
+
+
 def test_fp8_sequences_with_no_visible_row():
     _check(_fp8([0, 1, 70], s_q=2, seed=24), 4, "fp8 empty rows")
 

@@ -62,6 +62,13 @@ def test_four_query_tokens_causal(num_splits):
     _run_and_check(inp, num_splits, f"s_q=4 splits={num_splits}")
 
 
+@pytest.mark.parametrize("s_q,num_splits", [(3, 1), (3, 16), (5, 8), (8, 32), (16, 4)])
+def test_token_groups_causal(s_q, num_splits):
+    # s_q tokens run as groups of 4, 2 and 1 (one launch each) over the same partitions
+    inp = _small([s_q, s_q + 1, 64, 65, 131, 500, 1000], s_q=s_q, seed=17 + s_q)
+    _run_and_check(inp, num_splits, f"s_q={s_q} splits={num_splits}")
+
+
 @pytest.mark.parametrize("num_splits", [1, 16])
 def test_four_query_tokens_e4m3(num_splits):
     inp = _small([3, 66, 129, 700], s_q=4, seed=14, cache="fp8_e4m3")
@@ -221,3 +228,5 @@ def test_num_splits_hint_follows_the_cache_capacity():
     assert mla.mla_num_splits_hint(dev, 8, 1, 2) == 8              # 40 units: 5 per partition
     assert mla.mla_num_splits_hint(dev, 128, 2, 128) == full // 2  # two query tokens: two workgroups per partition
     assert mla.mla_num_splits_hint(dev, 128, 4, 128) == full // 4  # four tokens: four workgroups per partition
+    assert mla.mla_num_splits_hint(dev, 128, 3, 128) == full // 2  # groups of 2 + 1
+    assert mla.mla_num_splits_hint(dev, 128, 9, 128) == full // 4  # groups of 4 + 4 + 1

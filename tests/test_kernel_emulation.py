@@ -86,6 +86,14 @@ def test_four_query_tokens(cache, lens, splits):
     _check(_small(lens, s_q=4, seed=5, cache=cache), splits)
 
 
+@pytest.mark.parametrize("cache,lens,s_q,splits", [("bf16", [3, 70, 129], 3, 4), ("fp8_e4m3", [7, 66, 200], 7, 2),
+                                                    ("bf16", [8, 64, 65, 130], 8, 8)])
+def test_token_groups(cache, lens, s_q, splits):
+    # 3 = 2 + 1, 7 = 4 + 2 + 1, 8 = 4 + 4 tokens: one launch per group, each
+    # writing its tokens' rows of the shared outputs and partials
+    _check(_small(lens, s_q=s_q, seed=8, cache=cache), splits)
+
+
 def test_bf16_result_independent_of_wave_order():
     inp = _small([65, 130, 200], seed=7)
     a = ED.emulate_decode(inp, 4, seed=1)
