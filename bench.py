@@ -318,6 +318,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="the headline workload")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--around-only", action="store_true",
+                    help="time only the steps around the decode (absorption, projection, cache append) for "
+                         "the headline workload's batch shape, and print their record")
     ap.add_argument("--num-splits", type=int, default=0, help="0: the workload's, else the library's hint")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,6 +346,11 @@ def main(argv=None):
         return 0
     torch.cuda.set_device(0)
 
+    if args.around_only:
+        from mla_inputs import get_workload
+        wl = get_workload(args.workload)
+        print(json.dumps(measure_next_rows(wl["batch"], wl["s_q"], args.steps, args.warmup)), flush=True)
+        return 0
     head = measure(args.workload, args.steps, args.warmup, args.num_splits, args.seed)
     others = {}
     if not args.only:
