@@ -294,7 +294,8 @@ mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const 
   MLA_TRY(check_tensor(q_rope, MLA_DTYPE_BF16, 4, wr));
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return MLA_ERR_SHAPE;
   if (B * S > INT_MAX / (MLA_NUM_HEADS * MLA_LATENT_DIM)) return MLA_ERR_SHAPE;
-  if (!aligned16(q_c) || !aligned16(w_uk_t) || !aligned16(q_absorbed)) return MLA_ERR_SHAPE;
+  if (!aligned16(q_c) || !aligned16(w_uk_t) || !aligned16(q_absorbed) || !aligned16(q_r) || !aligned16(q_rope))
+    return MLA_ERR_SHAPE;
   MLA_TRY(check_device());
   mla::GemmParams g;
   g.a = q_c->data;

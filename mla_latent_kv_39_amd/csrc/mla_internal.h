@@ -89,8 +89,8 @@ struct GemmParams {
 };
 enum class GemmKind {
   kF32ToF32Wide,    // fp32 A (rounded to bf16 on load), fp32 C, 64 x 128 tiles
-  kBf16ToBf16Wide,  // bf16 A, bf16 C, 64 x 128 tiles
-  kBf16ToF32SplitK  // bf16 A, fp32 C, 16 x 32 tiles, K split over the four waves
+  kBf16ToBf16Wide,  // bf16 A, bf16 C, 128 x 128 tiles
+  kBf16ToF32SplitK  // bf16 A, fp32 C, 32 x 32 tiles, K split over the four waves
 };
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream);
 

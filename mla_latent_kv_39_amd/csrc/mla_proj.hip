@@ -74,11 +74,11 @@ __device__ __forceinline__ void store4(__bf16* p, const float* v) {
 // KW = 1: the four waves form a 2 x 2 grid, each owning (16 WM) x (16 WN)
 // outputs over all of K; KW = 4: all four own the same (16 WM) x (16 WN)
 // outputs, each over a quarter of K (for long K and few outputs), and the
-// quarters are summed in LDS in a fixed order.  Loads run four K-steps (128)
+// quarters are summed in LDS in a fixed order.  Loads run U K-steps (32 U)
 // ahead of their MFMAs.  The tile goes through LDS so that C is written in
 // 16-byte row chunks.  Requires k_len % (32 KW) == 0 and n_len a multiple of
 // the tile width; rows m >= m_len are neither read nor written.
-template <typename TA, typename TC, int WM, int WN, int KW>
+template <typename TA, typename TC, int WM, int WN, int KW, int U>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
   constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
@@ -112,7 +112,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
   int k = 0;
   for (; k + 32 * U <= kq; k += 32 * U) {
     bf16x8 a[U][WM], b[U][WN];
@@ -169,12 +168,12 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
   }
 }
 
-template <typename TA, typename TC, int WM, int WN, int KW>
+template <typename TA, typename TC, int WM, int WN, int KW, int U>
 hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
   constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
   const dim3 grid((unsigned)(g.n_len / TN), (unsigned)((g.m_len + TM - 1) / TM), (unsigned)batches);
-  hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW>), grid, dim3(256), 0, stream, g);
+  hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW, U>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -189,20 +188,38 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, in
   *y1 = (float)((double)x0 * sn + (double)x1 * cs);
 }
 
-// q_rope of query token t = b S_q + s, head h, pair i: position seq_len[b] - S_q + s.
+// q_rope of query token t = b S_q + s (one workgroup per token), position
+// seq_len[b] - S_q + s: the 32 angles' cosines and sines are computed once per
+// token (fp64) and shared by its 128 heads; each thread then rotates 16 pairs
+// (8-byte loads and stores of two pairs).
 __global__ __launch_bounds__(256) void query_rope_kernel(RopeParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t pairs = (int64_t)p.tokens * kHeads * (kRope / 2);
-  if (idx >= pairs) return;
-  const int i = (int)(idx % (kRope / 2));
-  const int64_t t = idx / ((int64_t)kHeads * (kRope / 2));
-  const int b = (int)(t / p.s_q), s = (int)(t % p.s_q);
+  __shared__ float s_cs[2][kRope / 2];
+  const int t = blockIdx.x;
+  const int b = t / p.s_q, s = t % p.s_q;
   const int pos = p.seq_lens[b] - p.s_q + s;
-  const __bf16* x = p.src + idx * 2;
-  float y0, y1;
-  rope_pair((float)x[0], (float)x[1], pos, i, kRope, p.base, &y0, &y1);
-  p.dst[idx * 2] = (__bf16)y0;
-  p.dst[idx * 2 + 1] = (__bf16)y1;
+  if (threadIdx.x < kRope / 2) {
+    const double theta = pow(p.base, -2.0 * (double)threadIdx.x / (double)kRope);
+    double sn, cs;
+    sincos((double)pos * theta, &sn, &cs);
+    s_cs[0][threadIdx.x] = (float)cs;
+    s_cs[1][threadIdx.x] = (float)sn;
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)t * kHeads * kRope;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  for (int e = threadIdx.x; e < kHeads * kRope / 4; e += 256) {   // four values = two pairs
+    const int i = (e % (kRope / 4)) * 2;                           // first pair of the four values
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p.src + base + 4 * e);
+    bf16x4 y;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float c = s_cs[0][i + q], sn = s_cs[1][i + q];
+      const float x0 = (float)x[2 * q], x1 = (float)x[2 * q + 1];
+      y[2 * q] = (__bf16)fmaf(x0, c, -x1 * sn);
+      y[2 * q + 1] = (__bf16)fmaf(x0, sn, x1 * c);
+    }
+    *reinterpret_cast<bf16x4*>(p.dst + base + 4 * e) = y;
+  }
 }
 
 // OCP E4M3 code of the value nearest to v (ties to the even code), saturated
@@ -268,16 +285,19 @@ __global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
 
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream) {
   switch (kind) {
-    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 2, 4, 1>(g, batches, stream);
-    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 2, 4, 1>(g, batches, stream);
-    case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 1, 2, 4>(g, batches, stream);
+    // tiles measured on the 256-token MTP step (rocprofv3-free HIP-event timing):
+    // output values 64 x 128 (38 us; 128 x 128: 48 us), absorbed query
+    // 128 x 128 (32 us; 64 x 128: 36 us), projection 32 x 32 with K over the
+    // four waves (29 us; 16 x 32: 40 us)
+    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 2, 4, 1, 4>(g, batches, stream);
+    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 4, 4, 1, 4>(g, batches, stream);
+    case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 2, 2, 4, 4>(g, batches, stream);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_query_rope(const RopeParams& p, hipStream_t stream) {
-  const int64_t pairs = (int64_t)p.tokens * kHeads * (kRope / 2);
-  hipLaunchKernelGGL(query_rope_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(query_rope_kernel, dim3((unsigned)p.tokens), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
