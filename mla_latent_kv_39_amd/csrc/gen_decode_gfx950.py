@@ -1922,8 +1922,6 @@ def unit_body_fp8(a):
       f"s_mov_b32 {s(S_CURVALID)}, {s(S_NVALID)}")
     take_prefetched(a)
     loader_page_fp8(a)
-    a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
-    dma_fp8(a, T + 21)
     a(f"s_add_u32 s{T + 19}, {s(S_UCUR)}, 1")
     prefetch_next(a, T + 19)
     dqfull, dqdone = a.new_label("dqfull"), a.new_label("dqdone")
@@ -1934,6 +1932,11 @@ def unit_body_fp8(a):
     a.label(dqfull)
     dequant_fp8(a, masked=False)
     a.label(dqdone)
+    # the next unit's raw pages: issued after the widening, whose LDS work
+    # then never waits behind these loads at issue (2-3% on the long-context
+    # workload)
+    a(f"s_xor_b32 s{T + 21}, {s(S_SLOT)}, 1")
+    dma_fp8(a, T + 21)
     a(s_waitcnt_lgkm(0), "s_barrier",
       "s_nop 1",
       f"v_readfirstlane_b32 s{T}, {vreg(V_T)}",
