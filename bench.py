@@ -234,17 +234,32 @@ def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int
     def rnd(*shape, dtype=torch.bfloat16, scale=1.0):
         return (torch.randn(shape, generator=g) * scale).to(dtype).to(dev)
 
-    def timed(fn, nbytes, flops, name):
+    def timed(fn, nbytes, flops, name, result):
+        """`steps` calls captured in a HIP graph and replayed, so that the
+        time is the kernels' and not the host's launch rate (the small
+        kernels here run for less than a Python call takes); the graph's last
+        result must equal an eager call's."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(steps):
-            fn(i)
+        graph.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         s = e0.elapsed_time(e1) / steps * 1e-3
+        replayed = result().clone()
+        fn(steps - 1)
+        torch.cuda.synchronize()
+        if not torch.equal(replayed, result()):
+            raise RuntimeError(f"{name}: graph replay differs from an eager call")
+        del graph
         rec = {"us": round(s * 1e6, 2), "algorithmic_bytes": nbytes, "mfma_flops": flops,
                "gbs": round(nbytes / s / 1e9, 1), "bound": binding_bound(nbytes, max(flops, 1)),
                "frac": round(roofline_frac(binding_bound(nbytes, max(flops, 1)), nbytes, flops, s), 4)}
@@ -264,10 +279,9 @@ def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int
     qa = torch.empty((batch, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
     qr = torch.empty((batch, s_q, 128, 64), dtype=torch.bfloat16, device=dev)
     lens_d = lens.to(dev)
-    out["absorb_query"] = timed(lambda i: mla.mla_absorb_query(qs[i % n][0], qs[i % n][1], w_uk_t, lens_d, qa, qr,
-                                                               stream=stream),
+    out["absorb_query"] = timed(lambda i: mla.mla_absorb_query(qs[i % n][0], qs[i % n][1], w_uk_t, lens_d, qa, qr),
                                 qb + w_uk_t.numel() * 2 + T * 128 * 576 * 2 + batch * 4,
-                                2 * T * 128 * 128 * 512, "absorb_query")
+                                2 * T * 128 * 128 * 512, "absorb_query", lambda: torch.cat([qa.flatten(), qr.flatten()]))
     del qs
     # output side
     w_uv = rnd(128, 128, 512, scale=512 ** -0.5)
@@ -275,8 +289,9 @@ def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int
     n = copies_for(ob)
     ols = [rnd(batch, s_q, 128, 512, dtype=torch.float32, scale=0.3) for _ in range(n)]
     vals = torch.empty((batch, s_q, 128, 128), device=dev)
-    out["absorb_output"] = timed(lambda i: mla.mla_absorb_output(ols[i % n], w_uv, vals, stream=stream),
-                                 ob + w_uv.numel() * 2 + T * 128 * 128 * 4, 2 * T * 128 * 512 * 128, "absorb_output")
+    out["absorb_output"] = timed(lambda i: mla.mla_absorb_output(ols[i % n], w_uv, vals),
+                                 ob + w_uv.numel() * 2 + T * 128 * 128 * 4, 2 * T * 128 * 512 * 128, "absorb_output",
+                                 lambda: vals)
     del ols
     # KV projection of the new tokens
     w_kv = rnd(576, hidden, scale=hidden ** -0.5)
@@ -285,16 +300,16 @@ def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int
     hs = [rnd(T, hidden) for _ in range(n)]
     w_kvs = [w_kv] + [w_kv.clone() for _ in range(n - 1)]
     kv = torch.empty((T, 576), device=dev)
-    out["kv_project"] = timed(lambda i: mla.mla_kv_project(hs[i % n], w_kvs[i % n], kv, stream=stream),
-                              hb + w_kv.numel() * 2 + T * 576 * 4, 2 * T * hidden * 576, "kv_project")
+    out["kv_project"] = timed(lambda i: mla.mla_kv_project(hs[i % n], w_kvs[i % n], kv),
+                              hb + w_kv.numel() * 2 + T * 576 * 4, 2 * T * hidden * 576, "kv_project", lambda: kv)
     del hs, w_kvs
     # cache append into a bf16 paged cache of the same batch shape
     rows = torch.zeros((batch * mb, 64, 576), dtype=torch.bfloat16, device=dev)
     cache = mla.LatentCache(mla.MLA_CACHE_BF16, rows)
     table_d = table.to(dev)
     kv3 = kv.view(batch, s_q, 576)
-    out["cache_append"] = timed(lambda i: mla.mla_cache_append(kv3, lens_d, table_d, cache, stream=stream),
-                                T * 576 * 4 + T * 1152 + batch * 4 + T * 4, 0, "cache_append")
+    out["cache_append"] = timed(lambda i: mla.mla_cache_append(kv3, lens_d, table_d, cache),
+                                T * 576 * 4 + T * 1152 + batch * 4 + T * 4, 0, "cache_append", lambda: rows)
     return out
 
 

@@ -12,10 +12,11 @@
 // The three projections are one kernel: C[M x N] = A[M x K] W[N x K]^T on
 // bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, batched over
 // heads.  M is the number of tokens of a decode step (a few hundred): every
-// weight is read once per 64-token tile, so the kernels are bound by the
+// weight is read once per 128-token tile, so the kernels are bound by the
 // weight and activation bytes, and operands go straight from global memory
-// into MFMA registers (16-byte loads); only the finished tile passes through
-// LDS, to be written in 16-byte row chunks.
+// into MFMA registers (16-byte loads, a stage of them always in flight); the
+// outputs come out of the MFMAs four consecutive columns per lane and are
+// stored from the accumulators.
 #include <hip/hip_bf16.h>
 
 #include "mla_internal.h"
@@ -26,39 +27,48 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// A fragment of the MFMA's A or B operand: 8 consecutive K values of one row.
-__device__ __forceinline__ bf16x8 frag_bf16(const __bf16* p, bool ok) {
-  uint4 u = make_uint4(0, 0, 0, 0);
-  if (ok) u = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ bf16x8 frag_f32(const float* p, bool ok) {
-  float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
-  if (ok) {
-    lo = reinterpret_cast<const float4*>(p)[0];
-    hi = reinterpret_cast<const float4*>(p)[1];
+// Raw operand fragments: 8 consecutive K values of one row, as loaded (16
+// bytes of bf16, or 32 bytes of fp32 rounded to bf16 only when used, so that
+// the rounding never waits on a load that the pipeline wants in flight).
+template <typename T>
+struct Raw;
+template <>
+struct Raw<__bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const __bf16* p, bool ok) {
+    u = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
   }
-  bf16x8 r;   // round to nearest even
-  r[0] = (__bf16)lo.x;
-  r[1] = (__bf16)lo.y;
-  r[2] = (__bf16)lo.z;
-  r[3] = (__bf16)lo.w;
-  r[4] = (__bf16)hi.x;
-  r[5] = (__bf16)hi.y;
-  r[6] = (__bf16)hi.z;
-  r[7] = (__bf16)hi.w;
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 frag(const __bf16* p, bool ok) { return frag_bf16(p, ok); }
-__device__ __forceinline__ bf16x8 frag(const float* p, bool ok) { return frag_f32(p, ok); }
+  __device__ __forceinline__ bf16x8 frag() const { return __builtin_bit_cast(bf16x8, u); }
+};
+template <>
+struct Raw<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ok) {
+      lo = reinterpret_cast<const float4*>(p)[0];
+      hi = reinterpret_cast<const float4*>(p)[1];
+    }
+  }
+  __device__ __forceinline__ bf16x8 frag() const {   // round to nearest even
+    bf16x8 r;
+    r[0] = (__bf16)lo.x;
+    r[1] = (__bf16)lo.y;
+    r[2] = (__bf16)lo.z;
+    r[3] = (__bf16)lo.w;
+    r[4] = (__bf16)hi.x;
+    r[5] = (__bf16)hi.y;
+    r[6] = (__bf16)hi.z;
+    r[7] = (__bf16)hi.w;
+    return r;
+  }
+};
 
 // four consecutive outputs: one 16-byte (fp32) or 8-byte (bf16) store
-__device__ __forceinline__ void store4(float* p, const float* v) {
+__device__ __forceinline__ void store4(float* p, const floatx4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ void store4(__bf16* p, const float* v) {
+__device__ __forceinline__ void store4(__bf16* p, const floatx4& v) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4 h;
   h[0] = (__bf16)v[0];
@@ -71,20 +81,24 @@ __device__ __forceinline__ void store4(__bf16* p, const float* v) {
 // C (m, n) = sum_k A (m, k) W (n, k), batch z:
 //   A (m, k) at a + z a_batch + m a_row + k,  W (n, k) at w + z w_batch + n k_len + k,
 //   C (m, n) at c + z c_batch + m c_row + n.
+// The MFMA takes W as its first operand and A as its second, so a 16 x 16
+// block comes out transposed: lane (r16, g) holds C (m = r16, n = 4g .. 4g+3),
+// four consecutive outputs of one row, stored straight from the accumulators.
 // KW = 1: the four waves form a 2 x 2 grid, each owning (16 WM) x (16 WN)
-// outputs over all of K; KW = 4: all four own the same (16 WM) x (16 WN)
-// outputs, each over a quarter of K (for long K and few outputs), and the
-// quarters are summed in LDS in a fixed order.  Loads run U K-steps (32 U)
-// ahead of their MFMAs.  The tile goes through LDS so that C is written in
-// 16-byte row chunks.  Requires k_len % (32 KW) == 0 and n_len a multiple of
-// the tile width; rows m >= m_len are neither read nor written.
-template <typename TA, typename TC, int WM, int WN, int KW, int U>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
+// outputs over all of K.  KW = NW: the NW waves own the same (16 WM) x (16 WN)
+// outputs, each over 1/NW of K (for long K and few outputs); their partial
+// tiles are summed in LDS in a fixed order.  K is walked in stages of U
+// K-steps (32 U values) with two register buffers: the loads of stage s + 1
+// are issued before the MFMAs of stage s, so a wave always has a stage of
+// loads in flight.  Requires k_len % (32 KW) == 0 and n_len a multiple of the
+// tile width; rows m >= m_len are neither read nor written.
+template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void gemm_nt_kernel(GemmParams g) {
+  static_assert(KW == 1 ? NW == 4 : KW == NW, "2 x 2 waves, or all waves over K");
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
   constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
-  constexpr int PITCH = TN + 4;                  // floats per LDS row
-  constexpr int COPIES = KW == 1 ? 1 : 4;
-  __shared__ float s_tile[COPIES * TM * PITCH];
+  constexpr int PITCH = TN + 4;                  // floats per LDS row (K split only)
+  __shared__ float s_tile[KW == 1 ? 1 : NW * TM * PITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
   const int wm0 = KW == 1 ? (wave & 1) * (16 * WM) : 0;     // this wave's block inside the tile
@@ -112,68 +126,89 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams g) {
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  int k = 0;
-  for (; k + 32 * U <= kq; k += 32 * U) {
-    bf16x8 a[U][WM], b[U][WN];
+
+  Raw<TA> ra[2][U][WM];
+  Raw<__bf16> rw[2][U][WN];
+  auto load = [&](int buf, int k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int i = 0; i < WM; ++i) a[u][i] = frag(arow[i] + k + 32 * u, aok[i]);
+      for (int j = 0; j < WN; ++j) rw[buf][u][j].load(wrow[j] + k + 32 * u, true);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) b[u][j] = frag_bf16(wrow[j] + k + 32 * u, true);
+      for (int i = 0; i < WM; ++i) ra[buf][u][i].load(arow[i] + k + 32 * u, aok[i]);
     }
+  };
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < WM; ++i) {
+        const bf16x8 x = ra[buf][u][i].frag();
 #pragma unroll
         for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rw[buf][u][j].frag(), x, acc[i][j], 0, 0, 0);
+      }
+  };
+  const int nst = kq / (32 * U);
+  int st = 0;
+  if (nst > 0) load(0, 0);
+  for (; st + 2 <= nst; st += 2) {
+    load(1, (st + 1) * 32 * U);
+    compute(0);
+    if (st + 2 < nst) load(0, (st + 2) * 32 * U);
+    compute(1);
   }
-  for (; k < kq; k += 32) {
-    bf16x8 a[WM], b[WN];
+  if (st < nst) compute(0);
+  for (int k = nst * 32 * U; k < kq; k += 32) {   // K-steps past the last whole stage
 #pragma unroll
-    for (int i = 0; i < WM; ++i) a[i] = frag(arow[i] + k, aok[i]);
+    for (int j = 0; j < WN; ++j) rw[0][0][j].load(wrow[j] + k, true);
 #pragma unroll
-    for (int j = 0; j < WN; ++j) b[j] = frag_bf16(wrow[j] + k, true);
+    for (int i = 0; i < WM; ++i) {
+      ra[0][0][i].load(arow[i] + k, aok[i]);
+      const bf16x8 x = ra[0][0][i].frag();
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rw[0][0][j].frag(), x, acc[i][j], 0, 0, 0);
+    }
   }
-  // lane (r16, kg) holds rows 4 kg .. 4 kg + 3 of column r16 of each 16 x 16 block
-  float* mine = s_tile + (KW == 1 ? 0 : wave * TM * PITCH);
+
+  TC* C = static_cast<TC*>(g.c) + z * g.c_batch;
+  if (KW == 1) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      if (!aok[i]) continue;
+      TC* crow = C + (int64_t)(m0 + 16 * i + r16) * g.c_row + n0 + 4 * kg;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) store4(crow + 16 * j, acc[i][j]);
+    }
+    return;
+  }
+  // K split: the NW partial tiles summed in LDS, then written row by row
+  float* mine = s_tile + wave * TM * PITCH;
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) mine[(wm0 + 16 * i + 4 * kg + q) * PITCH + wn0 + 16 * j + r16] = acc[i][j][q];
+      *reinterpret_cast<float4*>(mine + (16 * i + r16) * PITCH + 16 * j + 4 * kg) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
   __syncthreads();
-  // the tile, row by row, four columns per thread
-  TC* C = static_cast<TC*>(g.c) + z * g.c_batch;
   const int mt = blockIdx.y * TM, nt = blockIdx.x * TN;
-  for (int e = threadIdx.x; e < TM * (TN / 4); e += 256) {
+  for (int e = threadIdx.x; e < TM * (TN / 4); e += 64 * NW) {
     const int r = e / (TN / 4), c4 = (e % (TN / 4)) * 4;
     if (mt + r >= g.m_len) continue;
-    float v[4];
+    floatx4 v = *reinterpret_cast<const floatx4*>(s_tile + r * PITCH + c4);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      v[x] = s_tile[r * PITCH + c4 + x];
-#pragma unroll
-      for (int w = 1; w < COPIES; ++w) v[x] += s_tile[(w * TM + r) * PITCH + c4 + x];
-    }
-    TC* dst = C + (int64_t)(mt + r) * g.c_row + nt + c4;
-    store4(dst, v);
+    for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const floatx4*>(s_tile + (w * TM + r) * PITCH + c4);
+    store4(C + (int64_t)(mt + r) * g.c_row + nt + c4, v);
   }
 }
 
-template <typename TA, typename TC, int WM, int WN, int KW, int U>
+template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
 hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
   constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
   const dim3 grid((unsigned)(g.n_len / TN), (unsigned)((g.m_len + TM - 1) / TM), (unsigned)batches);
-  hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW, U>), grid, dim3(256), 0, stream, g);
+  hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW, NW, U>), grid, dim3(64 * NW), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -189,12 +224,19 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, in
 }
 
 // q_rope of query token t = b S_q + s (one workgroup per token), position
-// seq_len[b] - S_q + s: the 32 angles' cosines and sines are computed once per
-// token (fp64) and shared by its 128 heads; each thread then rotates 16 pairs
-// (8-byte loads and stores of two pairs).
+// seq_len[b] - S_q + s: each thread loads its 16 pairs first (8-byte loads of
+// two pairs), then the 32 angles' cosines and sines are computed once per
+// token (fp64) and shared by its 128 heads, so the trigonometry runs under
+// the loads instead of before them.
 __global__ __launch_bounds__(256) void query_rope_kernel(RopeParams p) {
   __shared__ float s_cs[2][kRope / 2];
+  constexpr int kPer = kHeads * kRope / 4 / 256;   // groups of four values per thread
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.x;
+  const int64_t base = (int64_t)t * kHeads * kRope;
+  bf16x4 x[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) x[k] = *reinterpret_cast<const bf16x4*>(p.src + base + 4 * (threadIdx.x + 256 * k));
   const int b = t / p.s_q, s = t % p.s_q;
   const int pos = p.seq_lens[b] - p.s_q + s;
   if (threadIdx.x < kRope / 2) {
@@ -205,16 +247,15 @@ __global__ __launch_bounds__(256) void query_rope_kernel(RopeParams p) {
     s_cs[1][threadIdx.x] = (float)sn;
   }
   __syncthreads();
-  const int64_t base = (int64_t)t * kHeads * kRope;
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  for (int e = threadIdx.x; e < kHeads * kRope / 4; e += 256) {   // four values = two pairs
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = threadIdx.x + 256 * k;
     const int i = (e % (kRope / 4)) * 2;                           // first pair of the four values
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p.src + base + 4 * e);
     bf16x4 y;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const float c = s_cs[0][i + q], sn = s_cs[1][i + q];
-      const float x0 = (float)x[2 * q], x1 = (float)x[2 * q + 1];
+      const float x0 = (float)x[k][2 * q], x1 = (float)x[k][2 * q + 1];
       y[2 * q] = (__bf16)fmaf(x0, c, -x1 * sn);
       y[2 * q + 1] = (__bf16)fmaf(x0, sn, x1 * c);
     }
@@ -285,13 +326,13 @@ __global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
 
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream) {
   switch (kind) {
-    // tiles measured on the 256-token MTP step (rocprofv3-free HIP-event timing):
-    // output values 64 x 128 (38 us; 128 x 128: 48 us), absorbed query
-    // 128 x 128 (32 us; 64 x 128: 36 us), projection 32 x 32 with K over the
-    // four waves (29 us; 16 x 32: 40 us)
-    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 2, 4, 1, 4>(g, batches, stream);
-    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 4, 4, 1, 4>(g, batches, stream);
-    case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 2, 2, 4, 4>(g, batches, stream);
+    // tiles measured on the 256-token MTP step (HIP events, inputs rotated past
+    // the Infinity Cache): output values 128 x 128 (30 us; 64 x 128: 38 us),
+    // absorbed query 128 x 256 (34 us with the RoPE; 128 x 128: 38 us),
+    // projection 32 x 32 with K over the four waves (28 us; eight waves: 28 us)
+    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 4, 4, 1, 4, 1>(g, batches, stream);
+    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 4, 8, 1, 4, 1>(g, batches, stream);
+    case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 2, 2, 4, 4, 2>(g, batches, stream);
   }
   return hipErrorInvalidValue;
 }
