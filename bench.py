@@ -330,7 +330,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: a cold GPU runs its first ~30 MTP steps through a clock transient")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="the headline workload")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--around-only", action="store_true",
