@@ -2009,6 +2009,7 @@ EPI_STORES_ROWS, EPI_STORES_PARTIAL = 66, 38
 # nontemporal (streaming), which measured 2-5% faster than the default policy.
 ROW_LOAD_POLICY = " nt"
 DMA_EARLY = 9                     # > 0: the loads of step t + 2 go out over fragments 0..DMA_EARLY
+PV_INTERLEAVE = 3                 # output fragments of step t - 1 placed among the score fragments of step t
 
 
 def lane_constants_hp(a):
@@ -2241,10 +2242,15 @@ def step_body_hp(a, kind, with_pv):
     if kind == "none":
         a(*[f"v_mov_b32 {vreg(H_S + i)}, 0" for i in range(8)])
     if qk and pv:
-        # scores interleaved with the first three output fragments (balances
-        # the LDS traffic), the last five output fragments carry the softmax
-        order = qk[0:9] + [pv[0]] + qk[9:18] + [pv[1]] + qk[18:27] + [pv[2]] + qk[27:36] + pv[3:]
-        tail = order.index(pv[3])
+        # scores interleaved with the first PV_INTERLEAVE output fragments
+        # (balances the LDS traffic), the other output fragments carry the softmax
+        k = PV_INTERLEAVE
+        cut = [36 * j // (k + 1) for j in range(k + 2)]
+        order = []
+        for j in range(k + 1):
+            order += qk[cut[j]:cut[j + 1]] + ([pv[j]] if j < k else [])
+        order += pv[k:]
+        tail = order.index(pv[k])
         sm = (softmax_lean if kind == "lean" else softmax_code)(0, S=H_S, P=H_S, tmp=H_SMT)
         # the softmax starts one fragment after the last score MFMA (MFMA
         # results -> VALU); the load groups stay whole (their carry chains)
