@@ -184,14 +184,17 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: i
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # whole steps; the events are recorded on the stream the kernels run on
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    # whole steps; the events are recorded on the stream the kernels run on, one
+    # between every two steps (the spread of single steps: p10 / p50 / p90)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
     for i in range(steps):
         step(i)
-    e1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    pct = {f"p{q}": per_step[min(steps - 1, (q * steps) // 100)] for q in (10, 50, 90)}
     # the dominant kernel alone, same launches back to back
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
@@ -204,13 +207,35 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: i
     torch.cuda.empty_cache()
     bound = binding_bound(nbytes, flops)
     res = {"workload": workload, "inp": inp, "rows": rows, "bytes": nbytes, "flops": flops, "splits": splits,
-           "copies": copies, "ms_step": ms_step, "ms_decode": ms_decode, "bound": bound,
+           "copies": copies, "ms_step": ms_step, "ms_decode": ms_decode, "bound": bound, "step_pct": pct,
            "frac_decode": roofline_frac(bound, nbytes, flops, ms_decode * 1e-3),
            "frac_step": roofline_frac(bound, nbytes, flops, ms_step * 1e-3)}
     print(f"[bench] {workload}: step {ms_step*1e3:.1f} us, decode kernel {ms_decode*1e3:.1f} us, "
           f"{bound}-bound fraction {res['frac_decode']:.3f} (decode) {res['frac_step']:.3f} (step)",
           file=sys.stderr, flush=True)
     return res
+
+
+def copy_bandwidth(mib: int = 1024, reps: int = 20) -> float:
+    """GB/s of a plain device-to-device copy of `mib` MiB (bytes read plus
+    bytes written per second): the HBM rate a streaming kernel can reach."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int = 7168, seed: int = 0):
@@ -317,6 +342,7 @@ def summary(r):
     """The per-workload record of config.workloads."""
     s = r["ms_step"] * 1e-3
     return {"step_us": round(r["ms_step"] * 1e3, 2), "decode_us": round(r["ms_decode"] * 1e3, 2),
+            **{f"step_us_{k}": round(v * 1e3, 2) for k, v in r["step_pct"].items()},
             "combine_us_est": round((r["ms_step"] - r["ms_decode"]) * 1e3, 2),
             "cache_tokens_per_s": round(r["rows"] / s, 1), "step_gbs": round(r["bytes"] / s / 1e9, 1),
             "step_tflops": round(r["flops"] / s / 1e12, 1), "bound": r["bound"],
@@ -375,6 +401,7 @@ def main(argv=None):
                 others[w] = summary(measure(w, args.steps, args.warmup, 0, args.seed))
     inp = head["inp"]
     next_rows = None if args.only else measure_next_rows(inp.batch, inp.s_q, args.steps, args.warmup)
+    copy_gbs = copy_bandwidth()
     ms_step, ms_decode = head["ms_step"], head["ms_decode"]
     nbytes, flops = head["bytes"], head["flops"]
     if head["bound"] == "hbm":
@@ -402,6 +429,9 @@ def main(argv=None):
                    "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
                    "query_row_pairs_per_s": round(flops / FLOP_PER_QROW_ROW / (ms_step * 1e-3), 1),
                    "decode_kernel_us": round(ms_decode * 1e3, 2),
+                   **{f"step_us_{k}": round(v * 1e3, 2) for k, v in head["step_pct"].items()},
+                   "copy_gbs": copy_gbs,
+                   "step_gbs_of_copy": round(nbytes / (ms_step * 1e-3) / 1e9 / copy_gbs, 4),
                    "algorithmic_bytes": nbytes, "mfma_flops": flops, "workloads": workloads,
                    "around_the_decode": next_rows},
         "roofline": roof,

@@ -149,22 +149,38 @@ def mla_init(device: int = 0) -> None:
 
 
 # ------------------------------------------------------------------ tensors
+_DTYPE_CODES = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.bfloat16: MLA_DTYPE_BF16, torch.float32: MLA_DTYPE_FP32, torch.int32: MLA_DTYPE_INT32,
-             torch.uint8: MLA_DTYPE_UINT8}
-    if hasattr(torch, "float8_e4m3fn"):
-        codes[torch.float8_e4m3fn] = MLA_DTYPE_FP8_E4M3
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        codes = {torch.bfloat16: MLA_DTYPE_BF16, torch.float32: MLA_DTYPE_FP32, torch.int32: MLA_DTYPE_INT32,
+                 torch.uint8: MLA_DTYPE_UINT8}
+        if hasattr(torch, "float8_e4m3fn"):
+            codes[torch.float8_e4m3fn] = MLA_DTYPE_FP8_E4M3
+        _DTYPE_CODES = codes
     # any other element type goes through with a code the library rejects (MLA_ERR_DTYPE)
-    return codes.get(t.dtype, 255)
+    return _DTYPE_CODES.get(t.dtype, 255)
 
 
 def tensor(t, dtype: Optional[int] = None, device_only: bool = True) -> MlaTensor:
     """The mla_tensor of a torch tensor (None -> an empty descriptor).  dtype
-    overrides the element type code (e4m3 codes held in a uint8 tensor)."""
-    d = MlaTensor()
+    overrides the element type code (e4m3 codes held in a uint8 tensor).
+    Built with one constructor call: a launch marshals ten of these, and
+    field-by-field assignment cost more host time than a short kernel."""
     if t is None:
-        return d
+        return MlaTensor()
+    if device_only and not t.is_cuda:
+        raise ValueError(f"tensor on {t.device} passed to libmla: device tensors only")
+    shape = tuple(t.shape)
+    n = len(shape)
+    if n > MAX_RANK:
+        raise ValueError(f"rank {n} above {MAX_RANK}")
+    pad = (0,) * (MAX_RANK - n)
+    return MlaTensor(t.data_ptr() or None, _dtype_code(t) if dtype is None else int(dtype), n,
+                     shape + pad, tuple(t.stride()) + pad)
     if device_only and t.device.type != "cuda":
         raise ValueError(f"tensor on {t.device} passed to libmla: device tensors only")
     if t.dim() > MAX_RANK:
