@@ -230,3 +230,32 @@ def test_num_splits_hint_follows_the_cache_capacity():
     assert mla.mla_num_splits_hint(dev, 128, 4, 128) == full // 4  # four tokens: four workgroups per partition
     assert mla.mla_num_splits_hint(dev, 128, 3, 128) == full // 2  # groups of 2 + 1
     assert mla.mla_num_splits_hint(dev, 128, 9, 128) == full // 4  # groups of 4 + 4 + 1
+
+
+@pytest.mark.parametrize("cache,s_q,splits", [("bf16", 1, 8), ("bf16", 2, 1), ("fp8_e4m3", 1, 4)])
+def test_prepared_step_repeats_the_eager_step(cache, s_q, splits):
+    """PreparedStep (descriptors built once) launched three times, with the
+    query changed in place between launches, gives what mla_decode +
+    mla_combine give on the same buffers, bit for bit, and the oracle's
+    result to the usual bound."""
+    import mla_latent_kv_39_amd as mla
+    from gpu_helpers import DeviceInputs, compare, OUT_TOL
+    from mla_latent_kv_39_amd.runner import DecodeWorkspace
+    inp = _small([5, 64, 200, 129], s_q=s_q, seed=11, cache=cache)
+    print(f"[gpu] prepared step: cache={cache} S_q={s_q} splits={splits}", flush=True)
+    dev = DeviceInputs(inp)
+    ws = DecodeWorkspace(inp.batch, inp.s_q, splits)
+    step = mla.PreparedStep(dev.q_absorbed, dev.q_rope, dev.cache, dev.block_table, dev.seq_lens, inp.scale,
+                            ws.out, ws.lse, ws.partial_out, ws.partial_lse)
+    q0 = dev.q_absorbed.clone()
+    for k in range(3):
+        dev.q_absorbed.copy_(q0 * (1.0 + 0.25 * k))
+        step()
+        torch.cuda.synchronize()
+        got = (ws.out.clone(), ws.lse.clone())
+        dev.run(splits, ws)
+        assert torch.equal(got[0], ws.out) and torch.equal(got[1], ws.lse), f"launch {k}"
+    inp.q_absorbed = dev.q_absorbed.cpu()
+    ref_out, ref_lse = O.mla_decode(inp)
+    compare(got[0].cpu().double().numpy(), got[1].cpu().double().numpy(), ref_out, ref_lse, "prepared step",
+            out_tol=OUT_TOL)
