@@ -750,8 +750,13 @@ def softmax_lean(ss, S=None, P=None, tmp=None):
     """Softmax of a fully visible sub-step once the segment's reference is
     set: P = 2^(scale S - m_ref), row sums, bf16 pack.  No max: a lane whose
     8-row sum passes 2^64 (the largest score more than ~64 above m_ref) flags a
-    restart, and V_PEAK keeps the largest such sum so that the restart can
-    raise m_ref past it.
+    restart.  V_PEAK: in the e4m3 kernel the largest such sum, so that the
+    restart can raise m_ref past it; in the bf16 kernel the exact running sum
+    (for lse), and at a restart every head whose running sum has passed 2^64
+    starts over from its first maximum.  That includes a head whose sum got
+    there without any one 8-row sum passing 2^64 (only when another head
+    overflowed): it costs that head a recomputation, not accuracy, since the
+    restarted segment is exact either way.
 
     The two row halves are interleaved so that no two exponentials (quarter
     rate) sit next to each other: spread between MFMAs, each MFMA then hides
