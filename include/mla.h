@@ -29,8 +29,12 @@
  *     freed or synchronised inside the calls; all work is enqueued on `stream`.
  *   - Every descriptor is validated on the host before any launch: dtypes
  *     (MLA_ERR_DTYPE), ranks, shapes, strides, the head count 128 and the
- *     widths 512 / 64 / 576 (MLA_ERR_SHAPE), missing pointers (MLA_ERR_NULL).
- *     A failed check returns its status and enqueues nothing.  The contents
+ *     widths 512 / 64 / 576 (MLA_ERR_SHAPE), missing pointers (MLA_ERR_NULL),
+ *     and data-pointer alignment (MLA_ERR_SHAPE): 16 bytes for bf16 / fp32 /
+ *     e4m3 data the kernels move in 16-byte pieces (queries, cache rows and
+ *     their e4m3 scales and rope, out_latent, the partials, the projection
+ *     operands), 4 bytes for int32 arrays and lse.  A failed check returns its
+ *     status and enqueues nothing.  The contents
  *     of device arrays (seq_lens, block_table) are the caller's contract and
  *     are not read on the host; mla_check_indices checks them on the device.
  *   - Calls on different streams may run concurrently as long as their output
@@ -69,7 +73,11 @@ typedef enum mla_status {
   MLA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. S_q > 64, block size 32) */
   MLA_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
   MLA_ERR_DEVICE = 6,      /* the current device is not gfx950 or cannot be queried */
-  MLA_ERR_SCRATCH = 7      /* mla_decode_noalloc: num_splits * S_q above MLA_NOALLOC_MAX_SPLIT_TOKENS */
+  MLA_ERR_SCRATCH = 7,     /* mla_decode_noalloc: num_splits * S_q above MLA_NOALLOC_MAX_SPLIT_TOKENS */
+  /* not statuses: they make every int32 value a valid mla_status, so that
+     mla_status_string may be given any number a caller holds */
+  MLA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  MLA_STATUS_RANGE_MAX_ = 2147483647
 } mla_status;
 
 typedef enum mla_dtype {

@@ -35,6 +35,7 @@ mla_status check_device() {
 bool present(const mla_tensor* t) { return t != nullptr && t->data != nullptr; }
 
 bool aligned16(const mla_tensor* t) { return ((uintptr_t)t->data & 15) == 0; }
+bool aligned4(const mla_tensor* t) { return ((uintptr_t)t->data & 3) == 0; }
 
 // dtype, then rank and shape (want[k] < 0: any size >= 1), then dense row-major strides
 mla_status check_tensor(const mla_tensor* t, mla_dtype dtype, int rank, const int64_t* want) {
@@ -170,6 +171,12 @@ mla_status prepare_decode(const mla_tensor* q_absorbed, const mla_tensor* q_rope
   MLA_TRY(check_cache(cache, paged, B, &cv));
   if (!paged) max_blocks = cv.contig_blocks;
   if (!std::isfinite(scale)) return MLA_ERR_SHAPE;
+  // the kernels move Q, cache rows and outputs in 16-byte pieces, lengths,
+  // table entries and lse in 4-byte ones
+  if (!aligned16(q_absorbed) || !aligned16(q_rope) || !aligned16(out_latent) || !aligned4(lse) ||
+      !aligned16(&cache->rows) || !aligned4(seq_lens) || (paged && !aligned4(block_table)))
+    return MLA_ERR_SHAPE;
+  if (cv.fp8 && (!aligned16(&cache->scales) || !aligned16(&cache->rope))) return MLA_ERR_SHAPE;
   // all units of the batch are counted in int32 inside the kernels
   if (max_blocks > INT_MAX / 2 || B * (max_blocks + mla::kSegWeight) > (int64_t)INT_MAX / 2) return MLA_ERR_SHAPE;
   p->q_abs = static_cast<const __bf16*>(q_absorbed->data);
@@ -259,6 +266,8 @@ mla_status mla_combine(const mla_tensor* partial_out, const mla_tensor* partial_
   int32_t parts = 1;
   MLA_TRY(check_partials(partial_out, partial_lse, S, &parts));
   if (parts == 1) return MLA_OK;  // a single partition holds every sequence whole
+  if (!aligned16(out_latent) || !aligned4(lse) || !aligned4(seq_lens) || !aligned4(partial_lse))
+    return MLA_ERR_SHAPE;
   MLA_TRY(check_device());
   mla::CombineParams p;
   p.part_out = partial_out->data;
@@ -402,7 +411,9 @@ mla_status mla_cache_append(const mla_tensor* kv, const mla_tensor* seq_lens, co
   if (!paged) max_blocks = cv.contig_blocks;
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return MLA_ERR_SHAPE;
   if (B * S > INT_MAX || max_blocks > INT_MAX / 128) return MLA_ERR_SHAPE;
-  if (!aligned16(kv) || !aligned16(&cache->rows)) return MLA_ERR_SHAPE;
+  if (!aligned16(kv) || !aligned16(&cache->rows) || !aligned4(seq_lens) || (paged && !aligned4(block_table)))
+    return MLA_ERR_SHAPE;
+  if (cv.fp8 && (!aligned4(&cache->scales) || !aligned4(&cache->rope))) return MLA_ERR_SHAPE;
   MLA_TRY(check_device());
   mla::AppendParams p;
   p.kv = static_cast<const float*>(kv->data);
@@ -442,6 +453,7 @@ mla_status mla_check_indices(const mla_latent_cache* cache, const mla_tensor* bl
   if (max_blocks > INT_MAX / 128) return MLA_ERR_SHAPE;
   const int64_t wc[1] = {2};
   MLA_TRY(check_tensor(counts, MLA_DTYPE_INT32, 1, wc));
+  if (!aligned4(seq_lens) || !aligned4(counts) || (paged && !aligned4(block_table))) return MLA_ERR_SHAPE;
   MLA_TRY(check_device());
   mla::CheckParams p;
   p.block_table = paged ? static_cast<const int32_t*>(block_table->data) : nullptr;
