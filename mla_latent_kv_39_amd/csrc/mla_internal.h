@@ -78,7 +78,7 @@ hipError_t launch_check_indices(const CheckParams& p, hipStream_t stream);
 // C[M x N] = A[M x K] W[N x K]^T per batch (mla_proj.hip): element offsets
 // A (m, k) = z a_batch + m a_row + k, W (n, k) = z w_batch + n k_len + k,
 // C (m, n) = z c_batch + m c_row + n.  k_len % 128 == 0; n_len a multiple of
-// the kind's tile width (128 for the wide kinds, 32 for the split-K kind);
+// the kind's tile width (128, 256 and 32 for the three kinds below);
 // 16-byte aligned A, W and C rows.
 struct GemmParams {
   const void* a;
@@ -88,8 +88,8 @@ struct GemmParams {
   int32_t m_len, n_len, k_len;
 };
 enum class GemmKind {
-  kF32ToF32Wide,    // fp32 A (rounded to bf16 on load), fp32 C, 64 x 128 tiles
-  kBf16ToBf16Wide,  // bf16 A, bf16 C, 128 x 128 tiles
+  kF32ToF32Wide,    // fp32 A (rounded to bf16 when used), fp32 C, 128 x 128 tiles
+  kBf16ToBf16Wide,  // bf16 A, bf16 C, 128 x 256 tiles
   kBf16ToF32SplitK  // bf16 A, fp32 C, 32 x 32 tiles, K split over the four waves
 };
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream);
