@@ -69,11 +69,15 @@ F8_CODES, F8_ROPE, F8_SCALES = 64 * 512, 64 * 128, 64 * 16
 F8_RAW = F8_CODES + F8_ROPE + F8_SCALES          # 41984
 F8_RAW0 = SLOT_BYTES
 F8_SCL = F8_RAW0 + 2 * F8_RAW                    # 157696
-# 1/scale of row r, block q, split into bf16 hi + lo (hi = bf16(1/s), lo =
-# bf16(1/s - hi)): the 16 bytes at F8_INV + 256 q + 16 (r / 4) hold
-# [hi(r0, r1), lo(r0, r1), hi(r2, r3), lo(r2, r3)] for rows r0 = 4 (r / 4) ..
-F8_INV = F8_SCL + 1024
-F8_FLAG = F8_INV + 1024
+# 1/scale of the unit's rows as MFMA operands, one 16 x 32 bf16 fragment per
+# sub-step ss (rows of the fragment x the sub-step's 32 cache rows, in the
+# order the probabilities hold them: lane group g has rows 4g .. 4g + 3, then
+# 16 + 4g .. 16 + 4g + 3): fragment row 4q holds bf16(1/s) of latent block q,
+# row 4q + 1 the remainder bf16(1/s - bf16(1/s)), rows 4q + 2, 4q + 3 zero.
+# Cache row t of the unit (u = t % 32), block q, part h (hi 0, lo 1) sits at
+# F8_RF + 1024 (t / 32) + 64 (4q + h) + 16 ((u % 16) / 4) + 8 (u / 16) + 2 (u % 4).
+F8_RF = F8_SCL + 1024
+F8_FLAG = F8_RF + 2048
 
 
 def configure(fp8):
@@ -1111,11 +1115,21 @@ def dequant_fp8(a, masked=True):
       f"v_cmp_gt_i32 s[{mk0}:{mk0 + 1}], {s(S_CURVALID)}, {vreg(t)}",
       f"v_add_u32 {vreg(t)}, 1, {vreg(t)}",
       f"v_cmp_gt_i32 s[{mk1}:{mk1 + 1}], {s(S_CURVALID)}, {vreg(t)}",
-      f"s_lshl_b32 s{T + 15}, {s(S_WAVE)}, 6",
-      f"s_add_u32 s{T + 15}, s{T + 15}, {F8_INV}",
-      f"v_lshlrev_b32 {vreg(t)}, 3, {vreg(pp)}",
+      # rows t0 = 16 (w & 1) + 2p, t0 + 1 of sub-step w >> 1, in the token order
+      # of the probabilities: F8_RF + 1024 (w >> 1) + 64 (4q) + 8 (w & 1)
+      # + 16 (p >> 1) + 4 (p & 1) for the hi pair, the lo pair 64 B on
+      f"s_lshr_b32 s{T + 15}, {s(S_WAVE)}, 1",
+      f"s_lshl_b32 s{T + 15}, s{T + 15}, 10",
+      f"s_and_b32 s{T + 14}, {s(S_WAVE)}, 1",
+      f"s_lshl_b32 s{T + 14}, s{T + 14}, 3",
+      f"s_add_u32 s{T + 15}, s{T + 15}, s{T + 14}",
+      f"s_add_u32 s{T + 15}, s{T + 15}, {F8_RF}",
+      f"v_and_b32 {vreg(t)}, 6, {vreg(pp)}",
+      f"v_lshlrev_b32 {vreg(t)}, 3, {vreg(t)}",
+      f"v_and_b32 {vreg(lo)}, 1, {vreg(pp)}",
+      f"v_lshl_add_u32 {vreg(t)}, {vreg(lo)}, 2, {vreg(t)}",
       f"v_lshl_add_u32 {vreg(t)}, {vreg(qq)}, 8, {vreg(t)}",
-      f"v_add_u32 {vreg(ia)}, s{T + 15}, {vreg(t)}")            # F8_INV + 256 q + 64 w + 8 p
+      f"v_add_u32 {vreg(ia)}, s{T + 15}, {vreg(t)}")
     a.lines += lds.wait(rr[1])
     if masked:
         a(f"v_cndmask_b32 {vreg(r0)}, 0, {vreg(r0)}, s[{mk0}:{mk0 + 1}]",
@@ -1134,7 +1148,9 @@ def dequant_fp8(a, masked=True):
       f"v_and_b32 {vreg(lo)}, 0xffff0000, {vreg(hi)}",
       f"v_sub_f32 {vreg(lo)}, {vreg(i1)}, {vreg(lo)}",
       f"v_cvt_pk_bf16_f32 {vreg(lo)}, {vreg(t)}, {vreg(lo)}",
-      f"ds_write_b64 {vreg(ia)}, {vr(hi, 2)}")
+      f"ds_write_b32 {vreg(ia)}, {vreg(hi)}",
+      f"ds_write_b32 {vreg(ia)}, {vreg(lo)} offset:64")
+    lds.issue()
     lds.issue()
     a("s_mov_b64 exec, -1")
 
@@ -1213,58 +1229,53 @@ def qk_fp8(a, ss):
     a.lines += update(3)
 
 
-PV_PART = 48    # e4m3 output phase: this sub-step's rounded-weight sums, (h, blk) at 48 + 4h + blk
-PV_INV = 56     # the current block's reciprocal-scale pairs of rows 32ss + 16tb + 4g .. +3 at 56 + 4tb
+PV_ACC = 48     # e4m3 output phase: rounded-weight sums, head half h at 48 + 4h (rows 4g.. of lane g)
+PV_RF = 56      # the sub-step's reciprocal-scale fragment (4 VGPRs)
+PV_RA = 60      # the fragment with the rows of other blocks cleared: one block's operand
 
 
-def f8_inv_reads(ss, blk):
-    """bf16 (hi, lo) pairs of 1/s of rows 32ss + 16tb + 4g .. +3, block blk ->
-    PV_INV + 4tb: [hi(i0, i1), lo(i0, i1), hi(i2, i3), lo(i2, i3)]."""
-    return [f"\tds_read_b128 {vr(PV_INV + 4 * tb, 4)}, {vreg(V_SCLB)} "
-            f"offset:{F8_INV - F8_SCL + 256 * blk + 128 * ss + 64 * tb}" for tb in range(2)]
+F8_RM = S_TMP   # s60..s67: lane masks r16 >> 2 == blk of the four blocks (output phase only)
 
 
-def block_weight_sums(blk):
-    """PV_PART[h][blk] = sum over this lane's 8 rows of bf16(P s) / s for
-    block blk: each packed pair of rounded weights dotted with the (hi, lo)
-    pairs of the rows' reciprocal scales, exact products accumulated in fp32.
-    The two heads' chains alternate (a DOT may take a DOT result as its
-    accumulator at once)."""
-    pb = F8_P[blk & 1]
-    out = []
-    for k in range(4):
-        tb, half = divmod(k, 2)
-        for part in range(2):
-            for h in range(2):
-                acc = PV_PART + 4 * h + blk
-                c = "0" if k == 0 and part == 0 else vreg(acc)
-                out.append(f"\tv_dot2_f32_bf16 {vreg(acc)}, {vreg(pb + 4 * h + k)}, "
-                           f"{vreg(PV_INV + 4 * tb + 2 * half + part)}, {c}")
+def f8_rf_read(ss):
+    """The sub-step's fragment: lane (g, r16) reads fragment row r16, cache
+    rows 32ss + 8g .. +7 of the unit (F8_RF + 64 r16 + 16 g, from V_SCLB =
+    F8_SCL + 16 g); and the four block masks."""
+    ad, sh = PV_RA, PV_RA + 1
+    out = [f"\tv_lshl_add_u32 {vreg(ad)}, {vreg(V_R16)}, 6, {vreg(V_SCLB)}",
+           f"\tds_read_b128 {vr(PV_RF, 4)}, {vreg(ad)} offset:{F8_RF - F8_SCL + 1024 * ss}",
+           f"\tv_lshrrev_b32 {vreg(sh)}, 2, {vreg(V_R16)}"]
+    out += [f"\tv_cmp_eq_u32 s[{F8_RM + 2 * b}:{F8_RM + 2 * b + 1}], {b}, {vreg(sh)}" for b in range(4)]
     return out
 
 
-def block_sums_reduce():
-    """Reduce-scatter of PV_PART over the four lanes g of a head: lane g keeps
-    block g's sum (permlane swaps), added to the segment's V_LBLK."""
-    out = ["\ts_nop 2"]            # DOT results -> another VALU
+def block_weight_operand(blk):
+    """PV_RA <- the fragment with every row outside 4blk .. 4blk + 3 zero
+    (lanes r16 >> 2 != blk), under the lane mask s[F8_RM + 2 blk]."""
+    return [f"\tv_cndmask_b32 {vreg(PV_RA + k)}, 0, {vreg(PV_RF + k)}, s[{F8_RM + 2 * blk}:{F8_RM + 2 * blk + 1}]"
+            for k in range(4)]
+
+
+def block_weight_mfmas(blk):
+    """PV_ACC[h] += (1/s fragment of block blk) x (rounded weights of block
+    blk): row 4blk of the result is the sum over the sub-step's rows of
+    bf16(P s) * bf16(1/s), row 4blk + 1 that of bf16(P s) * lo(1/s); the
+    products are exact and the sums fp32, as the dot products before were."""
+    pb = F8_P[blk & 1]
+    out = []
     for h in range(2):
-        v = [PV_PART + 4 * h + k for k in range(4)]
-        out += [f"\tv_permlane16_swap_b32 {vreg(v[0])}, {vreg(v[1])}",
-                f"\tv_permlane16_swap_b32 {vreg(v[2])}, {vreg(v[3])}"]
-    out.append("\ts_nop 1")
+        c = "0" if blk == 0 else vr(PV_ACC + 4 * h, 4)
+        out.append(f"\tv_mfma_f32_16x16x32_bf16 {vr(PV_ACC + 4 * h, 4)}, {vr(PV_RA, 4)}, {vr(pb + 4 * h, 4)}, {c}")
+    return out
+
+
+def block_sums_add():
+    """Lane (g, r16) adds block g's sums (rows 4g, 4g + 1 of PV_ACC) for
+    head 16h + r16 to its running V_LBLK[h]."""
+    out = ["\ts_nop 7", "\ts_nop 7", "\ts_nop 3"]      # MFMA results -> VALU
     for h in range(2):
-        v = [PV_PART + 4 * h + k for k in range(4)]
-        out += [f"\tv_add_f32 {vreg(v[0])}, {vreg(v[0])}, {vreg(v[1])}",
-                f"\tv_add_f32 {vreg(v[2])}, {vreg(v[2])}, {vreg(v[3])}"]
-    out.append("\ts_nop 1")
-    for h in range(2):
-        v = [PV_PART + 4 * h + k for k in range(4)]
-        out.append(f"\tv_permlane32_swap_b32 {vreg(v[0])}, {vreg(v[2])}")
-    out.append("\ts_nop 1")
-    for h in range(2):
-        v = [PV_PART + 4 * h + k for k in range(4)]
-        out += [f"\tv_add_f32 {vreg(v[0])}, {vreg(v[0])}, {vreg(v[2])}",
-                f"\tv_add_f32 {vreg(V_LBLK[h])}, {vreg(V_LBLK[h])}, {vreg(v[0])}"]
+        out += [f"\tv_add_f32 {vreg(V_LBLK[h])}, {vreg(V_LBLK[h])}, {vreg(PV_ACC + 4 * h)}",
+                f"\tv_add_f32 {vreg(V_LBLK[h])}, {vreg(V_LBLK[h])}, {vreg(PV_ACC + 4 * h + 1)}"]
     return out
 
 
@@ -1300,6 +1311,10 @@ def pv_fp8(a, ss):
     for r in f8_scale_reads(ss, 0, F8_T):
         a.lines.append(r)
     sid = lds.issue(), lds.issue()
+    rf = f8_rf_read(ss)
+    a.lines += rf[:2]
+    rfid = lds.issue()
+    a.lines += rf[2:]
     a.lines += lds.wait(sid[1])
     a.lines += scaled(0)
     a("s_nop 4")   # VALU writes of P -> MFMA reads
@@ -1312,11 +1327,8 @@ def pv_fp8(a, ss):
                 a.lines.append(r)
             sid = lds.issue(), lds.issue()
             nxt = scaled(blk + 1)
-        # this block's reciprocal scales (the previous block's sums are done with them)
-        for r in f8_inv_reads(ss, blk):
-            a.lines.append(r)
-        iid = lds.issue(), lds.issue()
-        sums = block_weight_sums(blk)
+        # this block's weight-sum operand: the fragment with other blocks' rows cleared
+        sums = block_weight_operand(blk)
         for j, cb in enumerate(range(8 * blk, 8 * blk + 8)):
             f = frags[cb]
             a.lines += lds.wait(max(f.read_ids))
@@ -1337,14 +1349,16 @@ def pv_fp8(a, ss):
                 k = 6 if j < 4 else len(nxt)
                 a.lines += nxt[:k]
                 nxt = nxt[k:]
-            # the block's weight sums over fragments 5 .. 7
-            if j >= 5:
-                if j == 5:
-                    a.lines += lds.wait(iid[1])
-                k = 6 if j < 7 else len(sums)
-                a.lines += sums[:k]
-                sums = sums[k:]
-    a.lines += block_sums_reduce()
+            # the block's weight-sum operand over fragments 5, 6; its MFMAs after the
+            # block's last output MFMAs (more than five wait states after the operand)
+            if j == 5:
+                a.lines += lds.wait(rfid)
+            if j in (5, 6):
+                a.lines += sums[:2]
+                sums = sums[2:]
+            if j == 7:
+                a.lines += block_weight_mfmas(blk)
+    a.lines += block_sums_add()
 
 
 def substep_fp8(a, ss, lean):
@@ -2660,6 +2674,12 @@ def kernel(fp8=False):
     a(f"v_mov_b32 {vreg(V_NEGINF)}, {NEG_INF}")
     if FP8:
         flag_write(a, 0)    # restart flag = 0
+        # the reciprocal fragments' zero rows (4q + 2, 4q + 3): written once
+        a(f"v_lshlrev_b32 {vreg(V_T)}, 3, {vreg(V_TID)}",
+          f"v_add_u32 {vreg(V_T)}, {F8_RF}, {vreg(V_T)}",
+          f"v_mov_b32 {vreg(V_T + 2)}, 0",
+          f"v_mov_b32 {vreg(V_T + 3)}, 0",
+          f"ds_write_b64 {vreg(V_T)}, {vr(V_T + 2, 2)}")
     a(s_waitcnt_lgkm(0), "s_barrier")
     if not FP8:
         kernel_tail_hp(a)

@@ -89,6 +89,7 @@ class Wave:
         x = [self.sval(v) for v in a[1:]]
         self.s[key] = {"s_mul_i32": lambda: x[0] * x[1], "s_add_u32": lambda: x[0] + x[1],
                        "s_addc_u32": lambda: x[0] + x[1], "s_lshl_b32": lambda: x[0] << x[1],
+                       "s_lshr_b32": lambda: x[0] >> x[1], "s_and_b32": lambda: x[0] & x[1],
                        "s_mov_b32": lambda: x[0]}[op]()
 
     def vector(self, op, a, L):
@@ -315,7 +316,7 @@ def test_fp8_staging_and_dequant(fp8_mode, valid):
         m.s[G.S_SLOT], m.s[G.S_CURVALID] = 1, valid
         m.run(lines_of(G.dequant_fp8))
     for addr in tile:
-        assert 0 <= addr < G.SLOT_BYTES or G.F8_SCL <= addr < G.F8_INV + 1024
+        assert 0 <= addr < G.SLOT_BYTES or G.F8_SCL <= addr < G.F8_RF + 2048
     for r in range(64):
         for c in range(72):
             for q in range(4):
@@ -333,14 +334,17 @@ def test_fp8_staging_and_dequant(fp8_mode, valid):
         for r in range(64):
             want = (ZERO,) * 4 if r >= valid else tuple(("g", SCALES + r * 16 + blk * 4 + i) for i in range(4))
             assert tile.get(G.F8_SCL + blk * 256 + r * 4) == want
-    # reciprocal scales: rows r, r + 1 (r even) of block blk as bf16 (hi, lo)
-    # pairs at F8_INV + 256 blk + 16 (r / 4) + 8 ((r % 4) / 2): the hi pair is
-    # formed from the two rows' own scales (zeroed past the valid rows), the
-    # lo pair from the same scales and the hi pair
+    # reciprocal scales: rows r, r + 1 (r even) of block blk as bf16 pairs in the
+    # 16 x 32 fragment of sub-step r / 32, in the probabilities' row order:
+    # the hi pair at F8_RF + 1024 (r / 32) + 64 (4 blk) + 16 ((u % 16) / 4)
+    # + 8 (u / 16) + 2 (u % 4), u = r % 32, the lo pair one fragment row (64 B)
+    # on; the hi pair is formed from the two rows' own scales (zeroed past the
+    # valid rows), the lo pair from the same scales and the hi pair
     for blk in range(4):
         for r in range(0, 64, 2):
-            at = G.F8_INV + blk * 256 + 16 * (r // 4) + 8 * ((r % 4) // 2)
-            hi, lo = tile.get(at), tile.get(at + 4)
+            u = r % 32
+            at = G.F8_RF + 1024 * (r // 32) + 256 * blk + 16 * ((u % 16) // 4) + 8 * (u // 16) + 2 * (u % 4)
+            hi, lo = tile.get(at), tile.get(at + 64)
             assert hi is not None and lo is not None, (blk, r)
             assert hi[:2] == ("op", "v_cvt_pk_bf16_f32") and lo[:2] == ("op", "v_cvt_pk_bf16_f32")
             for k, row in enumerate((r, r + 1)):
