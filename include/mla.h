@@ -63,6 +63,10 @@ extern "C" {
 #define MLA_BLOCK_SIZE 64   /* rows per cache page */
 #define MLA_FP8_GROUP 128   /* latent values per fp8 scale */
 #define MLA_MAX_SPLITS 65536
+/* Most num_splits * S_q a call with partials takes (MLA_ERR_SHAPE above): the
+ * kernels address a partial row's lse and descales with 32-bit offsets, which
+ * hold up to 2 * 2^19 blocks of 128 rows (a partial_out of ~140 GB). */
+#define MLA_MAX_SPLIT_TOKENS 524288
 #define MLA_MAX_RANK 5
 
 typedef enum mla_status {
@@ -140,7 +144,8 @@ typedef struct mla_latent_cache {
  * 2 and 1, one kernel launch each, and every group reads the rows again (the
  * decode of a few draft tokens, not a long prefill chunk).  The split count P is the
  * leading dimension of partial_lse (P = 1 when partial_lse is NULL): a power
- * of two, 1 .. MLA_MAX_SPLITS, the number of work partitions the rows of the
+ * of two, 1 .. MLA_MAX_SPLITS with P * S_q <= MLA_MAX_SPLIT_TOKENS, the number
+ * of work partitions the rows of the
  * whole batch are cut into.  The rows of all sequences, in 64-row pages
  * (units; a sequence owns max(1, ceil(seq_len / 64)) of them), are dealt out
  * in order, so one partition can cover the tail of one sequence, whole

@@ -119,6 +119,7 @@ mla_status check_partials(const mla_tensor* partial_out, const mla_tensor* parti
   MLA_TRY(check_tensor(partial_lse, MLA_DTYPE_FP32, 4, wl));
   const int64_t p = partial_lse->shape[0];
   if (p > MLA_MAX_SPLITS || (p & (p - 1)) != 0) return MLA_ERR_SHAPE;   // partitions are cut with shifts
+  if (p * s_q > MLA_MAX_SPLIT_TOKENS) return MLA_ERR_SHAPE;              // 32-bit row offsets in the kernels
   *parts = (int32_t)p;
   if (p == 1) return MLA_OK;
   const int64_t wo[1] = {-1};

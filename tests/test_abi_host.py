@@ -149,6 +149,8 @@ def test_decode_rejects_bad_descriptors(lib):
     assert _with(lib, table=None, cache=lambda a: rows((3, 128, 576))(a)) == E.MLA_ERR_SHAPE
     # partials: the split count is partial_lse's leading dimension, a power of two
     assert _with(lib, P=6) == E.MLA_ERR_SHAPE
+    # num_splits * S_q past MLA_MAX_SPLIT_TOKENS (2^19): the kernels' 32-bit row offsets
+    assert _with(lib, P=65536, S=16) == E.MLA_ERR_SHAPE
     assert _with(lib, pl=desc(lib, (4, 2, 1, 64), f32)) == E.MLA_ERR_SHAPE
     assert _with(lib, pl=desc(lib, (4, 1, 1, 128), f32)) == E.MLA_ERR_SHAPE
     assert _with(lib, po=None) == E.MLA_ERR_NULL
@@ -169,6 +171,7 @@ def test_a_valid_call_gets_past_every_host_check(lib):
     assert _decode(lib, _args(lib)) == lib.MLA_ERR_DEVICE
     assert _decode(lib, _args(lib, fp8=True, S=4)) == lib.MLA_ERR_DEVICE
     assert _decode(lib, _args(lib, S=7)) == lib.MLA_ERR_DEVICE
+    assert _decode(lib, _args(lib, P=65536, S=8)) == lib.MLA_ERR_DEVICE      # num_splits * S_q = 2^19
     a = _args(lib)
     a["table"] = None                                  # contiguous: [B * 5, 64, 576]
     a["cache"].rows = desc(lib, (10, 64, 576), lib.MLA_DTYPE_BF16)
@@ -208,6 +211,9 @@ def test_combine_rejects_bad_descriptors(lib):
     assert comb(out=desc(lib, (2, 65, 128, 512), lib.MLA_DTYPE_FP32),
                 lse=desc(lib, (2, 65, 128), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_UNSUPPORTED
     assert comb(out=desc(lib, (2, 1, 96, 512), lib.MLA_DTYPE_FP32)) == E.MLA_ERR_SHAPE
+    big = _args(lib, S=16, P=65536)                      # num_splits * S_q = 2^20
+    assert c.mla_combine(_ref(big["po"]), _ref(big["pl"]), _ref(big["lens"]), _ref(big["out"]),
+                         _ref(big["lse"]), None) == E.MLA_ERR_SHAPE
     # one partition: nothing to merge, no launch
     assert comb(po=None, pl=None) == E.MLA_OK
     assert comb(po=None, pl=desc(lib, (1, 2, 1, 128), lib.MLA_DTYPE_FP32)) == E.MLA_OK

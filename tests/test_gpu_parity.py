@@ -75,6 +75,46 @@ def test_four_query_tokens_e4m3(num_splits):
     _run_and_check(inp, num_splits, f"s_q=4 e4m3 splits={num_splits}")
 
 
+@pytest.mark.parametrize("cache,num_splits", [("bf16", 1), ("bf16", 8), ("fp8_e4m3", 4)])
+def test_most_query_tokens(cache, num_splits):
+    # S_q = 64, the most a call takes: sixteen launches of four-token groups;
+    # the 64-row sequence gives token s exactly s + 1 visible rows
+    inp = _small([64, 65, 130, 300], s_q=64, seed=23, cache=cache)
+    _run_and_check(inp, num_splits, f"s_q=64 {cache} splits={num_splits}")
+
+
+def test_most_partitions_at_the_split_token_limit():
+    """MLA_MAX_SPLITS partitions with num_splits * S_q = MLA_MAX_SPLIT_TOKENS:
+    the partitions that hold rows are spread over the whole index range, so
+    the last partial blocks (2^20 of them, a 140 GB workspace) sit past 2^37
+    bytes and their descales 2^31 bytes into the table."""
+    from gpu_helpers import DeviceInputs, compare, OUT_TOL
+    from mla_latent_kv_39_amd.runner import DecodeWorkspace
+    splits, s_q = 65536, 8
+    need = mla_partial_bytes(splits, s_q)
+    free, _ = torch.cuda.mem_get_info()
+    if free < need + (8 << 30):
+        pytest.skip(f"{need / 2**30:.0f} GiB partial workspace does not fit ({free / 2**30:.0f} GiB free)")
+    inp = _small([8, 700, 64, 129, 2000], s_q=s_q, seed=24)
+    print(f"[gpu] max partitions: B={inp.batch} S_q={s_q} splits={splits} workspace {need / 2**30:.0f} GiB",
+          flush=True)
+    dev = DeviceInputs(inp)
+    ws = DecodeWorkspace(inp.batch, s_q, splits)
+    try:
+        out, lse = dev.run(splits, ws)
+    finally:
+        del ws
+        torch.cuda.empty_cache()
+    ref_out, ref_lse = O.mla_decode(inp)
+    e = compare(out, lse, ref_out, ref_lse, "max partitions", out_tol=OUT_TOL)
+    print(f"[gpu] max partitions: max err out {e[0]:.2e} lse {e[1]:.2e}", flush=True)
+
+
+def mla_partial_bytes(splits, s_q):
+    import mla_latent_kv_39_amd as mla
+    return mla.mla_partial_out_bytes(splits, s_q) + mla.mla_partial_lse_bytes(splits, s_q)
+
+
 def test_check_indices_counts_contract_violations():
     """mla_check_indices: zero on the generated inputs; a length past the
     table's capacity and a table entry outside the cache are counted."""
