@@ -1260,7 +1260,7 @@ def block_weight_mfmas(blk):
     """PV_ACC[h] += (1/s fragment of block blk) x (rounded weights of block
     blk): row 4blk of the result is the sum over the sub-step's rows of
     bf16(P s) * bf16(1/s), row 4blk + 1 that of bf16(P s) * lo(1/s); the
-    products are exact and the sums fp32, as the dot products before were."""
+    products are exact and the sums fp32."""
     pb = F8_P[blk & 1]
     out = []
     for h in range(2):
