@@ -181,17 +181,6 @@ def tensor(t, dtype: Optional[int] = None, device_only: bool = True) -> MlaTenso
     pad = (0,) * (MAX_RANK - n)
     return MlaTensor(t.data_ptr() or None, _dtype_code(t) if dtype is None else int(dtype), n,
                      shape + pad, tuple(t.stride()) + pad)
-    if device_only and t.device.type != "cuda":
-        raise ValueError(f"tensor on {t.device} passed to libmla: device tensors only")
-    if t.dim() > MAX_RANK:
-        raise ValueError(f"rank {t.dim()} above {MAX_RANK}")
-    d.data = int(t.data_ptr()) or None
-    d.dtype = _dtype_code(t) if dtype is None else int(dtype)
-    d.rank = t.dim()
-    for k in range(t.dim()):
-        d.shape[k] = int(t.shape[k])
-        d.strides[k] = int(t.stride(k))
-    return d
 
 
 def _stream_handle(stream) -> Optional[int]:

@@ -4,7 +4,6 @@ values, k^R in bf16 (DeepSeek-V3 详解 §4.2 fine-grained scaling).  The kernel
 keeps the e4m3 values exact in the scores, rounds P * scale to bf16 for the
 output and normalises each 128-wide latent block by the sum of its own rounded
 weights, so the bf16 path's tolerances apply (1e-2 on out, 1e-3 on lse)."""
-import numpy as np
 import pytest
 import torch
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from mla_inputs import WORKLOADS, make_inputs
+from mla_inputs import make_inputs
 from oracle import mla_oracle as O
 
 pytestmark = [pytest.mark.gpu]
