@@ -135,9 +135,12 @@ def cpu_baseline(inp, budget_s: float):
                       f"and query tokens), {dt:.1f} s, numpy fp64 on the host"}
 
 
-def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: int = 0):
+def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: int = 0, min_warm_s: float = 0.0):
     """Time `steps` decode steps (decode + combine) and `steps` decode
-    launches alone on one stream with HIP events; returns a dict."""
+    launches alone on one stream with HIP events; returns a dict.  The
+    untimed warm-up runs `warmup` steps, and then more until `min_warm_s`
+    seconds have passed on the GPU (short steps need more than a hundred to
+    leave the slow first milliseconds behind)."""
     import torch
 
     import mla_latent_kv_39_amd as mla
@@ -187,15 +190,29 @@ def measure(workload: str, steps: int, warmup: int, num_splits: int = 0, seed: i
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # whole steps; the events are recorded on the stream the kernels run on, one
-    # between every two steps (the spread of single steps: p10 / p50 / p90)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for i in range(50):
+            step(i)
+        torch.cuda.synchronize()
+    # whole steps back to back, bracketed by two events on the stream the
+    # kernels run on: the timed region
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(steps):
+        step(i)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = s0.elapsed_time(s1) / steps
+    # the spread of single steps (p10 / p50 / p90) from a second pass with an
+    # event between every two steps; each event adds ~2-3 us to a step, so
+    # these run above ms_step on short steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record(stream)
     for i in range(steps):
         step(i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = evs[0].elapsed_time(evs[-1]) / steps
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     pct = {f"p{q}": per_step[min(steps - 1, (q * steps) // 100)] for q in (10, 50, 90)}
     # the dominant kernel alone, same launches back to back
@@ -401,7 +418,7 @@ def main(argv=None):
     if not args.only:
         for w in ALL_WORKLOADS:
             if w != args.workload:
-                others[w] = summary(measure(w, args.steps, args.warmup, 0, args.seed))
+                others[w] = summary(measure(w, args.steps, args.warmup, 0, args.seed, min_warm_s=0.25))
     inp = head["inp"]
     next_rows = None if args.only else measure_next_rows(inp.batch, inp.s_q, args.steps, args.warmup)
     copy_gbs = copy_bandwidth()
