@@ -94,6 +94,13 @@ def test_token_groups(cache, lens, s_q, splits):
     _check(_small(lens, s_q=s_q, seed=8, cache=cache), splits)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def test_most_query_tokens(cache):
+    # S_q = 64, the most a call takes: sixteen launches of four-token groups
+    # writing their tokens' rows of the shared outputs and partials
+    _check(_small([64, 70], s_q=64, seed=23, cache=cache), 2)
+
+
 def test_bf16_result_independent_of_wave_order():
     inp = _small([65, 130, 200], seed=7)
     a = ED.emulate_decode(inp, 4, seed=1)
