@@ -255,7 +255,7 @@ size_t mla_partial_lse_bytes(int32_t num_splits, int32_t s_q);
  *   rope_base   the RoPE base (10000), finite and positive
  *   q_absorbed  bf16 [B, S_q, 128, 512]   = W^UK_h^T q^C_h (fp32 accumulation, rounded once)
  *   q_rope      bf16 [B, S_q, 128, 64]    = RoPE(q^R, position); may be q_r itself (in place)
- * bf16 MFMA GEMM per head, then a RoPE kernel; any S_q >= 1.  Data pointers
+ * bf16 MFMA GEMM per head with the RoPE in the same launch; any S_q >= 1.  Data pointers
  * of q_c, q_r, w_uk_t, q_absorbed and q_rope 16-byte aligned.
  */
 mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const mla_tensor* w_uk_t,

@@ -319,8 +319,6 @@ mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const 
   g.m_len = (int32_t)(B * S);
   g.n_len = MLA_LATENT_DIM;
   g.k_len = MLA_HEAD_DIM;
-  if (mla::launch_gemm_nt(g, MLA_NUM_HEADS, mla::GemmKind::kBf16ToBf16Wide, stream) != hipSuccess)
-    return MLA_ERR_LAUNCH;
   mla::RopeParams r;
   r.src = static_cast<const __bf16*>(q_r->data);
   r.dst = static_cast<__bf16*>(q_rope->data);
@@ -328,7 +326,7 @@ mla_status mla_absorb_query(const mla_tensor* q_c, const mla_tensor* q_r, const 
   r.tokens = (int32_t)(B * S);
   r.s_q = (int32_t)S;
   r.base = rope_base;
-  return mla::launch_query_rope(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  return mla::launch_query_absorb(g, r, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 mla_status mla_absorb_output(const mla_tensor* out_latent, const mla_tensor* w_uv, const mla_tensor* out_values,
@@ -358,7 +356,7 @@ mla_status mla_absorb_output(const mla_tensor* out_latent, const mla_tensor* w_u
   g.m_len = (int32_t)(B * S);
   g.n_len = MLA_HEAD_DIM;
   g.k_len = MLA_LATENT_DIM;
-  return mla::launch_gemm_nt(g, MLA_NUM_HEADS, mla::GemmKind::kF32ToF32Wide, stream) == hipSuccess
+  return mla::launch_gemm_nt(g, MLA_NUM_HEADS, mla::GemmKind::kOutputAbsorb, stream) == hipSuccess
              ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

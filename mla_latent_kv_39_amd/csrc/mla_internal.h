@@ -77,9 +77,10 @@ hipError_t launch_check_indices(const CheckParams& p, hipStream_t stream);
 
 // C[M x N] = A[M x K] W[N x K]^T per batch (mla_proj.hip): element offsets
 // A (m, k) = z a_batch + m a_row + k, W (n, k) = z w_batch + n k_len + k,
-// C (m, n) = z c_batch + m c_row + n.  k_len % 128 == 0; n_len a multiple of
-// the kind's tile width (128, 256 and 32 for the three kinds below);
-// 16-byte aligned A, W and C rows.
+// C (m, n) = z c_batch + m c_row + n.  k_len % 128 == 0; the output
+// absorption takes K = 512, N = 128 per head, the query absorption K = 128,
+// N = 512 per head, the projection n_len a multiple of 32; 16-byte aligned
+// A, W and C rows.
 struct GemmParams {
   const void* a;
   const __bf16* w;
@@ -88,8 +89,7 @@ struct GemmParams {
   int32_t m_len, n_len, k_len;
 };
 enum class GemmKind {
-  kF32ToF32Wide,    // fp32 A (rounded to bf16 when used), fp32 C, 128 x 128 tiles
-  kBf16ToBf16Wide,  // bf16 A, bf16 C, 128 x 256 tiles
+  kOutputAbsorb,    // fp32 A (rounded to bf16 when used), fp32 C, K = 512, N = 128 per head
   kBf16ToF32SplitK  // bf16 A, fp32 C, 32 x 32 tiles, K split over the four waves
 };
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream);
@@ -104,7 +104,9 @@ struct RopeParams {
   int32_t s_q;
   double base;
 };
-hipError_t launch_query_rope(const RopeParams& p, hipStream_t stream);
+// The absorbed query (g: A = q^C, W = W^UK^T per head, C = q_absorbed; K = 128,
+// N = 512, 128 heads) and the RoPE of q^R (r), in one launch.
+hipError_t launch_query_absorb(const GemmParams& g, const RopeParams& r, hipStream_t stream);
 
 // New cache rows: kv [B S_q, 576] fp32 ([c^KV ; k^R before RoPE]) -> the page
 // slot of position seq_len[b] - S_q + s, bf16 rows or the e4m3 bundle.

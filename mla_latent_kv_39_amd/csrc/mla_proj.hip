@@ -9,14 +9,16 @@
 //                    bf16, or e4m3 with one fp32 scale per 128 values
 //                    (DeepSeek-V3 详解, yudonglee.me, §4.2)
 //
-// The three projections are one kernel: C[M x N] = A[M x K] W[N x K]^T on
-// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, batched over
-// heads.  M is the number of tokens of a decode step (a few hundred): every
-// weight is read once per 128-token tile, so the kernels are bound by the
-// weight and activation bytes, and operands go straight from global memory
-// into MFMA registers (16-byte loads, a stage of them always in flight); the
-// outputs come out of the MFMAs four consecutive columns per lane and are
-// stored from the accumulators.
+// The three projections are C[M x N] = A[M x K] W[N x K]^T on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation, batched over heads for
+// the two absorptions.  M is the number of tokens of a decode step (a few
+// hundred): every weight byte serves every token of its tile, so the kernels
+// are bound by the weight and activation bytes.  The two absorptions stage
+// their operands through LDS (each line crosses a compute unit's L1 once,
+// with loads always in flight); the projection, whose K of 7168 leaves few
+// output tiles, splits K over the waves of a workgroup and loads its operands
+// straight into MFMA registers.  Outputs come out of the MFMAs four
+// consecutive columns per lane and are stored from the accumulators.
 #include <hip/hip_bf16.h>
 
 #include "mla_internal.h"
@@ -203,6 +205,334 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_kernel(GemmParams g) {
   }
 }
 
+// q_rope of query token t = b S_q + s by one workgroup of 256 threads,
+// position seq_len[b] - S_q + s, in three steps: each thread loads its 16
+// pairs (8-byte loads of two pairs), threads 0..31 compute the 32 angles'
+// cosines and sines once for the token (fp64) into LDS, and after a barrier
+// every thread rotates its pairs.
+struct QueryRopeToken {
+  static constexpr int kPer = kHeads * kRope / 4 / 256;   // groups of four values per thread
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 x[kPer];
+  int64_t base;
+  int pos;
+  __device__ __forceinline__ void load(const RopeParams& p, int t) {
+    base = (int64_t)t * kHeads * kRope;
+    pos = p.seq_lens[t / p.s_q] - p.s_q + t % p.s_q;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) x[k] = *reinterpret_cast<const bf16x4*>(p.src + base + 4 * (threadIdx.x + 256 * k));
+  }
+  __device__ __forceinline__ void angles(const RopeParams& p, float (*s_cs)[kRope / 2]) const {
+    if (threadIdx.x < kRope / 2) {
+      const double theta = pow(p.base, -2.0 * (double)threadIdx.x / (double)kRope);
+      double sn, cs;
+      sincos((double)pos * theta, &sn, &cs);
+      s_cs[0][threadIdx.x] = (float)cs;
+      s_cs[1][threadIdx.x] = (float)sn;
+    }
+  }
+  __device__ __forceinline__ void rotate_store(const RopeParams& p, const float (*s_cs)[kRope / 2]) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = threadIdx.x + 256 * k;
+      const int i = (e % (kRope / 4)) * 2;                         // first pair of the four values
+      bf16x4 y;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float c = s_cs[0][i + q], sn = s_cs[1][i + q];
+        const float x0 = (float)x[k][2 * q], x1 = (float)x[k][2 * q + 1];
+        y[2 * q] = (__bf16)fmaf(x0, c, -x1 * sn);
+        y[2 * q + 1] = (__bf16)fmaf(x0, sn, x1 * c);
+      }
+      *reinterpret_cast<bf16x4*>(p.dst + base + 4 * e) = y;
+    }
+  }
+};
+
+// Absorbed query q_absorbed_h = W^UK_h^T q^C_h (K = 128, N = 512 per head),
+// and q_rope = RoPE(q^R, position) in the same launch: one workgroup per
+// (head, tile of 128 tokens), every tile of a head on one XCD (blockIdx.x is
+// the head: workgroups are dealt to the 8 XCDs by linear id), so the head's
+// weight is fetched from HBM once.  The token tile stays in LDS; the weight
+// goes through in four chunks of 128 output columns, two LDS buffers, each
+// thread keeping two chunks of loads in registers so that they are in
+// flight while a chunk's MFMAs run and its outputs are stored (loading the
+// weight and the tiles first and storing after them measured 20 us for 256
+// tokens).  LDS rows are 256 bytes (16 chunks of 16 bytes); chunk c of row r
+// sits at chunk c ^ (r & 15), so the 16 rows of an operand fragment read
+// (one chunk each) hit 16 different chunk positions of the bank row.
+// Workgroup i also rotates the q^R of tokens i, i + grid, ... (all heads;
+// each token's angles are evaluated once), token i's while the first loads
+// are in flight.  (Rotating each head's pairs in that head's workgroups
+// instead evaluates every angle 128 times: 24.6 us against 22.4 us for a
+// GEMM and a separate RoPE kernel.)
+constexpr int kAqTileM = 128;
+constexpr int kAqChunkN = 128;                // output columns per weight chunk
+constexpr int kAqN = 512;                     // d_c
+constexpr int kAqK = 128;                     // d_h: the chunks of a row
+constexpr int kAqChunks = kAqK / 8;           // 16-byte chunks per row
+constexpr int kAqNChunks = kAqN / kAqChunkN;
+constexpr int kAqPer = kAqTileM * kAqChunks / 256;   // 16-byte chunks per thread of a tile (8)
+
+__device__ __forceinline__ int aq_slot(int r, int c) { return r * kAqChunks + (c ^ (r & 15)); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct AqRegs {
+  u32x4 v[kAqPer];
+};
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+__global__ __launch_bounds__(256) void absorb_query_kernel(GemmParams g, RopeParams rp) {
+  __shared__ u32x4 s_a[kAqTileM * kAqChunks];            // 32 KB
+  __shared__ u32x4 s_w[2][kAqChunkN * kAqChunks];        // 2 x 32 KB
+  __shared__ float s_cs[2][kRope / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int head = blockIdx.x, m0 = blockIdx.y * kAqTileM;
+  const int id = blockIdx.x + gridDim.x * blockIdx.y;
+  const __bf16* A = static_cast<const __bf16*>(g.a) + (int64_t)head * g.a_batch + (int64_t)m0 * g.a_row;
+  const __bf16* W = g.w + (int64_t)head * g.w_batch;
+  __bf16* C = static_cast<__bf16*>(g.c) + (int64_t)head * g.c_batch;
+  const int mrows = g.m_len - m0;               // >= 1; token rows past it are read as its last one
+  // thread t moves chunks e = t + 256 i: row e / 16, chunk e % 16 (16 threads
+  // per 256-byte row: a wave's load covers four whole rows)
+  auto load_a = [&](AqRegs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kAqPer; ++i) {
+      const int e = tid + 256 * i, row = e / kAqChunks;
+      const int rr = row < mrows ? row : mrows - 1;
+      r.v[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)rr * g.a_row + 8 * (e % kAqChunks));
+    }
+  };
+  auto load_w = [&](AqRegs& r, int chunk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kAqPer; ++i) {
+      const int e = tid + 256 * i;
+      r.v[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)(chunk * kAqChunkN + e / kAqChunks) * kAqK +
+                                               8 * (e % kAqChunks));
+    }
+  };
+  auto put = [&](const AqRegs& r, u32x4* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kAqPer; ++i) {
+      const int e = tid + 256 * i;
+      dst[aq_slot(e / kAqChunks, e % kAqChunks)] = r.v[i];
+    }
+  };
+  QueryRopeToken rt;
+  const bool rope0 = id < rp.tokens;          // uniform over the workgroup
+  if (rope0) rt.load(rp, id);
+  AqRegs ra, rw0, rw1;
+  load_a(ra);
+  load_w(rw0, 0);
+  load_w(rw1, 1);
+  if (rope0) rt.angles(rp, s_cs);
+  put(ra, s_a);
+  put(rw0, s_w[0]);
+  load_w(rw0, 2);
+  __syncthreads();
+  if (rope0) rt.rotate_store(rp, s_cs);
+
+  // wave (wm, wn) owns tokens 64 wm .. +63 and columns 64 wn .. +63 of a chunk
+  const int wm = wave & 1, wn = wave >> 1;
+  auto chunk = [&](auto cc) __attribute__((always_inline)) {
+    constexpr int c = decltype(cc)::value;
+    const u32x4* sw = s_w[c & 1];
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kAqK / 32; ++u) {
+      bf16x8 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __builtin_bit_cast(bf16x8, s_a[aq_slot(64 * wm + 16 * i + r16, 4 * u + kg)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, sw[aq_slot(64 * wn + 16 * j + r16, 4 * u + kg)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, x[i], acc[i][j], 0, 0, 0);
+      }
+    }
+    // chunk c + 1 into the buffer whose last readers passed the previous
+    // barrier, then its registers take chunk c + 3
+    if constexpr (c + 1 < kAqNChunks && ((c + 1) & 1)) {
+      put(rw1, s_w[1]);
+      if constexpr (c + 3 < kAqNChunks) load_w(rw1, c + 3);
+    } else if constexpr (c + 1 < kAqNChunks) {
+      put(rw0, s_w[0]);
+      if constexpr (c + 3 < kAqNChunks) load_w(rw0, c + 3);
+    }
+    // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, columns
+    // 128 c + 64 wn + 16 j + 4 kg .. +3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 64 * wm + 16 * i + r16;
+      if (m >= g.m_len) continue;
+      __bf16* crow = C + (int64_t)m * g.c_row + kAqChunkN * c + 64 * wn + 4 * kg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store4(crow + 16 * j, acc[i][j]);
+    }
+    __syncthreads();
+  };
+  chunk(IntC<0>{});
+  chunk(IntC<1>{});
+  chunk(IntC<2>{});
+  chunk(IntC<3>{});
+  static_assert(kAqNChunks == 4, "one call per chunk above");
+  // more tokens than workgroups: the rest of this workgroup's share (s_cs is
+  // free: every thread has passed the barrier after its last reader)
+  const int grid = (int)(gridDim.x * gridDim.y);
+  for (int t = id + grid; t < rp.tokens; t += grid) {
+    rt.load(rp, t);
+    rt.angles(rp, s_cs);
+    __syncthreads();
+    rt.rotate_store(rp, s_cs);
+    __syncthreads();
+  }
+}
+
+// Output values o_h = W^UV_h out_latent_h (K = 512 fp32 values rounded to
+// bf16 when used, N = 128 per head, fp32 out): one workgroup per (head, tile
+// of 128 tokens), every tile of a head on one XCD (blockIdx.x is the head:
+// workgroups are dealt to the 8 XCDs by linear id), so its weight is fetched
+// from HBM once.  K runs in 8 stages of 64 through two LDS buffers; each
+// thread keeps two stages of loads in registers, so two are always in flight
+// while a stage's MFMAs run (direct-to-LDS loads would need the compiler to
+// wait for every load in flight before any LDS read: with them, one stage at
+// a time, 25.5 us for 256 tokens).  LDS rows: the tokens' 64 fp32 values as
+// 16 chunks of 16 bytes, chunk c at c ^ (r & 15); the weight's 64 bf16
+// values as 8 chunks, chunk c at c ^ ((r >> 1) & 7) (two 128-byte rows per
+// bank row): the 16 rows of a fragment read fall on 16 different bank
+// positions.
+constexpr int kAoTileM = 128;
+constexpr int kAoN = 128;                     // d_h
+constexpr int kAoK = 512;                     // d_c
+constexpr int kAoStage = 64;                  // K values per stage
+constexpr int kAoStages = kAoK / kAoStage;
+constexpr int kAoAChunks = kAoStage / 4;      // fp32 chunks per token row of a stage (16)
+constexpr int kAoWChunks = kAoStage / 8;      // bf16 chunks per weight row of a stage (8)
+constexpr int kAoAPer = kAoTileM * kAoAChunks / 256;   // chunks per thread and stage: 8 of tokens,
+constexpr int kAoWPer = kAoN * kAoWChunks / 256;       // 4 of weight
+
+__device__ __forceinline__ int ao_wslot(int r, int c) { return r * kAoWChunks + (c ^ ((r >> 1) & 7)); }
+
+// staging registers of one stage (clang vectors: HIP's uint4 is a class with
+// union storage, which kept arrays of it out of registers)
+struct AoStage {
+  u32x4 a[kAoAPer], w[kAoWPer];
+};
+
+__global__ __launch_bounds__(256) void absorb_output_kernel(GemmParams g) {
+  __shared__ u32x4 s_a[2][kAoTileM * kAoAChunks];      // 2 x 32 KB
+  __shared__ u32x4 s_w[2][kAoN * kAoWChunks];          // 2 x 16 KB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int head = blockIdx.x, m0 = blockIdx.y * kAoTileM;
+  const float* A = static_cast<const float*>(g.a) + (int64_t)head * g.a_batch + (int64_t)m0 * g.a_row;
+  const __bf16* W = g.w + (int64_t)head * g.w_batch;
+  float* C = static_cast<float*>(g.c) + (int64_t)head * g.c_batch;
+  const int mrows = g.m_len - m0;               // >= 1; token rows past it are read as its last one
+  // thread t moves chunks e = t + 256 i: token row e / 16, chunk e % 16 (16
+  // threads per 256-byte row); weight row e / 8, chunk e % 8
+  auto load = [&](AoStage& r, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kAoAPer; ++i) {
+      const int e = tid + 256 * i, row = e / kAoAChunks;
+      const int rr = row < mrows ? row : mrows - 1;
+      r.a[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)rr * g.a_row + st * kAoStage + 4 * (e % kAoAChunks));
+    }
+#pragma unroll
+    for (int i = 0; i < kAoWPer; ++i) {
+      const int e = tid + 256 * i;
+      r.w[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)(e / kAoWChunks) * kAoK + st * kAoStage +
+                                               8 * (e % kAoWChunks));
+    }
+  };
+  auto put = [&](const AoStage& r, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kAoAPer; ++i) {
+      const int e = tid + 256 * i, row = e / kAoAChunks;
+      s_a[buf][row * kAoAChunks + ((e % kAoAChunks) ^ (row & 15))] = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kAoWPer; ++i) {
+      const int e = tid + 256 * i;
+      s_w[buf][ao_wslot(e / kAoWChunks, e % kAoWChunks)] = r.w[i];
+    }
+  };
+  // wave (wm, wn) owns tokens 64 wm .. +63 and columns 64 wn .. +63
+  const int wm = wave & 1, wn = wave >> 1;
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // register set st % 2 holds stage st from its load until its LDS write
+  // (two named sets and a compile-time stage index keep them in registers)
+  AoStage rs0, rs1;
+  load(rs0, 0);
+  load(rs1, 1);
+  put(rs0, 0);
+  load(rs0, 2);
+  __syncthreads();
+  auto stage = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    const u32x4* sa = s_a[st & 1];
+    const u32x4* sw = s_w[st & 1];
+#pragma unroll
+    for (int u = 0; u < kAoStage / 32; ++u) {
+      bf16x8 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wm + 16 * i + r16;
+        Raw<float> raw;
+        raw.lo = __builtin_bit_cast(float4, sa[r * kAoAChunks + ((8 * u + 2 * kg) ^ (r & 15))]);
+        raw.hi = __builtin_bit_cast(float4, sa[r * kAoAChunks + ((8 * u + 2 * kg + 1) ^ (r & 15))]);
+        x[i] = raw.frag();
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, sw[ao_wslot(64 * wn + 16 * j + r16, 4 * u + kg)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, x[i], acc[i][j], 0, 0, 0);
+      }
+    }
+    // stage st + 1 into the buffer whose last readers passed the previous
+    // barrier, then its registers take stage st + 3
+    if constexpr (st + 1 < kAoStages && ((st + 1) & 1)) {
+      put(rs1, 1);
+      if constexpr (st + 3 < kAoStages) load(rs1, st + 3);
+    } else if constexpr (st + 1 < kAoStages) {
+      put(rs0, 0);
+      if constexpr (st + 3 < kAoStages) load(rs0, st + 3);
+    }
+    __syncthreads();
+  };
+  stage(IntC<0>{});
+  stage(IntC<1>{});
+  stage(IntC<2>{});
+  stage(IntC<3>{});
+  stage(IntC<4>{});
+  stage(IntC<5>{});
+  stage(IntC<6>{});
+  stage(IntC<7>{});
+  static_assert(kAoStages == 8, "one call per stage above");
+  // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, columns 64 wn + 16 j + 4 kg .. +3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r16;
+    if (m >= g.m_len) continue;
+    float* crow = C + (int64_t)m * g.c_row + 64 * wn + 4 * kg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store4(crow + 16 * j, acc[i][j]);
+  }
+}
+
 template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
 hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
@@ -221,46 +551,6 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, in
   sincos((double)pos * theta, &sn, &cs);
   *y0 = (float)((double)x0 * cs - (double)x1 * sn);
   *y1 = (float)((double)x0 * sn + (double)x1 * cs);
-}
-
-// q_rope of query token t = b S_q + s (one workgroup per token), position
-// seq_len[b] - S_q + s: each thread loads its 16 pairs first (8-byte loads of
-// two pairs), then the 32 angles' cosines and sines are computed once per
-// token (fp64) and shared by its 128 heads, so the trigonometry runs under
-// the loads instead of before them.
-__global__ __launch_bounds__(256) void query_rope_kernel(RopeParams p) {
-  __shared__ float s_cs[2][kRope / 2];
-  constexpr int kPer = kHeads * kRope / 4 / 256;   // groups of four values per thread
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const int t = blockIdx.x;
-  const int64_t base = (int64_t)t * kHeads * kRope;
-  bf16x4 x[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) x[k] = *reinterpret_cast<const bf16x4*>(p.src + base + 4 * (threadIdx.x + 256 * k));
-  const int b = t / p.s_q, s = t % p.s_q;
-  const int pos = p.seq_lens[b] - p.s_q + s;
-  if (threadIdx.x < kRope / 2) {
-    const double theta = pow(p.base, -2.0 * (double)threadIdx.x / (double)kRope);
-    double sn, cs;
-    sincos((double)pos * theta, &sn, &cs);
-    s_cs[0][threadIdx.x] = (float)cs;
-    s_cs[1][threadIdx.x] = (float)sn;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = threadIdx.x + 256 * k;
-    const int i = (e % (kRope / 4)) * 2;                           // first pair of the four values
-    bf16x4 y;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float c = s_cs[0][i + q], sn = s_cs[1][i + q];
-      const float x0 = (float)x[k][2 * q], x1 = (float)x[k][2 * q + 1];
-      y[2 * q] = (__bf16)fmaf(x0, c, -x1 * sn);
-      y[2 * q + 1] = (__bf16)fmaf(x0, sn, x1 * c);
-    }
-    *reinterpret_cast<bf16x4*>(p.dst + base + 4 * e) = y;
-  }
 }
 
 // OCP E4M3 code of the value nearest to v (ties to the even code), saturated
@@ -326,19 +616,25 @@ __global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
 
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream) {
   switch (kind) {
-    // tiles measured on the 256-token MTP step (HIP events, inputs rotated past
-    // the Infinity Cache): output values 128 x 128 (30 us; 64 x 128: 38 us),
-    // absorbed query 128 x 256 (34 us with the RoPE; 128 x 128: 38 us),
-    // projection 32 x 32 with K over the four waves (28 us; eight waves: 28 us)
-    case GemmKind::kF32ToF32Wide: return launch_gemm<float, float, 4, 4, 1, 4, 1>(g, batches, stream);
-    case GemmKind::kBf16ToBf16Wide: return launch_gemm<__bf16, __bf16, 4, 8, 1, 4, 1>(g, batches, stream);
+    // measured on the 256-token MTP step (HIP events around graph replays,
+    // inputs rotated past the Infinity Cache): output values 20 us (a 2 x 2
+    // wave grid loading its operands straight from global memory: 29 us);
+    // projection 32 x 32 tiles with K over the four waves (27 us; eight
+    // waves: 28 us)
+    case GemmKind::kOutputAbsorb:
+      if (g.k_len != kAoK || g.n_len != kAoN || batches != kHeads) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(absorb_output_kernel, dim3((unsigned)kHeads, (unsigned)((g.m_len + kAoTileM - 1) / kAoTileM)),
+                         dim3(256), 0, stream, g);
+      return hipGetLastError();
     case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 2, 2, 4, 4, 2>(g, batches, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_query_rope(const RopeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(query_rope_kernel, dim3((unsigned)p.tokens), dim3(256), 0, stream, p);
+hipError_t launch_query_absorb(const GemmParams& g, const RopeParams& r, hipStream_t stream) {
+  if (g.k_len != kAqK || g.n_len != kAqN || r.tokens != g.m_len) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(absorb_query_kernel, dim3((unsigned)kHeads, (unsigned)((g.m_len + kAqTileM - 1) / kAqTileM)),
+                     dim3(256), 0, stream, g, r);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t) {
 }
 hipError_t launch_check_indices(const CheckParams&, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t launch_gemm_nt(const GemmParams&, int, GemmKind, hipStream_t) { ++g_gemm_launches; return hipSuccess; }
-hipError_t launch_query_rope(const RopeParams&, hipStream_t) { ++g_other_launches; return hipSuccess; }
+hipError_t launch_query_absorb(const GemmParams&, const RopeParams&, hipStream_t) { ++g_gemm_launches; return hipSuccess; }
 hipError_t launch_cache_append(const AppendParams&, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t load_decode_module() { return hipSuccess; }
 hipError_t noalloc_scratch(void** ptr) {

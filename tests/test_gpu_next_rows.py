@@ -19,19 +19,23 @@ def _small(lens, s_q=1, seed=0, cache="bf16", layout="paged_shuffled"):
                             cache=cache, num_splits=None, unabsorbed=False, name="next"), seed=seed)
 
 
-@pytest.mark.parametrize("B,S", [(35, 2), (3, 1), (64, 4)])
-def test_absorb_query_and_rope(B, S):
+@pytest.mark.parametrize("B,S,in_place", [(35, 2, False), (3, 1, False), (64, 4, False), (100, 3, True)])
+def test_absorb_query_and_rope(B, S, in_place):
+    """Up to 256 tokens one tile or two, each workgroup rotating one token's
+    q^R; 300 tokens take three tiles and rotate the last 44 after them, with
+    q_rope written over q_r (the documented in-place use)."""
     import mla_latent_kv_39_amd as mla
     g = torch.Generator().manual_seed(40 + B)
     q_c = torch.randn((B, S, 128, 128), generator=g).to(torch.bfloat16)
     q_r = torch.randn((B, S, 128, 64), generator=g).to(torch.bfloat16)
     W_UK = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
     lens = torch.randint(S, 140000, (B,), generator=g, dtype=torch.int32)
-    print(f"[gpu] absorb_query B={B} S={S} tokens={B * S}", flush=True)
+    print(f"[gpu] absorb_query B={B} S={S} tokens={B * S} in_place={in_place}", flush=True)
     d = torch.device("cuda")
     q_abs = torch.full((B, S, 128, 512), float("nan"), dtype=torch.bfloat16, device=d)
-    q_rot = torch.full((B, S, 128, 64), float("nan"), dtype=torch.bfloat16, device=d)
-    mla.mla_absorb_query(q_c.to(d), q_r.to(d), W_UK.transpose(1, 2).contiguous().to(d), lens.to(d), q_abs, q_rot)
+    q_r_dev = q_r.to(d)
+    q_rot = q_r_dev if in_place else torch.full((B, S, 128, 64), float("nan"), dtype=torch.bfloat16, device=d)
+    mla.mla_absorb_query(q_c.to(d), q_r_dev, W_UK.transpose(1, 2).contiguous().to(d), lens.to(d), q_abs, q_rot)
     torch.cuda.synchronize()
     ref_abs, ref_rot = O.query_side(q_c.double().numpy(), q_r.double().numpy(), W_UK.double().numpy(), lens.numpy())
     got_abs, got_rot = q_abs.cpu().double().numpy(), q_rot.cpu().double().numpy()
