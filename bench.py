@@ -345,8 +345,15 @@ def measure_next_rows(batch: int, s_q: int, steps: int, warmup: int, hidden: int
     hs = [rnd(T, hidden) for _ in range(n)]
     w_kvs = [w_kv] + [w_kv.clone() for _ in range(n - 1)]
     kv = torch.empty((T, 576), device=dev)
-    out["kv_project"] = timed(lambda i: mla.mla_kv_project(hs[i % n], w_kvs[i % n], kv),
-                              hb + w_kv.numel() * 2 + T * 576 * 4, 2 * T * hidden * 576, "kv_project", lambda: kv)
+    kvb, kvf = hb + w_kv.numel() * 2 + T * 576 * 4, 2 * T * hidden * 576
+    splits = mla.mla_kv_project_splits(T, hidden)
+    ws = torch.empty((splits, T, 576), device=dev)
+    out["kv_project"] = timed(lambda i: mla.mla_kv_project_split(hs[i % n], w_kvs[i % n], kv, ws),
+                              kvb, kvf, "kv_project", lambda: kv)
+    out["kv_project"]["splits"] = splits
+    out["kv_project_unsplit"] = timed(lambda i: mla.mla_kv_project(hs[i % n], w_kvs[i % n], kv),
+                                      kvb, kvf, "kv_project_unsplit", lambda: kv)
+    del ws
     del hs, w_kvs
     # cache append into a bf16 paged cache of the same batch shape
     rows = torch.zeros((batch * mb, 64, 576), dtype=torch.bfloat16, device=dev)

@@ -289,6 +289,31 @@ mla_status mla_kv_project(const mla_tensor* hidden, const mla_tensor* w_kv, cons
                           hipStream_t stream);
 
 /*
+ * mla_kv_project_split: mla_kv_project with the d-deep contraction cut into S
+ * slices over workgroups, for steps with few tokens (a few hundred tokens and
+ * d = 7168 leave a 32 x 32 tiling with under a workgroup per compute unit).
+ * Same arguments, plus
+ *   workspace  fp32 [S, T, 576]   caller-owned partial sums, overwritten; S >= 1
+ *                                 divides d / 128 (mla_kv_project_splits)
+ * Slice s sums K values [s d / S, (s + 1) d / S) of every output on bf16
+ * MFMA in fp32; a second kernel adds the S partials of each output in slice
+ * order, so the result is the same on every run (it may differ from
+ * mla_kv_project's in the last bits: another summation order).  S = 1 writes
+ * kv directly.  hidden, w_kv, kv and workspace 16-byte aligned;
+ * MLA_ERR_SHAPE for an S that does not divide d / 128.
+ */
+mla_status mla_kv_project_split(const mla_tensor* hidden, const mla_tensor* w_kv, const mla_tensor* kv,
+                                const mla_tensor* workspace, hipStream_t stream);
+
+/*
+ * mla_kv_project_splits: the S for mla_kv_project_split that fills the GPU:
+ * the largest divisor of d / 128 with (64-feature x 128-token tiles) x S at
+ * most 256 (14 for 256 tokens and d = 7168).  0 for T < 1 or a d that
+ * mla_kv_project does not take.  Host only.
+ */
+int32_t mla_kv_project_splits(int64_t tokens, int64_t d);
+
+/*
  * mla_cache_append: write each new token's row into its page slot, the rows
  * mla_decode then reads (DeepSeek-V3 详解 §2.1: 576 values per token; §4.2:
  * fine-grained 1x128 fp8 scaling).

@@ -6,10 +6,11 @@ drives one decode step on device-resident inputs.
 """
 from .binding import (LatentCache, MlaError, PreparedStep, MLA_CACHE_BF16, MLA_CACHE_FP8_E4M3, ROPE_BASE, mla_absorb_output,
                       mla_absorb_query, mla_cache_append, mla_check_indices, mla_combine, mla_decode,
-                      mla_decode_noalloc, mla_init, mla_kv_project, mla_num_splits_hint, mla_partial_lse_bytes,
-                      mla_partial_out_bytes, mla_version, status_string)
+                      mla_decode_noalloc, mla_init, mla_kv_project, mla_kv_project_split, mla_kv_project_splits,
+                      mla_num_splits_hint, mla_partial_lse_bytes, mla_partial_out_bytes, mla_version, status_string)
 
 __all__ = ["LatentCache", "MlaError", "PreparedStep", "MLA_CACHE_BF16", "MLA_CACHE_FP8_E4M3", "ROPE_BASE", "mla_absorb_output",
            "mla_absorb_query", "mla_cache_append", "mla_check_indices", "mla_combine", "mla_decode",
-           "mla_decode_noalloc", "mla_init", "mla_kv_project", "mla_num_splits_hint", "mla_partial_lse_bytes",
+           "mla_decode_noalloc", "mla_init", "mla_kv_project", "mla_kv_project_split", "mla_kv_project_splits",
+           "mla_num_splits_hint", "mla_partial_lse_bytes",
            "mla_partial_out_bytes", "mla_version", "status_string"]

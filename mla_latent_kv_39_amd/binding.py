@@ -49,7 +49,8 @@ MAX_RANK = 5
 # every symbol include/mla.h declares
 EXPORTED_SYMBOLS = ("mla_decode", "mla_combine", "mla_decode_noalloc", "mla_num_splits_hint",
                     "mla_partial_out_bytes", "mla_partial_lse_bytes", "mla_absorb_query", "mla_absorb_output",
-                    "mla_kv_project", "mla_cache_append", "mla_check_indices", "mla_init",
+                    "mla_kv_project", "mla_kv_project_split", "mla_kv_project_splits", "mla_cache_append",
+                    "mla_check_indices", "mla_init",
                     "mla_status_string", "mla_version")
 ROPE_BASE = 10000.0
 
@@ -94,6 +95,10 @@ def _load():
     lib.mla_absorb_output.argtypes = [T, T, T, vp]
     lib.mla_kv_project.restype = i32
     lib.mla_kv_project.argtypes = [T, T, T, vp]
+    lib.mla_kv_project_split.restype = i32
+    lib.mla_kv_project_split.argtypes = [T, T, T, T, vp]
+    lib.mla_kv_project_splits.restype = i32
+    lib.mla_kv_project_splits.argtypes = [ctypes.c_int64, ctypes.c_int64]
     lib.mla_cache_append.restype = i32
     lib.mla_cache_append.argtypes = [T, T, T, C, f32, vp]
     lib.mla_check_indices.restype = i32
@@ -327,6 +332,20 @@ def mla_kv_project(hidden, w_kv, kv, stream=None) -> None:
     st = _lib.mla_kv_project(*[_ref(a) for a in args], _stream_handle(stream))
     if st != MLA_OK:
         raise MlaError(st, "mla_kv_project")
+
+
+def mla_kv_project_splits(tokens: int, d: int) -> int:
+    """The slice count mla_kv_project_split fills the GPU with (0: shape not taken)."""
+    return int(_lib.mla_kv_project_splits(int(tokens), int(d)))
+
+
+def mla_kv_project_split(hidden, w_kv, kv, workspace, stream=None) -> None:
+    """Enqueue mla_kv_project_split: kv as mla_kv_project, K cut into workspace.shape[0] slices
+    (workspace: fp32 [S, T, 576], overwritten)."""
+    args = [tensor(hidden), tensor(w_kv), tensor(kv), tensor(workspace)]
+    st = _lib.mla_kv_project_split(*[_ref(a) for a in args], _stream_handle(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_kv_project_split")
 
 
 def mla_cache_append(kv, seq_lens, block_table, cache: LatentCache, rope_base: float = ROPE_BASE,

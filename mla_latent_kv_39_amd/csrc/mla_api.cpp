@@ -388,6 +388,50 @@ mla_status mla_kv_project(const mla_tensor* hidden, const mla_tensor* w_kv, cons
   return mla::launch_gemm_nt(g, 1, mla::GemmKind::kBf16ToF32SplitK, stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+int32_t mla_kv_project_splits(int64_t tokens, int64_t d) {
+  if (tokens < 1 || d < 128 || d % 128 != 0 || d > (1 << 20)) return 0;
+  // the most slices (a divisor of d / 128) that keep the workgroups, 64-feature
+  // x 128-token tiles times slices, within one per compute unit of 256
+  const int64_t tiles = ((tokens + 127) / 128) * (MLA_ROW_DIM / 64);
+  int32_t best = 1;
+  for (int64_t s = 1; s <= d / 128; ++s)
+    if ((d / 128) % s == 0 && tiles * s <= 256) best = (int32_t)s;
+  return best;
+}
+
+mla_status mla_kv_project_split(const mla_tensor* hidden, const mla_tensor* w_kv, const mla_tensor* kv,
+                                const mla_tensor* workspace, hipStream_t stream) {
+  if (!present(hidden) || !present(workspace)) return MLA_ERR_NULL;
+  if (hidden->dtype != MLA_DTYPE_BF16) return MLA_ERR_DTYPE;
+  if (hidden->rank != 2 || workspace->rank != 3) return MLA_ERR_SHAPE;
+  const int64_t T = hidden->shape[0], D = hidden->shape[1], S = workspace->shape[0];
+  const int64_t wh[2] = {T, D};
+  const int64_t ww[2] = {MLA_ROW_DIM, D};
+  const int64_t wk[2] = {T, MLA_ROW_DIM};
+  const int64_t wws[3] = {S, T, MLA_ROW_DIM};
+  MLA_TRY(check_tensor(hidden, MLA_DTYPE_BF16, 2, wh));
+  MLA_TRY(check_tensor(w_kv, MLA_DTYPE_BF16, 2, ww));
+  MLA_TRY(check_tensor(kv, MLA_DTYPE_FP32, 2, wk));
+  MLA_TRY(check_tensor(workspace, MLA_DTYPE_FP32, 3, wws));
+  if (D % 128 != 0 || D > (1 << 20) || T > INT_MAX / MLA_ROW_DIM) return MLA_ERR_SHAPE;
+  if (S < 1 || (D / 128) % S != 0) return MLA_ERR_SHAPE;
+  if ((T + 127) / 128 > 65535) return MLA_ERR_SHAPE;
+  if (!aligned16(hidden) || !aligned16(w_kv) || !aligned16(kv) || !aligned16(workspace)) return MLA_ERR_SHAPE;
+  MLA_TRY(check_device());
+  mla::GemmParams g;
+  g.a = hidden->data;
+  g.w = static_cast<const __bf16*>(w_kv->data);
+  g.c = kv->data;
+  g.a_batch = g.w_batch = g.c_batch = 0;
+  g.a_row = D;
+  g.c_row = MLA_ROW_DIM;
+  g.m_len = (int32_t)T;
+  g.n_len = MLA_ROW_DIM;
+  g.k_len = (int32_t)D;
+  return mla::launch_kv_project_split(g, static_cast<float*>(workspace->data), (int)S, stream) == hipSuccess
+             ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 mla_status mla_cache_append(const mla_tensor* kv, const mla_tensor* seq_lens, const mla_tensor* block_table,
                             const mla_latent_cache* cache, float rope_base, hipStream_t stream) {
   if (!present(kv)) return MLA_ERR_NULL;
@@ -518,6 +562,6 @@ const char* mla_status_string(mla_status status) {
   return "unknown status";
 }
 
-int32_t mla_version(void) { return 30200; }  // 3.2.0: + absorption, KV projection and cache append
+int32_t mla_version(void) { return 30300; }  // 3.3.0: + the KV projection split over K
 
 }  // extern "C"

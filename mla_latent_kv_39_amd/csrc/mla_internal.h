@@ -94,6 +94,11 @@ enum class GemmKind {
 };
 hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipStream_t stream);
 
+// The KV projection with K cut into `slices` (a divisor of k_len / 128):
+// partial sums into ws [slices, m_len, n_len] (fp32; c_row == n_len), then
+// their sum in slice order into C.  slices == 1 writes C directly.
+hipError_t launch_kv_project_split(const GemmParams& g, float* ws, int slices, hipStream_t stream);
+
 // RoPE of the query's q^R: [tokens = B S_q, 128, 64] bf16 -> bf16, position
 // seq_len[b] - S_q + s of token b S_q + s.
 struct RopeParams {

@@ -533,6 +533,132 @@ __global__ __launch_bounds__(256) void absorb_output_kernel(GemmParams g) {
   }
 }
 
+// KV projection with K cut over workgroups (mla_kv_project_split): slice s of
+// S takes K values [s K / S, (s + 1) K / S) of one tile of 128 tokens x 64
+// output features and writes its fp32 partial sums to the caller's
+// workspace [S, T, 576]; kv_reduce_kernel then adds the S partials of each
+// output in slice order (the result does not depend on the order workgroups
+// run in).  For a decode step's few hundred tokens this spreads the 7168-deep
+// contraction over the whole GPU: each workgroup reads 192 KB of operands
+// instead of the 0.9 MB a 32 x 32 tile over all of K takes.  K runs in
+// stages of 64 through two LDS buffers, two stages of loads in registers
+// (as in the output absorption); rows of both operands are 128 bytes per
+// stage, 8 chunks, chunk c at c ^ ((r >> 1) & 7).
+constexpr int kKvTileM = 128;
+constexpr int kKvTileN = 64;
+constexpr int kKvStage = 64;
+constexpr int kKvChunks = kKvStage / 8;                    // 8 chunks of 16 bytes per row
+constexpr int kKvAPer = kKvTileM * kKvChunks / 256;         // 4 chunks per thread and stage
+constexpr int kKvWPer = kKvTileN * kKvChunks / 256;         // 2
+
+struct KvStage {
+  u32x4 a[kKvAPer], w[kKvWPer];
+};
+
+__global__ __launch_bounds__(256) void kv_partial_kernel(GemmParams g, float* ws, int slices) {
+  __shared__ u32x4 s_a[2][kKvTileM * kKvChunks];   // 2 x 16 KB
+  __shared__ u32x4 s_w[2][kKvTileN * kKvChunks];   // 2 x 8 KB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int m0 = blockIdx.x * kKvTileM, n0 = blockIdx.y * kKvTileN, slice = blockIdx.z;
+  const int klen = g.k_len / slices, k0 = slice * klen;
+  const int nst = klen / kKvStage;                 // even: klen is a multiple of 128
+  const __bf16* A = static_cast<const __bf16*>(g.a) + (int64_t)m0 * g.a_row + k0;
+  const __bf16* W = g.w + (int64_t)n0 * g.k_len + k0;
+  const int mrows = g.m_len - m0;                  // >= 1; token rows past it are read as its last one
+  // thread t moves chunks e = t + 256 i: row e / 8, chunk e % 8 (8 threads per 128-byte row)
+  auto load = [&](KvStage& r, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kKvAPer; ++i) {
+      const int e = tid + 256 * i, row = e / kKvChunks;
+      const int rr = row < mrows ? row : mrows - 1;
+      r.a[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)rr * g.a_row + st * kKvStage + 8 * (e % kKvChunks));
+    }
+#pragma unroll
+    for (int i = 0; i < kKvWPer; ++i) {
+      const int e = tid + 256 * i;
+      r.w[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)(e / kKvChunks) * g.k_len + st * kKvStage +
+                                               8 * (e % kKvChunks));
+    }
+  };
+  auto put = [&](const KvStage& r, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kKvAPer; ++i) {
+      const int e = tid + 256 * i;
+      s_a[buf][ao_wslot(e / kKvChunks, e % kKvChunks)] = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kKvWPer; ++i) {
+      const int e = tid + 256 * i;
+      s_w[buf][ao_wslot(e / kKvChunks, e % kKvChunks)] = r.w[i];
+    }
+  };
+  // wave (wm, wn) owns tokens 64 wm .. +63 and features 32 wn .. +31
+  const int wm = wave & 1, wn = wave >> 1;
+  floatx4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kKvStage / 32; ++u) {
+      bf16x8 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __builtin_bit_cast(bf16x8, s_a[buf][ao_wslot(64 * wm + 16 * i + r16, 4 * u + kg)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, s_w[buf][ao_wslot(32 * wn + 16 * j + r16, 4 * u + kg)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, x[i], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // register set st % 2 holds stage st from its load until its LDS write;
+  // stages go in pairs so that each set is named statically
+  KvStage rs0, rs1;
+  load(rs0, 0);
+  load(rs1, 1);
+  put(rs0, 0);
+  if (nst > 2) load(rs0, 2);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    compute(0);
+    put(rs1, 1);                              // stage st + 1 (nst is even)
+    if (st + 3 < nst) load(rs1, st + 3);
+    __syncthreads();
+    compute(1);
+    if (st + 2 < nst) {
+      put(rs0, 0);
+      if (st + 4 < nst) load(rs0, st + 4);
+    }
+    __syncthreads();
+  }
+  // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, features 32 wn + 16 j + 4 kg .. +3
+  float* out = slices == 1 ? static_cast<float*>(g.c) : ws + (int64_t)slice * g.m_len * g.c_row;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r16;
+    if (m >= g.m_len) continue;
+    float* crow = out + (int64_t)m * g.c_row + n0 + 32 * wn + 4 * kg;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) store4(crow + 16 * j, acc[i][j]);
+  }
+}
+
+// kv = sum over the S slices of the workspace, in slice order: thread t of
+// workgroup b adds float4 number 256 b + t of every slice
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const float4* ws, float4* kv, int64_t n4, int slices) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 v = ws[i];
+  for (int s = 1; s < slices; ++s) {
+    const float4 x = ws[(int64_t)s * n4 + i];
+    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+  }
+  kv[i] = v;
+}
+
 template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
 hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
   constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
@@ -629,6 +755,19 @@ hipError_t launch_gemm_nt(const GemmParams& g, int batches, GemmKind kind, hipSt
     case GemmKind::kBf16ToF32SplitK: return launch_gemm<__bf16, float, 2, 2, 4, 4, 2>(g, batches, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_project_split(const GemmParams& g, float* ws, int slices, hipStream_t stream) {
+  if (slices < 1 || g.n_len % kKvTileN != 0 || g.k_len % (128 * slices) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_partial_kernel,
+                     dim3((unsigned)((g.m_len + kKvTileM - 1) / kKvTileM), (unsigned)(g.n_len / kKvTileN), (unsigned)slices),
+                     dim3(256), 0, stream, g, ws, slices);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || slices == 1) return e;
+  const int64_t n4 = (int64_t)g.m_len * g.c_row / 4;
+  hipLaunchKernelGGL(kv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(ws), static_cast<float4*>(g.c), n4, slices);
+  return hipGetLastError();
 }
 
 hipError_t launch_query_absorb(const GemmParams& g, const RopeParams& r, hipStream_t stream) {

@@ -53,6 +53,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t) {
 hipError_t launch_check_indices(const CheckParams&, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t launch_gemm_nt(const GemmParams&, int, GemmKind, hipStream_t) { ++g_gemm_launches; return hipSuccess; }
 hipError_t launch_query_absorb(const GemmParams&, const RopeParams&, hipStream_t) { ++g_gemm_launches; return hipSuccess; }
+hipError_t launch_kv_project_split(const GemmParams&, float*, int, hipStream_t) { ++g_gemm_launches; return hipSuccess; }
 hipError_t launch_cache_append(const AppendParams&, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t load_decode_module() { return hipSuccess; }
 hipError_t noalloc_scratch(void** ptr) {
@@ -271,6 +272,11 @@ void directed_others() {
     EXPECT(mla_kv_project(&h, &wk, &kv, nullptr) == MLA_OK, "kv_project");
     mla_tensor h2 = dense(MLA_DTYPE_BF16, {70, 7072}), wk2 = dense(MLA_DTYPE_BF16, {576, 7072});
     EXPECT(mla_kv_project(&h2, &wk2, &kv, nullptr) == MLA_ERR_SHAPE, "hidden size not a multiple of 128");
+    mla_tensor kws = dense(MLA_DTYPE_FP32, {28, 70, 576}), kws5 = dense(MLA_DTYPE_FP32, {5, 70, 576});
+    EXPECT(mla_kv_project_split(&h, &wk, &kv, &kws, nullptr) == MLA_OK, "kv_project_split");
+    EXPECT(mla_kv_project_split(&h, &wk, &kv, &kws5, nullptr) == MLA_ERR_SHAPE, "slices not dividing d / 128");
+    EXPECT(mla_kv_project_split(&h, &wk, &kv, nullptr, nullptr) == MLA_ERR_NULL, "no workspace");
+    EXPECT(mla_kv_project_splits(70, 7168) == 28 && mla_kv_project_splits(1, 100) == 0, "split hint");
     mla_tensor kv3 = dense(MLA_DTYPE_FP32, {4, 2, 576});
     DecodeCall c(4, 2, 1, true, true);
     EXPECT(mla_cache_append(&kv3, &c.lens, &c.table, &c.cache, 10000.f, nullptr) == MLA_OK, "cache append");
@@ -333,7 +339,9 @@ void fuzz(int iters) {
       case 3: st = mla_absorb_query(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), maybe(&t[3]), f, maybe(&t[4]),
                                     maybe(&t[5]), nullptr); break;
       case 4: st = mla_absorb_output(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), nullptr); break;
-      case 5: st = mla_kv_project(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), nullptr); break;
+      case 5: st = (g() % 2) ? mla_kv_project(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), nullptr)
+                             : mla_kv_project_split(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), maybe(&t[3]), nullptr);
+              break;
       case 6: st = mla_cache_append(maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), (g() % 6) ? &c : nullptr, f, nullptr); break;
       case 7: st = mla_check_indices((g() % 6) ? &c : nullptr, maybe(&t[0]), maybe(&t[1]), maybe(&t[2]), nullptr); break;
       default: (void)mla_num_splits_hint((int32_t)(g() % 3), (int32_t)g(), (int32_t)g(), (int32_t)g());

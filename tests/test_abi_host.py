@@ -291,6 +291,19 @@ def test_next_rows_reject_bad_descriptors(lib):
                             _ref(kv), None) == E.MLA_ERR_SHAPE                             # d % 128
     assert c.mla_kv_project(_ref(h), _ref(desc(lib, (512, 7168), bf)), _ref(kv), None) == E.MLA_ERR_SHAPE
     assert c.mla_kv_project(_ref(h), _ref(w), _ref(desc(lib, (7, 576), bf)), None) == E.MLA_ERR_DTYPE
+    # the split projection's workspace: fp32 [S, T, 576], S dividing d / 128 = 56
+    assert c.mla_kv_project_split(_ref(h), _ref(w), _ref(kv), None, None) == E.MLA_ERR_NULL
+    assert c.mla_kv_project_split(_ref(h), _ref(w), _ref(kv), _ref(desc(lib, (5, 7, 576), f32)),
+                                  None) == E.MLA_ERR_SHAPE                               # 56 % 5
+    assert c.mla_kv_project_split(_ref(h), _ref(w), _ref(kv), _ref(desc(lib, (7, 8, 576), f32)),
+                                  None) == E.MLA_ERR_SHAPE                               # T
+    assert c.mla_kv_project_split(_ref(h), _ref(w), _ref(kv), _ref(desc(lib, (7, 7, 576), bf)),
+                                  None) == E.MLA_ERR_DTYPE
+    assert c.mla_kv_project_split(_ref(h), _ref(w), _ref(kv), _ref(desc(lib, (7, 576), f32)),
+                                  None) == E.MLA_ERR_SHAPE                               # rank
+    assert c.mla_kv_project_splits(256, 7168) == 14 and c.mla_kv_project_splits(70, 7168) == 28
+    assert c.mla_kv_project_splits(4096, 7168) == 1
+    assert c.mla_kv_project_splits(0, 7168) == 0 and c.mla_kv_project_splits(7, 7072) == 0
 
     a = _args(lib, B=B, S=S)
     kvb = desc(lib, (B, S, 576), f32)

@@ -89,6 +89,40 @@ def test_kv_project(T, D):
     print(f"[gpu] kv_project: max err {err.max():.2e}", flush=True)
 
 
+
+@pytest.mark.parametrize("T,D,S", [(70, 7168, None), (256, 7168, None), (300, 7168, None), (256, 7168, 1),
+                                   (256, 7168, 7), (5, 128, None), (33, 640, None)])
+def test_kv_project_split(T, D, S):
+    """K cut into S slices (None: the library's hint; 14 for 256 x 7168, 28 for
+    70 tokens) against the oracle, two calls bit for bit (the partials are
+    summed in slice order), and against the unsplit entry point within the
+    same fp32 bound."""
+    import mla_latent_kv_39_amd as mla
+    S = S or mla.mla_kv_project_splits(T, D)
+    g = torch.Generator().manual_seed(70 + T + S)
+    h = torch.randn((T, D), generator=g).to(torch.bfloat16)
+    W = (torch.randn((576, D), generator=g) / math.sqrt(D)).to(torch.bfloat16)
+    print(f"[gpu] kv_project_split T={T} d={D} S={S}", flush=True)
+    d = torch.device("cuda")
+    hd, Wd_ = h.to(d), W.to(d)
+    ws = torch.full((S, T, 576), float("nan"), device=d)
+    kv = torch.full((T, 576), float("nan"), device=d)
+    mla.mla_kv_project_split(hd, Wd_, kv, ws)
+    kv2 = torch.full((T, 576), float("nan"), device=d)
+    mla.mla_kv_project_split(hd, Wd_, kv2, ws)
+    kv1 = torch.full((T, 576), float("nan"), device=d)
+    mla.mla_kv_project(hd, Wd_, kv1)
+    torch.cuda.synchronize()
+    assert torch.equal(kv, kv2)
+    Wd = W.double().numpy()
+    ref = O.kv_project(h.double().numpy(), Wd[:512], Wd[512:])
+    bound = 1e-6 * (np.abs(h.double().numpy()) @ np.abs(Wd).T) + 1e-6
+    err = np.abs(kv.cpu().double().numpy() - ref)
+    assert np.all(err <= bound), (err / bound).max()
+    assert np.all(np.abs(kv.cpu().double().numpy() - kv1.cpu().double().numpy()) <= 2 * bound)
+    print(f"[gpu] kv_project_split: max err {err.max():.2e}", flush=True)
+
+
 def _cache_dict(inp):
     if inp.cache_dtype == "bf16":
         return {"rows": inp.cache.view(torch.int16).numpy().astype(np.uint16).copy()}
