@@ -647,14 +647,23 @@ __global__ __launch_bounds__(256) void kv_partial_kernel(GemmParams g, float* ws
 }
 
 // kv = sum over the S slices of the workspace, in slice order: thread t of
-// workgroup b adds float4 number 256 b + t of every slice
+// workgroup b adds float4 number 256 b + t of every slice, loading eight
+// slices at a time before adding them (one load, wait and add per slice
+// made 14 slices 14 memory round trips: 5.2 us for 256 tokens)
 __global__ __launch_bounds__(256) void kv_reduce_kernel(const float4* ws, float4* kv, int64_t n4, int slices) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   float4 v = ws[i];
-  for (int s = 1; s < slices; ++s) {
-    const float4 x = ws[(int64_t)s * n4 + i];
-    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+  for (int s = 1; s < slices; s += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s + j < slices) x[j] = ws[(int64_t)(s + j) * n4 + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s + j < slices) {
+        v.x += x[j].x; v.y += x[j].y; v.z += x[j].z; v.w += x[j].w;
+      }
   }
   kv[i] = v;
 }
