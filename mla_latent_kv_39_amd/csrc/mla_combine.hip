@@ -38,16 +38,24 @@ __device__ __forceinline__ float4 half4(uint2 h) {
   return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
 }
 
-template <int CB, int KC>
-__global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(CombineParams p) {
-  constexpr int kThreads = CB * 64 < 256 ? CB * 64 : 256;
+// TS > 1: TS groups of threads share a sequence's partitions (group g takes
+// chunks g, g + TS, ...) and their (max, sum, accumulator) triples are then
+// merged through LDS in group order, so that a sequence cut into many
+// partitions keeps TS times the waves loading.
+template <int CB, int KC, int TS>
+__global__ __launch_bounds__((CB * 64 < 256 ? CB * 64 : 256) * TS) void combine_kernel(CombineParams p) {
+  constexpr int kThreads = CB * 64 < 256 ? CB * 64 : 256;   // one group
+  constexpr int kBlock = kThreads * TS;
   constexpr int kSlices = 32 / CB;
   constexpr int kRun = 64 * CB;                 // 16-byte chunks of a slice
   constexpr int kPerThread = kRun / kThreads;   // 2 or 1
   constexpr int kChunk = KC;                    // partitions whose loads are in flight together
+  constexpr int kShared = (TS > 1 ? TS - 1 : 1) * kPerThread * 2 * kThreads;
   __shared__ float4 s_tile[2 * kRun];
-  __shared__ int s_red[2 * (kThreads / 64)];
-  const int tid = threadIdx.x;
+  __shared__ int s_red[2 * (kBlock / 64)];
+  __shared__ float s_gm[kShared], s_gw[kShared];
+  __shared__ float4 s_ga[kShared];
+  const int tid = threadIdx.x % kThreads, sub = threadIdx.x / kThreads;
   const int per_tok = (kHeads / kGroupHeads) * kSlices;
   const int b = blockIdx.x / (p.s_q * per_tok);
   const int s = (blockIdx.x / per_tok) % p.s_q;
@@ -56,7 +64,7 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
 
   // rebuild the partition map: total units U and the first unit u0 of sequence b
   int cnt = 0, before = 0;
-  for (int i = tid; i < p.batch; i += kThreads) {
+  for (int i = (int)threadIdx.x; i < p.batch; i += kBlock) {
     const int n = units_of_len(p.seq_lens[i]);
     cnt += n;
     if (i < b) before += n;
@@ -66,14 +74,14 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
     cnt += __shfl_xor(cnt, off);
     before += __shfl_xor(before, off);
   }
-  if ((tid & 63) == 0) {
-    s_red[2 * (tid >> 6)] = cnt;
-    s_red[2 * (tid >> 6) + 1] = before;
+  if ((threadIdx.x & 63) == 0) {
+    s_red[2 * (threadIdx.x >> 6)] = cnt;
+    s_red[2 * (threadIdx.x >> 6) + 1] = before;
   }
   __syncthreads();
   int total_units = 0, u0 = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < kBlock / 64; ++w) {
     total_units += s_red[2 * w];
     u0 += s_red[2 * w + 1];
   }
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
   // partitions in chunks of kChunk: all loads of a chunk go out before any is
   // used (one memory round trip per chunk), then the chunk is merged into the
   // running (m, wsum, acc) with a rescale when its largest lse is new
-  for (int qb = p0; qb <= p1; qb += kChunk) {
+  for (int qb = p0 + sub * kChunk; qb <= p1; qb += TS * kChunk) {
     float l[kChunk][kPerThread][2];
     float2 d[kChunk][kPerThread];
     uint4 v[kChunk][kPerThread];
@@ -163,16 +171,52 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
         }
       }
   }
+  if constexpr (TS > 1) {
+    // groups 1 .. TS - 1 hand their triples to group 0, which merges them in order
+    if (sub > 0) {
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k)
+      for (int k = 0; k < kPerThread; ++k)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const float ik = wsum[k][a] > 0.f ? 1.f / wsum[k][a] : 0.f;
-      s_tile[lds_slot(kRun * a + tid + kThreads * k)] =
-          make_float4(acc[k][a].x * ik, acc[k][a].y * ik, acc[k][a].z * ik, acc[k][a].w * ik);
+        for (int a = 0; a < 2; ++a) {
+          const int x = (((sub - 1) * kPerThread + k) * 2 + a) * kThreads + tid;
+          s_gm[x] = m[k][a];
+          s_gw[x] = wsum[k][a];
+          s_ga[x] = acc[k][a];
+        }
     }
+    __syncthreads();
+    // every thread goes on to the barrier below; only group 0 merges and writes
+#pragma unroll
+    for (int g = 1; g < (sub == 0 ? TS : 1); ++g)
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int x = (((g - 1) * kPerThread + k) * 2 + a) * kThreads + tid;
+          const float mg = s_gm[x], mc = fmaxf(m[k][a], mg);
+          if (mc == kNegInf) continue;
+          const float r = __expf(m[k][a] - mc), rg = __expf(mg - mc);   // 0 for -inf
+          const float4 ag = s_ga[x];
+          wsum[k][a] = wsum[k][a] * r + s_gw[x] * rg;
+          acc[k][a].x = acc[k][a].x * r + ag.x * rg;
+          acc[k][a].y = acc[k][a].y * r + ag.y * rg;
+          acc[k][a].z = acc[k][a].z * r + ag.z * rg;
+          acc[k][a].w = acc[k][a].w * r + ag.w * rg;
+          m[k][a] = mc;
+        }
+  }
   const size_t orow = ((size_t)b * p.s_q + s) * kHeads + grp * kGroupHeads;
-  if (slice == 0) {
+  if (sub == 0) {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const float ik = wsum[k][a] > 0.f ? 1.f / wsum[k][a] : 0.f;
+        s_tile[lds_slot(kRun * a + tid + kThreads * k)] =
+            make_float4(acc[k][a].x * ik, acc[k][a].y * ik, acc[k][a].z * ik, acc[k][a].w * ik);
+      }
+  }
+  if (sub == 0 && slice == 0) {
     // lse of the group's heads: the threads whose chunk sits in column block 0, g == 0
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -184,6 +228,7 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
     }
   }
   __syncthreads();
+  if (sub > 0) return;
   // row order: float4 e of the slice is head e / (4 CB), columns 16 CB slice + 4 (e % (4 CB)) .. +3
 #pragma unroll
   for (int k = 0; k < 2 * kPerThread; ++k) {
@@ -197,15 +242,18 @@ __global__ __launch_bounds__(CB * 64 < 256 ? CB * 64 : 256) void combine_kernel(
 
 }  // namespace
 
-template <int KC4, int KC8>
+template <int KC4, int KC8, int TS>
 void launch_slices(const CombineParams& p, long long base, hipStream_t stream) {
   const long long want = 2048;
   if (base * 4 >= want) {
-    combine_kernel<8, KC8><<<dim3((unsigned)(base * 4)), dim3(256), 0, stream>>>(p);
+    // at most 512 threads a workgroup: 1024 would cap a thread at 128 VGPRs
+    constexpr int TS2 = TS > 2 ? 2 : TS;
+    combine_kernel<8, KC8, TS2><<<dim3((unsigned)(base * 4)), dim3(256 * TS2), 0, stream>>>(p);
   } else if (base * 8 >= want) {
-    combine_kernel<4, KC4><<<dim3((unsigned)(base * 8)), dim3(256), 0, stream>>>(p);
+    constexpr int TS2 = TS > 2 ? 2 : TS;
+    combine_kernel<4, KC4, TS2><<<dim3((unsigned)(base * 8)), dim3(256 * TS2), 0, stream>>>(p);
   } else {
-    combine_kernel<2, KC4><<<dim3((unsigned)(base * 16)), dim3(128), 0, stream>>>(p);
+    combine_kernel<2, KC4, TS><<<dim3((unsigned)(base * 16)), dim3(128 * TS), 0, stream>>>(p);
   }
 }
 
@@ -214,14 +262,18 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   // unit: the shares of short and long sequences then mix on every unit.
   // Partitions merged per memory round trip: 4, or, when sequences average
   // 16 partitions or more (a few long sequences), 16 (8 with two chunks a
-  // thread).  Measured with rocprofv3: 17.2 -> 14.5 us on 4 x 128k rows; on
-  // 32 x 1k-4k and the paged mix the wider chunk would cost 18% and 52%
-  // (fewer resident waves, merges of partitions that are not there).
+  // thread) by each of four thread groups (two for the wider slices) sharing
+  // a sequence's partitions.  Measured with rocprofv3: 17.2 -> 14.5 us on
+  // 4 x 128k rows for the wider chunk, 13.0 -> 11.0 us for the groups (the
+  // launch had 512 waves on the GPU); on 32 x 1k-4k and the paged mix the
+  // wider chunk would cost 18% and 52% (fewer resident waves, merges of
+  // partitions that are not there), two groups 17% and 39% (more merge work
+  // in launches that already have 2048 workgroups).
   const long long base = (long long)p.batch * p.s_q * (kHeads / kGroupHeads);
   if ((long long)p.num_parts >= 16LL * p.batch) {
-    launch_slices<16, 8>(p, base, stream);
+    launch_slices<16, 8, 4>(p, base, stream);
   } else {
-    launch_slices<4, 4>(p, base, stream);
+    launch_slices<4, 4, 1>(p, base, stream);
   }
   return hipGetLastError();
 }
