@@ -69,3 +69,61 @@ def test_noalloc_decode_replays_like_eager():
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e), f"replay {k}"
     del graph
+
+
+def test_layer_kernels_replay_like_eager():
+    """The kernels around the decode captured together (split KV projection,
+    cache append into a bf16 cache, query absorption with RoPE, output
+    absorption) and replayed with their inputs changed in place and eager
+    work in between: every replay equals the same calls made eagerly."""
+    import mla_latent_kv_39_amd as mla
+    print("[gpu] graph of the kernels around the decode", flush=True)
+    d = torch.device("cuda")
+    g = torch.Generator(device="cpu").manual_seed(23)
+    B, S, D = 4, 2, 7168
+    T = B * S
+    lens = torch.tensor([70, 130, 2, 64], dtype=torch.int32, device=d)
+    table = torch.arange(B * 4, dtype=torch.int32, device=d).view(B, 4)
+    h = torch.randn((T, D), generator=g).to(torch.bfloat16).to(d)
+    w_kv = (torch.randn((576, D), generator=g) * D ** -0.5).to(torch.bfloat16).to(d)
+    q_c = torch.randn((B, S, 128, 128), generator=g).to(torch.bfloat16).to(d)
+    q_r = torch.randn((B, S, 128, 64), generator=g).to(torch.bfloat16).to(d)
+    w_uk_t = (torch.randn((128, 512, 128), generator=g) * 512 ** -0.5).to(torch.bfloat16).to(d)
+    out_lat = torch.randn((B, S, 128, 512), generator=g).to(d)
+    w_uv = (torch.randn((128, 128, 512), generator=g) * 512 ** -0.5).to(torch.bfloat16).to(d)
+    splits = mla.mla_kv_project_splits(T, D)
+
+    def buffers():
+        rows = torch.zeros((B * 4, 64, 576), dtype=torch.bfloat16, device=d)
+        return dict(ws=torch.empty((splits, T, 576), device=d), kv=torch.empty((T, 576), device=d), rows=rows,
+                    cache=mla.LatentCache(mla.MLA_CACHE_BF16, rows),
+                    qa=torch.empty((B, S, 128, 512), dtype=torch.bfloat16, device=d),
+                    qr=torch.empty((B, S, 128, 64), dtype=torch.bfloat16, device=d),
+                    ov=torch.empty((B, S, 128, 128), device=d))
+
+    def layer(o):
+        mla.mla_kv_project_split(h, w_kv, o["kv"], o["ws"])
+        mla.mla_cache_append(o["kv"].view(B, S, 576), lens, table, o["cache"])
+        mla.mla_absorb_query(q_c, q_r, w_uk_t, lens, o["qa"], o["qr"])
+        mla.mla_absorb_output(out_lat, w_uv, o["ov"])
+
+    og, oe = buffers(), buffers()
+    layer(og)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(og)
+    h0, q0, o0 = h.clone(), q_c.clone(), out_lat.clone()
+    for k in range(4):
+        f = 1.0 - 0.2 * k
+        h.copy_(h0 * f)
+        q_c.copy_(q0 * f)
+        out_lat.copy_(o0 * f)
+        noise = torch.randn(1 << 20, device="cuda").sum()      # eager work between the replays
+        graph.replay()
+        layer(oe)
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        for key in ("kv", "rows", "qa", "qr", "ov"):
+            assert torch.equal(og[key], oe[key]), f"replay {k}: {key}"
+    del graph
