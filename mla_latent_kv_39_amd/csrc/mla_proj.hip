@@ -86,29 +86,27 @@ __device__ __forceinline__ void store4(__bf16* p, const floatx4& v) {
 // The MFMA takes W as its first operand and A as its second, so a 16 x 16
 // block comes out transposed: lane (r16, g) holds C (m = r16, n = 4g .. 4g+3),
 // four consecutive outputs of one row, stored straight from the accumulators.
-// KW = 1: the four waves form a 2 x 2 grid, each owning (16 WM) x (16 WN)
-// outputs over all of K.  KW = NW: the NW waves own the same (16 WM) x (16 WN)
-// outputs, each over 1/NW of K (for long K and few outputs); their partial
-// tiles are summed in LDS in a fixed order.  K is walked in stages of U
+// The NW = KW waves own the same (16 WM) x (16 WN) outputs, each over 1/KW
+// of K (for long K and few outputs); their partial tiles are summed in LDS in
+// a fixed order.  K is walked in stages of U
 // K-steps (32 U values) with two register buffers: the loads of stage s + 1
 // are issued before the MFMAs of stage s, so a wave always has a stage of
 // loads in flight.  Requires k_len % (32 KW) == 0 and n_len a multiple of the
 // tile width; rows m >= m_len are neither read nor written.
 template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void gemm_nt_kernel(GemmParams g) {
-  static_assert(KW == 1 ? NW == 4 : KW == NW, "2 x 2 waves, or all waves over K");
-  constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
-  constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
+  static_assert(KW == NW && KW > 1, "all waves over K");
+  constexpr int TM = 16 * WM;
+  constexpr int TN = 16 * WN;
   constexpr int PITCH = TN + 4;                  // floats per LDS row (K split only)
-  __shared__ float s_tile[KW == 1 ? 1 : NW * TM * PITCH];
+  __shared__ float s_tile[NW * TM * PITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int wm0 = KW == 1 ? (wave & 1) * (16 * WM) : 0;     // this wave's block inside the tile
-  const int wn0 = KW == 1 ? (wave >> 1) * (16 * WN) : 0;
+  const int wm0 = 0, wn0 = 0;      // every wave covers the whole tile
   const int m0 = blockIdx.y * TM + wm0;
   const int n0 = blockIdx.x * TN + wn0;
   const int kq = g.k_len / KW;
-  const int kbeg = KW == 1 ? 0 : wave * kq;
+  const int kbeg = wave * kq;
   const int64_t z = blockIdx.z;
   const TA* A = static_cast<const TA*>(g.a) + z * g.a_batch;
   const __bf16* W = g.w + z * g.w_batch;
@@ -175,16 +173,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_kernel(GemmParams g) {
   }
 
   TC* C = static_cast<TC*>(g.c) + z * g.c_batch;
-  if (KW == 1) {
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      if (!aok[i]) continue;
-      TC* crow = C + (int64_t)(m0 + 16 * i + r16) * g.c_row + n0 + 4 * kg;
-#pragma unroll
-      for (int j = 0; j < WN; ++j) store4(crow + 16 * j, acc[i][j]);
-    }
-    return;
-  }
   // K split: the NW partial tiles summed in LDS, then written row by row
   float* mine = s_tile + wave * TM * PITCH;
 #pragma unroll
@@ -670,8 +658,8 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float4* ws, float4
 
 template <typename TA, typename TC, int WM, int WN, int KW, int NW, int U>
 hipError_t launch_gemm(const GemmParams& g, int batches, hipStream_t stream) {
-  constexpr int TM = KW == 1 ? 32 * WM : 16 * WM;
-  constexpr int TN = KW == 1 ? 32 * WN : 16 * WN;
+  constexpr int TM = 16 * WM;
+  constexpr int TN = 16 * WN;
   const dim3 grid((unsigned)(g.n_len / TN), (unsigned)((g.m_len + TM - 1) / TM), (unsigned)batches);
   hipLaunchKernelGGL((gemm_nt_kernel<TA, TC, WM, WN, KW, NW, U>), grid, dim3(64 * NW), 0, stream, g);
   return hipGetLastError();
