@@ -276,6 +276,7 @@ struct IntC {
 __global__ __launch_bounds__(256) void absorb_query_kernel(GemmParams g, RopeParams rp) {
   __shared__ u32x4 s_a[kAqTileM * kAqChunks];            // 32 KB
   __shared__ u32x4 s_w[2][kAqChunkN * kAqChunks];        // 2 x 32 KB
+  __shared__ u32x4 s_c[4][64 * 8];                         // 4 x 8 KB: each wave's outputs of a chunk
   __shared__ float s_cs[2][kRope / 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -355,15 +356,36 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(GemmParams g, RopePar
       put(rw0, s_w[0]);
       if constexpr (c + 3 < kAqNChunks) load_w(rw0, c + 3);
     }
-    // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, columns
-    // 128 c + 64 wn + 16 j + 4 kg .. +3
+    // outputs through this wave's own LDS area, so that they leave as whole
+    // 128-byte row segments (16 bytes a lane) instead of 8 bytes a lane, 16
+    // rows x 32 bytes a store.  Lane (r16, kg) of block (i, j) holds token
+    // 16 i + r16, columns 16 j + 4 kg .. +3 of the wave's 64 x 64 block; a row
+    // is 8 chunks of 16 bytes, chunk q at q ^ ((r >> 1) & 7).
+    u32x4* sc = s_c[wave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 64 * wm + 16 * i + r16;
-      if (m >= g.m_len) continue;
-      __bf16* crow = C + (int64_t)m * g.c_row + kAqChunkN * c + 64 * wn + 4 * kg;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) store4(crow + 16 * j, acc[i][j]);
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * i + r16, q = 2 * j + (kg >> 1);
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 h;
+        h[0] = (__bf16)acc[i][j][0];
+        h[1] = (__bf16)acc[i][j][1];
+        h[2] = (__bf16)acc[i][j][2];
+        h[3] = (__bf16)acc[i][j][3];
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(sc + r * 8 + (q ^ ((r >> 1) & 7))) + 8 * (kg & 1)) = h;
+      }
+    // the reads below take other lanes' writes: a wave's LDS instructions
+    // complete in order, and the compiler must not move the reads above them
+    asm volatile("" ::: "memory");
+    // lane L stores chunk L % 8 of rows L / 8 + 8 t: columns 128 c + 64 wn + 8 (L % 8) .. +7
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = lane / 8 + 8 * t, q = lane % 8;
+      const u32x4 v = sc[r * 8 + (q ^ ((r >> 1) & 7))];
+      const int m = m0 + 64 * wm + r;
+      if (m < g.m_len)
+        *reinterpret_cast<u32x4*>(C + (int64_t)m * g.c_row + kAqChunkN * c + 64 * wn + 8 * q) = v;
     }
     __syncthreads();
   };
