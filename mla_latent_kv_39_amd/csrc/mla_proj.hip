@@ -532,14 +532,30 @@ __global__ __launch_bounds__(256) void absorb_output_kernel(GemmParams g) {
   stage(IntC<6>{});
   stage(IntC<7>{});
   static_assert(kAoStages == 8, "one call per stage above");
-  // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, columns 64 wn + 16 j + 4 kg .. +3
+  // outputs through LDS (the token buffers are free after the last barrier:
+  // waves 2 w' and 2 w' + 1 take halves of buffer w'), so that they leave as
+  // whole 256-byte row segments rather than 64 bytes of 16 rows a store.
+  // Lane (r16, kg) of block (i, j) holds token 16 i + r16, columns 16 j +
+  // 4 kg .. +3 of the wave's 64 x 64 block; a row is 16 chunks of 16 bytes,
+  // chunk q at q ^ (r & 15).
+  u32x4* sc = s_a[wave >> 1] + (wave & 1) * (64 * 16);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r16;
-    if (m >= g.m_len) continue;
-    float* crow = C + (int64_t)m * g.c_row + 64 * wn + 4 * kg;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store4(crow + 16 * j, acc[i][j]);
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * i + r16, q = 4 * j + kg;
+      sc[r * 16 + (q ^ (r & 15))] = __builtin_bit_cast(u32x4, acc[i][j]);
+    }
+  // the reads below take other lanes' writes: a wave's LDS instructions
+  // complete in order, and the compiler must not move the reads above them
+  asm volatile("" ::: "memory");
+  // lane L stores chunk L % 16 of rows L / 16 + 4 t: columns 64 wn + 4 (L % 16) .. +3
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int r = lane / 16 + 4 * t, q = lane % 16;
+    const u32x4 v = sc[r * 16 + (q ^ (r & 15))];
+    const int m = m0 + 64 * wm + r;
+    if (m < g.m_len) *reinterpret_cast<u32x4*>(C + (int64_t)m * g.c_row + 64 * wn + 4 * q) = v;
   }
 }
 
