@@ -660,15 +660,30 @@ __global__ __launch_bounds__(256) void kv_partial_kernel(GemmParams g, float* ws
     }
     __syncthreads();
   }
-  // lane (r16, kg) of block (i, j): token 64 wm + 16 i + r16, features 32 wn + 16 j + 4 kg .. +3
+  // outputs through LDS (the token buffers are free after the last barrier:
+  // 8 KB a wave), so that each 128-byte row segment leaves in one piece.
+  // Lane (r16, kg) of block (i, j) holds token 16 i + r16, features 16 j +
+  // 4 kg .. +3 of the wave's 64 x 32 block; a row is 8 chunks of 16 bytes,
+  // chunk q at q ^ ((r >> 1) & 7).
   float* out = slices == 1 ? static_cast<float*>(g.c) : ws + (int64_t)slice * g.m_len * g.c_row;
+  u32x4* sc = s_a[wave >> 1] + (wave & 1) * (64 * 8);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r16;
-    if (m >= g.m_len) continue;
-    float* crow = out + (int64_t)m * g.c_row + n0 + 32 * wn + 4 * kg;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) store4(crow + 16 * j, acc[i][j]);
+    for (int j = 0; j < 2; ++j) {
+      const int r = 16 * i + r16, q = 4 * j + kg;
+      sc[r * 8 + (q ^ ((r >> 1) & 7))] = __builtin_bit_cast(u32x4, acc[i][j]);
+    }
+  // the reads below take other lanes' writes: a wave's LDS instructions
+  // complete in order, and the compiler must not move the reads above them
+  asm volatile("" ::: "memory");
+  // lane L stores chunk L % 8 of rows L / 8 + 8 t: features 32 wn + 4 (L % 8) .. +3
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int r = lane / 8 + 8 * t, q = lane % 8;
+    const u32x4 v = sc[r * 8 + (q ^ ((r >> 1) & 7))];
+    const int m = m0 + 64 * wm + r;
+    if (m < g.m_len) *reinterpret_cast<u32x4*>(out + (int64_t)m * g.c_row + n0 + 32 * wn + 4 * q) = v;
   }
 }
 
