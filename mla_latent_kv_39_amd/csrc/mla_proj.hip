@@ -761,15 +761,21 @@ __global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
   const float4 v = reinterpret_cast<const float4*>(row)[tid];
   float k0 = 0.f, k1 = 0.f;
   if (tid < kRope / 2) rope_pair(row[kLatent + 2 * tid], row[kLatent + 2 * tid + 1], pos, tid, kRope, p.base, &k0, &k1);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   if (!p.fp8) {
     __bf16* dst = static_cast<__bf16*>(p.rows) + slot * kRow;
-    dst[4 * tid] = (__bf16)v.x;
-    dst[4 * tid + 1] = (__bf16)v.y;
-    dst[4 * tid + 2] = (__bf16)v.z;
-    dst[4 * tid + 3] = (__bf16)v.w;
+    bf16x4 c;
+    c[0] = (__bf16)v.x;
+    c[1] = (__bf16)v.y;
+    c[2] = (__bf16)v.z;
+    c[3] = (__bf16)v.w;
+    *reinterpret_cast<bf16x4*>(dst + 4 * tid) = c;              // one 8-byte store
     if (tid < kRope / 2) {
-      dst[kLatent + 2 * tid] = (__bf16)k0;
-      dst[kLatent + 2 * tid + 1] = (__bf16)k1;
+      bf16x2 r;
+      r[0] = (__bf16)k0;
+      r[1] = (__bf16)k1;
+      *reinterpret_cast<bf16x2*>(dst + kLatent + 2 * tid) = r;
     }
     return;
   }
@@ -783,8 +789,10 @@ __global__ __launch_bounds__(128) void cache_append_kernel(AppendParams p) {
   reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.rows) + slot * kLatent)[tid] = code;
   if ((tid & 31) == 0) p.scales[slot * 4 + tid / 32] = sc;
   if (tid < kRope / 2) {
-    p.rope[slot * kRope + 2 * tid] = (__bf16)k0;
-    p.rope[slot * kRope + 2 * tid + 1] = (__bf16)k1;
+    bf16x2 r;
+    r[0] = (__bf16)k0;
+    r[1] = (__bf16)k1;
+    *reinterpret_cast<bf16x2*>(p.rope + slot * kRope + 2 * tid) = r;
   }
 }
 
