@@ -50,12 +50,15 @@ __global__ __launch_bounds__((CB * 64 < 256 ? CB * 64 : 256) * TS) void combine_
   constexpr int kRun = 64 * CB;                 // 16-byte chunks of a slice
   constexpr int kPerThread = kRun / kThreads;   // 2 or 1
   constexpr int kChunk = KC;                    // partitions whose loads are in flight together
-  constexpr int kShared = (TS > 1 ? TS - 1 : 1) * kPerThread * 2 * kThreads;
+  constexpr int kShared = TS > 1 ? (TS - 1) * kPerThread * 2 * kThreads : 1;   // no LDS for one group
   __shared__ float4 s_tile[2 * kRun];
   __shared__ int s_red[2 * (kBlock / 64)];
   __shared__ float s_gm[kShared], s_gw[kShared];
   __shared__ float4 s_ga[kShared];
-  const int tid = threadIdx.x % kThreads, sub = threadIdx.x / kThreads;
+  // one group: constants, so that the kernel is the plain one (a group index
+  // computed at run time cost the paged mix's merge 18%)
+  const int tid = TS == 1 ? (int)threadIdx.x : (int)threadIdx.x % kThreads;
+  const int sub = TS == 1 ? 0 : (int)threadIdx.x / kThreads;
   const int per_tok = (kHeads / kGroupHeads) * kSlices;
   const int b = blockIdx.x / (p.s_q * per_tok);
   const int s = (blockIdx.x / per_tok) % p.s_q;
