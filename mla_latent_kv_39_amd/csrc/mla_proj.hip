@@ -18,7 +18,8 @@
 // with loads always in flight); the projection, whose K of 7168 leaves few
 // output tiles, splits K over the waves of a workgroup and loads its operands
 // straight into MFMA registers.  Outputs come out of the MFMAs four
-// consecutive columns per lane and are stored from the accumulators.
+// consecutive columns per lane; the absorptions and the split projection
+// pass them through LDS so that whole row segments are stored.
 #include <hip/hip_bf16.h>
 
 #include "mla_internal.h"
