@@ -294,7 +294,8 @@ mla_status mla_kv_project(const mla_tensor* hidden, const mla_tensor* w_kv, cons
  * d = 7168 leave a 32 x 32 tiling with under a workgroup per compute unit).
  * Same arguments, plus
  *   workspace  fp32 [S, T, 576]   caller-owned partial sums, overwritten; S >= 1
- *                                 divides d / 128 (mla_kv_project_splits)
+ *                                 divides d / 128 (mla_kv_project_splits); must not
+ *                                 overlap kv or the inputs
  * Slice s sums K values [s d / S, (s + 1) d / S) of every output on bf16
  * MFMA in fp32; a second kernel adds the S partials of each output in slice
  * order, so the result is the same on every run (it may differ from
