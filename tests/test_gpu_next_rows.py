@@ -47,7 +47,7 @@ def test_absorb_query_and_rope(B, S, in_place):
     print(f"[gpu] absorb_query: max err q_absorbed {e_abs.max():.2e} q_rope {e_rot.max():.2e}", flush=True)
 
 
-@pytest.mark.parametrize("B,S", [(35, 2), (1, 1), (128, 2)])
+@pytest.mark.parametrize("B,S", [(35, 2), (1, 1), (128, 2), (150, 2)])
 def test_absorb_output(B, S):
     import mla_latent_kv_39_amd as mla
     g = torch.Generator().manual_seed(50 + B)
